@@ -1,0 +1,106 @@
+"""Newton–Schulz orthogonalisation — oracle (test infrastructure only).
+
+Source: Full-Stack FP4 (arXiv 2607.04422).
+* §2 "Root optimizer": X_{k+1} = a X_k + b X_k (X_k^T X_k) + c X_k (X_k^T X_k)^2,
+  coefficients per step, typically five steps.
+* §3.4 "NVFP4 Root Optimizer", the NVFP4 NS iteration: the same step in the
+  left-Gram form with every product taken on NVFP4 operands:
+      qX = Q_1x16(X),        A  = qX qX^T
+      qA = Q_1x16(A),        qA16 = Q_16x1(A),   B = b A + c qA qA16
+      qB = Q_1x16(B),        qX16 = Q_16x1(X),   X' = a X + qB qX16
+  Every quantization is RTN.  §3.4 also mentions p99 outlier clipping,
+  applied here as a clamp of the input before normalisation.
+
+Readings (the pages leave these open):
+* The random Hadamard transform and the adaptive 4/6 scaling of §3.4 are
+  not applied (the method computed here is plain NVFP4 RTN with the block
+  maximum mapped to 6).
+* Orientation: if m > n the iteration runs on G^T and the result is
+  transposed back, so the Gram matrix A is the smaller m x m side.
+* X_0 = clamp(G, -clip, clip) / (||clamp(G)||_F + eps), eps = 1e-7, the
+  clamp leaving NaN as NaN; clip = +inf disables it.
+* qX and qX16 share one s_g (from max|X|); A and B get their own.
+* b A and a X use the unquantized A and X; A itself is never re-rounded.
+* Because A is symmetric, Q_16x1(A) equals Q_1x16(A)^T, so the second
+  product is qA qA^T; the oracle still forms Q_16x1(A) from A itself.
+* All unquantized values are float64; products of quantized operands are
+  float64 matrix products of exactly dequantized values.
+"""
+import numpy as np
+
+from .nvfp4 import (quantize_rows, quantize_cols, dequantize_rows,
+                    dequantize_cols, tensor_amax)
+
+EPS = 1e-7
+
+
+def clip_and_normalize(G, clip=np.inf, eps=EPS):
+    """X_0 = clamp(G) / (||clamp(G)||_F + eps) in float64 (NaN stays NaN)."""
+    X = np.asarray(G, dtype=np.float64)
+    if np.isfinite(clip):
+        X = np.where(X > clip, clip, np.where(X < -clip, -clip, X))
+    norm = np.sqrt(np.sum(X * X))
+    return X / (norm + eps)
+
+
+def gemm_nt(P, Q):
+    """C = P Q^T in float64 (a library matrix product)."""
+    return np.asarray(P, np.float64) @ np.asarray(Q, np.float64).T
+
+
+def _orient(G):
+    G = np.asarray(G)
+    if G.ndim != 2:
+        raise ValueError("G must be 2-D")
+    return (G.T, True) if G.shape[0] > G.shape[1] else (G, False)
+
+
+def ns_exact(G, coeffs, clip=np.inf, eps=EPS):
+    """Newton–Schulz on unquantized float64 operands (left-Gram form).
+
+    X' = a X + (b A + c A A) X with A = X X^T, i.e. the Root recurrence of §2
+    written for the smaller Gram side.
+    """
+    Gt, transposed = _orient(G)
+    X = clip_and_normalize(Gt, clip, eps)
+    for a, b, c in coeffs:
+        A = gemm_nt(X, X)
+        B = b * A + c * (A @ A)
+        X = a * X + B @ X
+    return X.T if transposed else X
+
+
+def ns_nvfp4(G, coeffs, clip=np.inf, eps=EPS, trace=None):
+    """Newton–Schulz with NVFP4 operands for every product (§3.4 iteration).
+
+    ``trace``, if a list, receives one dict per step with the quantized
+    operands and the float64 intermediates (X before the step, A, B, X after).
+    """
+    Gt, transposed = _orient(G)
+    X = clip_and_normalize(Gt, clip, eps)
+    for a, b, c in coeffs:
+        amax_x = tensor_amax(X)
+        qX = quantize_rows(X, amax=amax_x)           # Q_1x16(X)
+        qX16 = quantize_cols(X, amax=amax_x)         # Q_16x1(X), stored as X^T rows
+        dX = dequantize_rows(qX)
+        A = gemm_nt(dX, dX)                          # qX qX^T
+        qA = quantize_rows(A)                        # Q_1x16(A)
+        qA16 = quantize_cols(A)                      # Q_16x1(A)
+        B = b * A + c * (dequantize_rows(qA) @ dequantize_cols(qA16))
+        qB = quantize_rows(B)                        # Q_1x16(B)
+        Xn = a * X + dequantize_rows(qB) @ dequantize_cols(qX16)
+        if trace is not None:
+            trace.append(dict(X=X, qX=qX, qX16=qX16, A=A, qA=qA, qA16=qA16,
+                              B=B, qB=qB, X_next=Xn, coeffs=(a, b, c)))
+        X = Xn
+    return X.T if transposed else X
+
+
+def ns_iteration_flops(m, n):
+    """Algorithmic flops of one step on an m x n (m <= n) iterate.
+
+    The two Gram products are symmetric, so only their upper triangle with
+    the diagonal counts: m(m+1)n + m(m+1)m; the third product is 2 m^2 n.
+    """
+    m, n = min(m, n), max(m, n)
+    return m * (m + 1) * n + m * (m + 1) * m + 2 * m * m * n
