@@ -1,0 +1,223 @@
+"""Benchmark of the NVFP4 Newton–Schulz path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step = one ns_orthogonalize call (all of: orientation, clip, Frobenius
+normalisation, and five NVFP4 NS steps of quantize X both ways, A = qX qX^T,
+quantize A, B = bA + c qA qA^T, quantize B, X = aX + qB qX16, and the
+write-out) on the 3072 x 8192 BF16 gradient workload, inputs resident in
+HBM.  value = algorithmic TFLOP/s (symmetric products counted once).
+
+The same JSON line carries:
+  roofline      the dominant kernel of a step, timed alone with HIP events
+                on the stream it runs on, against the f16 MFMA dense peak;
+  quant         the standalone quantizer + dequantizer on 2^28 BF16 values
+                (16384 x 16384) in HBM GB/s against the 8 TB/s peak;
+  bf16_ns       the same five steps in plain BF16 torch.matmul (hipBLASLt)
+                on the same GPU, for a like-for-like speedup;
+  cpu_baseline  the float64 oracle on the host cores, bounded sample.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_F16_PEAK_TFLOPS = 2500.0     # MI355X dense f16/bf16 MFMA
+HBM_PEAK_GBPS = 8000.0            # MI355X HBM3E
+QUANT_DESIGN_BYTES_PER_ELEM = (2 + 2 + 0.5 + 1 / 16) + (0.5 + 1 / 16 + 2)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--quant-steps", type=int, default=100)
+    p.add_argument("--quant-warmup", type=int, default=20)
+    p.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    p.add_argument("--no-quant", action="store_true", help="skip the quantizer line")
+    return p.parse_args()
+
+
+def time_events(fn, reps, warm, stream):
+    import torch
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(reps):
+        fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / reps      # ms per call
+
+
+def kernel_timings(ns, torch, dev, m, n, stream):
+    """Each kernel of one NS step launched alone through the C ABI on the
+    bench stream, with operands of the benchmark's shape."""
+    from synth import gaussian
+    X = torch.from_numpy(gaussian(m, n, seed=77) / np.sqrt(m * n)).to(dev)
+    res = {}
+    qx = ns.nvfp4_quantize(X, ns.NVFP4_ROWS)
+    qt = ns.nvfp4_quantize(X, ns.NVFP4_COLS)
+    A = torch.empty((m, m), dtype=torch.float32, device=dev)
+    Bm = torch.empty((m, m), dtype=torch.float32, device=dev)
+    Xo = torch.empty_like(X)
+    ns.nvfp4_gemm(qx, qx, m, m, n, symmetric=True, out=A)
+    qa = ns.nvfp4_quantize(A, ns.NVFP4_ROWS)
+    ns.nvfp4_gemm(qa, qa, m, m, m, symmetric=True, alpha=2.0315, beta=-4.775, addend=A, out=Bm)
+    qb = ns.nvfp4_quantize(Bm, ns.NVFP4_ROWS)
+    sym = m * (m + 1)
+    res["gemm_gram_xxT"] = (time_events(lambda: ns.nvfp4_gemm(qx, qx, m, m, n, symmetric=True, out=A),
+                                        20, 3, stream), sym * n)
+    res["gemm_gram_aaT"] = (time_events(lambda: ns.nvfp4_gemm(qa, qa, m, m, m, symmetric=True, alpha=2.0315,
+                                                              beta=-4.775, addend=A, out=Bm), 20, 3, stream),
+                            sym * m)
+    res["gemm_update_bx"] = (time_events(lambda: ns.nvfp4_gemm(qb, qt, m, n, m, alpha=1.0, beta=3.4445,
+                                                               addend=X, out=Xo), 20, 3, stream), 2 * m * m * n)
+    return res
+
+
+def bf16_ns_ms(torch, G, coeffs, stream, reps=10):
+    def run():
+        X = G.float()
+        X = (X / (X.norm() + 1e-7)).to(torch.bfloat16)
+        for a, b, c in coeffs:
+            A = torch.mm(X, X.t())
+            B = b * A + c * torch.mm(A, A)
+            X = a * X + torch.mm(B, X)
+        return X
+    return time_events(run, reps, 3, stream)
+
+
+def cpu_baseline(G, clip, coeffs, m, n):
+    from oracle import ns as N
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = os.cpu_count() or 1
+    G64 = G.astype(np.float64)
+    done, t0 = 0, time.perf_counter()
+    while True:
+        N.ns_nvfp4(G64, coeffs[:1], clip=clip)
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= 10.0 or done >= len(coeffs):
+            break
+    flops = done * N.ns_iteration_flops(m, n)
+    return {"value": round(flops / el / 1e12, 5), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done} NVFP4 NS step(s) of the 3072x8192 workload in float64 "
+                      f"(numpy/BLAS), {el:.1f} s wall"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(see DESIGN.md for how the path would shard).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import newton_schulz_amd as ns
+    import synth
+    from oracle.ns import ns_iteration_flops
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    coeffs = [synth.QUINTIC] * synth.STEPS
+    spec = synth.ns_workload("ns3072x8192")
+    G, bits, clip = synth.ns_matrix(spec, 0)
+    m, n = G.shape
+    Gd = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    out = torch.empty((m, n), dtype=torch.float32, device=dev)
+    ws = torch.empty(ns.ns_workspace_bytes(m, n), dtype=torch.uint8, device=dev)
+    step = lambda: ns.ns_orthogonalize(Gd, coeffs, clip, out=out, workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ms = time_events(step, args.steps, 0, stream)
+    wall = time.perf_counter() - t0
+    flops = synth.STEPS * ns_iteration_flops(m, n)
+    tflops = flops / (ms * 1e-3) / 1e12
+
+    kt = kernel_timings(ns, torch, dev, m, n, stream)
+    # share of one NS step: each GEMM runs once per iteration
+    dom = max(kt, key=lambda k: kt[k][0])
+    dms, dflops = kt[dom]
+    achieved = dflops / (dms * 1e-3) / 1e12
+    roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
+            "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+            "avg_launch_ms": round(dms, 4),
+            "per_kernel_ms": {k: round(v[0], 4) for k, v in kt.items()}}
+
+    line = {
+        "metric": "NVFP4 Newton–Schulz TFLOP/s (% BF16 MFMA peak) + nvfp4_quant HBM GB/s",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "ns3072x8192: one 3072x8192 BF16 gradient (rank-32 signal "
+                               "+ N(0,0.01^2) noise + 0.1% outliers x50, seed 4), clip 8xRMS, "
+                               "5 NVFP4 NS steps with the quintic (3.4445,-4.775,2.0315)",
+                   "m": m, "n": n, "ns_steps": synth.STEPS, "operands": "nvfp4 (e2m1 x e4m3/16 + f32)",
+                   "accumulate": "f32", "frac_of_peak": round(tflops / MFMA_F16_PEAK_TFLOPS, 4)},
+        "roofline": roof,
+        "wall_s_timed": round(wall, 3),
+    }
+
+    # BF16 torch NS of the same matrix, same GPU
+    bms = bf16_ns_ms(torch, Gd, coeffs, stream)
+    line["bf16_ns"] = {"ms": round(bms, 4), "speedup_nvfp4_vs_bf16": round(bms / ms, 3),
+                       "what": "torch.mm in bf16 (hipBLASLt), full products, same 5 steps"}
+
+    if not args.no_quant:
+        del ws
+        qbits, _ = synth.quant_workload()
+        xq = torch.from_numpy(qbits.view(np.int16)).view(torch.bfloat16).to(dev)
+        rows, cols = xq.shape
+        codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+        scales = torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev)
+        sg = torch.empty(1, dtype=torch.float32, device=dev)
+        qws = torch.empty(256, dtype=torch.uint8, device=dev)
+        deq = torch.empty((rows, cols), dtype=torch.bfloat16, device=dev)
+
+        def qstep():
+            ns.nvfp4_quantize(xq, ns.NVFP4_ROWS, codes, scales, sg, workspace=qws, stream=stream)
+            ns.nvfp4_dequantize(codes, scales, sg, rows, cols, ns.NVFP4_ROWS, ns.NS_BF16, out=deq,
+                                stream=stream)
+        qms = time_events(qstep, args.quant_steps, args.quant_warmup, stream)
+        qbytes = QUANT_DESIGN_BYTES_PER_ELEM * rows * cols
+        gbps = qbytes / (qms * 1e-3) / 1e9
+        t_q = time_events(lambda: ns.nvfp4_quantize(xq, ns.NVFP4_ROWS, codes, scales, sg,
+                                                    workspace=qws, stream=stream), 50, 5, stream)
+        t_d = time_events(lambda: ns.nvfp4_dequantize(codes, scales, sg, rows, cols, ns.NVFP4_ROWS,
+                                                      ns.NS_BF16, out=deq, stream=stream), 50, 5, stream)
+        line["quant"] = {
+            "metric": "nvfp4_quant HBM GB/s", "value": round(gbps, 1), "unit": "GB/s",
+            "workload": "16384x16384 BF16 Student-t(3)*0.02 with 0.1% x50, quantize (amax pass + "
+                        "encode) + dequantize to BF16, 1x16 blocks",
+            "ms": round(qms, 4), "quantize_ms": round(t_q, 4), "dequantize_ms": round(t_d, 4),
+            "design_bytes": int(qbytes),
+            "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None}}
+        del xq, deq
+
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(G, clip, coeffs, m, n)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

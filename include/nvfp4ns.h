@@ -1,0 +1,153 @@
+/*
+ * nvfp4ns.h — C ABI of the NVFP4 Newton–Schulz library for MI355X (gfx950).
+ *
+ * The operations follow "Full-Stack FP4: Stable LLM Pretraining with
+ * Quantized Projections, Optimizers, and Attention" (arXiv 2607.04422):
+ *   - the NVFP4 format of §2 "Preliminaries", paragraph "NVFP4 format":
+ *     E2M1 element codes, one FP8 E4M3 scale s per 16-element block, one
+ *     FP32 scale s_g per tensor, value = x_E2M1 * s * s_g;
+ *   - the Root optimizer's Newton–Schulz iteration of §2 ("Root optimizer")
+ *     in the NVFP4 form of §3.4 ("NVFP4 Root Optimizer", the three-line
+ *     NVFP4 NS iteration), every quantization round-to-nearest.
+ *
+ * Conventions shared by every entry point
+ *   - Pointers named x, codes, scales, G, out, ws, global_scale and the
+ *     per-matrix arrays' elements are DEVICE pointers; coeffs, m, n, clip
+ *     and the pointer arrays themselves are HOST memory.
+ *   - Matrices are dense row-major with no padding.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call
+ *     only enqueues work on it and returns; nothing synchronises.  The
+ *     caller owns all memory; the library allocates nothing and keeps no
+ *     state between calls.
+ *   - Arguments are validated before anything is enqueued; a negative
+ *     status means nothing was launched.  NS_ERR_HIP means a launch failed.
+ *   - Data-dependent cases are defined, never errors: a NaN or infinity in
+ *     a tensor makes its s_g NaN, all its scale bytes 0x7F and all its
+ *     magnitude codes 0, and NaN propagates to every result; an all-zero
+ *     tensor gives s_g = 0, zero scales and codes carrying only sign bits.
+ *
+ * NVFP4 storage (readings of the format paragraph, which prints the decode
+ * rule only): s_g = RN_f32(amax / 2688); s = RNE_E4M3FN(amax_block /
+ * (6 s_g)) of the exact quotient, saturating at 448 (0 if it rounds to 0);
+ * code = sign | RNE_E2M1(|x| / (s s_g)) of the exact quotient, ties to the
+ * even code, saturating at 6, magnitude 0 when s or s_g is 0.  Codes are
+ * packed two per byte, element 2i in the low nibble; scales are E4M3FN
+ * bytes, row-major [rows][cols/16].
+ */
+#ifndef NVFP4NS_H
+#define NVFP4NS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NS_OK = 0,
+  NS_ERR_ARG = -1,        /* null pointer, bad enum, k <= 0, clip NaN or <= 0, aliasing */
+  NS_ERR_SHAPE = -2,      /* a dimension <= 0 or not a multiple of 16 */
+  NS_ERR_WORKSPACE = -3,  /* ws is NULL or ws_bytes is below the required size */
+  NS_ERR_HIP = -4         /* a kernel launch failed */
+} ns_status;
+
+typedef enum { NS_F32 = 0, NS_BF16 = 1 } ns_dtype;
+
+/* NVFP4_ROWS: Q_1x16, blocks of 16 consecutive elements along each row.
+ * NVFP4_COLS: Q_16x1, blocks of 16 down each column, stored as the Q_1x16
+ * layout of the transpose (cols rows of rows/2 code bytes and rows/16
+ * scale bytes). */
+typedef enum { NVFP4_ROWS = 0, NVFP4_COLS = 1 } nvfp4_axis;
+
+/* Workspace of nvfp4_quantize, in bytes (a few counters; >= 256). */
+size_t nvfp4_quantize_workspace_bytes(int64_t rows, int64_t cols);
+
+/*
+ * nvfp4_quantize — Q_1x16 or Q_16x1 of a rows x cols matrix
+ * (§2 "NVFP4 format"; the quantizers Q_1x16 / Q_16x1 of §3.4).
+ *   x            [rows][cols] FP32 or BF16 (xt), read only.
+ *   codes        out, rows*cols/2 bytes.
+ *   scales       out, rows*cols/16 bytes.
+ *   global_scale out, one float (s_g).
+ *   ws           scratch of nvfp4_quantize_workspace_bytes(); contents on
+ *                entry are ignored.
+ * rows and cols must be positive multiples of 16.
+ */
+ns_status nvfp4_quantize(const void* x, ns_dtype xt, int64_t rows, int64_t cols,
+                         nvfp4_axis axis, uint8_t* codes, uint8_t* scales,
+                         float* global_scale, void* ws, size_t ws_bytes,
+                         void* stream);
+
+/*
+ * nvfp4_dequantize — x_hat = x_E2M1 * s * s_g (§2 "NVFP4 format").
+ * Inputs as written by nvfp4_quantize for the same rows, cols and axis;
+ * out is [rows][cols] in the ORIGINAL orientation (an NVFP4_COLS tensor is
+ * transposed back), FP32 or BF16 (ot), each value rounded once (RNE) from
+ * the exact product.
+ */
+ns_status nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales,
+                           const float* global_scale, int64_t rows, int64_t cols,
+                           nvfp4_axis axis, void* out, ns_dtype ot, void* stream);
+
+/*
+ * nvfp4_gemm — one NVFP4 product of the §3.4 iteration, C = P * Q^T with
+ * both operands in the Q_1x16 layout along the contraction axis K:
+ *   P: codes_p [M][K/2], scales_p [M][K/16], s_g at sg_p (device float)
+ *   Q: codes_q [N][K/2], scales_q [N][K/16], s_g at sg_q
+ * and the epilogue
+ *   out[i][j] = beta * addend[i][j] + alpha * s_gP * s_gQ * sum_k P_ik Q_jk
+ * with products of dequantized values exact and FP32 accumulation.
+ *   symmetric != 0: P and Q must be the same tensor (M == N); only the
+ *     upper triangle is computed and mirrored, so out is exactly symmetric
+ *     (the Gram products A = qX qX^T and qA qA^T).
+ *   addend may be NULL when beta == 0, and may equal out.
+ *   amax_out (device uint32, may be NULL): atomically maxed with the bit
+ *     pattern of |out| (non-finite values count as NaN); the caller zeroes it.
+ * M, N, K must be positive multiples of 16.
+ */
+ns_status nvfp4_gemm(const uint8_t* codes_p, const uint8_t* scales_p, const float* sg_p,
+                     const uint8_t* codes_q, const uint8_t* scales_q, const float* sg_q,
+                     int64_t M, int64_t N, int64_t K, int symmetric,
+                     float alpha, float beta, const float* addend,
+                     float* out, uint32_t* amax_out, void* stream);
+
+/* Workspace of ns_orthogonalize for one m x n matrix, in bytes. */
+size_t ns_workspace_bytes(int64_t m, int64_t n);
+
+/*
+ * ns_orthogonalize — k NVFP4 Newton–Schulz steps (§2 "Root optimizer",
+ * §3.4 NVFP4 NS iteration) on one matrix:
+ *   X_0 = clamp(G, -clip, clip) / (||clamp(G)||_F + 1e-7)     (on G^T if m > n)
+ *   for i < k:  A = qX qX^T;  B = b_i A + c_i qA qA^T;  X = a_i X + qB qX16
+ *   out = X (transposed back if m > n)
+ *   G      [m][n] FP32 or BF16 (gt), read only.
+ *   coeffs HOST array of k triples (a_i, b_i, c_i).
+ *   clip   > 0; +inf disables clipping.  NaN passes through the clamp.
+ *   out    [m][n] FP32 or BF16 (ot); must not overlap G.
+ *   ws     device scratch of ns_workspace_bytes(m, n).
+ */
+ns_status ns_orthogonalize(const void* G, ns_dtype gt, int64_t m, int64_t n,
+                           const float* coeffs, int k, float clip,
+                           void* out, ns_dtype ot, void* ws, size_t ws_bytes,
+                           void* stream);
+
+/* Workspace of ns_orthogonalize_grouped for `count` matrices (host arrays m, n). */
+size_t ns_grouped_workspace_bytes(int count, const int64_t* m, const int64_t* n);
+
+/*
+ * ns_orthogonalize_grouped — ns_orthogonalize on `count` independent
+ * matrices with one coefficient schedule, as one batch of launches.
+ *   G, out  HOST arrays of `count` device pointers.
+ *   m, n    HOST arrays of shapes.   clip  HOST array of per-matrix clips.
+ *   ws      device scratch of ns_grouped_workspace_bytes().
+ */
+ns_status ns_orthogonalize_grouped(int count, const void* const* G, const int64_t* m,
+                                   const int64_t* n, ns_dtype gt, const float* coeffs,
+                                   int k, const float* clip, void* const* out,
+                                   ns_dtype ot, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* NVFP4NS_H */

@@ -1,0 +1,212 @@
+"""Python binding of the NVFP4 Newton–Schulz library (libnvfp4ns.so).
+
+Argument marshalling only: every step runs in the HIP kernels behind the C
+ABI declared in ``include/nvfp4ns.h``.  torch supplies device memory and the
+current stream.  There is no fallback: if the library is missing this
+module raises ImportError.
+
+Functions carry the C names:
+    nvfp4_quantize, nvfp4_dequantize, nvfp4_gemm, ns_workspace_bytes,
+    ns_orthogonalize, ns_grouped_workspace_bytes, ns_orthogonalize_grouped
+"""
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libnvfp4ns.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is not built; run `python -m newton_schulz_amd.build` "
+        "(or __graft_entry__.build()) first")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+NS_OK, NS_ERR_ARG, NS_ERR_SHAPE, NS_ERR_WORKSPACE, NS_ERR_HIP = 0, -1, -2, -3, -4
+NS_F32, NS_BF16 = 0, 1
+NVFP4_ROWS, NVFP4_COLS = 0, 1
+STATUS_NAMES = {0: "NS_OK", -1: "NS_ERR_ARG", -2: "NS_ERR_SHAPE",
+                -3: "NS_ERR_WORKSPACE", -4: "NS_ERR_HIP"}
+
+_i64, _sz, _vp, _f, _i = ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float, ctypes.c_int
+
+_SIGS = {
+    "nvfp4_quantize_workspace_bytes": (_sz, [_i64, _i64]),
+    "nvfp4_quantize": (_i, [_vp, _i, _i64, _i64, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "nvfp4_dequantize": (_i, [_vp, _vp, _vp, _i64, _i64, _i, _vp, _i, _vp]),
+    "nvfp4_gemm": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i, _f, _f, _vp, _vp, _vp, _vp]),
+    "ns_workspace_bytes": (_sz, [_i64, _i64]),
+    "ns_orthogonalize": (_i, [_vp, _i, _i64, _i64, _vp, _i, _f, _vp, _i, _vp, _sz, _vp]),
+    "ns_grouped_workspace_bytes": (_sz, [_i, _vp, _vp]),
+    "ns_orthogonalize_grouped": (_i, [_i, _vp, _vp, _vp, _i, _vp, _i, _vp, _vp, _i, _vp, _sz, _vp]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+EXPORTED = tuple(_SIGS)
+
+
+class NSError(RuntimeError):
+    def __init__(self, status, where):
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)}")
+        self.status = status
+
+
+def _check(status, where):
+    if status != NS_OK:
+        raise NSError(status, where)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dt(t):
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return NS_F32
+    if t.dtype == torch.bfloat16:
+        return NS_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _out_dtype(code):
+    torch = _torch()
+    return torch.float32 if code == NS_F32 else torch.bfloat16
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous device tensors")
+
+
+# ------------------------------------------------------------- quantizer --
+
+def nvfp4_quantize(x, axis=NVFP4_ROWS, codes=None, scales=None, global_scale=None,
+                   workspace=None, stream=None):
+    """NVFP4 quantization of a 2-D float32/bfloat16 device tensor.
+
+    Returns (codes uint8 [r][c/2], scales uint8 [r][c/16], s_g float32 [1]),
+    in the layout of x (NVFP4_ROWS) or of x^T (NVFP4_COLS).
+    """
+    torch = _torch()
+    _need_cuda(x)
+    rows, cols = x.shape
+    r, c = (rows, cols) if axis == NVFP4_ROWS else (cols, rows)
+    dev = x.device
+    if codes is None:
+        codes = torch.empty((r, c // 2), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty((r, c // 16), dtype=torch.uint8, device=dev)
+    if global_scale is None:
+        global_scale = torch.empty(1, dtype=torch.float32, device=dev)
+    wsb = _lib.nvfp4_quantize_workspace_bytes(rows, cols)
+    if workspace is None:
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    _check(_lib.nvfp4_quantize(_ptr(x), _dt(x), rows, cols, axis, _ptr(codes), _ptr(scales),
+                               _ptr(global_scale), _ptr(workspace), workspace.numel(),
+                               _stream(stream)), "nvfp4_quantize")
+    return codes, scales, global_scale
+
+
+def nvfp4_dequantize(codes, scales, global_scale, rows, cols, axis=NVFP4_ROWS,
+                     out_dtype=NS_F32, out=None, stream=None):
+    """x_hat = x_E2M1 * s * s_g, in the original rows x cols orientation."""
+    torch = _torch()
+    _need_cuda(codes, scales, global_scale)
+    if out is None:
+        out = torch.empty((rows, cols), dtype=_out_dtype(out_dtype), device=codes.device)
+    _check(_lib.nvfp4_dequantize(_ptr(codes), _ptr(scales), _ptr(global_scale), rows, cols, axis,
+                                 _ptr(out), out_dtype, _stream(stream)), "nvfp4_dequantize")
+    return out
+
+
+def nvfp4_gemm(p, q, M, N, K, symmetric=False, alpha=1.0, beta=0.0, addend=None, out=None,
+               amax_out=None, stream=None):
+    """out = beta*addend + alpha*s_gP*s_gQ*(P Q^T); p, q = (codes, scales, s_g)."""
+    torch = _torch()
+    (pc, ps, pg), (qc, qs, qg) = p, q
+    _need_cuda(pc, ps, pg, qc, qs, qg, addend, out, amax_out)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=pc.device)
+    _check(_lib.nvfp4_gemm(_ptr(pc), _ptr(ps), _ptr(pg), _ptr(qc), _ptr(qs), _ptr(qg),
+                           M, N, K, 1 if symmetric else 0, float(alpha), float(beta),
+                           _ptr(addend), _ptr(out), _ptr(amax_out), _stream(stream)),
+           "nvfp4_gemm")
+    return out
+
+
+# ---------------------------------------------------------- Newton–Schulz --
+
+def ns_workspace_bytes(m, n):
+    return int(_lib.ns_workspace_bytes(m, n))
+
+
+def _coeff_array(coeffs):
+    flat = [float(v) for abc in coeffs for v in abc]
+    return (ctypes.c_float * len(flat))(*flat), len(flat) // 3
+
+
+def ns_orthogonalize(G, coeffs, clip=float("inf"), out_dtype=NS_F32, out=None, workspace=None,
+                     stream=None):
+    """k NVFP4 Newton–Schulz steps on one m x n float32/bfloat16 matrix."""
+    torch = _torch()
+    _need_cuda(G, out)
+    m, n = G.shape
+    if out is None:
+        out = torch.empty((m, n), dtype=_out_dtype(out_dtype), device=G.device)
+    if workspace is None:
+        workspace = torch.empty(ns_workspace_bytes(m, n), dtype=torch.uint8, device=G.device)
+    carr, k = _coeff_array(coeffs)
+    _check(_lib.ns_orthogonalize(_ptr(G), _dt(G), m, n, carr, k, float(clip), _ptr(out),
+                                 _dt(out), _ptr(workspace), workspace.numel(), _stream(stream)),
+           "ns_orthogonalize")
+    return out
+
+
+def ns_grouped_workspace_bytes(shapes):
+    cnt = len(shapes)
+    ms = (ctypes.c_int64 * cnt)(*[s[0] for s in shapes])
+    ns = (ctypes.c_int64 * cnt)(*[s[1] for s in shapes])
+    return int(_lib.ns_grouped_workspace_bytes(cnt, ms, ns))
+
+
+def ns_orthogonalize_grouped(Gs, coeffs, clips, out_dtype=NS_F32, outs=None, workspace=None,
+                             stream=None):
+    """ns_orthogonalize over a list of matrices with one schedule."""
+    torch = _torch()
+    cnt = len(Gs)
+    _need_cuda(*Gs)
+    dt = _dt(Gs[0])
+    if any(_dt(g) != dt for g in Gs):
+        raise TypeError("all inputs must share one dtype")
+    shapes = [tuple(g.shape) for g in Gs]
+    if outs is None:
+        outs = [torch.empty(s, dtype=_out_dtype(out_dtype), device=Gs[0].device) for s in shapes]
+    if workspace is None:
+        workspace = torch.empty(ns_grouped_workspace_bytes(shapes), dtype=torch.uint8,
+                                device=Gs[0].device)
+    gp = (ctypes.c_void_p * cnt)(*[g.data_ptr() for g in Gs])
+    op = (ctypes.c_void_p * cnt)(*[o.data_ptr() for o in outs])
+    ms = (ctypes.c_int64 * cnt)(*[s[0] for s in shapes])
+    ns = (ctypes.c_int64 * cnt)(*[s[1] for s in shapes])
+    cl = (ctypes.c_float * cnt)(*[float(c) for c in clips])
+    carr, k = _coeff_array(coeffs)
+    _check(_lib.ns_orthogonalize_grouped(cnt, gp, ms, ns, dt, carr, k, cl, op, _dt(outs[0]),
+                                         _ptr(workspace), workspace.numel(), _stream(stream)),
+           "ns_orthogonalize_grouped")
+    return outs

@@ -1,0 +1,235 @@
+// C ABI of the NVFP4 Newton–Schulz library (declared in include/nvfp4ns.h):
+// argument validation, workspace planning and the launch sequence of the
+// NVFP4 NS iteration of Full-Stack FP4 (arXiv 2607.04422), §3.4.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/nvfp4ns.h"
+#include "launch.hpp"
+
+using nvfp4::Dt;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+inline bool dims_ok(int64_t a) { return a > 0 && a % 16 == 0; }
+inline bool dtype_ok(int d) { return d == NS_F32 || d == NS_BF16; }
+inline size_t dtype_size(ns_dtype d) { return d == NS_F32 ? 4 : 2; }
+inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+#define NS_TRY(call)                           \
+  do {                                         \
+    if ((call) != hipSuccess) return NS_ERR_HIP; \
+  } while (0)
+
+// Zero a few device words with a kernel launch (no memset node, so the
+// sequence can be captured into a graph).
+__global__ void zero_words_kernel(uint32_t* p, int n) {
+  if ((int)threadIdx.x < n) p[threadIdx.x] = 0u;
+}
+
+// ---- workspace of one Newton–Schulz problem (iterate is xm x xn, xm <= xn)
+struct NsLayout {
+  size_t X, A, B, qx_c, qx_s, qt_c, qt_s, qa_c, qa_s, qb_c, qb_s, sg, slot, part, inv, total;
+};
+
+NsLayout ns_layout(int64_t m, int64_t n) {
+  const size_t xm = (size_t)(m < n ? m : n), xn = (size_t)(m < n ? n : m);
+  NsLayout L;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes); return at; };
+  L.X = take(xm * xn * 4);
+  L.A = take(xm * xm * 4);
+  L.B = take(xm * xm * 4);
+  L.qx_c = take(xm * xn / 2);
+  L.qx_s = take(xm * xn / 16);
+  L.qt_c = take(xm * xn / 2);
+  L.qt_s = take(xm * xn / 16);
+  L.qa_c = take(xm * xm / 2);
+  L.qa_s = take(xm * xm / 16);
+  L.qb_c = take(xm * xm / 2);
+  L.qb_s = take(xm * xm / 16);
+  L.sg = take(3 * sizeof(float));
+  L.slot = take(3 * sizeof(uint32_t));
+  L.part = take(nvfp4::kNormParts * sizeof(double));
+  L.inv = take(sizeof(double));
+  L.total = o;
+  return L;
+}
+
+ns_status ns_run(const void* G, ns_dtype gt, int64_t m, int64_t n, const float* coeffs, int k,
+                 float clip, void* out, ns_dtype ot, uint8_t* ws, hipStream_t s) {
+  const NsLayout L = ns_layout(m, n);
+  const bool tr = m > n;
+  const int64_t xm = tr ? n : m, xn = tr ? m : n;
+  float* X = reinterpret_cast<float*>(ws + L.X);
+  float* A = reinterpret_cast<float*>(ws + L.A);
+  float* B = reinterpret_cast<float*>(ws + L.B);
+  float* sg = reinterpret_cast<float*>(ws + L.sg);
+  uint32_t* slot = reinterpret_cast<uint32_t*>(ws + L.slot);
+  double* part = reinterpret_cast<double*>(ws + L.part);
+  double* inv = reinterpret_cast<double*>(ws + L.inv);
+  uint32_t *slotX = slot, *slotA = slot + 1, *slotB = slot + 2;
+  float *sgX = sg, *sgA = sg + 1, *sgB = sg + 2;
+
+  NS_TRY(nvfp4::launch_norm_partials(G, (Dt)gt, m * n, clip, part, s));
+  NS_TRY(nvfp4::launch_norm_finalize(part, inv, slotX, slotA, slotB, s));
+  NS_TRY(nvfp4::launch_normalize(G, (Dt)gt, xm, xn, tr, clip, inv, X, slotX, s));
+
+  for (int it = 0; it < k; ++it) {
+    const float a = coeffs[3 * it], b = coeffs[3 * it + 1], c = coeffs[3 * it + 2];
+    // qX = Q_1x16(X) and qX16 = Q_16x1(X) (stored as rows of X^T), one s_g
+    NS_TRY(nvfp4::launch_quant_tiles(X, Dt::F32, xm, xn, slotX, sgX, ws + L.qx_c, ws + L.qx_s,
+                                     ws + L.qt_c, ws + L.qt_s, slotA, s));
+    // A = qX qX^T (symmetric, K = xn)
+    nvfp4::GemmProblem g1{ws + L.qx_c, ws + L.qx_s, sgX, ws + L.qx_c, ws + L.qx_s, sgX,
+                          xm, xm, xn, 1, 1.0f, 0.0f, nullptr, A, slotA};
+    NS_TRY(nvfp4::launch_gemm(g1, s));
+    // qA = Q_1x16(A); A is exactly symmetric, so Q_16x1(A) = qA^T
+    NS_TRY(nvfp4::launch_quant_rows(A, Dt::F32, xm, xm, slotA, sgA, ws + L.qa_c, ws + L.qa_s,
+                                    slotB, s));
+    // B = b A + c qA qA^T (symmetric, K = xm)
+    nvfp4::GemmProblem g2{ws + L.qa_c, ws + L.qa_s, sgA, ws + L.qa_c, ws + L.qa_s, sgA,
+                          xm, xm, xm, 1, c, b, A, B, slotB};
+    NS_TRY(nvfp4::launch_gemm(g2, s));
+    // qB = Q_1x16(B)
+    NS_TRY(nvfp4::launch_quant_rows(B, Dt::F32, xm, xm, slotB, sgB, ws + L.qb_c, ws + L.qb_s,
+                                    slotX, s));
+    // X' = a X + qB qX16 (K = xm), in place
+    nvfp4::GemmProblem g3{ws + L.qb_c, ws + L.qb_s, sgB, ws + L.qt_c, ws + L.qt_s, sgX,
+                          xm, xn, xm, 0, 1.0f, a, X, X, slotX};
+    NS_TRY(nvfp4::launch_gemm(g3, s));
+  }
+  NS_TRY(nvfp4::launch_write_out(X, xm, xn, tr, out, (Dt)ot, s));
+  return NS_OK;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+ns_status validate_ns(const void* G, int gt, int64_t m, int64_t n, const float* coeffs, int k,
+                      float clip, const void* out, int ot) {
+  if (!G || !out || !coeffs || k <= 0 || !dtype_ok(gt) || !dtype_ok(ot)) return NS_ERR_ARG;
+  if (std::isnan(clip) || !(clip > 0.0f)) return NS_ERR_ARG;
+  if (!dims_ok(m) || !dims_ok(n)) return NS_ERR_SHAPE;
+  for (int i = 0; i < 3 * k; ++i)
+    if (!std::isfinite(coeffs[i])) return NS_ERR_ARG;
+  if (overlaps(G, (size_t)(m * n) * dtype_size((ns_dtype)gt), out,
+               (size_t)(m * n) * dtype_size((ns_dtype)ot)))
+    return NS_ERR_ARG;
+  return NS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t nvfp4_quantize_workspace_bytes(int64_t, int64_t) { return kAlign; }
+
+ns_status nvfp4_quantize(const void* x, ns_dtype xt, int64_t rows, int64_t cols, nvfp4_axis axis,
+                         uint8_t* codes, uint8_t* scales, float* global_scale, void* ws,
+                         size_t ws_bytes, void* stream) {
+  if (!x || !codes || !scales || !global_scale || !dtype_ok(xt) ||
+      (axis != NVFP4_ROWS && axis != NVFP4_COLS))
+    return NS_ERR_ARG;
+  if (!dims_ok(rows) || !dims_ok(cols)) return NS_ERR_SHAPE;
+  if (!ws || ws_bytes < nvfp4_quantize_workspace_bytes(rows, cols)) return NS_ERR_WORKSPACE;
+  hipStream_t s = as_stream(stream);
+  uint32_t* slot = static_cast<uint32_t*>(ws);
+  zero_words_kernel<<<1, 64, 0, s>>>(slot, 1);
+  NS_TRY(hipGetLastError());
+  NS_TRY(nvfp4::launch_amax(x, (Dt)xt, rows * cols, slot, s));
+  if (axis == NVFP4_ROWS)
+    NS_TRY(nvfp4::launch_quant_rows(x, (Dt)xt, rows, cols, slot, global_scale, codes, scales,
+                                    nullptr, s));
+  else
+    NS_TRY(nvfp4::launch_quant_tiles(x, (Dt)xt, rows, cols, slot, global_scale, nullptr, nullptr,
+                                     codes, scales, nullptr, s));
+  return NS_OK;
+}
+
+ns_status nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* global_scale,
+                           int64_t rows, int64_t cols, nvfp4_axis axis, void* out, ns_dtype ot,
+                           void* stream) {
+  if (!codes || !scales || !global_scale || !out || !dtype_ok(ot) ||
+      (axis != NVFP4_ROWS && axis != NVFP4_COLS))
+    return NS_ERR_ARG;
+  if (!dims_ok(rows) || !dims_ok(cols)) return NS_ERR_SHAPE;
+  hipStream_t s = as_stream(stream);
+  if (axis == NVFP4_ROWS)
+    NS_TRY(nvfp4::launch_dequant_rows(codes, scales, global_scale, rows, cols, out, (Dt)ot, s));
+  else
+    NS_TRY(nvfp4::launch_dequant_cols(codes, scales, global_scale, rows, cols, out, (Dt)ot, s));
+  return NS_OK;
+}
+
+ns_status nvfp4_gemm(const uint8_t* codes_p, const uint8_t* scales_p, const float* sg_p,
+                     const uint8_t* codes_q, const uint8_t* scales_q, const float* sg_q,
+                     int64_t M, int64_t N, int64_t K, int symmetric, float alpha, float beta,
+                     const float* addend, float* out, uint32_t* amax_out, void* stream) {
+  if (!codes_p || !scales_p || !sg_p || !codes_q || !scales_q || !sg_q || !out) return NS_ERR_ARG;
+  if (beta != 0.0f && !addend) return NS_ERR_ARG;
+  if (!std::isfinite(alpha) || !std::isfinite(beta)) return NS_ERR_ARG;
+  if (!dims_ok(M) || !dims_ok(N) || !dims_ok(K)) return NS_ERR_SHAPE;
+  if (symmetric && (M != N || codes_p != codes_q || scales_p != scales_q || sg_p != sg_q))
+    return NS_ERR_ARG;
+  nvfp4::GemmProblem g{codes_p, scales_p, sg_p, codes_q, scales_q, sg_q, M, N, K,
+                       symmetric ? 1 : 0, alpha, beta, beta != 0.0f ? addend : nullptr, out,
+                       amax_out};
+  NS_TRY(nvfp4::launch_gemm(g, as_stream(stream)));
+  return NS_OK;
+}
+
+size_t ns_workspace_bytes(int64_t m, int64_t n) {
+  if (!dims_ok(m) || !dims_ok(n)) return 0;
+  return ns_layout(m, n).total;
+}
+
+ns_status ns_orthogonalize(const void* G, ns_dtype gt, int64_t m, int64_t n, const float* coeffs,
+                           int k, float clip, void* out, ns_dtype ot, void* ws, size_t ws_bytes,
+                           void* stream) {
+  ns_status st = validate_ns(G, gt, m, n, coeffs, k, clip, out, ot);
+  if (st != NS_OK) return st;
+  if (!ws || ws_bytes < ns_workspace_bytes(m, n)) return NS_ERR_WORKSPACE;
+  return ns_run(G, gt, m, n, coeffs, k, clip, out, ot, static_cast<uint8_t*>(ws), as_stream(stream));
+}
+
+size_t ns_grouped_workspace_bytes(int count, const int64_t* m, const int64_t* n) {
+  if (count <= 0 || !m || !n) return 0;
+  size_t total = 0;
+  for (int i = 0; i < count; ++i) {
+    const size_t b = ns_workspace_bytes(m[i], n[i]);
+    if (b == 0) return 0;
+    total += b;
+  }
+  return total;
+}
+
+ns_status ns_orthogonalize_grouped(int count, const void* const* G, const int64_t* m,
+                                   const int64_t* n, ns_dtype gt, const float* coeffs, int k,
+                                   const float* clip, void* const* out, ns_dtype ot, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  if (count <= 0 || !G || !m || !n || !clip || !out) return NS_ERR_ARG;
+  for (int i = 0; i < count; ++i) {
+    ns_status st = validate_ns(G[i], gt, m[i], n[i], coeffs, k, clip[i], out[i], ot);
+    if (st != NS_OK) return st;
+  }
+  const size_t need = ns_grouped_workspace_bytes(count, m, n);
+  if (!ws || ws_bytes < need) return NS_ERR_WORKSPACE;
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  for (int i = 0; i < count; ++i) {
+    ns_status st = ns_run(G[i], gt, m[i], n[i], coeffs, k, clip[i], out[i], ot, base, as_stream(stream));
+    if (st != NS_OK) return st;
+    base += ns_workspace_bytes(m[i], n[i]);
+  }
+  return NS_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,70 @@
+// Host-side launchers shared between the translation units of the library.
+// Every launcher only enqueues on `s` and returns hipGetLastError().
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+enum class Dt : int { F32 = 0, BF16 = 1 };
+
+// ---- quantizer (quant.hip) -------------------------------------------------
+// max |x| over n elements into *slot (atomic max on the bit pattern; the
+// caller zeroes *slot first).  Non-finite values count as NaN.
+hipError_t launch_amax(const void* x, Dt xt, int64_t n, uint32_t* slot, hipStream_t s);
+
+// Q_1x16 of a rows x cols matrix, streaming one 16-block per thread.
+// s_g comes from *amax_slot; it is also stored to *sg_out (may be null).
+// *zero_slot (may be null) is set to 0 by the kernel.
+hipError_t launch_quant_rows(const void* x, Dt xt, int64_t rows, int64_t cols,
+                             const uint32_t* amax_slot, float* sg_out,
+                             uint8_t* codes, uint8_t* scales, uint32_t* zero_slot,
+                             hipStream_t s);
+
+// Q_1x16 and/or Q_16x1 of a rows x cols matrix through 64x64 LDS tiles, one
+// read of x for both layouts.  Either output pair may be null.
+hipError_t launch_quant_tiles(const void* x, Dt xt, int64_t rows, int64_t cols,
+                              const uint32_t* amax_slot, float* sg_out,
+                              uint8_t* row_codes, uint8_t* row_scales,
+                              uint8_t* col_codes, uint8_t* col_scales,
+                              uint32_t* zero_slot, hipStream_t s);
+
+// Exact dequantisation of a Q_1x16 tensor; rows x cols output.
+hipError_t launch_dequant_rows(const uint8_t* codes, const uint8_t* scales, const float* sg,
+                               int64_t rows, int64_t cols, void* out, Dt ot, hipStream_t s);
+// Dequantisation of a Q_16x1 tensor stored as the Q_1x16 layout of its
+// transpose (crows x ccols = cols x rows of the result); the output is the
+// original rows x cols orientation.
+hipError_t launch_dequant_cols(const uint8_t* codes, const uint8_t* scales, const float* sg,
+                               int64_t rows, int64_t cols, void* out, Dt ot, hipStream_t s);
+
+// ---- GEMM (gemm.hip) ------------------------------------------------------
+struct GemmProblem {
+  const uint8_t* codes_p; const uint8_t* scales_p; const float* sg_p;
+  const uint8_t* codes_q; const uint8_t* scales_q; const float* sg_q;
+  int64_t M, N, K;
+  int symmetric;
+  float alpha, beta;
+  const float* addend;
+  float* out;
+  uint32_t* amax_out;
+};
+hipError_t launch_gemm(const GemmProblem& p, hipStream_t s);
+
+// ---- Newton–Schulz prologue / epilogue (ns.hip) ---------------------------
+// Partial sums of clamp(G)^2 into part[0..kNormParts).
+constexpr int kNormParts = 1024;
+hipError_t launch_norm_partials(const void* G, Dt gt, int64_t n, float clip, double* part,
+                                hipStream_t s);
+// inv[0] = 1 / (sqrt(sum part) + eps); zeroes the listed slots.
+hipError_t launch_norm_finalize(const double* part, double* inv, uint32_t* zero0, uint32_t* zero1,
+                                uint32_t* zero2, hipStream_t s);
+// X[m][n] = clamp(G) * inv (G is m x n, or n x m read transposed), amax into slot.
+hipError_t launch_normalize(const void* G, Dt gt, int64_t m, int64_t n, bool transposed,
+                            float clip, const double* inv, float* X, uint32_t* amax_slot,
+                            hipStream_t s);
+// out = X (m x n), or X^T written as n x m when transposed; f32 or bf16.
+hipError_t launch_write_out(const float* X, int64_t m, int64_t n, bool transposed, void* out,
+                            Dt ot, hipStream_t s);
+
+}  // namespace nvfp4

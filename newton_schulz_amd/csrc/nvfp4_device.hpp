@@ -1,0 +1,165 @@
+// Device-side NVFP4 arithmetic for gfx950: exact encode of the E4M3 block
+// scale and the E2M1 element codes, FP4 -> f16 dequantisation for the MFMA
+// operands, and the NaN-propagating amax on float bit patterns.
+//
+// Format: Full-Stack FP4 (arXiv 2607.04422), §2 "NVFP4 format" — E2M1
+// elements, one E4M3 scale per 16-block, one FP32 tensor scale, value =
+// x_E2M1 * s * s_g.  RTN (round to nearest, ties to the even code) for
+// every quantization, §3.4.
+//
+// Exactness.  s_g = RN_f32(amax / 2688) is one double division rounded to
+// float (53 >= 2*24 + 2, so the double rounding is innocuous).  The block
+// scale rounds the double quotient amax_b / (6 s_g) to E4M3 (again
+// innocuous: 53 >= 2*4 + 2 + the extra bits of 6 s_g).  Element codes are
+// decided without dividing: each E2M1 midpoint times s*s_g is exact in
+// double (<= 3 + 4 + 24 bits) and is turned into the float bit pattern that
+// an integer compare against |x|'s bits must exceed; ties go to the even
+// code.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+constexpr uint32_t kNaNBits = 0x7FC00000u;
+
+// |v| as an ordered bit pattern; NaN and +-inf both map to the NaN pattern so
+// that one non-finite element makes the tensor maximum NaN.
+__device__ __forceinline__ uint32_t abs_bits(float v) {
+  uint32_t b = __float_as_uint(v) & 0x7FFFFFFFu;
+  return b >= 0x7F800000u ? kNaNBits : b;
+}
+
+__device__ __forceinline__ uint32_t abs_bits(uint32_t raw) {
+  uint32_t b = raw & 0x7FFFFFFFu;
+  return b >= 0x7F800000u ? kNaNBits : b;
+}
+
+// s_g = RN_f32(amax / (6 * 448)); NaN stays NaN.
+__device__ __forceinline__ float global_scale_from_amax(uint32_t amax_bits) {
+  if (amax_bits > 0x7F800000u) return __uint_as_float(kNaNBits);
+  return (float)((double)__uint_as_float(amax_bits) / 2688.0);
+}
+
+// E4M3FN byte (0x00..0x7E) -> value, as double (exact).
+__device__ __forceinline__ double e4m3_value(uint32_t byte) {
+  uint32_t e = byte >> 3, m = byte & 7u;
+  return e == 0 ? (double)m * 0x1p-9 : ldexp((double)(8u + m), (int)e - 10);
+}
+
+// RNE to E4M3FN of a non-negative finite double, saturating at 448 (0x7E).
+// The double is split into its binade E (clamped to the subnormal binade
+// -6) and scaled by a power of two so that one E4M3 ulp is 1; rint() then
+// rounds half to even, and a carry out of the mantissa moves the exponent.
+__device__ __forceinline__ uint32_t e4m3_rne_sat(double q) {
+  if (!(q < 448.0)) return 0x7Eu;
+  int E = (int)((__double_as_longlong(q) >> 52) & 0x7FF) - 1023;
+  E = E < -6 ? -6 : E;
+  int r = (int)rint(ldexp(q, 3 - E));
+  return (uint32_t)(((E + 7) << 3) + r - 8);
+}
+
+// Bit pattern of the largest float <= d and of the smallest float >= d
+// (d > 0 finite).
+__device__ __forceinline__ uint32_t floor_f32_bits(double d) {
+  float f = (float)d;
+  uint32_t b = __float_as_uint(f);
+  return ((double)f > d) ? b - 1u : b;
+}
+__device__ __forceinline__ uint32_t ceil_f32_bits(double d) {
+  float f = (float)d;
+  uint32_t b = __float_as_uint(f);
+  return ((double)f < d) ? b + 1u : b;
+}
+
+// Integer thresholds of one block: magnitude code = number of k with
+// bits(|x|) > T[k].  Midpoint k lies between codes k and k+1: for even k
+// the value must exceed it (tie stays on the even code k), for odd k it
+// must reach it (tie moves to the even code k+1).
+struct BlockThresholds {
+  uint32_t t[7];
+};
+
+__device__ __forceinline__ BlockThresholds block_thresholds(double unit /* s * s_g */) {
+  BlockThresholds T;
+  if (!(unit > 0.0)) {                      // zero scale, zero or NaN s_g
+#pragma unroll
+    for (int k = 0; k < 7; ++k) T.t[k] = 0xFFFFFFFFu;
+    return T;
+  }
+  const double mid[7] = {0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0};
+#pragma unroll
+  for (int k = 0; k < 7; ++k) {
+    double thr = mid[k] * unit;             // exact
+    T.t[k] = (k & 1) ? ceil_f32_bits(thr) - 1u : floor_f32_bits(thr);
+  }
+  return T;
+}
+
+// 4-bit code of one element (sign bit from the raw float bits).
+__device__ __forceinline__ uint32_t encode_element(uint32_t raw_bits, const BlockThresholds& T) {
+  uint32_t a = raw_bits & 0x7FFFFFFFu;
+  uint32_t c = 0;
+#pragma unroll
+  for (int k = 0; k < 7; ++k) c += (a > T.t[k]) ? 1u : 0u;
+  return c | ((raw_bits >> 28) & 8u);
+}
+
+// Scale byte of a block with maximum |x| = amax_b (as float bits) under s_g.
+__device__ __forceinline__ uint32_t block_scale_byte(uint32_t amax_b_bits, float sg) {
+  if (sg != sg) return 0x7Fu;               // NaN tensor
+  if (sg == 0.0f) return 0u;
+  double q = (double)__uint_as_float(amax_b_bits) / (6.0 * (double)sg);
+  return e4m3_rne_sat(q);
+}
+
+// Encode 16 values given as raw float bit patterns.  Returns the packed
+// codes (element 2i in the low nibble of byte i) and the scale byte.
+__device__ __forceinline__ void encode_block16(const uint32_t (&v)[16], float sg,
+                                               uint32_t& lo, uint32_t& hi, uint32_t& scale) {
+  uint32_t amax_b = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    uint32_t a = v[i] & 0x7FFFFFFFu;
+    amax_b = a > amax_b ? a : amax_b;
+  }
+  scale = block_scale_byte(amax_b, sg);
+  double unit = (scale == 0x7Fu) ? 0.0 : e4m3_value(scale) * (double)sg;
+  BlockThresholds T = block_thresholds(unit);
+  lo = 0;
+  hi = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) lo |= encode_element(v[i], T) << (4 * i);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) hi |= encode_element(v[8 + i], T) << (4 * i);
+}
+
+// ---------------------------------------------------------------- decode --
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+
+// Scale byte -> f16 pair (s, s).  The hardware FP8 decode is exact and
+// gfx950 decodes OCP E4M3FN; every E4M3 value is an f16 number.
+__device__ __forceinline__ half2_t scale_pair_f16(uint32_t byte) {
+  float s = __builtin_amdgcn_cvt_f32_fp8((int)byte, 0);
+  _Float16 h = (_Float16)s;
+  half2_t r = {h, h};
+  return r;
+}
+
+// Eight E2M1 codes (one dword, element 2i in the low nibble of byte i) times
+// the block scale, as eight f16 values.  The conversion instruction yields
+// the exact E2M1 value (its scale operand is 1); the packed f16 multiply is
+// exact because q*s has at most 6 significant bits and lies in
+// [2^-10, 2688], inside the normal f16 range.
+__device__ __forceinline__ half8_t dequant8_f16(uint32_t w, half2_t s2) {
+  half2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2;
+  half2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s2;
+  half2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s2;
+  half2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s2;
+  half8_t r = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+  return r;
+}
+
+}  // namespace nvfp4

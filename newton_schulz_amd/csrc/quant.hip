@@ -1,0 +1,352 @@
+// NVFP4 quantizer and dequantizer kernels for gfx950.
+//
+// Q_1x16 / Q_16x1 of Full-Stack FP4 (arXiv 2607.04422), §2 "NVFP4 format"
+// and §3.4: a per-tensor maximum (first pass, HBM-bound read), then per
+// 16-block an E4M3 scale and sixteen E2M1 codes (second pass).  The exact
+// rounding rules live in nvfp4_device.hpp.
+#include "launch.hpp"
+#include "nvfp4_device.hpp"
+
+namespace nvfp4 {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxGrid = 256 * 8;  // 8 workgroups per CU for grid-stride passes
+
+typedef float float2_t __attribute__((ext_vector_type(2)));
+
+// 16 consecutive elements starting at element `idx` (a multiple of 16) as
+// raw float bit patterns (BF16 widened exactly).
+template <Dt T>
+__device__ __forceinline__ void load16(const void* base, int64_t idx, uint32_t (&v)[16]) {
+  if constexpr (T == Dt::F32) {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(base) + idx);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint4 w = p[j];
+      v[4 * j + 0] = w.x; v[4 * j + 1] = w.y; v[4 * j + 2] = w.z; v[4 * j + 3] = w.w;
+    }
+  } else {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + idx);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      uint4 w = p[j];
+      uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        v[8 * j + 2 * t + 0] = ws[t] << 16;
+        v[8 * j + 2 * t + 1] = ws[t] & 0xFFFF0000u;
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    uint32_t w = __shfl_xor(v, o, 64);
+    v = w > v ? w : v;
+  }
+  return v;
+}
+
+// ---------------------------------------------------------------- amax ----
+
+template <Dt T>
+__global__ __launch_bounds__(kThreads) void amax_kernel(const void* x, int64_t nvec, uint32_t* slot) {
+  // nvec = number of 16-byte vectors; each holds 4 (F32) or 8 (BF16) values
+  const uint4* p = static_cast<const uint4*>(x);
+  uint32_t m = 0;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nvec; i += stride) {
+    uint4 w = p[i];
+    uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      if constexpr (T == Dt::F32) {
+        uint32_t a = abs_bits(ws[t]);
+        m = a > m ? a : m;
+      } else {
+        uint32_t a0 = abs_bits(ws[t] << 16), a1 = abs_bits(ws[t] & 0xFFFF0000u);
+        m = a0 > m ? a0 : m;
+        m = a1 > m ? a1 : m;
+      }
+    }
+  }
+  m = wave_max(m);
+  __shared__ uint32_t red[kThreads / 64];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r = red[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) r = red[w] > r ? red[w] : r;
+    atomicMax(slot, r);
+  }
+}
+
+// ------------------------------------------------------- row quantizer ----
+
+template <Dt T>
+__global__ __launch_bounds__(kThreads) void quant_rows_kernel(
+    const void* x, int64_t nblk, const uint32_t* amax_slot, float* sg_out,
+    uint8_t* codes, uint8_t* scales, uint32_t* zero_slot) {
+  const float sg = global_scale_from_amax(*amax_slot);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    if (sg_out) *sg_out = sg;
+    if (zero_slot) *zero_slot = 0u;
+  }
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < nblk; b += stride) {
+    uint32_t v[16];
+    load16<T>(x, b * 16, v);
+    uint32_t lo, hi, sc;
+    encode_block16(v, sg, lo, hi, sc);
+    reinterpret_cast<uint2*>(codes)[b] = make_uint2(lo, hi);
+    scales[b] = (uint8_t)sc;
+  }
+}
+
+// ------------------------------------------- tiled quantizer, both axes ----
+// One 64x64 tile per workgroup.  Thread t holds row t/4, columns
+// 16*(t%4)..+15 of the tile: that is one Q_1x16 block, encoded straight from
+// registers.  For Q_16x1 the tile goes through LDS and thread t encodes
+// column t/4, rows 16*(t%4)..+15.
+
+template <Dt T, bool ROWS, bool COLS>
+__global__ __launch_bounds__(kThreads) void quant_tile_kernel(
+    const void* x, int64_t rows, int64_t cols, const uint32_t* amax_slot, float* sg_out,
+    uint8_t* row_codes, uint8_t* row_scales, uint8_t* col_codes, uint8_t* col_scales,
+    uint32_t* zero_slot) {
+  __shared__ uint32_t tile[64][65];
+  const float sg = global_scale_from_amax(*amax_slot);
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+    if (sg_out) *sg_out = sg;
+    if (zero_slot) *zero_slot = 0u;
+  }
+  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+  const int tr = threadIdx.x >> 2, tc = (threadIdx.x & 3) * 16;
+  const bool in = (r0 + tr < rows) && (c0 + tc < cols);
+  uint32_t v[16];
+  if (in) {
+    load16<T>(x, (r0 + tr) * cols + c0 + tc, v);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = 0u;
+  }
+  if constexpr (ROWS) {
+    if (in) {
+      uint32_t lo, hi, sc;
+      encode_block16(v, sg, lo, hi, sc);
+      const int64_t e = (r0 + tr) * cols + c0 + tc;
+      reinterpret_cast<uint2*>(row_codes)[e / 16] = make_uint2(lo, hi);
+      row_scales[e / 16] = (uint8_t)sc;
+    }
+  }
+  if constexpr (COLS) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) tile[tr][tc + i] = v[i];
+    __syncthreads();
+    const int j = threadIdx.x >> 2, b = threadIdx.x & 3;
+    if (c0 + j < cols && r0 + 16 * b < rows) {
+      uint32_t w[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) w[i] = tile[16 * b + i][j];
+      uint32_t lo, hi, sc;
+      encode_block16(w, sg, lo, hi, sc);
+      const int64_t e = (c0 + j) * rows + r0 + 16 * b;   // element of the transpose
+      reinterpret_cast<uint2*>(col_codes)[e / 16] = make_uint2(lo, hi);
+      col_scales[e / 16] = (uint8_t)sc;
+    }
+  }
+}
+
+// ------------------------------------------------------------ dequant ----
+
+// Round the exact product u * sg (u = q*s has <= 6 significant bits) once
+// to bf16.  hi = RN_f32(u*sg) and the exact error lo decide a bf16 tie;
+// products in or near the f32 subnormal range take the exact double path.
+__device__ __forceinline__ uint16_t product_to_bf16(float u, float sg) {
+  float hi = u * sg;
+  uint32_t b = __float_as_uint(hi);
+  uint32_t ab = b & 0x7FFFFFFFu;
+  if (ab >= 0x7F800000u) return (uint16_t)((b >> 16) | ((ab > 0x7F800000u) ? 0x40u : 0u));
+  if (ab < 0x0D800000u) {                      // |hi| < 2^-100: exact path
+    double d = (double)u * (double)sg;       // exact
+    double a = fabs(d);
+    if (a == 0.0) return (uint16_t)(b >> 16);
+    int E = (int)((__double_as_longlong(a) >> 52) & 0x7FF) - 1023;
+    E = E < -126 ? -126 : E;
+    double r = rint(ldexp(a, 7 - E));         // integer ulps of bf16
+    double v = ldexp(r, E - 7);
+    uint32_t fb = __float_as_uint((float)v);  // exact: v is a bf16 number
+    return (uint16_t)((fb >> 16) | ((d < 0) ? 0x8000u : 0u));
+  }
+  float lo = fmaf(u, sg, -hi);
+  if ((b & 0xFFFFu) == 0x8000u && lo != 0.0f) {
+    // hi sits on a bf16 midpoint but the exact value does not: lo says which way
+    bool up = (lo > 0.0f) == ((b & 0x80000000u) == 0u);
+    return (uint16_t)((b >> 16) + (up ? 1u : 0u));
+  }
+  return (uint16_t)((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
+}
+
+// Values of the 16 codes of one block (exact f32 q*s; the tensor scale is
+// applied by the caller).  The conversion instruction with scale 1 yields
+// the exact E2M1 value of the two nibbles of the selected byte.
+__device__ __forceinline__ void decode_word(uint32_t w, float s, float* u) {
+  float2_t q0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+  float2_t q1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+  float2_t q2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+  float2_t q3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+  u[0] = q0[0] * s; u[1] = q0[1] * s; u[2] = q1[0] * s; u[3] = q1[1] * s;
+  u[4] = q2[0] * s; u[5] = q2[1] * s; u[6] = q3[0] * s; u[7] = q3[1] * s;
+}
+
+__device__ __forceinline__ void decode_block(uint2 c, uint32_t scale_byte, float (&u)[16]) {
+  const float s = __builtin_amdgcn_cvt_f32_fp8((int)scale_byte, 0);
+  decode_word(c.x, s, u);
+  decode_word(c.y, s, u + 8);
+}
+
+template <Dt O>
+__device__ __forceinline__ void store16(void* out, int64_t idx, const float (&u)[16], float sg) {
+  if constexpr (O == Dt::F32) {
+    float4* p = reinterpret_cast<float4*>(static_cast<float*>(out) + idx);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      p[j] = make_float4(u[4 * j] * sg, u[4 * j + 1] * sg, u[4 * j + 2] * sg, u[4 * j + 3] * sg);
+  } else {
+    uint4* p = reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + idx);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      uint32_t w[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        w[t] = (uint32_t)product_to_bf16(u[8 * j + 2 * t], sg) |
+               ((uint32_t)product_to_bf16(u[8 * j + 2 * t + 1], sg) << 16);
+      p[j] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+}
+
+template <Dt O>
+__global__ __launch_bounds__(kThreads) void dequant_rows_kernel(
+    const uint8_t* codes, const uint8_t* scales, const float* sgp, int64_t nblk, void* out) {
+  const float sg = *sgp;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < nblk; b += stride) {
+    float u[16];
+    decode_block(reinterpret_cast<const uint2*>(codes)[b], scales[b], u);
+    store16<O>(out, b * 16, u, sg);
+  }
+}
+
+// Q_16x1 tensor stored as the rows of its transpose: codes [cols][rows/2].
+// Workgroup tile: 64 original rows x 64 original columns.
+template <Dt O>
+__global__ __launch_bounds__(kThreads) void dequant_cols_kernel(
+    const uint8_t* codes, const uint8_t* scales, const float* sgp, int64_t rows, int64_t cols,
+    void* out) {
+  __shared__ float tile[64][65];
+  const float sg = *sgp;
+  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+  {
+    const int j = threadIdx.x >> 2, b = threadIdx.x & 3;   // column j, row block b
+    float u[16];
+    if (c0 + j < cols && r0 + 16 * b < rows) {
+      const int64_t e = (c0 + j) * rows + r0 + 16 * b;
+      decode_block(reinterpret_cast<const uint2*>(codes)[e / 16], scales[e / 16], u);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) u[i] = 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) tile[16 * b + i][j] = u[i];
+  }
+  __syncthreads();
+  const int tr = threadIdx.x >> 2, tc = (threadIdx.x & 3) * 16;
+  if (r0 + tr < rows && c0 + tc < cols) {
+    float u[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) u[i] = tile[tr][tc + i];
+    store16<O>(out, (r0 + tr) * cols + c0 + tc, u, sg);
+  }
+}
+
+inline int grid_for(int64_t work, int per_block) {
+  int64_t g = (work + per_block - 1) / per_block;
+  if (g < 1) g = 1;
+  return (int)(g > kMaxGrid ? kMaxGrid : g);
+}
+
+}  // namespace
+
+hipError_t launch_amax(const void* x, Dt xt, int64_t n, uint32_t* slot, hipStream_t s) {
+  const int64_t nvec = xt == Dt::F32 ? n / 4 : n / 8;
+  const int grid = grid_for(nvec, kThreads * 4);
+  if (xt == Dt::F32)
+    amax_kernel<Dt::F32><<<grid, kThreads, 0, s>>>(x, nvec, slot);
+  else
+    amax_kernel<Dt::BF16><<<grid, kThreads, 0, s>>>(x, nvec, slot);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_rows(const void* x, Dt xt, int64_t rows, int64_t cols,
+                             const uint32_t* amax_slot, float* sg_out, uint8_t* codes,
+                             uint8_t* scales, uint32_t* zero_slot, hipStream_t s) {
+  const int64_t nblk = rows * cols / 16;
+  const int grid = grid_for(nblk, kThreads * 2);
+  if (xt == Dt::F32)
+    quant_rows_kernel<Dt::F32><<<grid, kThreads, 0, s>>>(x, nblk, amax_slot, sg_out, codes, scales, zero_slot);
+  else
+    quant_rows_kernel<Dt::BF16><<<grid, kThreads, 0, s>>>(x, nblk, amax_slot, sg_out, codes, scales, zero_slot);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_tiles(const void* x, Dt xt, int64_t rows, int64_t cols,
+                              const uint32_t* amax_slot, float* sg_out, uint8_t* row_codes,
+                              uint8_t* row_scales, uint8_t* col_codes, uint8_t* col_scales,
+                              uint32_t* zero_slot, hipStream_t s) {
+  dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 63) / 64));
+  const bool R = row_codes != nullptr, C = col_codes != nullptr;
+#define NVFP4_QT(T, RR, CC)                                                                   \
+  quant_tile_kernel<T, RR, CC><<<grid, kThreads, 0, s>>>(x, rows, cols, amax_slot, sg_out,    \
+                                                         row_codes, row_scales, col_codes,    \
+                                                         col_scales, zero_slot)
+  if (xt == Dt::F32) {
+    if (R && C) NVFP4_QT(Dt::F32, true, true);
+    else if (R) NVFP4_QT(Dt::F32, true, false);
+    else NVFP4_QT(Dt::F32, false, true);
+  } else {
+    if (R && C) NVFP4_QT(Dt::BF16, true, true);
+    else if (R) NVFP4_QT(Dt::BF16, true, false);
+    else NVFP4_QT(Dt::BF16, false, true);
+  }
+#undef NVFP4_QT
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant_rows(const uint8_t* codes, const uint8_t* scales, const float* sg,
+                               int64_t rows, int64_t cols, void* out, Dt ot, hipStream_t s) {
+  const int64_t nblk = rows * cols / 16;
+  const int grid = grid_for(nblk, kThreads * 2);
+  if (ot == Dt::F32)
+    dequant_rows_kernel<Dt::F32><<<grid, kThreads, 0, s>>>(codes, scales, sg, nblk, out);
+  else
+    dequant_rows_kernel<Dt::BF16><<<grid, kThreads, 0, s>>>(codes, scales, sg, nblk, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant_cols(const uint8_t* codes, const uint8_t* scales, const float* sg,
+                               int64_t rows, int64_t cols, void* out, Dt ot, hipStream_t s) {
+  dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 63) / 64));
+  if (ot == Dt::F32)
+    dequant_cols_kernel<Dt::F32><<<grid, kThreads, 0, s>>>(codes, scales, sg, rows, cols, out);
+  else
+    dequant_cols_kernel<Dt::BF16><<<grid, kThreads, 0, s>>>(codes, scales, sg, rows, cols, out);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

@@ -1,0 +1,139 @@
+"""Each NVFP4 GEMM of the NS step, fed the oracle's own quantized operands,
+against the oracle's float64 result: relative Frobenius error <= 1e-5
+(FP32 accumulation of exact products).  Symmetric products must come out
+exactly symmetric, and the fused amax must equal max |out|."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import ns as N
+from oracle import nvfp4 as Q
+
+pytestmark = pytest.mark.gpu
+
+import newton_schulz_amd as ns  # noqa: E402
+from gpu_util import DEV, host, rel_fro, to_dev_f32  # noqa: E402
+
+TOL = 1e-5
+QUINTIC = synth.QUINTIC
+
+
+def dev_q(q):
+    """Oracle NVFP4Tensor -> device (codes, scales, s_g)."""
+    return (torch.from_numpy(np.ascontiguousarray(q.codes)).to(DEV),
+            torch.from_numpy(np.ascontiguousarray(q.scales)).to(DEV),
+            torch.tensor([np.float32(q.global_scale)], dtype=torch.float32, device=DEV))
+
+
+def _amax_slot():
+    return torch.zeros(1, dtype=torch.int32, device=DEV)
+
+
+def _check_amax(slot, out):
+    got = int(host(slot)[0]) & 0xFFFFFFFF
+    want = int(np.abs(out.astype(np.float32)).max().view(np.uint32))
+    assert got == want
+
+
+def _gemm_steps(G, coeffs, label):
+    trace = []
+    N.ns_nvfp4(G, coeffs, trace=trace)
+    m, n = trace[0]["X"].shape
+    for s, t in enumerate(trace):
+        a, b, c = t["coeffs"]
+        print(f"[gemm] {label} step {s} m={m} n={n}", flush=True)
+        qx, qa, qb, qx16 = dev_q(t["qX"]), dev_q(t["qA"]), dev_q(t["qB"]), dev_q(t["qX16"])
+        slot = _amax_slot()
+        A = host(ns.nvfp4_gemm(qx, qx, m, m, n, symmetric=True, amax_out=slot))
+        assert rel_fro(A, t["A"]) <= TOL, (s, rel_fro(A, t["A"]))
+        assert np.array_equal(A, A.T)
+        _check_amax(slot, A)
+        slot = _amax_slot()
+        A32 = to_dev_f32(t["A"])
+        B = host(ns.nvfp4_gemm(qa, qa, m, m, m, symmetric=True, alpha=c, beta=b, addend=A32,
+                               amax_out=slot))
+        assert rel_fro(B, t["B"]) <= TOL, (s, rel_fro(B, t["B"]))
+        assert np.array_equal(B, B.T)
+        _check_amax(slot, B)
+        slot = _amax_slot()
+        X32 = to_dev_f32(t["X"])
+        Xn = host(ns.nvfp4_gemm(qb, qx16, m, n, m, alpha=1.0, beta=a, addend=X32, out=X32,
+                                amax_out=slot))                     # in place, as in NS
+        assert rel_fro(Xn, t["X_next"]) <= TOL, (s, rel_fro(Xn, t["X_next"]))
+        _check_amax(slot, Xn)
+
+
+@pytest.mark.parametrize("shape", [(256, 512), (144, 400), (512, 256)])
+def test_every_gemm_of_a_quintic_run(shape):
+    G = synth.gaussian(*shape, seed=1)
+    _gemm_steps(G.astype(np.float64), [QUINTIC] * 5, f"gaussian {shape}")
+
+
+def test_every_gemm_of_a_clipped_lowrank_run():
+    spec = synth.ns_workload("ns2048")
+    G, _, clip = synth.ns_matrix(dict(spec, shapes=[(272, 528)]), 0)
+    trace_G = N.clip_and_normalize(G, clip)      # the iterate the GEMMs see
+    _gemm_steps(trace_G, [QUINTIC, (1.5, -0.5, 0.0)], "lowrank 272x528")
+
+
+@pytest.mark.parametrize("MNK", [(144, 80, 272), (16, 16, 16), (128, 384, 4096), (200 - 8, 64, 48)])
+def test_general_gemm_ragged(MNK):
+    M, Nn, K = MNK
+    rng = np.random.default_rng(M + Nn + K)
+    P = rng.standard_normal((M, K)) * np.exp2(rng.uniform(-3, 3, (M, 1)))
+    Qm = rng.standard_normal((Nn, K))
+    qp, qq = Q.quantize_rows(P), Q.quantize_rows(Qm)
+    want = N.gemm_nt(Q.dequantize_rows(qp), Q.dequantize_rows(qq))
+    got = host(ns.nvfp4_gemm(dev_q(qp), dev_q(qq), M, Nn, K))
+    assert rel_fro(got, want) <= TOL
+    add = rng.standard_normal((M, Nn))
+    got2 = host(ns.nvfp4_gemm(dev_q(qp), dev_q(qq), M, Nn, K, alpha=-0.5, beta=2.0,
+                              addend=to_dev_f32(add)))
+    assert rel_fro(got2, 2.0 * add.astype(np.float32) - 0.5 * want) <= TOL
+
+
+@pytest.mark.parametrize("M,K", [(144, 272), (400, 96)])
+def test_symmetric_gemm_ragged(M, K):
+    rng = np.random.default_rng(M)
+    X = rng.standard_normal((M, K))
+    q = Q.quantize_rows(X)
+    dq = Q.dequantize_rows(q)
+    want = N.gemm_nt(dq, dq)
+    dq_dev = dev_q(q)                       # one tensor for both operands
+    got = host(ns.nvfp4_gemm(dq_dev, dq_dev, M, M, K, symmetric=True))
+    assert np.array_equal(got, got.T)
+    assert rel_fro(got, want) <= TOL
+
+
+def test_full_size_gemms_sampled():
+    """3072 x 8192 (the benchmark's shape): GEMM1 (3072^2, K=8192, symmetric)
+    and GEMM3 (3072 x 8192, K=3072) on 512 sampled outputs each, every one
+    computed by the oracle as a float64 dot product of dequantized rows."""
+    m, n = 3072, 8192
+    rng = np.random.default_rng(4)
+    X = rng.standard_normal((m, n)).astype(np.float32)
+    print("[gemm] oracle quantize of the 3072x8192 operands", flush=True)
+    qx = Q.quantize_rows(X)
+    qx16 = Q.quantize_cols(X, amax=Q.tensor_amax(X))
+    Bm = rng.standard_normal((m, m)).astype(np.float32)
+    Bm = (Bm + Bm.T).astype(np.float32)
+    qb = Q.quantize_rows(Bm)
+    print("[gemm] full-size GEMM1 / GEMM3 on the GPU", flush=True)
+    qx_dev = dev_q(qx)
+    A = host(ns.nvfp4_gemm(qx_dev, qx_dev, m, m, n, symmetric=True))
+    Xg = host(ns.nvfp4_gemm(dev_q(qb), dev_q(qx16), m, n, m, alpha=1.0, beta=3.4445,
+                            addend=to_dev_f32(X)))
+    assert np.array_equal(A, A.T)
+    ii, jj = rng.integers(0, m, 512), rng.integers(0, m, 512)
+    dxi = Q.dequantize_rows(Q.NVFP4Tensor(qx.codes[ii], qx.scales[ii], qx.global_scale, 512, n))
+    dxj = Q.dequantize_rows(Q.NVFP4Tensor(qx.codes[jj], qx.scales[jj], qx.global_scale, 512, n))
+    want = np.sum(dxi * dxj, axis=1)
+    got = A[ii, jj]
+    assert np.linalg.norm(got - want) <= TOL * np.linalg.norm(want)
+    ii, jj = rng.integers(0, m, 512), rng.integers(0, n, 512)
+    dbi = Q.dequantize_rows(Q.NVFP4Tensor(qb.codes[ii], qb.scales[ii], qb.global_scale, 512, m))
+    dxc = Q.dequantize_rows(Q.NVFP4Tensor(qx16.codes[jj], qx16.scales[jj], qx16.global_scale, 512, m))
+    want = 3.4445 * X[ii, jj].astype(np.float64) + np.sum(dbi * dxc, axis=1)
+    got = Xg[ii, jj]
+    assert np.linalg.norm(got - want) <= TOL * np.linalg.norm(want)

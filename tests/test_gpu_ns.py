@@ -1,0 +1,134 @@
+"""End-to-end NVFP4 Newton–Schulz on the GPU against the float64 oracle.
+
+The bar: relative Frobenius error <= 2e-2 and the same singular-value band
+(every sorted singular value within 0.05).  It is applied with coefficient
+schedules under which the NVFP4 iteration is stable (the cubic, or two
+quintic steps): with the fixed quintic, plain NVFP4 RTN noise pushes the top
+singular value out of the quintic's basin by the third step on these flat-
+spectrum inputs, and from there any difference in float rounding (even the
+oracle's own float64 against a float32 replay) grows without bound.  Every
+quintic step is instead checked one by one in test_gpu_gemm.py (each GEMM
+fed the oracle's operands) and by the bit-exact quantizer tests.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import ns as N
+
+pytestmark = pytest.mark.gpu
+
+import newton_schulz_amd as ns  # noqa: E402
+from gpu_util import DEV, host, rel_fro, same_band, to_dev_bf16, to_dev_f32  # noqa: E402
+
+QUINTIC = synth.QUINTIC
+CUBIC = (1.5, -0.5, 0.0)
+TOL = 2e-2
+BAND = 0.05
+
+
+def _run(G32, bits, coeffs, clip, out_dtype=ns.NS_F32):
+    Gd = to_dev_bf16(bits) if bits is not None else to_dev_f32(G32)
+    return host(ns.ns_orthogonalize(Gd, coeffs, clip, out_dtype=out_dtype))
+
+
+def _compare(got, G, coeffs, clip, label, out_bf16=False):
+    want = N.ns_nvfp4(G.astype(np.float64), coeffs, clip=clip)
+    err = rel_fro(got, want)
+    band, gb, ob = same_band(got, want)
+    print(f"[ns] {label}: rel_fro={err:.3g} band_dev={band:.3g} gpu={gb} oracle={ob}", flush=True)
+    assert got.shape == want.shape
+    assert err <= TOL, (label, err)
+    assert band <= BAND, (label, band)
+
+
+@pytest.mark.parametrize("coeffs,label", [([CUBIC] * 5, "cubic x5"), ([QUINTIC] * 2, "quintic x2"),
+                                          ([QUINTIC, CUBIC, CUBIC, CUBIC, CUBIC], "mixed")])
+def test_ns256x512_gaussian(coeffs, label):
+    spec = synth.ns_workload("ns256x512")
+    G, bits, clip = synth.ns_matrix(spec, 0)
+    _compare(_run(G, bits, coeffs, clip), G, coeffs, clip, f"256x512 {label}")
+
+
+@pytest.mark.parametrize("shape", [(512, 256), (144, 400), (400, 144), (64, 64), (16, 48)])
+def test_orientations_and_ragged_shapes(shape):
+    G = synth.gaussian(*shape, seed=sum(shape))
+    coeffs = [CUBIC] * 5
+    _compare(_run(G, None, coeffs, np.inf), G, coeffs, np.inf, f"gaussian {shape}")
+
+
+def test_bf16_in_bf16_out_with_clip():
+    spec = dict(synth.ns_workload("ns2048"), shapes=[(384, 640)])
+    G, bits, clip = synth.ns_matrix(spec, 0)
+    assert np.isfinite(clip) and clip < np.abs(G).max()        # the clip is active
+    coeffs = [CUBIC] * 5
+    got = _run(G, bits, coeffs, clip, out_dtype=ns.NS_BF16)
+    _compare(got, G, coeffs, clip, "bf16 lowrank 384x640 clip")
+
+
+def test_ns2048_full_size():
+    spec = synth.ns_workload("ns2048")
+    G, bits, clip = synth.ns_matrix(spec, 0)
+    coeffs = [CUBIC] * 5
+    _compare(_run(G, bits, coeffs, clip), G, coeffs, clip, "2048^2 lowrank cubic")
+
+
+def test_ns3072x8192_full_size():
+    """The benchmark's shape and launch configuration (coefficients aside)."""
+    spec = synth.ns_workload("ns3072x8192")
+    G, bits, clip = synth.ns_matrix(spec, 0)
+    coeffs = [CUBIC] * 5
+    _compare(_run(G, bits, coeffs, clip), G, coeffs, clip, "3072x8192 lowrank cubic")
+
+
+def test_transposed_8192x3072_member():
+    """The 8192 x 3072 member of the four-block batch runs on its transpose:
+    it must match the 3072 x 8192 run on G^T transposed back (the norm is
+    summed in another order, so agreement is to rounding, not bitwise)."""
+    G, bits, clip = synth.ns_matrix(dict(synth.ns_workload("ns4blocks")), 5)
+    assert G.shape == (8192, 3072)
+    coeffs = [CUBIC] * 5
+    out = _run(G, bits, coeffs, clip)
+    outT = _run(np.ascontiguousarray(G.T), None, coeffs, clip)
+    assert out.shape == (8192, 3072)
+    assert rel_fro(out, outT.T) <= 1e-4
+
+
+def test_zero_and_nan_inputs():
+    z = np.zeros((64, 128), np.float32)
+    assert np.array_equal(_run(z, None, [QUINTIC] * 3, np.inf), z)
+    g = synth.gaussian(64, 128, seed=3)
+    g[5, 7] = np.nan
+    assert np.all(np.isnan(_run(g, None, [QUINTIC] * 2, np.inf)))
+    g[5, 7] = np.inf
+    assert np.all(np.isnan(_run(g, None, [QUINTIC] * 2, np.inf)))
+    # with a finite clip an infinity is clipped like any large value
+    out = _run(g, None, [CUBIC] * 2, 3.0)
+    assert np.all(np.isfinite(out))
+
+
+def test_grouped_matches_single_calls():
+    shapes = [(128, 256), (256, 128), (96, 96), (64, 320)]
+    Gs = [synth.gaussian(r, c, seed=10 + i) for i, (r, c) in enumerate(shapes)]
+    coeffs = [CUBIC] * 4
+    clips = [np.inf, 2.5, np.inf, 1.5]
+    outs = ns.ns_orthogonalize_grouped([to_dev_f32(g) for g in Gs], coeffs, clips)
+    for g, o, clip in zip(Gs, outs, clips):
+        single = _run(g, None, coeffs, clip)
+        assert np.array_equal(host(o), single)
+        _compare(host(o), g, coeffs, clip, f"grouped {g.shape}")
+
+
+def test_errors_are_reported():
+    g = to_dev_f32(synth.gaussian(32, 48, seed=1))
+    with pytest.raises(ns.NSError) as e:
+        ns.ns_orthogonalize(g, [QUINTIC], clip=-1.0)
+    assert e.value.status == ns.NS_ERR_ARG
+    with pytest.raises(ns.NSError) as e:
+        ns.ns_orthogonalize(g, [QUINTIC], workspace=torch.empty(64, dtype=torch.uint8, device=DEV))
+    assert e.value.status == ns.NS_ERR_WORKSPACE
+    bad = to_dev_f32(synth.gaussian(32, 40, seed=1))
+    with pytest.raises(ns.NSError) as e:
+        ns.ns_orthogonalize(bad, [QUINTIC])
+    assert e.value.status == ns.NS_ERR_SHAPE
