@@ -64,7 +64,7 @@ def kernel_timings(ns, torch, dev, m, n, stream):
     """Each kernel of one NS step launched alone through the C ABI on the
     bench stream, with operands of the benchmark's shape."""
     from synth import gaussian
-    X = torch.from_numpy(gaussian(m, n, seed=77) / np.sqrt(m * n)).to(dev)
+    X = torch.from_numpy((gaussian(m, n, seed=77) / np.sqrt(m * n)).astype(np.float32)).to(dev)
     res = {}
     qx = ns.nvfp4_quantize(X, ns.NVFP4_ROWS)
     qt = ns.nvfp4_quantize(X, ns.NVFP4_COLS)
