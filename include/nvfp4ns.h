@@ -47,7 +47,8 @@ extern "C" {
 typedef enum {
   NS_OK = 0,
   NS_ERR_ARG = -1,        /* null pointer, bad enum, k <= 0, clip NaN or <= 0, aliasing */
-  NS_ERR_SHAPE = -2,      /* a dimension <= 0 or not a multiple of 16 */
+  NS_ERR_SHAPE = -2,      /* a dimension <= 0 or not a multiple of 16, or a matrix of
+                             2^31 or more elements in ns_orthogonalize / nvfp4_gemm */
   NS_ERR_WORKSPACE = -3,  /* ws is NULL or ws_bytes is below the required size */
   NS_ERR_HIP = -4         /* a kernel launch failed */
 } ns_status;
@@ -104,13 +105,19 @@ ns_status nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales,
  *   addend may be NULL when beta == 0, and may equal out.
  *   amax_out (device uint32, may be NULL): atomically maxed with the bit
  *     pattern of |out| (non-finite values count as NaN); the caller zeroes it.
+ *   ws: device scratch of nvfp4_gemm_workspace_bytes(); it lets symmetric
+ *     products split K across workgroups (FP32 partials summed in a fixed
+ *     order, so results do not depend on timing).  ws = NULL, ws_bytes = 0
+ *     runs the product unsplit.  Calls sharing one ws must not overlap.
  * M, N, K must be positive multiples of 16.
  */
+size_t nvfp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int symmetric);
 ns_status nvfp4_gemm(const uint8_t* codes_p, const uint8_t* scales_p, const float* sg_p,
                      const uint8_t* codes_q, const uint8_t* scales_q, const float* sg_q,
                      int64_t M, int64_t N, int64_t K, int symmetric,
                      float alpha, float beta, const float* addend,
-                     float* out, uint32_t* amax_out, void* stream);
+                     float* out, uint32_t* amax_out, void* ws, size_t ws_bytes,
+                     void* stream);
 
 /* Workspace of ns_orthogonalize for one m x n matrix, in bytes. */
 size_t ns_workspace_bytes(int64_t m, int64_t n);

@@ -6,7 +6,8 @@ current stream.  There is no fallback: if the library is missing this
 module raises ImportError.
 
 Functions carry the C names:
-    nvfp4_quantize, nvfp4_dequantize, nvfp4_gemm, ns_workspace_bytes,
+    nvfp4_quantize, nvfp4_dequantize, nvfp4_gemm_workspace_bytes, nvfp4_gemm,
+    ns_workspace_bytes,
     ns_orthogonalize, ns_grouped_workspace_bytes, ns_orthogonalize_grouped
 """
 import ctypes
@@ -17,7 +18,7 @@ LIB_PATH = os.path.join(HERE, "libnvfp4ns.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is not built; run `python -m newton_schulz_amd.build` "
+        f"{LIB_PATH} is not built; run `python newton_schulz_amd/build.py` "
         "(or __graft_entry__.build()) first")
 
 _lib = ctypes.CDLL(LIB_PATH)
@@ -34,7 +35,9 @@ _SIGS = {
     "nvfp4_quantize_workspace_bytes": (_sz, [_i64, _i64]),
     "nvfp4_quantize": (_i, [_vp, _i, _i64, _i64, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
     "nvfp4_dequantize": (_i, [_vp, _vp, _vp, _i64, _i64, _i, _vp, _i, _vp]),
-    "nvfp4_gemm": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i, _f, _f, _vp, _vp, _vp, _vp]),
+    "nvfp4_gemm_workspace_bytes": (_sz, [_i64, _i64, _i64, _i]),
+    "nvfp4_gemm": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i, _f, _f, _vp, _vp, _vp,
+                        _vp, _sz, _vp]),
     "ns_workspace_bytes": (_sz, [_i64, _i64]),
     "ns_orthogonalize": (_i, [_vp, _i, _i64, _i64, _vp, _i, _f, _vp, _i, _vp, _sz, _vp]),
     "ns_grouped_workspace_bytes": (_sz, [_i, _vp, _vp]),
@@ -135,17 +138,30 @@ def nvfp4_dequantize(codes, scales, global_scale, rows, cols, axis=NVFP4_ROWS,
     return out
 
 
+def nvfp4_gemm_workspace_bytes(M, N, K, symmetric=False):
+    return int(_lib.nvfp4_gemm_workspace_bytes(M, N, K, 1 if symmetric else 0))
+
+
 def nvfp4_gemm(p, q, M, N, K, symmetric=False, alpha=1.0, beta=0.0, addend=None, out=None,
-               amax_out=None, stream=None):
-    """out = beta*addend + alpha*s_gP*s_gQ*(P Q^T); p, q = (codes, scales, s_g)."""
+               amax_out=None, workspace=None, split=True, stream=None):
+    """out = beta*addend + alpha*s_gP*s_gQ*(P Q^T); p, q = (codes, scales, s_g).
+
+    With split=True (default) a workspace of nvfp4_gemm_workspace_bytes() is
+    allocated when none is given, so the product runs with the same launch
+    schedule as inside ns_orthogonalize.
+    """
     torch = _torch()
     (pc, ps, pg), (qc, qs, qg) = p, q
     _need_cuda(pc, ps, pg, qc, qs, qg, addend, out, amax_out)
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=pc.device)
+    if workspace is None and split:
+        nb = nvfp4_gemm_workspace_bytes(M, N, K, symmetric)
+        workspace = torch.empty(max(nb, 1), dtype=torch.uint8, device=pc.device)
+    wsp, wsn = (_ptr(workspace), workspace.numel()) if workspace is not None else (_ptr(None), 0)
     _check(_lib.nvfp4_gemm(_ptr(pc), _ptr(ps), _ptr(pg), _ptr(qc), _ptr(qs), _ptr(qg),
                            M, N, K, 1 if symmetric else 0, float(alpha), float(beta),
-                           _ptr(addend), _ptr(out), _ptr(amax_out), _stream(stream)),
+                           _ptr(addend), _ptr(out), _ptr(amax_out), wsp, wsn, _stream(stream)),
            "nvfp4_gemm")
     return out
 

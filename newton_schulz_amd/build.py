@@ -1,6 +1,6 @@
 """Build the NVFP4 Newton–Schulz HIP library in-tree for gfx950.
 
-    python -m newton_schulz_amd.build
+    python newton_schulz_amd/build.py
 
 Compiles every ``csrc/*.hip`` with hipcc (one process per source, in
 parallel) and links ``libnvfp4ns.so`` next to this file.

@@ -18,6 +18,8 @@ constexpr size_t kAlign = 256;
 inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 inline bool dims_ok(int64_t a) { return a > 0 && a % 16 == 0; }
+// tile-local offsets in the GEMM epilogue are 32-bit
+constexpr int64_t kMaxElems = (int64_t)1 << 31;
 inline bool dtype_ok(int d) { return d == NS_F32 || d == NS_BF16; }
 inline size_t dtype_size(ns_dtype d) { return d == NS_F32 ? 4 : 2; }
 inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
@@ -35,12 +37,20 @@ __global__ void zero_words_kernel(uint32_t* p, int n) {
 
 // ---- workspace of one Newton–Schulz problem (iterate is xm x xn, xm <= xn)
 struct NsLayout {
-  size_t X, A, B, qx_c, qx_s, qt_c, qt_s, qa_c, qa_s, qb_c, qb_s, sg, slot, part, inv, total;
+  size_t X, A, B, qx_c, qx_s, qt_c, qt_s, qa_c, qa_s, qb_c, qb_s, sg, slot, part, inv;
+  size_t gemm_part, total;
+  nvfp4::GemmPlan p1, p2, p3;
 };
 
 NsLayout ns_layout(int64_t m, int64_t n) {
   const size_t xm = (size_t)(m < n ? m : n), xn = (size_t)(m < n ? n : m);
   NsLayout L;
+  L.p1 = nvfp4::plan_gemm((int64_t)xm, (int64_t)xm, (int64_t)xn, true, true);
+  L.p2 = nvfp4::plan_gemm((int64_t)xm, (int64_t)xm, (int64_t)xm, true, true);
+  L.p3 = nvfp4::plan_gemm((int64_t)xm, (int64_t)xn, (int64_t)xm, false, true);
+  size_t part_bytes = 0;
+  for (const nvfp4::GemmPlan* p : {&L.p1, &L.p2, &L.p3})
+    part_bytes = p->partial_bytes > part_bytes ? p->partial_bytes : part_bytes;
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes); return at; };
   L.X = take(xm * xn * 4);
@@ -58,6 +68,7 @@ NsLayout ns_layout(int64_t m, int64_t n) {
   L.slot = take(3 * sizeof(uint32_t));
   L.part = take(nvfp4::kNormParts * sizeof(double));
   L.inv = take(sizeof(double));
+  L.gemm_part = take(part_bytes);
   L.total = o;
   return L;
 }
@@ -77,6 +88,8 @@ ns_status ns_run(const void* G, ns_dtype gt, int64_t m, int64_t n, const float* 
   uint32_t *slotX = slot, *slotA = slot + 1, *slotB = slot + 2;
   float *sgX = sg, *sgA = sg + 1, *sgB = sg + 2;
 
+  float* gpart = reinterpret_cast<float*>(ws + L.gemm_part);
+
   NS_TRY(nvfp4::launch_norm_partials(G, (Dt)gt, m * n, clip, part, s));
   NS_TRY(nvfp4::launch_norm_finalize(part, inv, slotX, slotA, slotB, s));
   NS_TRY(nvfp4::launch_normalize(G, (Dt)gt, xm, xn, tr, clip, inv, X, slotX, s));
@@ -89,21 +102,21 @@ ns_status ns_run(const void* G, ns_dtype gt, int64_t m, int64_t n, const float* 
     // A = qX qX^T (symmetric, K = xn)
     nvfp4::GemmProblem g1{ws + L.qx_c, ws + L.qx_s, sgX, ws + L.qx_c, ws + L.qx_s, sgX,
                           xm, xm, xn, 1, 1.0f, 0.0f, nullptr, A, slotA};
-    NS_TRY(nvfp4::launch_gemm(g1, s));
+    NS_TRY(nvfp4::launch_gemm(g1, L.p1, gpart, s));
     // qA = Q_1x16(A); A is exactly symmetric, so Q_16x1(A) = qA^T
     NS_TRY(nvfp4::launch_quant_rows(A, Dt::F32, xm, xm, slotA, sgA, ws + L.qa_c, ws + L.qa_s,
                                     slotB, s));
     // B = b A + c qA qA^T (symmetric, K = xm)
     nvfp4::GemmProblem g2{ws + L.qa_c, ws + L.qa_s, sgA, ws + L.qa_c, ws + L.qa_s, sgA,
                           xm, xm, xm, 1, c, b, A, B, slotB};
-    NS_TRY(nvfp4::launch_gemm(g2, s));
+    NS_TRY(nvfp4::launch_gemm(g2, L.p2, gpart, s));
     // qB = Q_1x16(B)
     NS_TRY(nvfp4::launch_quant_rows(B, Dt::F32, xm, xm, slotB, sgB, ws + L.qb_c, ws + L.qb_s,
                                     slotX, s));
     // X' = a X + qB qX16 (K = xm), in place
     nvfp4::GemmProblem g3{ws + L.qb_c, ws + L.qb_s, sgB, ws + L.qt_c, ws + L.qt_s, sgX,
                           xm, xn, xm, 0, 1.0f, a, X, X, slotX};
-    NS_TRY(nvfp4::launch_gemm(g3, s));
+    NS_TRY(nvfp4::launch_gemm(g3, L.p3, gpart, s));
   }
   NS_TRY(nvfp4::launch_write_out(X, xm, xn, tr, out, (Dt)ot, s));
   return NS_OK;
@@ -119,6 +132,7 @@ ns_status validate_ns(const void* G, int gt, int64_t m, int64_t n, const float* 
   if (!G || !out || !coeffs || k <= 0 || !dtype_ok(gt) || !dtype_ok(ot)) return NS_ERR_ARG;
   if (std::isnan(clip) || !(clip > 0.0f)) return NS_ERR_ARG;
   if (!dims_ok(m) || !dims_ok(n)) return NS_ERR_SHAPE;
+  if (m * n >= kMaxElems) return NS_ERR_SHAPE;
   for (int i = 0; i < 3 * k; ++i)
     if (!std::isfinite(coeffs[i])) return NS_ERR_ARG;
   if (overlaps(G, (size_t)(m * n) * dtype_size((ns_dtype)gt), out,
@@ -170,20 +184,32 @@ ns_status nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const fl
   return NS_OK;
 }
 
+size_t nvfp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int symmetric) {
+  if (!dims_ok(M) || !dims_ok(N) || !dims_ok(K)) return 0;
+  return nvfp4::plan_gemm(M, N, K, symmetric != 0, true).ws_bytes;
+}
+
 ns_status nvfp4_gemm(const uint8_t* codes_p, const uint8_t* scales_p, const float* sg_p,
                      const uint8_t* codes_q, const uint8_t* scales_q, const float* sg_q,
                      int64_t M, int64_t N, int64_t K, int symmetric, float alpha, float beta,
-                     const float* addend, float* out, uint32_t* amax_out, void* stream) {
+                     const float* addend, float* out, uint32_t* amax_out, void* ws,
+                     size_t ws_bytes, void* stream) {
   if (!codes_p || !scales_p || !sg_p || !codes_q || !scales_q || !sg_q || !out) return NS_ERR_ARG;
   if (beta != 0.0f && !addend) return NS_ERR_ARG;
   if (!std::isfinite(alpha) || !std::isfinite(beta)) return NS_ERR_ARG;
   if (!dims_ok(M) || !dims_ok(N) || !dims_ok(K)) return NS_ERR_SHAPE;
+  if (M * N >= kMaxElems || M * K >= kMaxElems || N * K >= kMaxElems) return NS_ERR_SHAPE;
   if (symmetric && (M != N || codes_p != codes_q || scales_p != scales_q || sg_p != sg_q))
     return NS_ERR_ARG;
+  // with a workspace of nvfp4_gemm_workspace_bytes() the split-K schedule is
+  // used; without one (ws == NULL, ws_bytes == 0) the product runs unsplit
+  const bool split_ok = ws != nullptr;
+  nvfp4::GemmPlan plan = nvfp4::plan_gemm(M, N, K, symmetric != 0, split_ok);
+  if (split_ok && ws_bytes < plan.ws_bytes) return NS_ERR_WORKSPACE;
   nvfp4::GemmProblem g{codes_p, scales_p, sg_p, codes_q, scales_q, sg_q, M, N, K,
                        symmetric ? 1 : 0, alpha, beta, beta != 0.0f ? addend : nullptr, out,
                        amax_out};
-  NS_TRY(nvfp4::launch_gemm(g, as_stream(stream)));
+  NS_TRY(nvfp4::launch_gemm(g, plan, static_cast<float*>(ws), as_stream(stream)));
   return NS_OK;
 }
 

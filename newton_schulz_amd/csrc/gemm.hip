@@ -5,17 +5,29 @@
 // Every one is C = P Q^T with both operands stored as packed E2M1 codes plus
 // E4M3 scales blocked by 16 along the contraction axis K.
 //
-// Data path: packed codes and scale bytes (0.5625 B per element) are staged
-// in LDS; each lane then turns one 32-bit word of 8 codes and its block
-// scale into 8 f16 values (exact: q*s has <= 6 significant bits inside the
-// normal f16 range) and feeds v_mfma_f32_32x32x16_f16, FP32 accumulation.
-// The tensor scales s_g of both operands multiply the accumulator once in
-// the epilogue.
+// Data path: packed codes and scale bytes (0.5625 B per element) go from
+// global memory straight into LDS (global_load_lds, no staging registers);
+// each lane then turns one 32-bit word of 8 codes and its block scale into
+// 8 f16 values (exact: q*s has <= 6 significant bits inside the normal f16
+// range) and feeds v_mfma_f32_32x32x16_f16 with FP32 accumulation.  The
+// tensor scales s_g of both operands multiply the accumulator once in the
+// epilogue.
 //
 // K order inside an MFMA: a product sums over K, so any permutation of K
-// applied to both operands leaves it unchanged.  Lane l (row l%32, half
-// h = l/32) takes bytes [32h, 32h+32) of each row's 64-byte K chunk and
-// MFMA step s uses its 4-byte word s: both operands use the same map.
+// applied to both operands leaves it unchanged.  For each 128-wide K stage,
+// lane l (row l%32 of its 32-row group, half h = l/32) owns bytes
+// [32h, 32h+32) of the row's 64 code bytes; MFMA step s of half-stage hs
+// uses its word s of bytes [32h + 16hs, +16).  Both operands use this map.
+//
+// LDS is laid out fragment-major: for each 32-row group and half-stage a
+// 1 KB region holds lane l's 16 bytes at 16*l, exactly what both the DMA
+// load of lane l writes and the fragment read of lane l reads, so every LDS
+// access of a wave is one contiguous conflict-free kilobyte.
+//
+// Symmetric products compute only tiles that touch the upper triangle
+// (row <= col); each element there is written once and mirrored.  When the
+// tile count is small they are split along K into `splits` work units whose
+// FP32 partials a second kernel sums in split order (deterministic).
 #include "launch.hpp"
 #include "nvfp4_device.hpp"
 
@@ -23,29 +35,391 @@ namespace nvfp4 {
 namespace {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-constexpr int BM = 128, BN = 128;      // workgroup tile
-constexpr int BK = 128;                // K elements per LDS stage
-constexpr int kThreads = 256;          // 4 waves in a 2 x 2 grid of 64 x 64
-constexpr int kCodeRow = BK / 2;       // 64 bytes of codes per row per stage
-constexpr int kCodeStride = kCodeRow + 16;   // padded LDS row (bank spread)
-constexpr int kScaleStride = 12;       // 8 scale bytes per row, padded
-constexpr int kCodeTile = BM * kCodeStride;
-constexpr int kScaleTile = BM * kScaleStride;
-constexpr int kStage = 2 * kCodeTile + 2 * kScaleTile;
+constexpr int kXcds = 8;   // MI355X: workgroups go round-robin to 8 XCDs
+
+// ===========================================================================
+// Fast path: K % 128 == 0, DMA loads into fragment-major LDS.
+// ===========================================================================
+
+template <int WM_, int WN_, int FM_, int FN_, int NST_>
+struct Cfg {
+  static constexpr int WM = WM_, WN = WN_, FM = FM_, FN = FN_;
+  static constexpr int NST = NST_;                    // LDS stages in flight
+  static constexpr int kWaves = WM * WN;
+  static constexpr int kThreads = kWaves * 64;
+  static constexpr int BM = WM * FM * 32, BN = WN * FN * 32;
+  static constexpr int GP = BM / 32, GQ = BN / 32;   // 32-row groups per operand
+  static constexpr int kGroups = GP + GQ;
+  static constexpr int kCodeBytes = kGroups * 2 * 1024;
+  static constexpr int kScaleBytes = kGroups * 256;
+  static constexpr int kStage = kCodeBytes + kScaleBytes;
+  static constexpr int kAcc = FM * FN * 16;           // accumulators per lane
+  // two resident workgroups per CU unless the accumulators alone need more
+  // than half the register file
+#ifndef NVFP4_MIN_BLOCKS
+  static constexpr int kMinBlocks = (kWaves <= 4 && kAcc <= 128) ? 2 : 1;
+#else
+  static constexpr int kMinBlocks = NVFP4_MIN_BLOCKS;
+#endif
+  // DMA instructions each wave issues per stage (code regions + scale rows)
+  static_assert((kGroups * 2) % kWaves == 0 && kGroups % kWaves == 0, "uneven stage split");
+  static constexpr int kLoadsPerWave = (kGroups * 2) / kWaves + kGroups / kWaves;
+};
+
+struct FastArgs {
+  GemmProblem g;
+  int splits;
+  int64_t TM, TN;       // tile grid
+  int64_t tiles, units;
+  float* partials;
+};
+
+// Tile t of the grid: row-block I, col-block J.  Symmetric problems list only
+// tiles whose first row is <= their last column.
+template <int BM, int BN, bool SYM>
+__device__ __forceinline__ void tile_of(int64_t t, int64_t TM, int64_t TN, int64_t& I, int64_t& J) {
+  if constexpr (SYM) {
+    for (int64_t i = 0; i < TM; ++i) {
+      // first column block whose last column reaches row i*BM
+      const int64_t jmin = i * BM - BN + 1 <= 0 ? 0 : (i * BM) / BN;
+      if (jmin >= TN) continue;
+      const int64_t cnt = TN - jmin;
+      if (t < cnt) { I = i; J = jmin + t; return; }
+      t -= cnt;
+    }
+    I = TM; J = 0;   // unreachable for t < tiles
+  } else {
+    I = t % TM;      // column-major: an XCD's run of tiles shares Q columns
+    J = t / TM;
+  }
+}
+
+// Global -> LDS DMA of 16 (or 4) bytes per lane: lane l's bytes land at LDS
+// address lds + 16*l (4*l).  Written as inline asm so the compiler does not
+// treat the asynchronous LDS write as pending before every later LDS read;
+// the kernel orders it explicitly with s_waitcnt vmcnt + s_barrier.  The
+// instruction has no register results; its address operands are read at
+// issue.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(lds)
+               : "memory", "m0");
+}
+
+// Per-lane DMA sources of the regions this wave loads, at k = 0, and their
+// offsets inside a stage.  Computed once per tile; each stage then adds its
+// K offset.  Rows past the matrix edge are clamped to the last row: they
+// feed only outputs that the epilogue masks.
+template <class C>
+struct StageSrc {
+  static constexpr int kCode = C::kGroups * 2 / C::kWaves;
+  static constexpr int kScale = C::kGroups / C::kWaves;
+  const uint8_t* code[kCode];
+  const uint8_t* scale[kScale];
+};
+
+template <class C>
+__device__ __forceinline__ void init_sources(const GemmProblem& g, int64_t m0, int64_t n0, int wave,
+                                             int lane, StageSrc<C>& src) {
+  const int64_t kb = g.K / 2, sb = g.K / 16;
+#pragma unroll
+  for (int q = 0; q < StageSrc<C>::kCode; ++q) {
+    const int r = wave + q * C::kWaves, grp = r >> 1, hs = r & 1;
+    const bool isP = grp < C::GP;
+    int64_t row = (isP ? m0 + 32 * grp : n0 + 32 * (grp - C::GP)) + (lane & 31);
+    const int64_t lim = isP ? g.M : g.N;
+    row = row < lim ? row : lim - 1;
+    src.code[q] = (isP ? g.codes_p : g.codes_q) + row * kb + 32 * (lane >> 5) + 16 * hs;
+  }
+#pragma unroll
+  for (int q = 0; q < StageSrc<C>::kScale; ++q) {
+    const int grp = wave + q * C::kWaves;
+    const bool isP = grp < C::GP;
+    int64_t row = (isP ? m0 + 32 * grp : n0 + 32 * (grp - C::GP)) + (lane & 31);
+    const int64_t lim = isP ? g.M : g.N;
+    row = row < lim ? row : lim - 1;
+    src.scale[q] = (isP ? g.scales_p : g.scales_q) + row * sb + 4 * (lane >> 5);
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void issue_stage(const StageSrc<C>& src, int64_t k0, uint8_t* stage,
+                                            int wave) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(stage));
+#pragma unroll
+  for (int q = 0; q < StageSrc<C>::kCode; ++q)
+    dma16(src.code[q] + k0 / 2, base + (uint32_t)(wave + q * C::kWaves) * 1024u);
+#pragma unroll
+  for (int q = 0; q < StageSrc<C>::kScale; ++q)
+    dma4(src.scale[q] + k0 / 16, base + (uint32_t)C::kCodeBytes + (uint32_t)(wave + q * C::kWaves) * 256u);
+}
+
+// out = beta * addend + alpha * sgP * sgQ * acc for the tile at (m0, n0);
+// symmetric products write row <= col and mirror row < col.  amax of the
+// written values goes to amax_out.  Offsets inside a tile are 32-bit
+// (BM * N < 2^31 is checked at the API); tiles wholly inside the matrix
+// (and, if symmetric, wholly above the diagonal) skip the per-element tests.
+template <class C, bool SYM, bool PRE>
+__device__ __forceinline__ void epilogue(const GemmProblem& g, floatx16 (&acc)[C::FM][C::FN],
+                                         const floatx16 (&pre)[C::FM][C::FN],
+                                         int64_t m0, int64_t n0, int wm, int wn, int lane) {
+  const float scale = g.alpha * (*g.sg_p) * (*g.sg_q);
+  const float beta = g.beta;
+  const int h = lane >> 5, c32 = lane & 31;
+  const int N = (int)g.N;
+  const int64_t r0 = m0 + wm * C::FM * 32 + 4 * h;     // first row of this lane
+  const int64_t c0 = n0 + wn * C::FN * 32 + c32;       // first column of this lane
+  float* obase = g.out + r0 * g.N + c0;
+  const float* abase = g.addend ? g.addend + r0 * g.N + c0 : nullptr;
+  float* mbase = g.out + c0 * g.N + r0;                // mirror: (col, row)
+  const bool inside = m0 + C::BM <= g.M && n0 + C::BN <= g.N;
+  const bool upper = !SYM || (m0 + C::BM <= n0);       // every element has row < col
+  uint32_t amax = 0;
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float v4[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int r = 4 * q + t;
+          const int dr = i * 32 + 8 * q + t;           // row offset from r0
+          const int off = dr * N + j * 32;
+          bool ok = true;
+          if (!(inside && upper)) {
+            const int64_t row = r0 + dr, col = c0 + j * 32;
+            ok = row < g.M && col < g.N && (!SYM || row <= col);
+          }
+          float v = scale * acc[i][j][r];
+          if (ok) {
+            if constexpr (PRE) {
+              v = fmaf(beta, pre[i][j][r], v);
+            } else {
+              if (abase) v = fmaf(beta, abase[off], v);
+            }
+            obase[off] = v;
+            const uint32_t ab = abs_bits(v);
+            amax = ab > amax ? ab : amax;
+          }
+          v4[t] = v;
+        }
+        if constexpr (SYM) {
+          // mirror: rows r0+dr..+3 of column c become 4 consecutive floats
+          const int moff = (j * 32) * N + i * 32 + 8 * q;
+          if (inside && upper) {
+            *reinterpret_cast<float4*>(mbase + moff) = make_float4(v4[0], v4[1], v4[2], v4[3]);
+          } else {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const int64_t row = r0 + i * 32 + 8 * q + t, col = c0 + j * 32;
+              if (row < g.M && col < g.N && row < col) mbase[moff + t] = v4[t];
+            }
+          }
+        }
+      }
+  if (g.amax_out) amax_publish(amax, g.amax_out);
+}
+
+// The addend values this lane's epilogue will need, loaded before the K loop
+// so that their latency hides under it (rows/cols past the edge read 0).
+template <class C>
+__device__ __forceinline__ void prefetch_addend(const GemmProblem& g, floatx16 (&pre)[C::FM][C::FN],
+                                                int64_t m0, int64_t n0, int wm, int wn, int lane) {
+  const int h = lane >> 5, c32 = lane & 31;
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = m0 + (wm * C::FM + i) * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        const int64_t col = n0 + (wn * C::FN + j) * 32 + c32;
+        pre[i][j][r] = (row < g.M && col < g.N) ? g.addend[row * g.N + col] : 0.0f;
+      }
+}
+
+template <class C, bool SYM, bool PRE>
+__global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_fast_kernel(FastArgs a) {
+  // PRE: the launch has an addend and no K split, so the epilogue runs here
+  __shared__ __attribute__((aligned(16))) uint8_t smem[C::NST * C::kStage];
+  const GemmProblem& g = a.g;
+
+  // ---- work unit -> (tile, split), XCD-aware: each XCD gets a contiguous run
+  const int64_t per_xcd = (a.units + kXcds - 1) / kXcds;
+  const int64_t u = (int64_t)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  if (u >= a.units) return;
+  const int64_t tile = u / a.splits;
+  const int split = (int)(u % a.splits);
+  int64_t I, J;
+  tile_of<C::BM, C::BN, SYM>(tile, a.TM, a.TN, I, J);
+  const int64_t m0 = I * C::BM, n0 = J * C::BN;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / C::WN, wn = wave % C::WN;
+
+  floatx16 acc[C::FM][C::FN];
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  floatx16 pre[C::FM][C::FN];
+  if constexpr (PRE) prefetch_addend<C>(g, pre, m0, n0, wm, wn, lane);
+  StageSrc<C> src;
+  init_sources<C>(g, m0, n0, wave, lane, src);
+
+  const int64_t nk_all = g.K / 128;
+  const int64_t kc0 = nk_all * split / a.splits, kc1 = nk_all * (split + 1) / a.splits;
+
+  // prologue: stages kc0 .. kc0 + NST - 2 in flight
+#pragma unroll
+  for (int p = 0; p < C::NST - 1; ++p)
+    if (kc0 + p < kc1) issue_stage<C>(src, (kc0 + p) * 128, smem + p * C::kStage, wave);
+
+  for (int64_t kc = kc0; kc < kc1; ++kc) {
+    // wait for this wave's loads of stage kc (later stages may stay in
+    // flight), then for every wave's; the barrier also retires all reads of
+    // the buffer the next issue overwrites
+    if (kc + C::NST - 2 < kc1) {
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"((C::NST - 2) * C::kLoadsPerWave) : "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    __syncthreads();
+    if (kc + C::NST - 1 < kc1)
+      issue_stage<C>(src, (kc + C::NST - 1) * 128,
+                     smem + ((kc - kc0 + C::NST - 1) % C::NST) * C::kStage, wave);
+    const uint8_t* st = smem + ((kc - kc0) % C::NST) * C::kStage;
+
+    uint32_t sp[C::FM], sq[C::FN];
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+      sp[i] = *reinterpret_cast<const uint32_t*>(st + C::kCodeBytes + (wm * C::FM + i) * 256 + 4 * lane);
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+      sq[j] = *reinterpret_cast<const uint32_t*>(st + C::kCodeBytes + (C::GP + wn * C::FN + j) * 256 + 4 * lane);
+
+#pragma unroll
+    for (int hs = 0; hs < 2; ++hs) {
+      uint4 cp[C::FM], cq[C::FN];
+      half2_t spf[C::FM][2], sqf[C::FN][2];
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i) {
+        cp[i] = *reinterpret_cast<const uint4*>(st + ((wm * C::FM + i) * 2 + hs) * 1024 + 16 * lane);
+        spf[i][0] = scale_pair_f16((sp[i] >> (16 * hs)) & 0xFFu);
+        spf[i][1] = scale_pair_f16((sp[i] >> (16 * hs + 8)) & 0xFFu);
+      }
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) {
+        cq[j] = *reinterpret_cast<const uint4*>(st + ((C::GP + wn * C::FN + j) * 2 + hs) * 1024 + 16 * lane);
+        sqf[j][0] = scale_pair_f16((sq[j] >> (16 * hs)) & 0xFFu);
+        sqf[j][1] = scale_pair_f16((sq[j] >> (16 * hs + 8)) & 0xFFu);
+      }
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        half8_t av[C::FM], bv[C::FN];
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i) {
+          const uint32_t w = s == 0 ? cp[i].x : s == 1 ? cp[i].y : s == 2 ? cp[i].z : cp[i].w;
+          av[i] = dequant8_f16(w, spf[i][s >> 1]);
+        }
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) {
+          const uint32_t w = s == 0 ? cq[j].x : s == 1 ? cq[j].y : s == 2 ? cq[j].z : cq[j].w;
+          bv[j] = dequant8_f16(w, sqf[j][s >> 1]);
+        }
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+          for (int j = 0; j < C::FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
+      }
+    }
+  }
+
+  if (a.splits > 1) {
+    // split-K: store the FP32 partial; gemm_reduce_kernel sums the splits in
+    // order and runs the epilogue (a kernel boundary makes the partials
+    // visible without per-workgroup cache flushes)
+    float* part = a.partials + (size_t)u * C::kAcc * C::kThreads;
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          part[((i * C::FN + j) * 16 + r) * C::kThreads + threadIdx.x] = acc[i][j][r];
+    return;
+  }
+  epilogue<C, SYM, PRE>(g, acc, pre, m0, n0, wm, wn, lane);
+}
+
+// Sum the split-K partials of one tile in split order, then the epilogue.
+template <class C, bool SYM>
+__global__ __launch_bounds__(C::kThreads) void gemm_reduce_kernel(FastArgs a) {
+  const int64_t per_xcd = (a.tiles + kXcds - 1) / kXcds;
+  const int64_t tile = (int64_t)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  if (tile >= a.tiles) return;
+  int64_t I, J;
+  tile_of<C::BM, C::BN, SYM>(tile, a.TM, a.TN, I, J);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / C::WN, wn = wave % C::WN;
+  const float* base = a.partials + (size_t)tile * a.splits * C::kAcc * C::kThreads;
+  floatx16 acc[C::FM][C::FN];
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int e = (i * C::FN + j) * 16 + r;
+        float v = base[(size_t)e * C::kThreads + threadIdx.x];
+        for (int sp = 1; sp < a.splits; ++sp)
+          v += base[((size_t)sp * C::kAcc + e) * C::kThreads + threadIdx.x];
+        acc[i][j][r] = v;
+      }
+  const floatx16 (&none)[C::FM][C::FN] = acc;   // unused: the addend is read in place
+  epilogue<C, SYM, false>(a.g, acc, none, I * C::BM, J * C::BN, wm, wn, lane);
+}
+
+// ===========================================================================
+// General path: any K that is a multiple of 16 (register-staged loads with
+// zero fill past K).  128 x 128 tile, 4 waves of 64 x 64.
+// ===========================================================================
+
+constexpr int GBM = 128, GBN = 128, GBK = 128, GThreads = 256;
+constexpr int kCodeStride = GBK / 2 + 16;
+constexpr int kScaleStride = 12;
+constexpr int kCodeTile = GBM * kCodeStride;
+constexpr int kScaleTile = GBM * kScaleStride;
+constexpr int kGStage = 2 * kCodeTile + 2 * kScaleTile;
 
 struct TileLoad {
-  uint2 pc[4], qc[4];   // 8-byte code chunks
-  uint32_t ps, qs;      // 4 scale bytes
+  uint2 pc[4], qc[4];
+  uint32_t ps, qs;
 };
 
 __device__ __forceinline__ void load_tile(const GemmProblem& g, int64_t m0, int64_t n0, int64_t k0,
                                           TileLoad& t) {
   const int tid = threadIdx.x;
-  const int64_t kb = g.K / 2;     // code bytes per row
+  const int64_t kb = g.K / 2;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int idx = tid + kThreads * i;
+    const int idx = tid + GThreads * i;
     const int row = idx >> 3, chunk = idx & 7;
     const int64_t kk = k0 + chunk * 16;
     const bool kin = kk < g.K;
@@ -56,21 +430,19 @@ __device__ __forceinline__ void load_tile(const GemmProblem& g, int64_t m0, int6
                   ? *reinterpret_cast<const uint2*>(g.codes_q + (n0 + row) * kb + kk / 2)
                   : make_uint2(0u, 0u);
   }
-  {
-    const int row = tid >> 1, part = tid & 1;
-    const int64_t sb = g.K / 16;  // scale bytes per row
-    const int64_t blk = k0 / 16 + part * 4;
-    uint32_t ps = 0, qs = 0;
+  const int row = tid >> 1, part = tid & 1;
+  const int64_t sb = g.K / 16;
+  const int64_t blk = k0 / 16 + part * 4;
+  uint32_t ps = 0, qs = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (blk + j < sb) {
-        if (m0 + row < g.M) ps |= (uint32_t)g.scales_p[(m0 + row) * sb + blk + j] << (8 * j);
-        if (n0 + row < g.N) qs |= (uint32_t)g.scales_q[(n0 + row) * sb + blk + j] << (8 * j);
-      }
+  for (int j = 0; j < 4; ++j) {
+    if (blk + j < sb) {
+      if (m0 + row < g.M) ps |= (uint32_t)g.scales_p[(m0 + row) * sb + blk + j] << (8 * j);
+      if (n0 + row < g.N) qs |= (uint32_t)g.scales_q[(n0 + row) * sb + blk + j] << (8 * j);
     }
-    t.ps = ps;
-    t.qs = qs;
   }
+  t.ps = ps;
+  t.qs = qs;
 }
 
 __device__ __forceinline__ void store_tile(uint8_t* stage, const TileLoad& t) {
@@ -81,7 +453,7 @@ __device__ __forceinline__ void store_tile(uint8_t* stage, const TileLoad& t) {
   uint8_t* sqs = sps + kScaleTile;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int idx = tid + kThreads * i;
+    const int idx = tid + GThreads * i;
     const int row = idx >> 3, chunk = idx & 7;
     *reinterpret_cast<uint2*>(sp + row * kCodeStride + chunk * 8) = t.pc[i];
     *reinterpret_cast<uint2*>(sq + row * kCodeStride + chunk * 8) = t.qc[i];
@@ -91,8 +463,6 @@ __device__ __forceinline__ void store_tile(uint8_t* stage, const TileLoad& t) {
   *reinterpret_cast<uint32_t*>(sqs + row * kScaleStride + part * 4) = t.qs;
 }
 
-// Fragment of one 32-row subtile for a whole stage: 8 code words (one per
-// MFMA step) and the 4 block scales they use.
 struct Frag {
   uint32_t w[8];
   half2_t s[4];
@@ -109,23 +479,12 @@ __device__ __forceinline__ void read_frag(const uint8_t* codes, const uint8_t* s
   for (int j = 0; j < 4; ++j) f.s[j] = scale_pair_f16((sc >> (8 * j)) & 0xFFu);
 }
 
-__device__ __forceinline__ void wave_amax_atomic(uint32_t m, uint32_t* slot) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    uint32_t w = __shfl_xor(m, o, 64);
-    m = w > m ? w : m;
-  }
-  if ((threadIdx.x & 63) == 0) atomicMax(slot, m);
-}
-
 template <bool SYM>
-__global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmProblem g) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
-
-  // ---- tile of this workgroup
+__global__ __launch_bounds__(GThreads, 2) void gemm_general_kernel(GemmProblem g) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kGStage];
   int64_t ti, tj;
   if constexpr (SYM) {
-    const int64_t nt = (g.M + BM - 1) / BM;
+    const int64_t nt = (g.M + GBM - 1) / GBM;
     int64_t rem = blockIdx.x, r = 0;
     while (rem >= nt - r) { rem -= nt - r; ++r; }
     ti = r;
@@ -134,8 +493,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmProblem g) {
     ti = blockIdx.y;
     tj = blockIdx.x;
   }
-  const int64_t m0 = ti * BM, n0 = tj * BN;
-
+  const int64_t m0 = ti * GBM, n0 = tj * GBN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int h = lane >> 5, r32 = lane & 31;
@@ -148,17 +506,15 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmProblem g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const int64_t nk = (g.K + BK - 1) / BK;
+  const int64_t nk = (g.K + GBK - 1) / GBK;
   TileLoad tl;
   load_tile(g, m0, n0, 0, tl);
   store_tile(smem, tl);
   __syncthreads();
-
   for (int64_t kc = 0; kc < nk; ++kc) {
     const bool more = kc + 1 < nk;
-    if (more) load_tile(g, m0, n0, (kc + 1) * BK, tl);
-
-    const uint8_t* stage = smem + (kc & 1) * kStage;
+    if (more) load_tile(g, m0, n0, (kc + 1) * GBK, tl);
+    const uint8_t* stage = smem + (kc & 1) * kGStage;
     Frag fp[2], fq[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -167,24 +523,22 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmProblem g) {
     }
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      half8_t a[2], b[2];
+      half8_t av[2], bv[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        a[i] = dequant8_f16(fp[i].w[s], fp[i].s[s >> 1]);
-        b[i] = dequant8_f16(fq[i].w[s], fq[i].s[s >> 1]);
+        av[i] = dequant8_f16(fp[i].w[s], fp[i].s[s >> 1]);
+        bv[i] = dequant8_f16(fq[i].w[s], fq[i].s[s >> 1]);
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
     }
-
-    if (more) store_tile(smem + ((kc + 1) & 1) * kStage, tl);
+    if (more) store_tile(smem + ((kc + 1) & 1) * kGStage, tl);
     __syncthreads();
   }
 
-  // ---- epilogue: out = beta * addend + alpha * sgP * sgQ * acc
   const float scale = g.alpha * (*g.sg_p) * (*g.sg_q);
   const float beta = g.beta;
   const bool off_diag = ti < tj;
@@ -206,19 +560,100 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmProblem g) {
         const uint32_t a = abs_bits(v);
         amax = a > amax ? a : amax;
       }
-  if (g.amax_out) wave_amax_atomic(amax, g.amax_out);
+  if (g.amax_out) amax_publish(amax, g.amax_out);
+}
+
+// ---------------------------------------------------------------- plans ----
+
+#ifndef NVFP4_FAST_WM
+#define NVFP4_FAST_WM 2
+#define NVFP4_FAST_WN 2
+#define NVFP4_FAST_FM 2
+#define NVFP4_FAST_FN 2
+#endif
+#ifndef NVFP4_FAST_NST
+#define NVFP4_FAST_NST 2
+#endif
+using FastCfg = Cfg<NVFP4_FAST_WM, NVFP4_FAST_WN, NVFP4_FAST_FM, NVFP4_FAST_FN, NVFP4_FAST_NST>;
+
+#ifndef NVFP4_TARGET_UNITS
+#define NVFP4_TARGET_UNITS 512   // 256 CUs x 2 resident workgroups
+#endif
+constexpr int64_t kTargetUnits = NVFP4_TARGET_UNITS;
+constexpr int64_t kMinStagesPerSplit = 4;
+
+int64_t sym_tiles(int64_t TM, int64_t TN, int64_t BM, int64_t BN) {
+  int64_t t = 0;
+  for (int64_t i = 0; i < TM; ++i) {
+    const int64_t jmin = i * BM - BN + 1 <= 0 ? 0 : (i * BM) / BN;
+    if (jmin < TN) t += TN - jmin;
+  }
+  return t;
 }
 
 }  // namespace
 
-hipError_t launch_gemm(const GemmProblem& p, hipStream_t s) {
-  if (p.symmetric) {
-    const int64_t nt = (p.M + BM - 1) / BM;
-    gemm_kernel<true><<<dim3((unsigned)(nt * (nt + 1) / 2)), kThreads, 0, s>>>(p);
-  } else {
-    dim3 grid((unsigned)((p.N + BN - 1) / BN), (unsigned)((p.M + BM - 1) / BM));
-    gemm_kernel<false><<<grid, kThreads, 0, s>>>(p);
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool symmetric, bool allow_split) {
+  GemmPlan p{};
+  if (K % 128 != 0) {
+    p.fast = false;
+    p.splits = 1;
+    return p;
   }
+  p.fast = true;
+  p.TM = (M + FastCfg::BM - 1) / FastCfg::BM;
+  p.TN = (N + FastCfg::BN - 1) / FastCfg::BN;
+  p.tiles = symmetric ? sym_tiles(p.TM, p.TN, FastCfg::BM, FastCfg::BN) : p.TM * p.TN;
+  int64_t splits = 1;
+  const int64_t stages = K / 128;
+  if (allow_split && symmetric) {
+    while (p.tiles * splits < kTargetUnits && stages / (2 * splits) >= kMinStagesPerSplit) splits *= 2;
+  }
+  p.splits = (int)splits;
+  p.units = p.tiles * splits;
+  if (splits > 1) {
+    const size_t part = (size_t)p.units * FastCfg::kAcc * FastCfg::kThreads * sizeof(float);
+    p.partial_bytes = (part + 255) / 256 * 256;
+  }
+  p.ws_bytes = p.partial_bytes;
+  return p;
+}
+
+hipError_t launch_gemm(const GemmProblem& g, const GemmPlan& p, float* partials, hipStream_t s) {
+  if (!p.fast) {
+    if (g.symmetric) {
+      const int64_t nt = (g.M + GBM - 1) / GBM;
+      gemm_general_kernel<true><<<dim3((unsigned)(nt * (nt + 1) / 2)), GThreads, 0, s>>>(g);
+    } else {
+      dim3 grid((unsigned)((g.N + GBN - 1) / GBN), (unsigned)((g.M + GBM - 1) / GBM));
+      gemm_general_kernel<false><<<grid, GThreads, 0, s>>>(g);
+    }
+    return hipGetLastError();
+  }
+  FastArgs a;
+  a.g = g;
+  a.splits = p.splits;
+  a.TM = p.TM;
+  a.TN = p.TN;
+  a.tiles = p.tiles;
+  a.units = p.units;
+  a.partials = p.splits > 1 ? partials : nullptr;
+  const int64_t grid = (p.units + kXcds - 1) / kXcds * kXcds;
+  const bool pre = false;   // register prefetch of the addend costs occupancy; measured slower
+  if (g.symmetric) {
+    if (pre) gemm_fast_kernel<FastCfg, true, true><<<dim3((unsigned)grid), FastCfg::kThreads, 0, s>>>(a);
+    else gemm_fast_kernel<FastCfg, true, false><<<dim3((unsigned)grid), FastCfg::kThreads, 0, s>>>(a);
+  } else {
+    if (pre) gemm_fast_kernel<FastCfg, false, true><<<dim3((unsigned)grid), FastCfg::kThreads, 0, s>>>(a);
+    else gemm_fast_kernel<FastCfg, false, false><<<dim3((unsigned)grid), FastCfg::kThreads, 0, s>>>(a);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.splits == 1) return e;
+  const int64_t rgrid = (p.tiles + kXcds - 1) / kXcds * kXcds;
+  if (g.symmetric)
+    gemm_reduce_kernel<FastCfg, true><<<dim3((unsigned)rgrid), FastCfg::kThreads, 0, s>>>(a);
+  else
+    gemm_reduce_kernel<FastCfg, false><<<dim3((unsigned)rgrid), FastCfg::kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 

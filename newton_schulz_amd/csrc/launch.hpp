@@ -49,7 +49,18 @@ struct GemmProblem {
   float* out;
   uint32_t* amax_out;
 };
-hipError_t launch_gemm(const GemmProblem& p, hipStream_t s);
+
+// Launch plan of one product: the fast path needs K % 128 == 0; symmetric
+// products on the fast path may be split along K, which needs a workspace
+// of ws_bytes for the FP32 partials.
+struct GemmPlan {
+  bool fast;
+  int splits;
+  int64_t TM, TN, tiles, units;
+  size_t partial_bytes, ws_bytes;
+};
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool symmetric, bool allow_split);
+hipError_t launch_gemm(const GemmProblem& g, const GemmPlan& p, float* partials, hipStream_t s);
 
 // ---- Newton–Schulz prologue / epilogue (ns.hip) ---------------------------
 // Partial sums of clamp(G)^2 into part[0..kNormParts).

@@ -135,12 +135,7 @@ __global__ __launch_bounds__(kThreads) void normalize_kernel(const void* G, int6
 #pragma unroll
     for (int j = 0; j < 4; ++j) o[j] = make_float4(y[4 * j], y[4 * j + 1], y[4 * j + 2], y[4 * j + 3]);
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    uint32_t w = __shfl_xor(amax, o, 64);
-    amax = w > amax ? w : amax;
-  }
-  if ((threadIdx.x & 63) == 0) atomicMax(amax_slot, amax);
+  amax_publish(amax, amax_slot);
 }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {

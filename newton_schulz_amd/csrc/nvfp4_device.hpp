@@ -35,6 +35,22 @@ __device__ __forceinline__ uint32_t abs_bits(uint32_t raw) {
   return b >= 0x7F800000u ? kNaNBits : b;
 }
 
+// Wave-reduce m and fold it into *slot with one atomic per wave, skipped when
+// the slot already holds at least m.  The slot only grows, so a stale read
+// can only cost an extra atomic, never a lost maximum; skipping keeps
+// thousands of waves from serialising on one address.
+__device__ __forceinline__ void amax_publish(uint32_t m, uint32_t* slot) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    uint32_t w = __shfl_xor(m, o, 64);
+    m = w > m ? w : m;
+  }
+  if ((threadIdx.x & 63) == 0) {
+    uint32_t cur = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (m > cur) atomicMax(slot, m);
+  }
+}
+
 // s_g = RN_f32(amax / (6 * 448)); NaN stays NaN.
 __device__ __forceinline__ float global_scale_from_amax(uint32_t amax_bits) {
   if (amax_bits > 0x7F800000u) return __uint_as_float(kNaNBits);

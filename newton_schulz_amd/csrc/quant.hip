@@ -82,7 +82,8 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(const void* x, int64_t n
     uint32_t r = red[0];
 #pragma unroll
     for (int w = 1; w < kThreads / 64; ++w) r = red[w] > r ? red[w] : r;
-    atomicMax(slot, r);
+    uint32_t cur = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (r > cur) atomicMax(slot, r);
   }
 }
 

@@ -36,8 +36,9 @@ def test_workspace_sizes_and_validation_on_host():
     lib = ns._lib
     assert lib.ns_workspace_bytes(3072, 8192) == lib.ns_workspace_bytes(8192, 3072)
     wb = lib.ns_workspace_bytes(3072, 8192)
-    # X, A, B in fp32 plus four packed NVFP4 tensors: about 215 MB
-    assert 200e6 < wb < 240e6 and wb % 256 == 0
+    # X, A, B in fp32, four packed NVFP4 tensors (215 MB) and the split-K
+    # partials of the Gram products
+    assert 215e6 < wb < 320e6 and wb % 256 == 0
     assert lib.ns_workspace_bytes(3072, 8190) == 0
     assert lib.nvfp4_quantize_workspace_bytes(16, 16) >= 4
     coeffs = (ctypes.c_float * 3)(3.4445, -4.775, 2.0315)
@@ -61,7 +62,12 @@ def test_workspace_sizes_and_validation_on_host():
     assert lib.nvfp4_quantize(fake, 0, 16, 16, 0, fake, fake, fake, None, 256, None) == ns.NS_ERR_WORKSPACE
     # symmetric GEMM with different operands
     assert lib.nvfp4_gemm(fake, fake, fake, other, fake, fake, 32, 32, 32, 1, 1.0, 0.0,
-                          None, fake, None, None) == ns.NS_ERR_ARG
+                          None, fake, None, None, 0, None) == ns.NS_ERR_ARG
     # beta != 0 without an addend
     assert lib.nvfp4_gemm(fake, fake, fake, fake, fake, fake, 32, 32, 32, 0, 1.0, 2.0,
-                          None, fake, None, None) == ns.NS_ERR_ARG
+                          None, fake, None, None, 0, None) == ns.NS_ERR_ARG
+    # symmetric 3072^2 x 8192 splits K: it needs a workspace, and a too-small one is refused
+    wsg = lib.nvfp4_gemm_workspace_bytes(3072, 3072, 8192, 1)
+    assert wsg > 0
+    assert lib.nvfp4_gemm(fake, fake, fake, fake, fake, fake, 3072, 3072, 8192, 1, 1.0, 0.0,
+                          None, other, None, fake, wsg - 1, None) == ns.NS_ERR_WORKSPACE
