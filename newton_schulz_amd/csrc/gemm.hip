@@ -43,16 +43,19 @@ constexpr int kXcds = 8;   // MI355X: workgroups go round-robin to 8 XCDs
 // Fast path: K % 128 == 0, DMA loads into fragment-major LDS.
 // ===========================================================================
 
-template <int WM_, int WN_, int FM_, int FN_, int NST_>
+template <int WM_, int WN_, int FM_, int FN_, int NST_, int BK_>
 struct Cfg {
   static constexpr int WM = WM_, WN = WN_, FM = FM_, FN = FN_;
   static constexpr int NST = NST_;                    // LDS stages in flight
+  static constexpr int BK = BK_;                      // K elements per stage (64 or 128)
+  static constexpr int kHalves = BK / 64;             // 16-byte lane slices per row per stage
+  static_assert(BK == 64 || BK == 128, "BK must be 64 or 128");
   static constexpr int kWaves = WM * WN;
   static constexpr int kThreads = kWaves * 64;
   static constexpr int BM = WM * FM * 32, BN = WN * FN * 32;
   static constexpr int GP = BM / 32, GQ = BN / 32;   // 32-row groups per operand
   static constexpr int kGroups = GP + GQ;
-  static constexpr int kCodeBytes = kGroups * 2 * 1024;
+  static constexpr int kCodeBytes = kGroups * kHalves * 1024;
   static constexpr int kScaleBytes = kGroups * 256;
   static constexpr int kStage = kCodeBytes + kScaleBytes;
   static constexpr int kAcc = FM * FN * 16;           // accumulators per lane
@@ -64,8 +67,8 @@ struct Cfg {
   static constexpr int kMinBlocks = NVFP4_MIN_BLOCKS;
 #endif
   // DMA instructions each wave issues per stage (code regions + scale rows)
-  static_assert((kGroups * 2) % kWaves == 0 && kGroups % kWaves == 0, "uneven stage split");
-  static constexpr int kLoadsPerWave = (kGroups * 2) / kWaves + kGroups / kWaves;
+  static_assert((kGroups * kHalves) % kWaves == 0 && kGroups % kWaves == 0, "uneven stage split");
+  static constexpr int kLoadsPerWave = (kGroups * kHalves) / kWaves + kGroups / kWaves;
 };
 
 struct FastArgs {
@@ -114,13 +117,21 @@ __device__ __forceinline__ void dma4(const void* src, uint32_t lds) {
                : "memory", "m0");
 }
 
+// Which byte of the lane's scale dword covers MFMA steps 2b, 2b+1 of
+// half-stage hs: a 16-byte slice holds 32 codes = 2 blocks.
+template <class C>
+__device__ __forceinline__ int scale_byte(int hs, int lane, int b) {
+  if constexpr (C::BK == 128) return 2 * hs + b;     // dword = blocks 4h..4h+3
+  else return 2 * (lane >> 5) + b;                   // dword = blocks 0..3 of the row
+}
+
 // Per-lane DMA sources of the regions this wave loads, at k = 0, and their
 // offsets inside a stage.  Computed once per tile; each stage then adds its
 // K offset.  Rows past the matrix edge are clamped to the last row: they
 // feed only outputs that the epilogue masks.
 template <class C>
 struct StageSrc {
-  static constexpr int kCode = C::kGroups * 2 / C::kWaves;
+  static constexpr int kCode = C::kGroups * C::kHalves / C::kWaves;
   static constexpr int kScale = C::kGroups / C::kWaves;
   const uint8_t* code[kCode];
   const uint8_t* scale[kScale];
@@ -132,12 +143,13 @@ __device__ __forceinline__ void init_sources(const GemmProblem& g, int64_t m0, i
   const int64_t kb = g.K / 2, sb = g.K / 16;
 #pragma unroll
   for (int q = 0; q < StageSrc<C>::kCode; ++q) {
-    const int r = wave + q * C::kWaves, grp = r >> 1, hs = r & 1;
+    const int r = wave + q * C::kWaves, grp = r / C::kHalves, hs = r % C::kHalves;
     const bool isP = grp < C::GP;
     int64_t row = (isP ? m0 + 32 * grp : n0 + 32 * (grp - C::GP)) + (lane & 31);
     const int64_t lim = isP ? g.M : g.N;
     row = row < lim ? row : lim - 1;
-    src.code[q] = (isP ? g.codes_p : g.codes_q) + row * kb + 32 * (lane >> 5) + 16 * hs;
+    // lane half h owns bytes [h*BK/4, (h+1)*BK/4) of the row's BK/2 stage bytes
+    src.code[q] = (isP ? g.codes_p : g.codes_q) + row * kb + (C::BK / 4) * (lane >> 5) + 16 * hs;
   }
 #pragma unroll
   for (int q = 0; q < StageSrc<C>::kScale; ++q) {
@@ -146,7 +158,9 @@ __device__ __forceinline__ void init_sources(const GemmProblem& g, int64_t m0, i
     int64_t row = (isP ? m0 + 32 * grp : n0 + 32 * (grp - C::GP)) + (lane & 31);
     const int64_t lim = isP ? g.M : g.N;
     row = row < lim ? row : lim - 1;
-    src.scale[q] = (isP ? g.scales_p : g.scales_q) + row * sb + 4 * (lane >> 5);
+    // BK = 128: 8 scale bytes per row and stage, lane half h loads its 4;
+    // BK = 64: 4 bytes per row, both halves load them and pick their 2
+    src.scale[q] = (isP ? g.scales_p : g.scales_q) + row * sb + (C::BK == 128 ? 4 * (lane >> 5) : 0);
   }
 }
 
@@ -281,13 +295,13 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_fast_kernel(F
   StageSrc<C> src;
   init_sources<C>(g, m0, n0, wave, lane, src);
 
-  const int64_t nk_all = g.K / 128;
+  const int64_t nk_all = g.K / C::BK;
   const int64_t kc0 = nk_all * split / a.splits, kc1 = nk_all * (split + 1) / a.splits;
 
   // prologue: stages kc0 .. kc0 + NST - 2 in flight
 #pragma unroll
   for (int p = 0; p < C::NST - 1; ++p)
-    if (kc0 + p < kc1) issue_stage<C>(src, (kc0 + p) * 128, smem + p * C::kStage, wave);
+    if (kc0 + p < kc1) issue_stage<C>(src, (kc0 + p) * C::BK, smem + p * C::kStage, wave);
 
   for (int64_t kc = kc0; kc < kc1; ++kc) {
     // wait for this wave's loads of stage kc (later stages may stay in
@@ -300,7 +314,7 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_fast_kernel(F
     }
     __syncthreads();
     if (kc + C::NST - 1 < kc1)
-      issue_stage<C>(src, (kc + C::NST - 1) * 128,
+      issue_stage<C>(src, (kc + C::NST - 1) * C::BK,
                      smem + ((kc - kc0 + C::NST - 1) % C::NST) * C::kStage, wave);
     const uint8_t* st = smem + ((kc - kc0) % C::NST) * C::kStage;
 
@@ -313,20 +327,20 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_fast_kernel(F
       sq[j] = *reinterpret_cast<const uint32_t*>(st + C::kCodeBytes + (C::GP + wn * C::FN + j) * 256 + 4 * lane);
 
 #pragma unroll
-    for (int hs = 0; hs < 2; ++hs) {
+    for (int hs = 0; hs < C::kHalves; ++hs) {
       uint4 cp[C::FM], cq[C::FN];
       half2_t spf[C::FM][2], sqf[C::FN][2];
 #pragma unroll
       for (int i = 0; i < C::FM; ++i) {
-        cp[i] = *reinterpret_cast<const uint4*>(st + ((wm * C::FM + i) * 2 + hs) * 1024 + 16 * lane);
-        spf[i][0] = scale_pair_f16((sp[i] >> (16 * hs)) & 0xFFu);
-        spf[i][1] = scale_pair_f16((sp[i] >> (16 * hs + 8)) & 0xFFu);
+        cp[i] = *reinterpret_cast<const uint4*>(st + ((wm * C::FM + i) * C::kHalves + hs) * 1024 + 16 * lane);
+        spf[i][0] = scale_pair_f16((sp[i] >> (8 * scale_byte<C>(hs, lane, 0))) & 0xFFu);
+        spf[i][1] = scale_pair_f16((sp[i] >> (8 * scale_byte<C>(hs, lane, 1))) & 0xFFu);
       }
 #pragma unroll
       for (int j = 0; j < C::FN; ++j) {
-        cq[j] = *reinterpret_cast<const uint4*>(st + ((C::GP + wn * C::FN + j) * 2 + hs) * 1024 + 16 * lane);
-        sqf[j][0] = scale_pair_f16((sq[j] >> (16 * hs)) & 0xFFu);
-        sqf[j][1] = scale_pair_f16((sq[j] >> (16 * hs + 8)) & 0xFFu);
+        cq[j] = *reinterpret_cast<const uint4*>(st + ((C::GP + wn * C::FN + j) * C::kHalves + hs) * 1024 + 16 * lane);
+        sqf[j][0] = scale_pair_f16((sq[j] >> (8 * scale_byte<C>(hs, lane, 0))) & 0xFFu);
+        sqf[j][1] = scale_pair_f16((sq[j] >> (8 * scale_byte<C>(hs, lane, 1))) & 0xFFu);
       }
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
@@ -574,13 +588,19 @@ __global__ __launch_bounds__(GThreads, 2) void gemm_general_kernel(GemmProblem g
 #ifndef NVFP4_FAST_NST
 #define NVFP4_FAST_NST 2
 #endif
-using FastCfg = Cfg<NVFP4_FAST_WM, NVFP4_FAST_WN, NVFP4_FAST_FM, NVFP4_FAST_FN, NVFP4_FAST_NST>;
+#ifndef NVFP4_FAST_BK
+#define NVFP4_FAST_BK 128
+#endif
+using FastCfg = Cfg<NVFP4_FAST_WM, NVFP4_FAST_WN, NVFP4_FAST_FM, NVFP4_FAST_FN, NVFP4_FAST_NST,
+                    NVFP4_FAST_BK>;
 
 #ifndef NVFP4_TARGET_UNITS
 #define NVFP4_TARGET_UNITS 512   // 256 CUs x 2 resident workgroups
 #endif
 constexpr int64_t kTargetUnits = NVFP4_TARGET_UNITS;
-constexpr int64_t kMinStagesPerSplit = 4;
+// a split must keep at least 4096 of K: shorter splits cost more in FP32
+// partial traffic and the reduce launch than the extra parallelism returns
+constexpr int64_t kMinKPerSplit = 4096;
 
 int64_t sym_tiles(int64_t TM, int64_t TN, int64_t BM, int64_t BN) {
   int64_t t = 0;
@@ -605,9 +625,10 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool symmetric, bool allow_s
   p.TN = (N + FastCfg::BN - 1) / FastCfg::BN;
   p.tiles = symmetric ? sym_tiles(p.TM, p.TN, FastCfg::BM, FastCfg::BN) : p.TM * p.TN;
   int64_t splits = 1;
-  const int64_t stages = K / 128;
+  const int64_t stages = K / FastCfg::BK;
   if (allow_split && symmetric) {
-    while (p.tiles * splits < kTargetUnits && stages / (2 * splits) >= kMinStagesPerSplit) splits *= 2;
+    while (p.tiles * splits < kTargetUnits && (stages / (2 * splits)) * FastCfg::BK >= kMinKPerSplit)
+      splits *= 2;
   }
   p.splits = (int)splits;
   p.units = p.tiles * splits;

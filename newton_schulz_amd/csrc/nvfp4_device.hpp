@@ -112,12 +112,16 @@ __device__ __forceinline__ BlockThresholds block_thresholds(double unit /* s * s
   return T;
 }
 
-// 4-bit code of one element (sign bit from the raw float bits).
+// 4-bit code of one element (sign bit from the raw float bits).  The
+// thresholds are non-decreasing, so the count of those below |x| is found
+// by a three-step binary search: T3 splits codes 0-3 from 4-7, then T5 or
+// T1, then T6/T4/T2/T0.
 __device__ __forceinline__ uint32_t encode_element(uint32_t raw_bits, const BlockThresholds& T) {
-  uint32_t a = raw_bits & 0x7FFFFFFFu;
-  uint32_t c = 0;
-#pragma unroll
-  for (int k = 0; k < 7; ++k) c += (a > T.t[k]) ? 1u : 0u;
+  const uint32_t a = raw_bits & 0x7FFFFFFFu;
+  const bool hi = a > T.t[3];
+  const bool mid = a > (hi ? T.t[5] : T.t[1]);
+  const uint32_t t2 = hi ? (mid ? T.t[6] : T.t[4]) : (mid ? T.t[2] : T.t[0]);
+  const uint32_t c = (hi ? 4u : 0u) | (mid ? 2u : 0u) | (a > t2 ? 1u : 0u);
   return c | ((raw_bits >> 28) & 8u);
 }
 
@@ -129,25 +133,102 @@ __device__ __forceinline__ uint32_t block_scale_byte(uint32_t amax_b_bits, float
   return e4m3_rne_sat(q);
 }
 
-// Encode 16 values given as raw float bit patterns.  Returns the packed
-// codes (element 2i in the low nibble of byte i) and the scale byte.
-__device__ __forceinline__ void encode_block16(const uint32_t (&v)[16], float sg,
-                                               uint32_t& lo, uint32_t& hi, uint32_t& scale) {
-  uint32_t amax_b = 0;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    uint32_t a = v[i] & 0x7FFFFFFFu;
-    amax_b = a > amax_b ? a : amax_b;
-  }
-  scale = block_scale_byte(amax_b, sg);
-  double unit = (scale == 0x7Fu) ? 0.0 : e4m3_value(scale) * (double)sg;
-  BlockThresholds T = block_thresholds(unit);
+// Exact encode of 16 values by thresholds (the reference rule above).
+__device__ __forceinline__ void encode_block16_exact(const uint32_t (&v)[16], float sg, uint32_t scale,
+                                                  uint32_t& lo, uint32_t& hi) {
+  const double unit = (scale == 0x7Fu) ? 0.0 : e4m3_value(scale) * (double)sg;
+  const BlockThresholds T = block_thresholds(unit);
   lo = 0;
   hi = 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) lo |= encode_element(v[i], T) << (4 * i);
 #pragma unroll
   for (int i = 0; i < 8; ++i) hi |= encode_element(v[8 + i], T) << (4 * i);
+}
+
+// Encode 16 values given as raw float bit patterns.  Returns the packed
+// codes (element 2i in the low nibble of byte i) and the scale byte.
+//
+// Fast path: the hardware f32 -> E2M1 conversion (RNE, ties to even,
+// saturating at 6, sign kept — measured on gfx950) is applied to x times two
+// approximations of 1/(s*s_g), one below and one above by ~2^-19 relative.
+// The exact quotient |x|/(s*s_g) lies strictly between the two products, and
+// rounding is monotone, so when both give the same code that code is the
+// exact RNE of the quotient.  A block where any element's two codes differ
+// (a tie or a near-tie), or whose s*s_g is outside [2^-120, 2^120], is
+// encoded by the exact threshold rule instead.
+__device__ __forceinline__ void encode_block16(const uint32_t (&v)[16], float sg,
+                                               uint32_t& lo, uint32_t& hi, uint32_t& scale) {
+  uint32_t amax_b = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t a = v[i] & 0x7FFFFFFFu;
+    amax_b = a > amax_b ? a : amax_b;
+  }
+  scale = block_scale_byte(amax_b, sg);
+  const float s = (scale == 0x7Fu) ? 0.0f : __builtin_amdgcn_cvt_f32_fp8((int)scale, 0);
+  const float unit = s * sg;
+  if (unit > 0x1p-120f && unit < 0x1p120f) {
+    const float r = __builtin_amdgcn_rcpf(unit);          // within 1 ulp of 1/unit
+    const float rl = r * (1.0f - 0x1p-19f), rh = r * (1.0f + 0x1p-19f);
+    uint32_t l0 = 0, l1 = 0, h0 = 0, h1 = 0;
+#define NVFP4_PAIR(dl, dh, i, sel)                                                              \
+    dl = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(dl, __uint_as_float(v[i]) * rl,              \
+                                                  __uint_as_float(v[i + 1]) * rl, 1.0f, sel);  \
+    dh = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(dh, __uint_as_float(v[i]) * rh,              \
+                                                  __uint_as_float(v[i + 1]) * rh, 1.0f, sel)
+    NVFP4_PAIR(l0, h0, 0, 0);
+    NVFP4_PAIR(l0, h0, 2, 1);
+    NVFP4_PAIR(l0, h0, 4, 2);
+    NVFP4_PAIR(l0, h0, 6, 3);
+    NVFP4_PAIR(l1, h1, 8, 0);
+    NVFP4_PAIR(l1, h1, 10, 1);
+    NVFP4_PAIR(l1, h1, 12, 2);
+    NVFP4_PAIR(l1, h1, 14, 3);
+#undef NVFP4_PAIR
+    if (l0 == h0 && l1 == h1) {
+      lo = l0;
+      hi = l1;
+      return;
+    }
+  }
+  encode_block16_exact(v, sg, scale, lo, hi);
+}
+
+// Codes of the EPL (4 or 8) elements one lane holds of a block whose scale
+// byte is known: the same bracketed fast path as encode_block16, falling
+// back to the exact thresholds for this lane's elements.  Returns EPL
+// nibbles, element 2i in the low nibble of byte i.
+template <int EPL>
+__device__ __forceinline__ uint32_t encode_lane(const uint32_t (&v)[EPL], float sg, uint32_t scale) {
+  const float s = (scale == 0x7Fu) ? 0.0f : __builtin_amdgcn_cvt_f32_fp8((int)scale, 0);
+  const float unit = s * sg;
+  if (unit > 0x1p-120f && unit < 0x1p120f) {
+    const float r = __builtin_amdgcn_rcpf(unit);
+    const float rl = r * (1.0f - 0x1p-19f), rh = r * (1.0f + 0x1p-19f);
+    uint32_t l = 0, h = 0;
+#pragma unroll
+    for (int p = 0; p < EPL / 2; ++p) {
+      const float x0 = __uint_as_float(v[2 * p]), x1 = __uint_as_float(v[2 * p + 1]);
+      switch (p) {   // the byte selector must be a constant
+        case 0: l = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(l, x0 * rl, x1 * rl, 1.0f, 0);
+                h = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(h, x0 * rh, x1 * rh, 1.0f, 0); break;
+        case 1: l = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(l, x0 * rl, x1 * rl, 1.0f, 1);
+                h = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(h, x0 * rh, x1 * rh, 1.0f, 1); break;
+        case 2: l = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(l, x0 * rl, x1 * rl, 1.0f, 2);
+                h = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(h, x0 * rh, x1 * rh, 1.0f, 2); break;
+        default: l = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(l, x0 * rl, x1 * rl, 1.0f, 3);
+                 h = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(h, x0 * rh, x1 * rh, 1.0f, 3); break;
+      }
+    }
+    if (l == h) return l;
+  }
+  const double unitd = (scale == 0x7Fu) ? 0.0 : e4m3_value(scale) * (double)sg;
+  const BlockThresholds T = block_thresholds(unitd);
+  uint32_t c = 0;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) c |= encode_element(v[e], T) << (4 * e);
+  return c;
 }
 
 // ---------------------------------------------------------------- decode --

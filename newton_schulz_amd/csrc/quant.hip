@@ -12,7 +12,10 @@ namespace nvfp4 {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kMaxGrid = 256 * 8;  // 8 workgroups per CU for grid-stride passes
+#ifndef NVFP4_QUANT_MAX_GRID
+#define NVFP4_QUANT_MAX_GRID (256 * 8)
+#endif
+constexpr int kMaxGrid = NVFP4_QUANT_MAX_GRID;  // workgroups of the grid-stride passes
 
 typedef float float2_t __attribute__((ext_vector_type(2)));
 
@@ -58,9 +61,7 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(const void* x, int64_t n
   // nvec = number of 16-byte vectors; each holds 4 (F32) or 8 (BF16) values
   const uint4* p = static_cast<const uint4*>(x);
   uint32_t m = 0;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nvec; i += stride) {
-    uint4 w = p[i];
+  auto fold = [&](uint4 w) {
     uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -73,7 +74,15 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(const void* x, int64_t n
         m = a1 > m ? a1 : m;
       }
     }
+  };
+  // four independent 16-byte loads in flight per thread
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  for (; i + 3 * stride < nvec; i += 4 * stride) {
+    const uint4 w0 = p[i], w1 = p[i + stride], w2 = p[i + 2 * stride], w3 = p[i + 3 * stride];
+    fold(w0); fold(w1); fold(w2); fold(w3);
   }
+  for (; i < nvec; i += stride) fold(p[i]);
   m = wave_max(m);
   __shared__ uint32_t red[kThreads / 64];
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
@@ -89,24 +98,64 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(const void* x, int64_t n
 
 // ------------------------------------------------------- row quantizer ----
 
+// Each lane owns 16 bytes of input (8 BF16 or 4 FP32 values), so every
+// load instruction of a wave reads one contiguous kilobyte; the 2 or 4
+// lanes of a block combine their maxima with lane shuffles.  The grid walks
+// the tensor from its end to its start: the amax pass just read it front to
+// back, so the last part it read may still be in the Infinity Cache.
 template <Dt T>
 __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
-    const void* x, int64_t nblk, const uint32_t* amax_slot, float* sg_out,
+    const void* x, int64_t nelem, const uint32_t* amax_slot, float* sg_out,
     uint8_t* codes, uint8_t* scales, uint32_t* zero_slot) {
+  constexpr int EPL = T == Dt::F32 ? 4 : 8;   // elements per lane
+  constexpr int G = 16 / EPL;                 // lanes per block
   const float sg = global_scale_from_amax(*amax_slot);
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     if (sg_out) *sg_out = sg;
     if (zero_slot) *zero_slot = 0u;
   }
+  const int64_t items = nelem / EPL, groups = items / G;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < nblk; b += stride) {
-    uint32_t v[16];
-    load16<T>(x, b * 16, v);
-    uint32_t lo, hi, sc;
-    encode_block16(v, sg, lo, hi, sc);
-    reinterpret_cast<uint2*>(codes)[b] = make_uint2(lo, hi);
-    scales[b] = (uint8_t)sc;
+  auto encode_item = [&](int64_t i, uint4 w) {
+    const int li = (int)(i % G);
+    const int64_t blk = groups - 1 - i / G;
+    const int64_t item = blk * G + li;
+    uint32_t v[EPL];
+    if constexpr (T == Dt::F32) {
+      v[0] = w.x; v[1] = w.y; v[2] = w.z; v[3] = w.w;
+    } else {
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) { v[2 * t] = ws[t] << 16; v[2 * t + 1] = ws[t] & 0xFFFF0000u; }
+    }
+    uint32_t amax = 0;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      const uint32_t a = v[e] & 0x7FFFFFFFu;
+      amax = a > amax ? a : amax;
+    }
+#pragma unroll
+    for (int o = 1; o < G; o <<= 1) {
+      const uint32_t t = __shfl_xor(amax, o, 64);
+      amax = t > amax ? t : amax;
+    }
+    const uint32_t sc = block_scale_byte(amax, sg);
+    const uint32_t c = encode_lane<EPL>(v, sg, sc);
+    if constexpr (EPL == 8) reinterpret_cast<uint32_t*>(codes)[item] = c;
+    else reinterpret_cast<uint16_t*>(codes)[item] = (uint16_t)c;
+    if (li == 0) scales[blk] = (uint8_t)sc;
+  };
+  auto src = [&](int64_t i) {
+    return reinterpret_cast<const uint4*>(x)[(groups - 1 - i / G) * G + i % G];
+  };
+  // two items per lane per trip, both loads issued before either is encoded
+  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  for (; i + stride < items; i += 2 * stride) {
+    const uint4 w0 = src(i), w1 = src(i + stride);
+    encode_item(i, w0);
+    encode_item(i + stride, w1);
   }
+  if (i < items) encode_item(i, src(i));
 }
 
 // ------------------------------------------- tiled quantizer, both axes ----
@@ -165,32 +214,36 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(
 
 // ------------------------------------------------------------ dequant ----
 
-// Round the exact product u * sg (u = q*s has <= 6 significant bits) once
-// to bf16.  hi = RN_f32(u*sg) and the exact error lo decide a bf16 tie;
-// products in or near the f32 subnormal range take the exact double path.
-__device__ __forceinline__ uint16_t product_to_bf16(float u, float sg) {
-  float hi = u * sg;
-  uint32_t b = __float_as_uint(hi);
-  uint32_t ab = b & 0x7FFFFFFFu;
-  if (ab >= 0x7F800000u) return (uint16_t)((b >> 16) | ((ab > 0x7F800000u) ? 0x40u : 0u));
-  if (ab < 0x0D800000u) {                      // |hi| < 2^-100: exact path
-    double d = (double)u * (double)sg;       // exact
-    double a = fabs(d);
-    if (a == 0.0) return (uint16_t)(b >> 16);
-    int E = (int)((__double_as_longlong(a) >> 52) & 0x7FF) - 1023;
-    E = E < -126 ? -126 : E;
-    double r = rint(ldexp(a, 7 - E));         // integer ulps of bf16
-    double v = ldexp(r, E - 7);
-    uint32_t fb = __float_as_uint((float)v);  // exact: v is a bf16 number
-    return (uint16_t)((fb >> 16) | ((d < 0) ? 0x8000u : 0u));
-  }
-  float lo = fmaf(u, sg, -hi);
-  if ((b & 0xFFFFu) == 0x8000u && lo != 0.0f) {
-    // hi sits on a bf16 midpoint but the exact value does not: lo says which way
-    bool up = (lo > 0.0f) == ((b & 0x80000000u) == 0u);
-    return (uint16_t)((b >> 16) + (up ? 1u : 0u));
-  }
-  return (uint16_t)((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
+// Round the exact products u * sg (u = q*s has <= 6 significant bits) once
+// to bf16, two at a time.  hi = RN_f32(u*sg) then RN_bf16(hi) equals the
+// single rounding unless hi landed exactly on a bf16 midpoint (low half
+// 0x8000) or is tiny (the f32 product may have lost bits to underflow);
+// those rare lanes take the exact double path.
+__device__ __forceinline__ uint16_t product_to_bf16_exact(float u, float sg) {
+  const double d = (double)u * (double)sg;   // exact
+  const double a = fabs(d);
+  if (!(a == a)) return 0x7FC0u;
+  if (a == 0.0) return (uint16_t)((__float_as_uint(u * sg)) >> 16);
+  if (a >= 0x1p128) return (uint16_t)(d < 0 ? 0xFF80u : 0x7F80u);
+  int E = (int)((__double_as_longlong(a) >> 52) & 0x7FF) - 1023;
+  E = E < -126 ? -126 : E;
+  const double r = ldexp(rint(ldexp(a, 7 - E)), E - 7);   // RNE at the bf16 ulp
+  if (r >= 0x1p128) return (uint16_t)(d < 0 ? 0xFF80u : 0x7F80u);
+  const uint32_t fb = __float_as_uint((float)r);           // r is a bf16 number
+  return (uint16_t)((fb >> 16) | (d < 0 ? 0x8000u : 0u));
+}
+
+__device__ __forceinline__ uint32_t products_to_bf16x2(float u0, float u1, float sg) {
+  const float h0 = u0 * sg, h1 = u1 * sg;
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t r = {(__bf16)h0, (__bf16)h1};             // hardware RNE
+  uint32_t out = __builtin_bit_cast(uint32_t, r);
+  const uint32_t b0 = __float_as_uint(h0), b1 = __float_as_uint(h1);
+  const bool bad0 = (b0 & 0xFFFFu) == 0x8000u || (b0 & 0x7F800000u) < 0x0D800000u;
+  const bool bad1 = (b1 & 0xFFFFu) == 0x8000u || (b1 & 0x7F800000u) < 0x0D800000u;
+  if (bad0) out = (out & 0xFFFF0000u) | product_to_bf16_exact(u0, sg);
+  if (bad1) out = (out & 0x0000FFFFu) | ((uint32_t)product_to_bf16_exact(u1, sg) << 16);
+  return out;
 }
 
 // Values of the 16 codes of one block (exact f32 q*s; the tensor scale is
@@ -224,23 +277,40 @@ __device__ __forceinline__ void store16(void* out, int64_t idx, const float (&u)
     for (int j = 0; j < 2; ++j) {
       uint32_t w[4];
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-        w[t] = (uint32_t)product_to_bf16(u[8 * j + 2 * t], sg) |
-               ((uint32_t)product_to_bf16(u[8 * j + 2 * t + 1], sg) << 16);
+      for (int t = 0; t < 4; ++t) w[t] = products_to_bf16x2(u[8 * j + 2 * t], u[8 * j + 2 * t + 1], sg);
       p[j] = make_uint4(w[0], w[1], w[2], w[3]);
     }
   }
 }
 
+// Each lane writes 16 bytes (8 BF16 or 4 FP32 values) of one block, so every
+// store instruction of a wave covers one contiguous kilobyte.
 template <Dt O>
 __global__ __launch_bounds__(kThreads) void dequant_rows_kernel(
-    const uint8_t* codes, const uint8_t* scales, const float* sgp, int64_t nblk, void* out) {
+    const uint8_t* codes, const uint8_t* scales, const float* sgp, int64_t nelem, void* out) {
+  constexpr int EPL = O == Dt::F32 ? 4 : 8;
+  constexpr int G = 16 / EPL;
   const float sg = *sgp;
+  const int64_t items = nelem / EPL;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < nblk; b += stride) {
-    float u[16];
-    decode_block(reinterpret_cast<const uint2*>(codes)[b], scales[b], u);
-    store16<O>(out, b * 16, u, sg);
+  for (int64_t item = (int64_t)blockIdx.x * kThreads + threadIdx.x; item < items; item += stride) {
+    const float s = __builtin_amdgcn_cvt_f32_fp8((int)scales[item / G], 0);
+    if constexpr (O == Dt::BF16) {
+      float u[8];
+      decode_word(reinterpret_cast<const uint32_t*>(codes)[item], s, u);
+      uint4 r;
+      r.x = products_to_bf16x2(u[0], u[1], sg);
+      r.y = products_to_bf16x2(u[2], u[3], sg);
+      r.z = products_to_bf16x2(u[4], u[5], sg);
+      r.w = products_to_bf16x2(u[6], u[7], sg);
+      reinterpret_cast<uint4*>(out)[item] = r;
+    } else {
+      const uint32_t w = reinterpret_cast<const uint16_t*>(codes)[item];
+      const float2_t q0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+      const float2_t q1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+      reinterpret_cast<float4*>(out)[item] =
+          make_float4(q0[0] * s * sg, q0[1] * s * sg, q1[0] * s * sg, q1[1] * s * sg);
+    }
   }
 }
 
@@ -297,12 +367,13 @@ hipError_t launch_amax(const void* x, Dt xt, int64_t n, uint32_t* slot, hipStrea
 hipError_t launch_quant_rows(const void* x, Dt xt, int64_t rows, int64_t cols,
                              const uint32_t* amax_slot, float* sg_out, uint8_t* codes,
                              uint8_t* scales, uint32_t* zero_slot, hipStream_t s) {
-  const int64_t nblk = rows * cols / 16;
-  const int grid = grid_for(nblk, kThreads * 2);
+  const int64_t nelem = rows * cols;
   if (xt == Dt::F32)
-    quant_rows_kernel<Dt::F32><<<grid, kThreads, 0, s>>>(x, nblk, amax_slot, sg_out, codes, scales, zero_slot);
+    quant_rows_kernel<Dt::F32><<<grid_for(nelem / 4, kThreads * 4), kThreads, 0, s>>>(
+        x, nelem, amax_slot, sg_out, codes, scales, zero_slot);
   else
-    quant_rows_kernel<Dt::BF16><<<grid, kThreads, 0, s>>>(x, nblk, amax_slot, sg_out, codes, scales, zero_slot);
+    quant_rows_kernel<Dt::BF16><<<grid_for(nelem / 8, kThreads * 4), kThreads, 0, s>>>(
+        x, nelem, amax_slot, sg_out, codes, scales, zero_slot);
   return hipGetLastError();
 }
 
@@ -331,12 +402,13 @@ hipError_t launch_quant_tiles(const void* x, Dt xt, int64_t rows, int64_t cols,
 
 hipError_t launch_dequant_rows(const uint8_t* codes, const uint8_t* scales, const float* sg,
                                int64_t rows, int64_t cols, void* out, Dt ot, hipStream_t s) {
-  const int64_t nblk = rows * cols / 16;
-  const int grid = grid_for(nblk, kThreads * 2);
+  const int64_t nelem = rows * cols;
   if (ot == Dt::F32)
-    dequant_rows_kernel<Dt::F32><<<grid, kThreads, 0, s>>>(codes, scales, sg, nblk, out);
+    dequant_rows_kernel<Dt::F32><<<grid_for(nelem / 4, kThreads * 4), kThreads, 0, s>>>(
+        codes, scales, sg, nelem, out);
   else
-    dequant_rows_kernel<Dt::BF16><<<grid, kThreads, 0, s>>>(codes, scales, sg, nblk, out);
+    dequant_rows_kernel<Dt::BF16><<<grid_for(nelem / 8, kThreads * 4), kThreads, 0, s>>>(
+        codes, scales, sg, nelem, out);
   return hipGetLastError();
 }
 

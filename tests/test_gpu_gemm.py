@@ -137,3 +137,28 @@ def test_full_size_gemms_sampled():
     want = 3.4445 * X[ii, jj].astype(np.float64) + np.sum(dbi * dxc, axis=1)
     got = Xg[ii, jj]
     assert np.linalg.norm(got - want) <= TOL * np.linalg.norm(want)
+
+
+def test_symmetric_gemm_split_k():
+    """A symmetric product long enough in K to be split (two K halves whose
+    FP32 partials a second kernel sums in order)."""
+    M, K = 384, 8192
+    assert ns.nvfp4_gemm_workspace_bytes(M, M, K, True) > 0       # split schedule
+    rng = np.random.default_rng(8)
+    X = rng.standard_normal((M, K))
+    q = Q.quantize_rows(X)
+    dq = Q.dequantize_rows(q)
+    want = N.gemm_nt(dq, dq)
+    qd = dev_q(q)
+    add = rng.standard_normal((M, M))
+    add = (add + add.T).astype(np.float32)
+    slot = _amax_slot()
+    got = host(ns.nvfp4_gemm(qd, qd, M, M, K, symmetric=True, alpha=0.75, beta=-1.5,
+                             addend=to_dev_f32(add), amax_out=slot))
+    assert np.array_equal(got, got.T)
+    assert rel_fro(got, 0.75 * want - 1.5 * add.astype(np.float64)) <= TOL
+    _check_amax(slot, got)
+    # the same product unsplit (no workspace) agrees to accumulation order
+    got1 = host(ns.nvfp4_gemm(qd, qd, M, M, K, symmetric=True, alpha=0.75, beta=-1.5,
+                              addend=to_dev_f32(add), split=False))
+    assert rel_fro(got1, got) <= 1e-6
