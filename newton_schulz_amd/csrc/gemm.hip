@@ -31,6 +31,10 @@
 #include "launch.hpp"
 #include "nvfp4_device.hpp"
 
+#ifndef NVFP4_SCHED
+#define NVFP4_SCHED 0
+#endif
+
 namespace nvfp4 {
 namespace {
 
@@ -55,7 +59,8 @@ struct Cfg {
   static constexpr int BM = WM * FM * 32, BN = WN * FN * 32;
   static constexpr int GP = BM / 32, GQ = BN / 32;   // 32-row groups per operand
   static constexpr int kGroups = GP + GQ;
-  static constexpr int kCodeBytes = kGroups * kHalves * 1024;
+  static constexpr int kRegions = kGroups * kHalves;  // 1 KB code regions per stage
+  static constexpr int kCodeBytes = kRegions * 1024;
   static constexpr int kScaleBytes = kGroups * 256;
   static constexpr int kStage = kCodeBytes + kScaleBytes;
   static constexpr int kAcc = FM * FN * 16;           // accumulators per lane
@@ -66,9 +71,14 @@ struct Cfg {
 #else
   static constexpr int kMinBlocks = NVFP4_MIN_BLOCKS;
 #endif
-  // DMA instructions each wave issues per stage (code regions + scale rows)
-  static_assert((kGroups * kHalves) % kWaves == 0 && kGroups % kWaves == 0, "uneven stage split");
-  static constexpr int kLoadsPerWave = (kGroups * kHalves) / kWaves + kGroups / kWaves;
+  // DMA instructions each wave issues per stage.  Regions are dealt out
+  // round-robin; when they do not divide evenly, a wave with one fewer
+  // repeats its previous load (same bytes to the same LDS address) so that
+  // every wave waits on the same count.
+  static_assert(kRegions >= kWaves && kGroups >= kWaves, "fewer regions than waves");
+  static constexpr int kCodeLoads = (kRegions + kWaves - 1) / kWaves;
+  static constexpr int kScaleLoads = (kGroups + kWaves - 1) / kWaves;
+  static constexpr int kLoadsPerWave = kCodeLoads + kScaleLoads;
 };
 
 struct FastArgs {
@@ -108,72 +118,80 @@ __device__ __forceinline__ void tile_of(int64_t t, int64_t TM, int64_t TN, int64
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds)
+__device__ __forceinline__ void dma16(const uint8_t* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds)
                : "memory", "m0");
 }
-__device__ __forceinline__ void dma4(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(lds)
+__device__ __forceinline__ void dma4(const uint8_t* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(base), "s"(lds)
                : "memory", "m0");
 }
 
-// Which byte of the lane's scale dword covers MFMA steps 2b, 2b+1 of
-// half-stage hs: a 16-byte slice holds 32 codes = 2 blocks.
-template <class C>
-__device__ __forceinline__ int scale_byte(int hs, int lane, int b) {
-  if constexpr (C::BK == 128) return 2 * hs + b;     // dword = blocks 4h..4h+3
-  else return 2 * (lane >> 5) + b;                   // dword = blocks 0..3 of the row
-}
-
-// Per-lane DMA sources of the regions this wave loads, at k = 0, and their
-// offsets inside a stage.  Computed once per tile; each stage then adds its
-// K offset.  Rows past the matrix edge are clamped to the last row: they
-// feed only outputs that the epilogue masks.
+// Per-lane DMA sources of the regions this wave loads, as byte offsets from
+// the operand's base at k = 0 (codes < 2^30 bytes, checked at the API); the
+// base, advanced by each stage's K offset, is wave-uniform and lives in
+// scalar registers.  Rows past the matrix edge are clamped to the last row:
+// they feed only outputs that the epilogue masks.
 template <class C>
 struct StageSrc {
-  static constexpr int kCode = C::kGroups * C::kHalves / C::kWaves;
-  static constexpr int kScale = C::kGroups / C::kWaves;
-  const uint8_t* code[kCode];
-  const uint8_t* scale[kScale];
+  uint32_t code[C::kCodeLoads];
+  uint32_t scale[C::kScaleLoads];
 };
+
+template <class C>
+__device__ __forceinline__ int code_region(int wave, int q) {
+  const int r = wave + q * C::kWaves;
+  return r < C::kRegions ? r : r - C::kWaves;
+}
+template <class C>
+__device__ __forceinline__ int scale_group(int wave, int q) {
+  const int r = wave + q * C::kWaves;
+  return r < C::kGroups ? r : r - C::kWaves;
+}
 
 template <class C>
 __device__ __forceinline__ void init_sources(const GemmProblem& g, int64_t m0, int64_t n0, int wave,
                                              int lane, StageSrc<C>& src) {
   const int64_t kb = g.K / 2, sb = g.K / 16;
 #pragma unroll
-  for (int q = 0; q < StageSrc<C>::kCode; ++q) {
-    const int r = wave + q * C::kWaves, grp = r / C::kHalves, hs = r % C::kHalves;
+  for (int q = 0; q < C::kCodeLoads; ++q) {
+    const int r = code_region<C>(wave, q), grp = r / C::kHalves, hs = r % C::kHalves;
     const bool isP = grp < C::GP;
     int64_t row = (isP ? m0 + 32 * grp : n0 + 32 * (grp - C::GP)) + (lane & 31);
     const int64_t lim = isP ? g.M : g.N;
     row = row < lim ? row : lim - 1;
     // lane half h owns bytes [h*BK/4, (h+1)*BK/4) of the row's BK/2 stage bytes
-    src.code[q] = (isP ? g.codes_p : g.codes_q) + row * kb + (C::BK / 4) * (lane >> 5) + 16 * hs;
+    src.code[q] = (uint32_t)(row * kb + (C::BK / 4) * (lane >> 5) + 16 * hs);
   }
 #pragma unroll
-  for (int q = 0; q < StageSrc<C>::kScale; ++q) {
-    const int grp = wave + q * C::kWaves;
+  for (int q = 0; q < C::kScaleLoads; ++q) {
+    const int grp = scale_group<C>(wave, q);
     const bool isP = grp < C::GP;
     int64_t row = (isP ? m0 + 32 * grp : n0 + 32 * (grp - C::GP)) + (lane & 31);
     const int64_t lim = isP ? g.M : g.N;
     row = row < lim ? row : lim - 1;
     // BK = 128: 8 scale bytes per row and stage, lane half h loads its 4;
     // BK = 64: 4 bytes per row, both halves load them and pick their 2
-    src.scale[q] = (isP ? g.scales_p : g.scales_q) + row * sb + (C::BK == 128 ? 4 * (lane >> 5) : 0);
+    src.scale[q] = (uint32_t)(row * sb + (C::BK == 128 ? 4 * (lane >> 5) : 0));
   }
 }
 
 template <class C>
-__device__ __forceinline__ void issue_stage(const StageSrc<C>& src, int64_t k0, uint8_t* stage,
-                                            int wave) {
+__device__ __forceinline__ void issue_stage(const GemmProblem& g, const StageSrc<C>& src, int64_t k0,
+                                            uint8_t* stage, int wave) {
   const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(stage));
 #pragma unroll
-  for (int q = 0; q < StageSrc<C>::kCode; ++q)
-    dma16(src.code[q] + k0 / 2, base + (uint32_t)(wave + q * C::kWaves) * 1024u);
+  for (int q = 0; q < C::kCodeLoads; ++q) {
+    const int r = code_region<C>(wave, q);
+    const uint8_t* op = (r / C::kHalves < C::GP ? g.codes_p : g.codes_q) + k0 / 2;
+    dma16(op, src.code[q], base + (uint32_t)r * 1024u);
+  }
 #pragma unroll
-  for (int q = 0; q < StageSrc<C>::kScale; ++q)
-    dma4(src.scale[q] + k0 / 16, base + (uint32_t)C::kCodeBytes + (uint32_t)(wave + q * C::kWaves) * 256u);
+  for (int q = 0; q < C::kScaleLoads; ++q) {
+    const int grp = scale_group<C>(wave, q);
+    const uint8_t* op = (grp < C::GP ? g.scales_p : g.scales_q) + k0 / 16;
+    dma4(op, src.scale[q], base + (uint32_t)C::kCodeBytes + (uint32_t)grp * 256u);
+  }
 }
 
 // out = beta * addend + alpha * sgP * sgQ * acc for the tile at (m0, n0);
@@ -181,9 +199,15 @@ __device__ __forceinline__ void issue_stage(const StageSrc<C>& src, int64_t k0, 
 // written values goes to amax_out.  Offsets inside a tile are 32-bit
 // (BM * N < 2^31 is checked at the API); tiles wholly inside the matrix
 // (and, if symmetric, wholly above the diagonal) skip the per-element tests.
-template <class C, bool SYM, bool PRE>
+//
+// The addend may be the output itself, so the compiler must keep every
+// store after the loads it could alias; the 16 addend loads of each 32 x 32
+// sub-tile are therefore issued together before any of its stores: one
+// memory round trip per sub-tile instead of one per element.  This
+// is safe in place: each position is read only by the lane that writes it,
+// and mirrored stores land below the diagonal, which no tile reads.
+template <class C, bool SYM>
 __device__ __forceinline__ void epilogue(const GemmProblem& g, floatx16 (&acc)[C::FM][C::FN],
-                                         const floatx16 (&pre)[C::FM][C::FN],
                                          int64_t m0, int64_t n0, int wm, int wn, int lane) {
   const float scale = g.alpha * (*g.sg_p) * (*g.sg_q);
   const float beta = g.beta;
@@ -196,11 +220,24 @@ __device__ __forceinline__ void epilogue(const GemmProblem& g, floatx16 (&acc)[C
   float* mbase = g.out + c0 * g.N + r0;                // mirror: (col, row)
   const bool inside = m0 + C::BM <= g.M && n0 + C::BN <= g.N;
   const bool upper = !SYM || (m0 + C::BM <= n0);       // every element has row < col
+  auto valid = [&](int dr, int j) {
+    if (inside && upper) return true;
+    const int64_t row = r0 + dr, col = c0 + j * 32;
+    return row < g.M && col < g.N && (!SYM || row <= col);
+  };
   uint32_t amax = 0;
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-    for (int j = 0; j < C::FN; ++j)
+    for (int j = 0; j < C::FN; ++j) {
+      float ad[16];
+      if (abase) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int dr = i * 32 + 8 * (r >> 2) + (r & 3);
+          ad[r] = valid(dr, j) ? abase[dr * N + j * 32] : 0.0f;
+        }
+      }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         float v4[4];
@@ -208,20 +245,10 @@ __device__ __forceinline__ void epilogue(const GemmProblem& g, floatx16 (&acc)[C
         for (int t = 0; t < 4; ++t) {
           const int r = 4 * q + t;
           const int dr = i * 32 + 8 * q + t;           // row offset from r0
-          const int off = dr * N + j * 32;
-          bool ok = true;
-          if (!(inside && upper)) {
-            const int64_t row = r0 + dr, col = c0 + j * 32;
-            ok = row < g.M && col < g.N && (!SYM || row <= col);
-          }
           float v = scale * acc[i][j][r];
-          if (ok) {
-            if constexpr (PRE) {
-              v = fmaf(beta, pre[i][j][r], v);
-            } else {
-              if (abase) v = fmaf(beta, abase[off], v);
-            }
-            obase[off] = v;
+          if (abase) v = fmaf(beta, ad[r], v);
+          if (valid(dr, j)) {
+            obase[dr * N + j * 32] = v;
             const uint32_t ab = abs_bits(v);
             amax = ab > amax ? ab : amax;
           }
@@ -241,30 +268,12 @@ __device__ __forceinline__ void epilogue(const GemmProblem& g, floatx16 (&acc)[C
           }
         }
       }
+    }
   if (g.amax_out) amax_publish(amax, g.amax_out);
 }
 
-// The addend values this lane's epilogue will need, loaded before the K loop
-// so that their latency hides under it (rows/cols past the edge read 0).
-template <class C>
-__device__ __forceinline__ void prefetch_addend(const GemmProblem& g, floatx16 (&pre)[C::FM][C::FN],
-                                                int64_t m0, int64_t n0, int wm, int wn, int lane) {
-  const int h = lane >> 5, c32 = lane & 31;
-#pragma unroll
-  for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-    for (int j = 0; j < C::FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = m0 + (wm * C::FM + i) * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        const int64_t col = n0 + (wn * C::FN + j) * 32 + c32;
-        pre[i][j][r] = (row < g.M && col < g.N) ? g.addend[row * g.N + col] : 0.0f;
-      }
-}
-
-template <class C, bool SYM, bool PRE>
+template <class C, bool SYM>
 __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_fast_kernel(FastArgs a) {
-  // PRE: the launch has an addend and no K split, so the epilogue runs here
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::NST * C::kStage];
   const GemmProblem& g = a.g;
 
@@ -290,18 +299,17 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_fast_kernel(F
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  floatx16 pre[C::FM][C::FN];
-  if constexpr (PRE) prefetch_addend<C>(g, pre, m0, n0, wm, wn, lane);
   StageSrc<C> src;
   init_sources<C>(g, m0, n0, wave, lane, src);
 
   const int64_t nk_all = g.K / C::BK;
   const int64_t kc0 = nk_all * split / a.splits, kc1 = nk_all * (split + 1) / a.splits;
 
+
   // prologue: stages kc0 .. kc0 + NST - 2 in flight
 #pragma unroll
   for (int p = 0; p < C::NST - 1; ++p)
-    if (kc0 + p < kc1) issue_stage<C>(src, (kc0 + p) * C::BK, smem + p * C::kStage, wave);
+    if (kc0 + p < kc1) issue_stage<C>(g, src, (kc0 + p) * C::BK, smem + p * C::kStage, wave);
 
   for (int64_t kc = kc0; kc < kc1; ++kc) {
     // wait for this wave's loads of stage kc (later stages may stay in
@@ -314,10 +322,12 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_fast_kernel(F
     }
     __syncthreads();
     if (kc + C::NST - 1 < kc1)
-      issue_stage<C>(src, (kc + C::NST - 1) * C::BK,
+      issue_stage<C>(g, src, (kc + C::NST - 1) * C::BK,
                      smem + ((kc - kc0 + C::NST - 1) % C::NST) * C::kStage, wave);
     const uint8_t* st = smem + ((kc - kc0) % C::NST) * C::kStage;
 
+    // this lane's scale dword per fragment: blocks 4h..4h+3 of the stage
+    // (BK = 128) or the row's 4 blocks (BK = 64), as E4M3 bytes
     uint32_t sp[C::FM], sq[C::FN];
 #pragma unroll
     for (int i = 0; i < C::FM; ++i)
@@ -325,41 +335,70 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_fast_kernel(F
 #pragma unroll
     for (int j = 0; j < C::FN; ++j)
       sq[j] = *reinterpret_cast<const uint32_t*>(st + C::kCodeBytes + (C::GP + wn * C::FN + j) * 256 + 4 * lane);
+    if constexpr (C::BK == 64) {
+      // this lane half's two blocks into the low half-word
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i) sp[i] >>= 16 * (lane >> 5);
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) sq[j] >>= 16 * (lane >> 5);
+    }
 
 #pragma unroll
     for (int hs = 0; hs < C::kHalves; ++hs) {
       uint4 cp[C::FM], cq[C::FN];
-      half2_t spf[C::FM][2], sqf[C::FN][2];
+      half2_t spf[C::FM], sqf[C::FN];   // the half-stage's two block scales as f16
 #pragma unroll
       for (int i = 0; i < C::FM; ++i) {
         cp[i] = *reinterpret_cast<const uint4*>(st + ((wm * C::FM + i) * C::kHalves + hs) * 1024 + 16 * lane);
-        spf[i][0] = scale_pair_f16((sp[i] >> (8 * scale_byte<C>(hs, lane, 0))) & 0xFFu);
-        spf[i][1] = scale_pair_f16((sp[i] >> (8 * scale_byte<C>(hs, lane, 1))) & 0xFFu);
+        spf[i] = scale_pair2_f16(sp[i], hs);
       }
 #pragma unroll
       for (int j = 0; j < C::FN; ++j) {
         cq[j] = *reinterpret_cast<const uint4*>(st + ((C::GP + wn * C::FN + j) * C::kHalves + hs) * 1024 + 16 * lane);
-        sqf[j][0] = scale_pair_f16((sq[j] >> (8 * scale_byte<C>(hs, lane, 0))) & 0xFFu);
-        sqf[j][1] = scale_pair_f16((sq[j] >> (8 * scale_byte<C>(hs, lane, 1))) & 0xFFu);
+        sqf[j] = scale_pair2_f16(sq[j], hs);
       }
+      // software pipeline: step s + 1 is dequantized while step s multiplies
+      half8_t av[C::FM], bv[C::FN];
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i) av[i] = dequant8_f16(cp[i].x, splat_lo(spf[i]));
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) bv[j] = dequant8_f16(cq[j].x, splat_lo(sqf[j]));
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        half8_t av[C::FM], bv[C::FN];
+        half8_t an[C::FM], bn[C::FN];
+        if (s < 3) {
 #pragma unroll
-        for (int i = 0; i < C::FM; ++i) {
-          const uint32_t w = s == 0 ? cp[i].x : s == 1 ? cp[i].y : s == 2 ? cp[i].z : cp[i].w;
-          av[i] = dequant8_f16(w, spf[i][s >> 1]);
-        }
+          for (int i = 0; i < C::FM; ++i) {
+            const uint32_t w = s == 0 ? cp[i].y : s == 1 ? cp[i].z : cp[i].w;
+            an[i] = dequant8_f16(w, s + 1 < 2 ? splat_lo(spf[i]) : splat_hi(spf[i]));
+          }
 #pragma unroll
-        for (int j = 0; j < C::FN; ++j) {
-          const uint32_t w = s == 0 ? cq[j].x : s == 1 ? cq[j].y : s == 2 ? cq[j].z : cq[j].w;
-          bv[j] = dequant8_f16(w, sqf[j][s >> 1]);
+          for (int j = 0; j < C::FN; ++j) {
+            const uint32_t w = s == 0 ? cq[j].y : s == 1 ? cq[j].z : cq[j].w;
+            bn[j] = dequant8_f16(w, s + 1 < 2 ? splat_lo(sqf[j]) : splat_hi(sqf[j]));
+          }
         }
 #pragma unroll
         for (int i = 0; i < C::FM; ++i)
 #pragma unroll
           for (int j = 0; j < C::FN; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
+#if NVFP4_SCHED
+        if (s < 3) {
+          // interleave: after each MFMA, a share of the next step's dequant
+#pragma unroll
+          for (int t = 0; t < C::FM * C::FN; ++t) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, NVFP4_SCHED, 0);
+          }
+        }
+#endif
+        if (s < 3) {
+#pragma unroll
+          for (int i = 0; i < C::FM; ++i) av[i] = an[i];
+#pragma unroll
+          for (int j = 0; j < C::FN; ++j) bv[j] = bn[j];
+        }
       }
     }
   }
@@ -378,7 +417,7 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_fast_kernel(F
           part[((i * C::FN + j) * 16 + r) * C::kThreads + threadIdx.x] = acc[i][j][r];
     return;
   }
-  epilogue<C, SYM, PRE>(g, acc, pre, m0, n0, wm, wn, lane);
+  epilogue<C, SYM>(g, acc, m0, n0, wm, wn, lane);
 }
 
 // Sum the split-K partials of one tile in split order, then the epilogue.
@@ -406,8 +445,7 @@ __global__ __launch_bounds__(C::kThreads) void gemm_reduce_kernel(FastArgs a) {
           v += base[((size_t)sp * C::kAcc + e) * C::kThreads + threadIdx.x];
         acc[i][j][r] = v;
       }
-  const floatx16 (&none)[C::FM][C::FN] = acc;   // unused: the addend is read in place
-  epilogue<C, SYM, false>(a.g, acc, none, I * C::BM, J * C::BN, wm, wn, lane);
+  epilogue<C, SYM>(a.g, acc, I * C::BM, J * C::BN, wm, wn, lane);
 }
 
 // ===========================================================================
@@ -600,7 +638,10 @@ using FastCfg = Cfg<NVFP4_FAST_WM, NVFP4_FAST_WN, NVFP4_FAST_FM, NVFP4_FAST_FN, 
 constexpr int64_t kTargetUnits = NVFP4_TARGET_UNITS;
 // a split must keep at least 4096 of K: shorter splits cost more in FP32
 // partial traffic and the reduce launch than the extra parallelism returns
-constexpr int64_t kMinKPerSplit = 4096;
+#ifndef NVFP4_MIN_K_SPLIT
+#define NVFP4_MIN_K_SPLIT 4096
+#endif
+constexpr int64_t kMinKPerSplit = NVFP4_MIN_K_SPLIT;
 
 int64_t sym_tiles(int64_t TM, int64_t TN, int64_t BM, int64_t BN) {
   int64_t t = 0;
@@ -660,14 +701,10 @@ hipError_t launch_gemm(const GemmProblem& g, const GemmPlan& p, float* partials,
   a.units = p.units;
   a.partials = p.splits > 1 ? partials : nullptr;
   const int64_t grid = (p.units + kXcds - 1) / kXcds * kXcds;
-  const bool pre = false;   // register prefetch of the addend costs occupancy; measured slower
-  if (g.symmetric) {
-    if (pre) gemm_fast_kernel<FastCfg, true, true><<<dim3((unsigned)grid), FastCfg::kThreads, 0, s>>>(a);
-    else gemm_fast_kernel<FastCfg, true, false><<<dim3((unsigned)grid), FastCfg::kThreads, 0, s>>>(a);
-  } else {
-    if (pre) gemm_fast_kernel<FastCfg, false, true><<<dim3((unsigned)grid), FastCfg::kThreads, 0, s>>>(a);
-    else gemm_fast_kernel<FastCfg, false, false><<<dim3((unsigned)grid), FastCfg::kThreads, 0, s>>>(a);
-  }
+  if (g.symmetric)
+    gemm_fast_kernel<FastCfg, true><<<dim3((unsigned)grid), FastCfg::kThreads, 0, s>>>(a);
+  else
+    gemm_fast_kernel<FastCfg, false><<<dim3((unsigned)grid), FastCfg::kThreads, 0, s>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
   const int64_t rgrid = (p.tiles + kXcds - 1) / kXcds * kXcds;

@@ -245,6 +245,15 @@ __device__ __forceinline__ half2_t scale_pair_f16(uint32_t byte) {
   return r;
 }
 
+// Bytes 2w and 2w+1 of a dword of E4M3 scale bytes as an f16 pair (the
+// hardware FP8 decode with unit scale is exact).
+__device__ __forceinline__ half2_t scale_pair2_f16(uint32_t dword, int w) {
+  return w == 0 ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(dword, 1.0f, false)
+                : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(dword, 1.0f, true);
+}
+__device__ __forceinline__ half2_t splat_lo(half2_t v) { half2_t r = {v[0], v[0]}; return r; }
+__device__ __forceinline__ half2_t splat_hi(half2_t v) { half2_t r = {v[1], v[1]}; return r; }
+
 // Eight E2M1 codes (one dword, element 2i in the low nibble of byte i) times
 // the block scale, as eight f16 values.  The conversion instruction yields
 // the exact E2M1 value (its scale operand is 1); the packed f16 multiply is
