@@ -632,8 +632,11 @@ __global__ __launch_bounds__(GThreads, 2) void gemm_general_kernel(GemmProblem g
 using FastCfg = Cfg<NVFP4_FAST_WM, NVFP4_FAST_WN, NVFP4_FAST_FM, NVFP4_FAST_FN, NVFP4_FAST_NST,
                     NVFP4_FAST_BK>;
 
+// Symmetric products are split along K only while the tiles alone would
+// leave CUs idle: the FP32 partials and the reduce pass cost more than the
+// extra parallelism returns once every CU has a tile.
 #ifndef NVFP4_TARGET_UNITS
-#define NVFP4_TARGET_UNITS 512   // 256 CUs x 2 resident workgroups
+#define NVFP4_TARGET_UNITS 256   // MI355X compute units
 #endif
 constexpr int64_t kTargetUnits = NVFP4_TARGET_UNITS;
 // a split must keep at least 4096 of K: shorter splits cost more in FP32

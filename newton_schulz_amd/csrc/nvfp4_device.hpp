@@ -89,47 +89,74 @@ __device__ __forceinline__ uint32_t ceil_f32_bits(double d) {
 }
 
 // Integer thresholds of one block: magnitude code = number of k with
-// bits(|x|) > T[k].  Midpoint k lies between codes k and k+1: for even k
+// bits(|x|) > t_k.  Midpoint k lies between codes k and k+1: for even k
 // the value must exceed it (tie stays on the even code k), for odd k it
-// must reach it (tie moves to the even code k+1).
+// must reach it (tie moves to the even code k+1).  Seven named fields, not
+// an array, so that nothing is indexed at run time.
 struct BlockThresholds {
-  uint32_t t[7];
+  uint32_t t0, t1, t2, t3, t4, t5, t6;
 };
+
+__device__ __forceinline__ uint32_t midpoint_threshold(double mid, double unit, bool odd) {
+  const double thr = mid * unit;            // exact
+  return odd ? ceil_f32_bits(thr) - 1u : floor_f32_bits(thr);
+}
 
 __device__ __forceinline__ BlockThresholds block_thresholds(double unit /* s * s_g */) {
   BlockThresholds T;
   if (!(unit > 0.0)) {                      // zero scale, zero or NaN s_g
-#pragma unroll
-    for (int k = 0; k < 7; ++k) T.t[k] = 0xFFFFFFFFu;
+    T.t0 = T.t1 = T.t2 = T.t3 = T.t4 = T.t5 = T.t6 = 0xFFFFFFFFu;
     return T;
   }
-  const double mid[7] = {0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0};
-#pragma unroll
-  for (int k = 0; k < 7; ++k) {
-    double thr = mid[k] * unit;             // exact
-    T.t[k] = (k & 1) ? ceil_f32_bits(thr) - 1u : floor_f32_bits(thr);
-  }
+  // E2M1 midpoints 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5
+  T.t0 = midpoint_threshold(0.25, unit, false);
+  T.t1 = midpoint_threshold(0.75, unit, true);
+  T.t2 = midpoint_threshold(1.25, unit, false);
+  T.t3 = midpoint_threshold(1.75, unit, true);
+  T.t4 = midpoint_threshold(2.5, unit, false);
+  T.t5 = midpoint_threshold(3.5, unit, true);
+  T.t6 = midpoint_threshold(5.0, unit, false);
   return T;
 }
 
-// 4-bit code of one element (sign bit from the raw float bits).  The
-// thresholds are non-decreasing, so the count of those below |x| is found
-// by a three-step binary search: T3 splits codes 0-3 from 4-7, then T5 or
-// T1, then T6/T4/T2/T0.
+// 4-bit code of one element (sign bit from the raw float bits): the
+// magnitude is the count of thresholds below |x|.
 __device__ __forceinline__ uint32_t encode_element(uint32_t raw_bits, const BlockThresholds& T) {
   const uint32_t a = raw_bits & 0x7FFFFFFFu;
-  const bool hi = a > T.t[3];
-  const bool mid = a > (hi ? T.t[5] : T.t[1]);
-  const uint32_t t2 = hi ? (mid ? T.t[6] : T.t[4]) : (mid ? T.t[2] : T.t[0]);
-  const uint32_t c = (hi ? 4u : 0u) | (mid ? 2u : 0u) | (a > t2 ? 1u : 0u);
+  const uint32_t c = (uint32_t)(a > T.t0) + (uint32_t)(a > T.t1) + (uint32_t)(a > T.t2) +
+                     (uint32_t)(a > T.t3) + (uint32_t)(a > T.t4) + (uint32_t)(a > T.t5) +
+                     (uint32_t)(a > T.t6);
   return c | ((raw_bits >> 28) & 8u);
 }
 
-// Scale byte of a block with maximum |x| = amax_b (as float bits) under s_g.
+// RNE to E4M3FN of a non-negative finite float, saturating at 448 (0x7E).
+// Below 2^-6 the E4M3 grid is uniform with step 2^-9, so the byte is the
+// RNE integer of x * 2^9 (a value of 8 is the byte of 2^-6); above, the
+// float's mantissa is rounded to 3 bits in place (a carry moves the
+// exponent) and the exponent rebased from 127 to 7.
+__device__ __forceinline__ uint32_t e4m3_rne_sat_f32(float x) {
+  if (!(x < 448.0f)) return 0x7Eu;
+  if (x < 0x1p-6f) return (uint32_t)__builtin_rintf(x * 512.0f);
+  const uint32_t b = __float_as_uint(x);
+  return ((b + 0x7FFFFu + ((b >> 20) & 1u)) >> 20) - ((127u - 7u) << 3);
+}
+
+// Scale byte of a block with maximum |x| = amax_b (as float bits) under s_g:
+// RNE_E4M3(amax_b / (6 s_g)) of the exact quotient.  Fast path: the float
+// quotient through the hardware reciprocal is within 2^-22 relative of the
+// exact one; widened by 2^-19 either way it brackets it, and when both ends
+// round to the same byte (rounding is monotone) that byte is exact.
+// Otherwise, or for extreme s_g, the exact double quotient decides.
 __device__ __forceinline__ uint32_t block_scale_byte(uint32_t amax_b_bits, float sg) {
   if (sg != sg) return 0x7Fu;               // NaN tensor
   if (sg == 0.0f) return 0u;
-  double q = (double)__uint_as_float(amax_b_bits) / (6.0 * (double)sg);
+  if (sg > 0x1p-100f && sg < 0x1p100f) {
+    const float q = __uint_as_float(amax_b_bits) * __builtin_amdgcn_rcpf(6.0f * sg);
+    const uint32_t lo = e4m3_rne_sat_f32(q * (1.0f - 0x1p-19f));
+    const uint32_t hi = e4m3_rne_sat_f32(q * (1.0f + 0x1p-19f));
+    if (lo == hi) return lo;
+  }
+  const double q = (double)__uint_as_float(amax_b_bits) / (6.0 * (double)sg);
   return e4m3_rne_sat(q);
 }
 

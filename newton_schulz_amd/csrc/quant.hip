@@ -4,6 +4,8 @@
 // and §3.4: a per-tensor maximum (first pass, HBM-bound read), then per
 // 16-block an E4M3 scale and sixteen E2M1 codes (second pass).  The exact
 // rounding rules live in nvfp4_device.hpp.
+#include <type_traits>
+
 #include "launch.hpp"
 #include "nvfp4_device.hpp"
 
@@ -16,6 +18,10 @@ constexpr int kThreads = 256;
 #define NVFP4_QUANT_MAX_GRID (256 * 8)
 #endif
 constexpr int kMaxGrid = NVFP4_QUANT_MAX_GRID;  // workgroups of the grid-stride passes
+#ifndef NVFP4_QUANT_UNROLL
+#define NVFP4_QUANT_UNROLL 4
+#endif
+constexpr int kUnroll = NVFP4_QUANT_UNROLL;     // items per lane per trip
 
 typedef float float2_t __attribute__((ext_vector_type(2)));
 
@@ -148,14 +154,17 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
   auto src = [&](int64_t i) {
     return reinterpret_cast<const uint4*>(x)[(groups - 1 - i / G) * G + i % G];
   };
-  // two items per lane per trip, both loads issued before either is encoded
+  // kUnroll items per lane per trip, all loads issued before any is encoded,
+  // so that each lane keeps kUnroll * 16 bytes in flight
   int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  for (; i + stride < items; i += 2 * stride) {
-    const uint4 w0 = src(i), w1 = src(i + stride);
-    encode_item(i, w0);
-    encode_item(i + stride, w1);
+  for (; i + (kUnroll - 1) * stride < items; i += kUnroll * stride) {
+    uint4 w[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) w[u] = src(i + u * stride);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) encode_item(i + u * stride, w[u]);
   }
-  if (i < items) encode_item(i, src(i));
+  for (; i < items; i += stride) encode_item(i, src(i));
 }
 
 // ------------------------------------------- tiled quantizer, both axes ----
@@ -293,11 +302,12 @@ __global__ __launch_bounds__(kThreads) void dequant_rows_kernel(
   const float sg = *sgp;
   const int64_t items = nelem / EPL;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t item = (int64_t)blockIdx.x * kThreads + threadIdx.x; item < items; item += stride) {
-    const float s = __builtin_amdgcn_cvt_f32_fp8((int)scales[item / G], 0);
+  using Word = typename std::conditional<O == Dt::F32, uint16_t, uint32_t>::type;
+  auto emit = [&](int64_t item, uint32_t w, uint32_t sbyte) {
+    const float s = __builtin_amdgcn_cvt_f32_fp8((int)sbyte, 0);
     if constexpr (O == Dt::BF16) {
       float u[8];
-      decode_word(reinterpret_cast<const uint32_t*>(codes)[item], s, u);
+      decode_word(w, s, u);
       uint4 r;
       r.x = products_to_bf16x2(u[0], u[1], sg);
       r.y = products_to_bf16x2(u[2], u[3], sg);
@@ -305,13 +315,25 @@ __global__ __launch_bounds__(kThreads) void dequant_rows_kernel(
       r.w = products_to_bf16x2(u[6], u[7], sg);
       reinterpret_cast<uint4*>(out)[item] = r;
     } else {
-      const uint32_t w = reinterpret_cast<const uint16_t*>(codes)[item];
       const float2_t q0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
       const float2_t q1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
       reinterpret_cast<float4*>(out)[item] =
           make_float4(q0[0] * s * sg, q0[1] * s * sg, q1[0] * s * sg, q1[1] * s * sg);
     }
+  };
+  // kUnroll items per lane per trip, loads first (see quant_rows_kernel)
+  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  for (; i + (kUnroll - 1) * stride < items; i += kUnroll * stride) {
+    uint32_t w[kUnroll], sb[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      w[u] = reinterpret_cast<const Word*>(codes)[i + u * stride];
+      sb[u] = scales[(i + u * stride) / G];
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) emit(i + u * stride, w[u], sb[u]);
   }
+  for (; i < items; i += stride) emit(i, reinterpret_cast<const Word*>(codes)[i], scales[i / G]);
 }
 
 // Q_16x1 tensor stored as the rows of its transpose: codes [cols][rows/2].

@@ -36,8 +36,7 @@ def test_workspace_sizes_and_validation_on_host():
     lib = ns._lib
     assert lib.ns_workspace_bytes(3072, 8192) == lib.ns_workspace_bytes(8192, 3072)
     wb = lib.ns_workspace_bytes(3072, 8192)
-    # X, A, B in fp32, four packed NVFP4 tensors (215 MB) and the split-K
-    # partials of the Gram products
+    # X, A, B in fp32 and four packed NVFP4 tensors (215 MB)
     assert 215e6 < wb < 320e6 and wb % 256 == 0
     assert lib.ns_workspace_bytes(3072, 8190) == 0
     assert lib.nvfp4_quantize_workspace_bytes(16, 16) >= 4
@@ -66,8 +65,11 @@ def test_workspace_sizes_and_validation_on_host():
     # beta != 0 without an addend
     assert lib.nvfp4_gemm(fake, fake, fake, fake, fake, fake, 32, 32, 32, 0, 1.0, 2.0,
                           None, fake, None, None, 0, None) == ns.NS_ERR_ARG
-    # symmetric 3072^2 x 8192 splits K: it needs a workspace, and a too-small one is refused
-    wsg = lib.nvfp4_gemm_workspace_bytes(3072, 3072, 8192, 1)
+    # a symmetric 1024^2 x 16384 product has too few tiles to fill the GPU and
+    # splits K: it needs a workspace, and a too-small one is refused
+    wsg = lib.nvfp4_gemm_workspace_bytes(1024, 1024, 16384, 1)
     assert wsg > 0
-    assert lib.nvfp4_gemm(fake, fake, fake, fake, fake, fake, 3072, 3072, 8192, 1, 1.0, 0.0,
+    assert lib.nvfp4_gemm(fake, fake, fake, fake, fake, fake, 1024, 1024, 16384, 1, 1.0, 0.0,
                           None, other, None, fake, wsg - 1, None) == ns.NS_ERR_WORKSPACE
+    # 3072^2 x 8192 has a tile for every CU and runs unsplit
+    assert lib.nvfp4_gemm_workspace_bytes(3072, 3072, 8192, 1) == 0
