@@ -9,8 +9,9 @@ write-out) on the 3072 x 8192 BF16 gradient workload, inputs resident in
 HBM.  value = algorithmic TFLOP/s (symmetric products counted once).
 
 The same JSON line carries:
-  roofline      the dominant kernel of a step, timed alone with HIP events
-                on the stream it runs on, against the f16 MFMA dense peak;
+  roofline      the dominant kernel of a step, launched in the iteration's
+                order with HIP events around each launch on the stream it
+                runs on, against the f16 MFMA dense peak;
   quant         the standalone quantizer + dequantizer on 2^28 BF16 values
                 (16384 x 16384) in HBM GB/s against the 8 TB/s peak;
   bf16_ns       the same five steps in plain BF16 torch.matmul (hipBLASLt)
@@ -42,6 +43,9 @@ def parse():
     p.add_argument("--quant-warmup", type=int, default=20)
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     p.add_argument("--no-quant", action="store_true", help="skip the quantizer line")
+    p.add_argument("--copy-probe", action="store_true",
+                   help="finish with a plain 256 MiB device copy, the reference kernel that "
+                        "scales the FETCH_SIZE / WRITE_SIZE counters of a profiled run")
     return p.parse_args()
 
 
@@ -60,30 +64,59 @@ def time_events(fn, reps, warm, stream):
     return start.elapsed_time(end) / reps      # ms per call
 
 
-def kernel_timings(ns, torch, dev, m, n, stream):
-    """Each kernel of one NS step launched alone through the C ABI on the
-    bench stream, with operands of the benchmark's shape."""
+def kernel_timings(ns, torch, dev, m, n, stream, reps=10):
+    """The three products of an NS iteration launched through the C ABI on
+    the bench stream in the iteration's order, each operand quantized just
+    before its product as inside ns_orthogonalize, so caches hold what they
+    hold there.  Each product is bracketed by its own pair of HIP events;
+    returns {name: (average ms per launch, algorithmic flops per launch)}."""
     from synth import gaussian
     X = torch.from_numpy((gaussian(m, n, seed=77) / np.sqrt(m * n)).astype(np.float32)).to(dev)
-    res = {}
-    qx = ns.nvfp4_quantize(X, ns.NVFP4_ROWS)
-    qt = ns.nvfp4_quantize(X, ns.NVFP4_COLS)
     A = torch.empty((m, m), dtype=torch.float32, device=dev)
     Bm = torch.empty((m, m), dtype=torch.float32, device=dev)
     Xo = torch.empty_like(X)
-    ns.nvfp4_gemm(qx, qx, m, m, n, symmetric=True, out=A)
-    qa = ns.nvfp4_quantize(A, ns.NVFP4_ROWS)
-    ns.nvfp4_gemm(qa, qa, m, m, m, symmetric=True, alpha=2.0315, beta=-4.775, addend=A, out=Bm)
-    qb = ns.nvfp4_quantize(Bm, ns.NVFP4_ROWS)
     sym = m * (m + 1)
-    res["gemm_gram_xxT"] = (time_events(lambda: ns.nvfp4_gemm(qx, qx, m, m, n, symmetric=True, out=A),
-                                        20, 3, stream), sym * n)
-    res["gemm_gram_aaT"] = (time_events(lambda: ns.nvfp4_gemm(qa, qa, m, m, m, symmetric=True, alpha=2.0315,
-                                                              beta=-4.775, addend=A, out=Bm), 20, 3, stream),
-                            sym * m)
-    res["gemm_update_bx"] = (time_events(lambda: ns.nvfp4_gemm(qb, qt, m, n, m, alpha=1.0, beta=3.4445,
-                                                               addend=X, out=Xo), 20, 3, stream), 2 * m * m * n)
-    return res
+    flops = {"gemm_gram_xxT": sym * n, "gemm_gram_aaT": sym * m, "gemm_update_bx": 2 * m * m * n}
+    ev = {k: [] for k in flops}
+
+    def timed(name, fn):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record(stream)
+        fn()
+        e.record(stream)
+        ev[name].append((s, e))
+
+    for r in range(reps + 2):
+        qx = ns.nvfp4_quantize(X, ns.NVFP4_ROWS, stream=stream)
+        qt = ns.nvfp4_quantize(X, ns.NVFP4_COLS, stream=stream)
+        timed("gemm_gram_xxT", lambda: ns.nvfp4_gemm(qx, qx, m, m, n, symmetric=True, out=A, stream=stream))
+        qa = ns.nvfp4_quantize(A, ns.NVFP4_ROWS, stream=stream)
+        timed("gemm_gram_aaT", lambda: ns.nvfp4_gemm(qa, qa, m, m, m, symmetric=True, alpha=2.0315,
+                                                     beta=-4.775, addend=A, out=Bm, stream=stream))
+        qb = ns.nvfp4_quantize(Bm, ns.NVFP4_ROWS, stream=stream)
+        timed("gemm_update_bx", lambda: ns.nvfp4_gemm(qb, qt, m, n, m, alpha=1.0, beta=3.4445,
+                                                      addend=X, out=Xo, stream=stream))
+    torch.cuda.synchronize()
+    # the first two rounds are warm-up
+    return {k: (sum(s.elapsed_time(e) for s, e in v[2:]) / reps, flops[k]) for k, v in ev.items()}
+
+
+def source_digest():
+    """sha256 over the GEMM kernel sources; recorded HBM-traffic counters
+    apply only to the kernel they were taken from."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "nvfp4_device.hpp"):
+        with open(os.path.join(ROOT, "newton_schulz_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+# HBM bytes per launch of the dominant kernel (X = a X + qB qX16^T at
+# 3072 x 8192), from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE, each scaled by
+# what the counter reads for a plain copy of known size; see profiles/.
+DOMINANT_TRAFFIC = {"src_sha256": "deb9f8ebb0b4b338f735cb29bbb7997324e7fe55f5c03cc28afa92723df68533",
+                    "bytes_per_launch": 396745830}
 
 
 def bf16_ns_ms(torch, G, coeffs, stream, reps=10):
@@ -156,10 +189,13 @@ def main():
     dom = max(kt, key=lambda k: kt[k][0])
     dms, dflops = kt[dom]
     achieved = dflops / (dms * 1e-3) / 1e12
+    traffic = None
+    if dom == "gemm_update_bx" and DOMINANT_TRAFFIC["src_sha256"] == source_digest():
+        traffic = DOMINANT_TRAFFIC["bytes_per_launch"]
     roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
             "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
-            "avg_launch_ms": round(dms, 4),
+            "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": traffic,
+            "traffic_unit": "HBM bytes per launch", "avg_launch_ms": round(dms, 4),
             "per_kernel_ms": {k: round(v[0], 4) for k, v in kt.items()}}
 
     line = {
@@ -216,6 +252,12 @@ def main():
 
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(G, clip, coeffs, m, n)
+    if args.copy_probe:
+        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
     print(json.dumps(line), flush=True)
 
 

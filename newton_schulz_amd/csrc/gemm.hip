@@ -617,20 +617,22 @@ __global__ __launch_bounds__(GThreads, 2) void gemm_general_kernel(GemmProblem g
 
 // ---------------------------------------------------------------- plans ----
 
-#ifndef NVFP4_FAST_WM
-#define NVFP4_FAST_WM 2
-#define NVFP4_FAST_WN 2
-#define NVFP4_FAST_FM 2
-#define NVFP4_FAST_FN 2
-#endif
+// Two tile shapes: 128 x 128 (four 64 x 64 waves), and 64 x 128 (two waves)
+// for products with short K whose 128 x 128 tiles would leave most of the
+// GPU's workgroup slots empty, such as qA qA^T at 3072^2 (300 tiles for 256
+// CUs).  Measured inside the iteration, the small tiles lose on long K (the
+// 3072^2 x 8192 Gram product: more operand re-reads) and win on short K.
 #ifndef NVFP4_FAST_NST
 #define NVFP4_FAST_NST 2
 #endif
-#ifndef NVFP4_FAST_BK
-#define NVFP4_FAST_BK 128
+using BigCfg = Cfg<2, 2, 2, 2, NVFP4_FAST_NST, 128>;
+using SmallCfg = Cfg<1, 2, 2, 2, NVFP4_FAST_NST, 128>;
+#ifndef NVFP4_SMALL_BELOW
+#define NVFP4_SMALL_BELOW 512   // big-tile count below which the small tiles run
 #endif
-using FastCfg = Cfg<NVFP4_FAST_WM, NVFP4_FAST_WN, NVFP4_FAST_FM, NVFP4_FAST_FN, NVFP4_FAST_NST,
-                    NVFP4_FAST_BK>;
+#ifndef NVFP4_SMALL_MAX_K
+#define NVFP4_SMALL_MAX_K 4096  // ... when K is at most this
+#endif
 
 // Symmetric products are split along K only while the tiles alone would
 // leave CUs idle: the FP32 partials and the reduce pass cost more than the
@@ -655,33 +657,67 @@ int64_t sym_tiles(int64_t TM, int64_t TN, int64_t BM, int64_t BN) {
   return t;
 }
 
-}  // namespace
-
-GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool symmetric, bool allow_split) {
+template <class C>
+GemmPlan plan_with(int64_t M, int64_t N, int64_t K, bool symmetric, bool allow_split, int cfg) {
   GemmPlan p{};
-  if (K % 128 != 0) {
-    p.fast = false;
-    p.splits = 1;
-    return p;
-  }
   p.fast = true;
-  p.TM = (M + FastCfg::BM - 1) / FastCfg::BM;
-  p.TN = (N + FastCfg::BN - 1) / FastCfg::BN;
-  p.tiles = symmetric ? sym_tiles(p.TM, p.TN, FastCfg::BM, FastCfg::BN) : p.TM * p.TN;
+  p.cfg = cfg;
+  p.TM = (M + C::BM - 1) / C::BM;
+  p.TN = (N + C::BN - 1) / C::BN;
+  p.tiles = symmetric ? sym_tiles(p.TM, p.TN, C::BM, C::BN) : p.TM * p.TN;
   int64_t splits = 1;
-  const int64_t stages = K / FastCfg::BK;
+  const int64_t stages = K / C::BK;
   if (allow_split && symmetric) {
-    while (p.tiles * splits < kTargetUnits && (stages / (2 * splits)) * FastCfg::BK >= kMinKPerSplit)
+    while (p.tiles * splits < kTargetUnits && (stages / (2 * splits)) * C::BK >= kMinKPerSplit)
       splits *= 2;
   }
   p.splits = (int)splits;
   p.units = p.tiles * splits;
   if (splits > 1) {
-    const size_t part = (size_t)p.units * FastCfg::kAcc * FastCfg::kThreads * sizeof(float);
+    const size_t part = (size_t)p.units * C::kAcc * C::kThreads * sizeof(float);
     p.partial_bytes = (part + 255) / 256 * 256;
   }
   p.ws_bytes = p.partial_bytes;
   return p;
+}
+
+template <class C>
+hipError_t launch_with(const GemmProblem& g, const GemmPlan& p, float* partials, hipStream_t s) {
+  FastArgs a;
+  a.g = g;
+  a.splits = p.splits;
+  a.TM = p.TM;
+  a.TN = p.TN;
+  a.tiles = p.tiles;
+  a.units = p.units;
+  a.partials = p.splits > 1 ? partials : nullptr;
+  const int64_t grid = (p.units + kXcds - 1) / kXcds * kXcds;
+  if (g.symmetric)
+    gemm_fast_kernel<C, true><<<dim3((unsigned)grid), C::kThreads, 0, s>>>(a);
+  else
+    gemm_fast_kernel<C, false><<<dim3((unsigned)grid), C::kThreads, 0, s>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.splits == 1) return e;
+  const int64_t rgrid = (p.tiles + kXcds - 1) / kXcds * kXcds;
+  if (g.symmetric)
+    gemm_reduce_kernel<C, true><<<dim3((unsigned)rgrid), C::kThreads, 0, s>>>(a);
+  else
+    gemm_reduce_kernel<C, false><<<dim3((unsigned)rgrid), C::kThreads, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool symmetric, bool allow_split) {
+  if (K % 128 != 0) {
+    GemmPlan p{};
+    p.fast = false;
+    p.splits = 1;
+    return p;
+  }
+  const GemmPlan big = plan_with<BigCfg>(M, N, K, symmetric, allow_split, 0);
+  if (big.tiles >= NVFP4_SMALL_BELOW || K > NVFP4_SMALL_MAX_K) return big;
+  return plan_with<SmallCfg>(M, N, K, symmetric, allow_split, 1);
 }
 
 hipError_t launch_gemm(const GemmProblem& g, const GemmPlan& p, float* partials, hipStream_t s) {
@@ -695,27 +731,7 @@ hipError_t launch_gemm(const GemmProblem& g, const GemmPlan& p, float* partials,
     }
     return hipGetLastError();
   }
-  FastArgs a;
-  a.g = g;
-  a.splits = p.splits;
-  a.TM = p.TM;
-  a.TN = p.TN;
-  a.tiles = p.tiles;
-  a.units = p.units;
-  a.partials = p.splits > 1 ? partials : nullptr;
-  const int64_t grid = (p.units + kXcds - 1) / kXcds * kXcds;
-  if (g.symmetric)
-    gemm_fast_kernel<FastCfg, true><<<dim3((unsigned)grid), FastCfg::kThreads, 0, s>>>(a);
-  else
-    gemm_fast_kernel<FastCfg, false><<<dim3((unsigned)grid), FastCfg::kThreads, 0, s>>>(a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.splits == 1) return e;
-  const int64_t rgrid = (p.tiles + kXcds - 1) / kXcds * kXcds;
-  if (g.symmetric)
-    gemm_reduce_kernel<FastCfg, true><<<dim3((unsigned)rgrid), FastCfg::kThreads, 0, s>>>(a);
-  else
-    gemm_reduce_kernel<FastCfg, false><<<dim3((unsigned)rgrid), FastCfg::kThreads, 0, s>>>(a);
-  return hipGetLastError();
+  return p.cfg == 0 ? launch_with<BigCfg>(g, p, partials, s) : launch_with<SmallCfg>(g, p, partials, s);
 }
 
 }  // namespace nvfp4

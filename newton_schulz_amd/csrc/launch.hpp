@@ -50,11 +50,13 @@ struct GemmProblem {
   uint32_t* amax_out;
 };
 
-// Launch plan of one product: the fast path needs K % 128 == 0; symmetric
-// products on the fast path may be split along K, which needs a workspace
-// of ws_bytes for the FP32 partials.
+// Launch plan of one product: the fast path needs K % 128 == 0 and picks a
+// tile shape from the tile count; symmetric products on the fast path may
+// be split along K, which needs a workspace of ws_bytes for the FP32
+// partials.
 struct GemmPlan {
   bool fast;
+  int cfg;                // tile shape of the fast path (0: 128 x 128, 1: 64 x 128)
   int splits;
   int64_t TM, TN, tiles, units;
   size_t partial_bytes, ws_bytes;
