@@ -9,9 +9,12 @@ Projections, Optimizers, and Attention" (arXiv 2607.04422):
   closed form and encoded by exact comparison (round to nearest, ties to even).
 * ``nvfp4``    — the 1x16 / 16x1 block quantizer and the dequantizer
   (x_hat = x_E2M1 * s * s_g, §2 "NVFP4 format"; RTN per §3.4).
+* ``rht``      — the random 16 x 16 Hadamard transform that §3.4 applies to
+  every quantized operand along the contraction axis.
 * ``ns``       — the Newton–Schulz iteration of the Root optimizer, exact
   (§2 "Root optimizer") and with NVFP4 operands (§3.4, the three-line NVFP4
-  NS iteration), plus the caller-side clip and Frobenius normalisation.
+  NS iteration, with or without the transform), plus the caller-side clip
+  and Frobenius normalisation.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this package.  The GPU library never calls it and
@@ -21,7 +24,10 @@ Pins (what each function is checked against, in ``tests/test_oracle_*.py``):
 codecs against the format's closed form and torch's float8_e4m3fn cast;
 rounding against brute-force nearest-grid search with exact rationals;
 round-trip of exactly representable tensors; idempotence; the per-block error
-bound; the FP64 GEMM against a pure-Python triple loop; exact NS against the
+bound; the FP64 GEMM against a pure-Python triple loop; the Hadamard matrix
+against its recursive construction, its orthogonality, the transform against
+its definition in plain loops, the FP32 butterfly against the FP64 product,
+and the cancellation of the transform in every NS product; exact NS against the
 SVD closed form of its scalar map and, for the cubic, the polar factor; the
 quantized NS against the scalar map on matrices whose quantization is benign.
 The quantized NS on general inputs has no pin beyond the composition of these

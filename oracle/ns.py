@@ -11,15 +11,25 @@ Source: Full-Stack FP4 (arXiv 2607.04422).
   Every quantization is RTN.  §3.4 also mentions p99 outlier clipping,
   applied here as a clamp of the input before normalisation.
 
+* With ``rht_masks`` (one 16-bit sign mask per step) the iteration takes
+  the random Hadamard transform of §3.4 on every quantized operand:
+      qX = Q_1x16(X H),  qX16 = Q_16x1(H^T X),
+      qA = Q_1x16(A H),  qA16 = Q_16x1(H^T A),  B = b A + c qA qA16,
+      qB = Q_1x16(B H),  X' = a X + qB qX16,
+  H = H_16^r of that step (see ``rht``); H H^T = I, so each product still
+  approximates the untransformed one.
+
 Readings (the pages leave these open):
-* The random Hadamard transform and the adaptive 4/6 scaling of §3.4 are
-  not applied (the method computed here is plain NVFP4 RTN with the block
-  maximum mapped to 6).
+* The adaptive 4/6 scaling of §3.4 is not applied (the method computed
+  here is NVFP4 RTN with the block maximum mapped to 6); without
+  ``rht_masks`` neither is the Hadamard transform.
 * Orientation: if m > n the iteration runs on G^T and the result is
   transposed back, so the Gram matrix A is the smaller m x m side.
 * X_0 = clamp(G, -clip, clip) / (||clamp(G)||_F + eps), eps = 1e-7, the
   clamp leaving NaN as NaN; clip = +inf disables it.
-* qX and qX16 share one s_g (from max|X|); A and B get their own.
+* Without the transform qX and qX16 share one s_g (from max|X|); with it
+  X H and H^T X are different tensors and each has its own s_g.  A and B
+  always get their own.
 * b A and a X use the unquantized A and X; A itself is never re-rounded.
 * Because A is symmetric, Q_16x1(A) equals Q_1x16(A)^T, so the second
   product is qA qA^T; the oracle still forms Q_16x1(A) from A itself.
@@ -30,6 +40,7 @@ import numpy as np
 
 from .nvfp4 import (quantize_rows, quantize_cols, dequantize_rows,
                     dequantize_cols, tensor_amax)
+from .rht import rht_rows, rht_cols
 
 EPS = 1e-7
 
@@ -70,28 +81,42 @@ def ns_exact(G, coeffs, clip=np.inf, eps=EPS):
     return X.T if transposed else X
 
 
-def ns_nvfp4(G, coeffs, clip=np.inf, eps=EPS, trace=None):
+def ns_nvfp4(G, coeffs, clip=np.inf, eps=EPS, trace=None, rht_masks=None):
     """Newton–Schulz with NVFP4 operands for every product (§3.4 iteration).
 
-    ``trace``, if a list, receives one dict per step with the quantized
-    operands and the float64 intermediates (X before the step, A, B, X after).
+    ``rht_masks``: None, or one 16-bit sign mask per step for the random
+    Hadamard transform of that step.  ``trace``, if a list, receives one
+    dict per step with the quantized operands and the float64 intermediates
+    (X before the step, A, B, X after).
     """
     Gt, transposed = _orient(G)
     X = clip_and_normalize(Gt, clip, eps)
-    for a, b, c in coeffs:
-        amax_x = tensor_amax(X)
-        qX = quantize_rows(X, amax=amax_x)           # Q_1x16(X)
-        qX16 = quantize_cols(X, amax=amax_x)         # Q_16x1(X), stored as X^T rows
+    if rht_masks is not None and len(rht_masks) != len(coeffs):
+        raise ValueError("one Hadamard mask per step")
+    for it, (a, b, c) in enumerate(coeffs):
+        if rht_masks is None:
+            amax_x = tensor_amax(X)
+            qX = quantize_rows(X, amax=amax_x)       # Q_1x16(X)
+            qX16 = quantize_cols(X, amax=amax_x)     # Q_16x1(X), stored as X^T rows
+        else:
+            h = rht_masks[it]
+            qX = quantize_rows(rht_rows(X, h))       # Q_1x16(X H)
+            qX16 = quantize_cols(rht_cols(X, h))     # Q_16x1(H^T X)
         dX = dequantize_rows(qX)
         A = gemm_nt(dX, dX)                          # qX qX^T
-        qA = quantize_rows(A)                        # Q_1x16(A)
-        qA16 = quantize_cols(A)                      # Q_16x1(A)
+        if rht_masks is None:
+            qA = quantize_rows(A)                    # Q_1x16(A)
+            qA16 = quantize_cols(A)                  # Q_16x1(A)
+        else:
+            qA = quantize_rows(rht_rows(A, h))       # Q_1x16(A H)
+            qA16 = quantize_cols(rht_cols(A, h))     # Q_16x1(H^T A)
         B = b * A + c * (dequantize_rows(qA) @ dequantize_cols(qA16))
-        qB = quantize_rows(B)                        # Q_1x16(B)
+        qB = quantize_rows(B if rht_masks is None else rht_rows(B, h))   # Q_1x16(B [H])
         Xn = a * X + dequantize_rows(qB) @ dequantize_cols(qX16)
         if trace is not None:
             trace.append(dict(X=X, qX=qX, qX16=qX16, A=A, qA=qA, qA16=qA16,
-                              B=B, qB=qB, X_next=Xn, coeffs=(a, b, c)))
+                              B=B, qB=qB, X_next=Xn, coeffs=(a, b, c),
+                              rht_mask=None if rht_masks is None else rht_masks[it]))
         X = Xn
     return X.T if transposed else X
 

@@ -81,6 +81,12 @@ QUINTIC = (3.4445, -4.7750, 2.0315)
 STEPS = 5
 
 
+def rht_masks(k, seed):
+    """k 16-bit sign masks for the random Hadamard transform (one per NS
+    step; bit j set = sign -1 on element j of every 16-block)."""
+    return [int(v) for v in rng(seed).integers(0, 1 << 16, size=k)]
+
+
 def ns_workload(name):
     """Return dict(G=list of (rows, cols) specs, dtype, coeffs, seeds).
 
