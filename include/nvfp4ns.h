@@ -81,6 +81,25 @@ ns_status nvfp4_quantize(const void* x, ns_dtype xt, int64_t rows, int64_t cols,
                          void* stream);
 
 /*
+ * nvfp4_quantize_rht — the quantizers of the §3.4 NS iteration with the
+ * random Hadamard transform: Q_1x16(x H) (NVFP4_ROWS) or Q_16x1(H^T x)
+ * (NVFP4_COLS, stored as the Q_1x16 layout of the transpose), where
+ * H = H_16^r acts on every 16-block along the blocked axis.
+ *   mask  H_16^r = diag(s) H_16 / 4 with H_16 the Sylvester Hadamard matrix,
+ *         s_j = -1 where bit j of mask is set, else +1.
+ *   The transformed values are computed in FP32 by the radix-2 butterfly:
+ *   signs applied, then half-widths 1, 2, 4, 8, each pair (a, b) becoming
+ *   (a + b, a - b) rounded to nearest even, then times 1/4.  The tensor
+ *   scale s_g is that of the transformed tensor.
+ * Other arguments, layout and errors as nvfp4_quantize.  nvfp4_dequantize
+ * of the result returns the transformed tensor's approximation (the
+ * transform is not undone).
+ */
+ns_status nvfp4_quantize_rht(const void* x, ns_dtype xt, int64_t rows, int64_t cols,
+                             nvfp4_axis axis, uint16_t mask, uint8_t* codes, uint8_t* scales,
+                             float* global_scale, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * nvfp4_dequantize — x_hat = x_E2M1 * s * s_g (§2 "NVFP4 format").
  * Inputs as written by nvfp4_quantize for the same rows, cols and axis;
  * out is [rows][cols] in the ORIGINAL orientation (an NVFP4_COLS tensor is
@@ -138,6 +157,22 @@ ns_status ns_orthogonalize(const void* G, ns_dtype gt, int64_t m, int64_t n,
                            const float* coeffs, int k, float clip,
                            void* out, ns_dtype ot, void* ws, size_t ws_bytes,
                            void* stream);
+
+/*
+ * ns_orthogonalize_rht — ns_orthogonalize with the random Hadamard transform
+ * of the §3.4 iteration on every quantized operand:
+ *   qX = Q_1x16(X H), qX16 = Q_16x1(H^T X), A = qX qX^T
+ *   qA = Q_1x16(A H), qA16 = Q_16x1(H^T A), B = b A + c qA qA16
+ *   qB = Q_1x16(B H), X' = a X + qB qX16
+ * with H = H_16^r of step i built from masks[i] as in nvfp4_quantize_rht
+ * (H H^T = I, so each product still approximates the untransformed one).
+ *   masks  HOST array of k 16-bit sign masks, one per step (not NULL).
+ * X H and H^T X each take their own s_g.  Other arguments, workspace
+ * (ns_workspace_bytes) and errors as ns_orthogonalize.
+ */
+ns_status ns_orthogonalize_rht(const void* G, ns_dtype gt, int64_t m, int64_t n,
+                               const float* coeffs, int k, float clip, const uint16_t* masks,
+                               void* out, ns_dtype ot, void* ws, size_t ws_bytes, void* stream);
 
 /* Workspace of ns_orthogonalize_grouped for `count` matrices (host arrays m, n). */
 size_t ns_grouped_workspace_bytes(int count, const int64_t* m, const int64_t* n);

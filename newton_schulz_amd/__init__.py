@@ -6,12 +6,18 @@ current stream.  There is no fallback: if the library is missing this
 module raises ImportError.
 
 Functions carry the C names:
-    nvfp4_quantize, nvfp4_dequantize, nvfp4_gemm_workspace_bytes, nvfp4_gemm,
-    ns_workspace_bytes,
-    ns_orthogonalize, ns_grouped_workspace_bytes, ns_orthogonalize_grouped
+    nvfp4_quantize, nvfp4_quantize_rht, nvfp4_dequantize,
+    nvfp4_gemm_workspace_bytes, nvfp4_gemm, ns_workspace_bytes,
+    ns_orthogonalize, ns_orthogonalize_rht,
+    ns_grouped_workspace_bytes, ns_orthogonalize_grouped
 """
 import ctypes
 import os
+
+# torch first: the library must bind to the HIP runtime torch has loaded (the
+# one that owns the devices, streams and memory it is handed), not bring in
+# a second copy ahead of it.
+import torch  # noqa: F401
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libnvfp4ns.so")
@@ -30,16 +36,19 @@ STATUS_NAMES = {0: "NS_OK", -1: "NS_ERR_ARG", -2: "NS_ERR_SHAPE",
                 -3: "NS_ERR_WORKSPACE", -4: "NS_ERR_HIP"}
 
 _i64, _sz, _vp, _f, _i = ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float, ctypes.c_int
+_u16 = ctypes.c_uint16
 
 _SIGS = {
     "nvfp4_quantize_workspace_bytes": (_sz, [_i64, _i64]),
     "nvfp4_quantize": (_i, [_vp, _i, _i64, _i64, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "nvfp4_quantize_rht": (_i, [_vp, _i, _i64, _i64, _i, _u16, _vp, _vp, _vp, _vp, _sz, _vp]),
     "nvfp4_dequantize": (_i, [_vp, _vp, _vp, _i64, _i64, _i, _vp, _i, _vp]),
     "nvfp4_gemm_workspace_bytes": (_sz, [_i64, _i64, _i64, _i]),
     "nvfp4_gemm": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i, _f, _f, _vp, _vp, _vp,
                         _vp, _sz, _vp]),
     "ns_workspace_bytes": (_sz, [_i64, _i64]),
     "ns_orthogonalize": (_i, [_vp, _i, _i64, _i64, _vp, _i, _f, _vp, _i, _vp, _sz, _vp]),
+    "ns_orthogonalize_rht": (_i, [_vp, _i, _i64, _i64, _vp, _i, _f, _vp, _vp, _i, _vp, _sz, _vp]),
     "ns_grouped_workspace_bytes": (_sz, [_i, _vp, _vp]),
     "ns_orthogonalize_grouped": (_i, [_i, _vp, _vp, _vp, _i, _vp, _i, _vp, _vp, _i, _vp, _sz, _vp]),
 }
@@ -126,6 +135,31 @@ def nvfp4_quantize(x, axis=NVFP4_ROWS, codes=None, scales=None, global_scale=Non
     return codes, scales, global_scale
 
 
+def nvfp4_quantize_rht(x, mask, axis=NVFP4_ROWS, codes=None, scales=None, global_scale=None,
+                       workspace=None, stream=None):
+    """Q_1x16(x H) (NVFP4_ROWS) or Q_16x1(H^T x) (NVFP4_COLS) with the random
+    Hadamard transform H_16^r of the 16-bit sign mask; outputs as
+    nvfp4_quantize."""
+    torch = _torch()
+    _need_cuda(x)
+    rows, cols = x.shape
+    r, c = (rows, cols) if axis == NVFP4_ROWS else (cols, rows)
+    dev = x.device
+    if codes is None:
+        codes = torch.empty((r, c // 2), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty((r, c // 16), dtype=torch.uint8, device=dev)
+    if global_scale is None:
+        global_scale = torch.empty(1, dtype=torch.float32, device=dev)
+    wsb = _lib.nvfp4_quantize_workspace_bytes(rows, cols)
+    if workspace is None:
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    _check(_lib.nvfp4_quantize_rht(_ptr(x), _dt(x), rows, cols, axis, int(mask) & 0xFFFF,
+                                   _ptr(codes), _ptr(scales), _ptr(global_scale), _ptr(workspace),
+                                   workspace.numel(), _stream(stream)), "nvfp4_quantize_rht")
+    return codes, scales, global_scale
+
+
 def nvfp4_dequantize(codes, scales, global_scale, rows, cols, axis=NVFP4_ROWS,
                      out_dtype=NS_F32, out=None, stream=None):
     """x_hat = x_E2M1 * s * s_g, in the original rows x cols orientation."""
@@ -191,6 +225,27 @@ def ns_orthogonalize(G, coeffs, clip=float("inf"), out_dtype=NS_F32, out=None, w
     _check(_lib.ns_orthogonalize(_ptr(G), _dt(G), m, n, carr, k, float(clip), _ptr(out),
                                  _dt(out), _ptr(workspace), workspace.numel(), _stream(stream)),
            "ns_orthogonalize")
+    return out
+
+
+def ns_orthogonalize_rht(G, coeffs, masks, clip=float("inf"), out_dtype=NS_F32, out=None,
+                         workspace=None, stream=None):
+    """ns_orthogonalize with the random Hadamard transform of each step
+    (one 16-bit sign mask per coefficient triple)."""
+    torch = _torch()
+    _need_cuda(G, out)
+    m, n = G.shape
+    if out is None:
+        out = torch.empty((m, n), dtype=_out_dtype(out_dtype), device=G.device)
+    if workspace is None:
+        workspace = torch.empty(ns_workspace_bytes(m, n), dtype=torch.uint8, device=G.device)
+    carr, k = _coeff_array(coeffs)
+    if len(masks) != k:
+        raise ValueError("one Hadamard mask per step")
+    marr = (ctypes.c_uint16 * k)(*[int(v) & 0xFFFF for v in masks])
+    _check(_lib.ns_orthogonalize_rht(_ptr(G), _dt(G), m, n, carr, k, float(clip), marr, _ptr(out),
+                                     _dt(out), _ptr(workspace), workspace.numel(), _stream(stream)),
+           "ns_orthogonalize_rht")
     return out
 
 

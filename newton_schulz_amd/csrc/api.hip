@@ -5,6 +5,8 @@
 
 #include <cmath>
 #include <cstdint>
+#include <cstdio>
+#include <cstdlib>
 #include <cstring>
 
 #include "../../include/nvfp4ns.h"
@@ -24,9 +26,19 @@ inline bool dtype_ok(int d) { return d == NS_F32 || d == NS_BF16; }
 inline size_t dtype_size(ns_dtype d) { return d == NS_F32 ? 4 : 2; }
 inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
-#define NS_TRY(call)                           \
-  do {                                         \
-    if ((call) != hipSuccess) return NS_ERR_HIP; \
+// A failed launch returns NS_ERR_HIP; with NVFP4NS_DEBUG set in the
+// environment the HIP error and the failing call are also printed.
+inline ns_status hip_failed(hipError_t e, const char* what, int line) {
+  if (std::getenv("NVFP4NS_DEBUG"))
+    std::fprintf(stderr, "nvfp4ns: %s (%d) from %s, api.hip:%d\n", hipGetErrorString(e), (int)e, what,
+                 line);
+  return NS_ERR_HIP;
+}
+
+#define NS_TRY(call)                                          \
+  do {                                                        \
+    const hipError_t ns_e_ = (call);                          \
+    if (ns_e_ != hipSuccess) return hip_failed(ns_e_, #call, __LINE__); \
   } while (0)
 
 // Zero a few device words with a kernel launch (no memset node, so the
@@ -64,8 +76,8 @@ NsLayout ns_layout(int64_t m, int64_t n) {
   L.qa_s = take(xm * xm / 16);
   L.qb_c = take(xm * xm / 2);
   L.qb_s = take(xm * xm / 16);
-  L.sg = take(3 * sizeof(float));
-  L.slot = take(3 * sizeof(uint32_t));
+  L.sg = take(4 * sizeof(float));
+  L.slot = take(4 * sizeof(uint32_t));
   L.part = take(nvfp4::kNormParts * sizeof(double));
   L.inv = take(sizeof(double));
   L.gemm_part = take(part_bytes);
@@ -73,8 +85,14 @@ NsLayout ns_layout(int64_t m, int64_t n) {
   return L;
 }
 
+// The iteration of §3.4.  With `masks` (k host masks) every quantized
+// operand is first multiplied along K by that step's random Hadamard
+// transform H^r: qX = Q_1x16(X H), qX16 = Q_16x1(H^T X) (own s_g),
+// qA = Q_1x16(A H) (= Q_16x1(H^T A)^T since A is symmetric), qB = Q_1x16(B H);
+// the maxima of the transformed tensors come from their own tiled pass.
 ns_status ns_run(const void* G, ns_dtype gt, int64_t m, int64_t n, const float* coeffs, int k,
-                 float clip, void* out, ns_dtype ot, uint8_t* ws, hipStream_t s) {
+                 float clip, const uint16_t* masks, void* out, ns_dtype ot, uint8_t* ws,
+                 hipStream_t s) {
   const NsLayout L = ns_layout(m, n);
   const bool tr = m > n;
   const int64_t xm = tr ? n : m, xn = tr ? m : n;
@@ -85,8 +103,8 @@ ns_status ns_run(const void* G, ns_dtype gt, int64_t m, int64_t n, const float* 
   uint32_t* slot = reinterpret_cast<uint32_t*>(ws + L.slot);
   double* part = reinterpret_cast<double*>(ws + L.part);
   double* inv = reinterpret_cast<double*>(ws + L.inv);
-  uint32_t *slotX = slot, *slotA = slot + 1, *slotB = slot + 2;
-  float *sgX = sg, *sgA = sg + 1, *sgB = sg + 2;
+  uint32_t *slotX = slot, *slotA = slot + 1, *slotB = slot + 2, *slotXc = slot + 3;
+  float *sgX = sg, *sgA = sg + 1, *sgB = sg + 2, *sgXc = sg + 3;
 
   float* gpart = reinterpret_cast<float*>(ws + L.gemm_part);
 
@@ -96,6 +114,33 @@ ns_status ns_run(const void* G, ns_dtype gt, int64_t m, int64_t n, const float* 
 
   for (int it = 0; it < k; ++it) {
     const float a = coeffs[3 * it], b = coeffs[3 * it + 1], c = coeffs[3 * it + 2];
+    if (masks) {
+      const nvfp4::RhtArg h{1u, (uint32_t)masks[it]};
+      zero_words_kernel<<<1, 64, 0, s>>>(slot, 4);
+      NS_TRY(hipGetLastError());
+      // qX = Q_1x16(X H), qX16 = Q_16x1(H^T X), each with its own s_g
+      NS_TRY(nvfp4::launch_amax_tiles(X, Dt::F32, xm, xn, slotX, slotXc, h, s));
+      NS_TRY(nvfp4::launch_quant_tiles(X, Dt::F32, xm, xn, slotX, sgX, ws + L.qx_c, ws + L.qx_s,
+                                       ws + L.qt_c, ws + L.qt_s, nullptr, s, slotXc, sgXc, h));
+      nvfp4::GemmProblem g1{ws + L.qx_c, ws + L.qx_s, sgX, ws + L.qx_c, ws + L.qx_s, sgX,
+                            xm, xm, xn, 1, 1.0f, 0.0f, nullptr, A, nullptr};
+      NS_TRY(nvfp4::launch_gemm(g1, L.p1, gpart, s));
+      // qA = Q_1x16(A H)
+      NS_TRY(nvfp4::launch_amax_tiles(A, Dt::F32, xm, xm, slotA, nullptr, h, s));
+      NS_TRY(nvfp4::launch_quant_tiles(A, Dt::F32, xm, xm, slotA, sgA, ws + L.qa_c, ws + L.qa_s,
+                                       nullptr, nullptr, nullptr, s, nullptr, nullptr, h));
+      nvfp4::GemmProblem g2{ws + L.qa_c, ws + L.qa_s, sgA, ws + L.qa_c, ws + L.qa_s, sgA,
+                            xm, xm, xm, 1, c, b, A, B, nullptr};
+      NS_TRY(nvfp4::launch_gemm(g2, L.p2, gpart, s));
+      // qB = Q_1x16(B H)
+      NS_TRY(nvfp4::launch_amax_tiles(B, Dt::F32, xm, xm, slotB, nullptr, h, s));
+      NS_TRY(nvfp4::launch_quant_tiles(B, Dt::F32, xm, xm, slotB, sgB, ws + L.qb_c, ws + L.qb_s,
+                                       nullptr, nullptr, nullptr, s, nullptr, nullptr, h));
+      nvfp4::GemmProblem g3{ws + L.qb_c, ws + L.qb_s, sgB, ws + L.qt_c, ws + L.qt_s, sgXc,
+                            xm, xn, xm, 0, 1.0f, a, X, X, nullptr};
+      NS_TRY(nvfp4::launch_gemm(g3, L.p3, gpart, s));
+      continue;
+    }
     // qX = Q_1x16(X) and qX16 = Q_16x1(X) (stored as rows of X^T), one s_g
     NS_TRY(nvfp4::launch_quant_tiles(X, Dt::F32, xm, xn, slotX, sgX, ws + L.qx_c, ws + L.qx_s,
                                      ws + L.qt_c, ws + L.qt_s, slotA, s));
@@ -169,6 +214,31 @@ ns_status nvfp4_quantize(const void* x, ns_dtype xt, int64_t rows, int64_t cols,
   return NS_OK;
 }
 
+ns_status nvfp4_quantize_rht(const void* x, ns_dtype xt, int64_t rows, int64_t cols,
+                             nvfp4_axis axis, uint16_t mask, uint8_t* codes, uint8_t* scales,
+                             float* global_scale, void* ws, size_t ws_bytes, void* stream) {
+  if (!x || !codes || !scales || !global_scale || !dtype_ok(xt) ||
+      (axis != NVFP4_ROWS && axis != NVFP4_COLS))
+    return NS_ERR_ARG;
+  if (!dims_ok(rows) || !dims_ok(cols)) return NS_ERR_SHAPE;
+  if (!ws || ws_bytes < nvfp4_quantize_workspace_bytes(rows, cols)) return NS_ERR_WORKSPACE;
+  hipStream_t s = as_stream(stream);
+  uint32_t* slot = static_cast<uint32_t*>(ws);
+  const nvfp4::RhtArg h{1u, (uint32_t)mask};
+  zero_words_kernel<<<1, 64, 0, s>>>(slot, 1);
+  NS_TRY(hipGetLastError());
+  if (axis == NVFP4_ROWS) {
+    NS_TRY(nvfp4::launch_amax_tiles(x, (Dt)xt, rows, cols, slot, nullptr, h, s));
+    NS_TRY(nvfp4::launch_quant_tiles(x, (Dt)xt, rows, cols, slot, global_scale, codes, scales,
+                                     nullptr, nullptr, nullptr, s, nullptr, nullptr, h));
+  } else {
+    NS_TRY(nvfp4::launch_amax_tiles(x, (Dt)xt, rows, cols, nullptr, slot, h, s));
+    NS_TRY(nvfp4::launch_quant_tiles(x, (Dt)xt, rows, cols, slot, global_scale, nullptr, nullptr,
+                                     codes, scales, nullptr, s, nullptr, nullptr, h));
+  }
+  return NS_OK;
+}
+
 ns_status nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* global_scale,
                            int64_t rows, int64_t cols, nvfp4_axis axis, void* out, ns_dtype ot,
                            void* stream) {
@@ -224,7 +294,19 @@ ns_status ns_orthogonalize(const void* G, ns_dtype gt, int64_t m, int64_t n, con
   ns_status st = validate_ns(G, gt, m, n, coeffs, k, clip, out, ot);
   if (st != NS_OK) return st;
   if (!ws || ws_bytes < ns_workspace_bytes(m, n)) return NS_ERR_WORKSPACE;
-  return ns_run(G, gt, m, n, coeffs, k, clip, out, ot, static_cast<uint8_t*>(ws), as_stream(stream));
+  return ns_run(G, gt, m, n, coeffs, k, clip, nullptr, out, ot, static_cast<uint8_t*>(ws),
+                as_stream(stream));
+}
+
+ns_status ns_orthogonalize_rht(const void* G, ns_dtype gt, int64_t m, int64_t n,
+                               const float* coeffs, int k, float clip, const uint16_t* masks,
+                               void* out, ns_dtype ot, void* ws, size_t ws_bytes, void* stream) {
+  if (!masks) return NS_ERR_ARG;
+  ns_status st = validate_ns(G, gt, m, n, coeffs, k, clip, out, ot);
+  if (st != NS_OK) return st;
+  if (!ws || ws_bytes < ns_workspace_bytes(m, n)) return NS_ERR_WORKSPACE;
+  return ns_run(G, gt, m, n, coeffs, k, clip, masks, out, ot, static_cast<uint8_t*>(ws),
+                as_stream(stream));
 }
 
 size_t ns_grouped_workspace_bytes(int count, const int64_t* m, const int64_t* n) {
@@ -251,7 +333,8 @@ ns_status ns_orthogonalize_grouped(int count, const void* const* G, const int64_
   if (!ws || ws_bytes < need) return NS_ERR_WORKSPACE;
   uint8_t* base = static_cast<uint8_t*>(ws);
   for (int i = 0; i < count; ++i) {
-    ns_status st = ns_run(G[i], gt, m[i], n[i], coeffs, k, clip[i], out[i], ot, base, as_stream(stream));
+    ns_status st = ns_run(G[i], gt, m[i], n[i], coeffs, k, clip[i], nullptr, out[i], ot, base,
+                          as_stream(stream));
     if (st != NS_OK) return st;
     base += ns_workspace_bytes(m[i], n[i]);
   }

@@ -8,6 +8,13 @@ namespace nvfp4 {
 
 enum class Dt : int { F32 = 0, BF16 = 1 };
 
+// Random Hadamard transform option of the tiled quantizer kernels: when `on`,
+// every 16-block is multiplied by H^r = diag(s) H_16 / 4 before it is used,
+// s_j = -1 where bit j of `mask` is set.
+struct RhtArg {
+  uint32_t on, mask;
+};
+
 // ---- quantizer (quant.hip) -------------------------------------------------
 // max |x| over n elements into *slot (atomic max on the bit pattern; the
 // caller zeroes *slot first).  Non-finite values count as NaN.
@@ -22,12 +29,20 @@ hipError_t launch_quant_rows(const void* x, Dt xt, int64_t rows, int64_t cols,
                              hipStream_t s);
 
 // Q_1x16 and/or Q_16x1 of a rows x cols matrix through 64x64 LDS tiles, one
-// read of x for both layouts.  Either output pair may be null.
+// read of x for both layouts.  Either output pair may be null.  The column
+// layout takes its s_g from amax_c / sg_out_c when given (else the row
+// ones); with rht.on every block is transformed first.
 hipError_t launch_quant_tiles(const void* x, Dt xt, int64_t rows, int64_t cols,
                               const uint32_t* amax_slot, float* sg_out,
                               uint8_t* row_codes, uint8_t* row_scales,
                               uint8_t* col_codes, uint8_t* col_scales,
-                              uint32_t* zero_slot, hipStream_t s);
+                              uint32_t* zero_slot, hipStream_t s,
+                              const uint32_t* amax_c = nullptr, float* sg_out_c = nullptr,
+                              RhtArg rht = RhtArg{0u, 0u});
+// Maxima of |x H^r| over the row blocks into slot_r and of |H^r^T x| over the
+// column blocks into slot_c (either may be null); the caller zeroes them.
+hipError_t launch_amax_tiles(const void* x, Dt xt, int64_t rows, int64_t cols, uint32_t* slot_r,
+                             uint32_t* slot_c, RhtArg rht, hipStream_t s);
 
 // Exact dequantisation of a Q_1x16 tensor; rows x cols output.
 hipError_t launch_dequant_rows(const uint8_t* codes, const uint8_t* scales, const float* sg,

@@ -258,6 +258,33 @@ __device__ __forceinline__ uint32_t encode_lane(const uint32_t (&v)[EPL], float 
   return c;
 }
 
+// ------------------------------------------------ random Hadamard, 16 ----
+
+// One 16-block (raw float bits, in place) times H^r = diag(s) H_16 / 4, the
+// random Hadamard transform of the NVFP4 NS iteration (Full-Stack FP4,
+// §3.4): sign j flipped where bit j of `mask` is set, then the radix-2
+// butterfly of the Sylvester matrix H_16 with half-widths 1, 2, 4, 8 --
+// each pair (a, b) -> (a + b, a - b) rounded to nearest even in FP32 -- and
+// a final multiplication by 1/4.  The fixed order makes the transformed
+// values, and so the codes, reproducible bit for bit.
+__device__ __forceinline__ void rht16(uint32_t (&v)[16], uint32_t mask) {
+  float f[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) f[j] = __uint_as_float(v[j] ^ (((mask >> j) & 1u) << 31));
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i & h) continue;
+      const float a = f[i], b = f[i + h];
+      f[i] = a + b;
+      f[i + h] = a - b;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 16; ++j) v[j] = __float_as_uint(f[j] * 0.25f);
+}
+
 // ---------------------------------------------------------------- decode --
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));

@@ -171,17 +171,21 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
 // One 64x64 tile per workgroup.  Thread t holds row t/4, columns
 // 16*(t%4)..+15 of the tile: that is one Q_1x16 block, encoded straight from
 // registers.  For Q_16x1 the tile goes through LDS and thread t encodes
-// column t/4, rows 16*(t%4)..+15.
+// column t/4, rows 16*(t%4)..+15.  With `rht` every block is first replaced
+// by its random Hadamard transform (rht16), and the column layout may take
+// its own tensor scale (amax_c, sg_out_c) since X H and H^T X differ.
 
 template <Dt T, bool ROWS, bool COLS>
 __global__ __launch_bounds__(kThreads) void quant_tile_kernel(
     const void* x, int64_t rows, int64_t cols, const uint32_t* amax_slot, float* sg_out,
     uint8_t* row_codes, uint8_t* row_scales, uint8_t* col_codes, uint8_t* col_scales,
-    uint32_t* zero_slot) {
+    uint32_t* zero_slot, const uint32_t* amax_c, float* sg_out_c, RhtArg rht) {
   __shared__ uint32_t tile[64][65];
   const float sg = global_scale_from_amax(*amax_slot);
+  const float sgc = amax_c ? global_scale_from_amax(*amax_c) : sg;
   if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
     if (sg_out) *sg_out = sg;
+    if (sg_out_c) *sg_out_c = sgc;
     if (zero_slot) *zero_slot = 0u;
   }
   const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
@@ -194,8 +198,13 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) v[i] = 0u;
   }
+  if constexpr (COLS) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) tile[tr][tc + i] = v[i];
+  }
   if constexpr (ROWS) {
     if (in) {
+      if (rht.on) rht16(v, rht.mask);
       uint32_t lo, hi, sc;
       encode_block16(v, sg, lo, hi, sc);
       const int64_t e = (r0 + tr) * cols + c0 + tc;
@@ -204,20 +213,68 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(
     }
   }
   if constexpr (COLS) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) tile[tr][tc + i] = v[i];
     __syncthreads();
     const int j = threadIdx.x >> 2, b = threadIdx.x & 3;
     if (c0 + j < cols && r0 + 16 * b < rows) {
       uint32_t w[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) w[i] = tile[16 * b + i][j];
+      if (rht.on) rht16(w, rht.mask);
       uint32_t lo, hi, sc;
-      encode_block16(w, sg, lo, hi, sc);
+      encode_block16(w, sgc, lo, hi, sc);
       const int64_t e = (c0 + j) * rows + r0 + 16 * b;   // element of the transpose
       reinterpret_cast<uint2*>(col_codes)[e / 16] = make_uint2(lo, hi);
       col_scales[e / 16] = (uint8_t)sc;
     }
+  }
+}
+
+// Tensor maxima of the transformed row blocks (x H^r, into slot_r) and/or
+// column blocks (H^r^T x, into slot_c), same tiling as quant_tile_kernel.
+template <Dt T>
+__global__ __launch_bounds__(kThreads) void amax_tiles_kernel(
+    const void* x, int64_t rows, int64_t cols, uint32_t* slot_r, uint32_t* slot_c, RhtArg rht) {
+  __shared__ uint32_t tile[64][65];
+  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+  const int tr = threadIdx.x >> 2, tc = (threadIdx.x & 3) * 16;
+  const bool in = (r0 + tr < rows) && (c0 + tc < cols);
+  uint32_t v[16];
+  if (in) {
+    load16<T>(x, (r0 + tr) * cols + c0 + tc, v);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = 0u;
+  }
+  if (slot_c) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) tile[tr][tc + i] = v[i];
+  }
+  if (slot_r) {
+    if (rht.on) rht16(v, rht.mask);
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t a = abs_bits(v[i]);
+      m = a > m ? a : m;
+    }
+    amax_publish(m, slot_r);
+  }
+  if (slot_c) {
+    __syncthreads();
+    const int j = threadIdx.x >> 2, b = threadIdx.x & 3;
+    uint32_t m = 0;
+    if (c0 + j < cols && r0 + 16 * b < rows) {
+      uint32_t w[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) w[i] = tile[16 * b + i][j];
+      if (rht.on) rht16(w, rht.mask);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t a = abs_bits(w[i]);
+        m = a > m ? a : m;
+      }
+    }
+    amax_publish(m, slot_c);
   }
 }
 
@@ -402,13 +459,15 @@ hipError_t launch_quant_rows(const void* x, Dt xt, int64_t rows, int64_t cols,
 hipError_t launch_quant_tiles(const void* x, Dt xt, int64_t rows, int64_t cols,
                               const uint32_t* amax_slot, float* sg_out, uint8_t* row_codes,
                               uint8_t* row_scales, uint8_t* col_codes, uint8_t* col_scales,
-                              uint32_t* zero_slot, hipStream_t s) {
+                              uint32_t* zero_slot, hipStream_t s, const uint32_t* amax_c,
+                              float* sg_out_c, RhtArg rht) {
   dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 63) / 64));
   const bool R = row_codes != nullptr, C = col_codes != nullptr;
 #define NVFP4_QT(T, RR, CC)                                                                   \
   quant_tile_kernel<T, RR, CC><<<grid, kThreads, 0, s>>>(x, rows, cols, amax_slot, sg_out,    \
                                                          row_codes, row_scales, col_codes,    \
-                                                         col_scales, zero_slot)
+                                                         col_scales, zero_slot, amax_c,       \
+                                                         sg_out_c, rht)
   if (xt == Dt::F32) {
     if (R && C) NVFP4_QT(Dt::F32, true, true);
     else if (R) NVFP4_QT(Dt::F32, true, false);
@@ -419,6 +478,16 @@ hipError_t launch_quant_tiles(const void* x, Dt xt, int64_t rows, int64_t cols,
     else NVFP4_QT(Dt::BF16, false, true);
   }
 #undef NVFP4_QT
+  return hipGetLastError();
+}
+
+hipError_t launch_amax_tiles(const void* x, Dt xt, int64_t rows, int64_t cols, uint32_t* slot_r,
+                             uint32_t* slot_c, RhtArg rht, hipStream_t s) {
+  dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 63) / 64));
+  if (xt == Dt::F32)
+    amax_tiles_kernel<Dt::F32><<<grid, kThreads, 0, s>>>(x, rows, cols, slot_r, slot_c, rht);
+  else
+    amax_tiles_kernel<Dt::BF16><<<grid, kThreads, 0, s>>>(x, rows, cols, slot_r, slot_c, rht);
   return hipGetLastError();
 }
 
