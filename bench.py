@@ -213,6 +213,17 @@ def main():
         "wall_s_timed": round(wall, 3),
     }
 
+    # the same step with the random Hadamard transform of every quantized
+    # operand (one sign mask per NS step)
+    masks = synth.rht_masks(synth.STEPS, seed=spec["seeds"][0])
+    rstep = lambda: ns.ns_orthogonalize_rht(Gd, coeffs, masks, clip, out=out, workspace=ws,
+                                            stream=stream)
+    rms_ = time_events(rstep, args.steps, args.warmup, stream)
+    line["ns_rht"] = {"ms": round(rms_, 4), "value": round(flops / (rms_ * 1e-3) / 1e12, 2),
+                      "unit": "TFLOP/s",
+                      "what": "ns_orthogonalize_rht: the same step with H_16^r on every "
+                              "quantized operand (extra amax passes over the transformed tensors)"}
+
     # BF16 torch NS of the same matrix, same GPU
     bms = bf16_ns_ms(torch, Gd, coeffs, stream)
     line["bf16_ns"] = {"ms": round(bms, 4), "speedup_nvfp4_vs_bf16": round(bms / ms, 3),
@@ -226,7 +237,7 @@ def main():
         codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
         scales = torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev)
         sg = torch.empty(1, dtype=torch.float32, device=dev)
-        qws = torch.empty(256, dtype=torch.uint8, device=dev)
+        qws = torch.empty(ns.nvfp4_quantize_workspace_bytes(rows, cols), dtype=torch.uint8, device=dev)
         deq = torch.empty((rows, cols), dtype=torch.bfloat16, device=dev)
 
         def qstep():

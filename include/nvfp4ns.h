@@ -61,7 +61,8 @@ typedef enum { NS_F32 = 0, NS_BF16 = 1 } ns_dtype;
  * scale bytes). */
 typedef enum { NVFP4_ROWS = 0, NVFP4_COLS = 1 } nvfp4_axis;
 
-/* Workspace of nvfp4_quantize, in bytes (a few counters; >= 256). */
+/* Workspace of nvfp4_quantize and nvfp4_quantize_rht, in bytes (the partial
+ * tensor maxima: 2 KiB, independent of the shape). */
 size_t nvfp4_quantize_workspace_bytes(int64_t rows, int64_t cols);
 
 /*

@@ -172,6 +172,10 @@ def nvfp4_dequantize(codes, scales, global_scale, rows, cols, axis=NVFP4_ROWS,
     return out
 
 
+def nvfp4_quantize_workspace_bytes(rows, cols):
+    return int(_lib.nvfp4_quantize_workspace_bytes(rows, cols))
+
+
 def nvfp4_gemm_workspace_bytes(M, N, K, symmetric=False):
     return int(_lib.nvfp4_gemm_workspace_bytes(M, N, K, 1 if symmetric else 0))
 

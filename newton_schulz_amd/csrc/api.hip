@@ -41,11 +41,13 @@ inline ns_status hip_failed(hipError_t e, const char* what, int line) {
     if (ns_e_ != hipSuccess) return hip_failed(ns_e_, #call, __LINE__); \
   } while (0)
 
-// Zero a few device words with a kernel launch (no memset node, so the
-// sequence can be captured into a graph).
+// Zero device words with a kernel launch (no memset node, so the sequence
+// can be captured into a graph).
 __global__ void zero_words_kernel(uint32_t* p, int n) {
-  if ((int)threadIdx.x < n) p[threadIdx.x] = 0u;
+  for (int i = (int)threadIdx.x; i < n; i += (int)blockDim.x) p[i] = 0u;
 }
+
+constexpr int kSlotWords = nvfp4::kAmaxSlotWords;
 
 // ---- workspace of one Newton–Schulz problem (iterate is xm x xn, xm <= xn)
 struct NsLayout {
@@ -77,7 +79,7 @@ NsLayout ns_layout(int64_t m, int64_t n) {
   L.qb_c = take(xm * xm / 2);
   L.qb_s = take(xm * xm / 16);
   L.sg = take(4 * sizeof(float));
-  L.slot = take(4 * sizeof(uint32_t));
+  L.slot = take(4 * kSlotWords * sizeof(uint32_t));
   L.part = take(nvfp4::kNormParts * sizeof(double));
   L.inv = take(sizeof(double));
   L.gemm_part = take(part_bytes);
@@ -103,7 +105,8 @@ ns_status ns_run(const void* G, ns_dtype gt, int64_t m, int64_t n, const float* 
   uint32_t* slot = reinterpret_cast<uint32_t*>(ws + L.slot);
   double* part = reinterpret_cast<double*>(ws + L.part);
   double* inv = reinterpret_cast<double*>(ws + L.inv);
-  uint32_t *slotX = slot, *slotA = slot + 1, *slotB = slot + 2, *slotXc = slot + 3;
+  uint32_t *slotX = slot, *slotA = slot + kSlotWords, *slotB = slot + 2 * kSlotWords,
+           *slotXc = slot + 3 * kSlotWords;
   float *sgX = sg, *sgA = sg + 1, *sgB = sg + 2, *sgXc = sg + 3;
 
   float* gpart = reinterpret_cast<float*>(ws + L.gemm_part);
@@ -116,28 +119,28 @@ ns_status ns_run(const void* G, ns_dtype gt, int64_t m, int64_t n, const float* 
     const float a = coeffs[3 * it], b = coeffs[3 * it + 1], c = coeffs[3 * it + 2];
     if (masks) {
       const nvfp4::RhtArg h{1u, (uint32_t)masks[it]};
-      zero_words_kernel<<<1, 64, 0, s>>>(slot, 4);
+      zero_words_kernel<<<1, 256, 0, s>>>(slot, 4 * kSlotWords);
       NS_TRY(hipGetLastError());
       // qX = Q_1x16(X H), qX16 = Q_16x1(H^T X), each with its own s_g
       NS_TRY(nvfp4::launch_amax_tiles(X, Dt::F32, xm, xn, slotX, slotXc, h, s));
       NS_TRY(nvfp4::launch_quant_tiles(X, Dt::F32, xm, xn, slotX, sgX, ws + L.qx_c, ws + L.qx_s,
                                        ws + L.qt_c, ws + L.qt_s, nullptr, s, slotXc, sgXc, h));
       nvfp4::GemmProblem g1{ws + L.qx_c, ws + L.qx_s, sgX, ws + L.qx_c, ws + L.qx_s, sgX,
-                            xm, xm, xn, 1, 1.0f, 0.0f, nullptr, A, nullptr};
+                            xm, xm, xn, 1, 1.0f, 0.0f, nullptr, A, nullptr, 0};
       NS_TRY(nvfp4::launch_gemm(g1, L.p1, gpart, s));
       // qA = Q_1x16(A H)
       NS_TRY(nvfp4::launch_amax_tiles(A, Dt::F32, xm, xm, slotA, nullptr, h, s));
       NS_TRY(nvfp4::launch_quant_tiles(A, Dt::F32, xm, xm, slotA, sgA, ws + L.qa_c, ws + L.qa_s,
                                        nullptr, nullptr, nullptr, s, nullptr, nullptr, h));
       nvfp4::GemmProblem g2{ws + L.qa_c, ws + L.qa_s, sgA, ws + L.qa_c, ws + L.qa_s, sgA,
-                            xm, xm, xm, 1, c, b, A, B, nullptr};
+                            xm, xm, xm, 1, c, b, A, B, nullptr, 0};
       NS_TRY(nvfp4::launch_gemm(g2, L.p2, gpart, s));
       // qB = Q_1x16(B H)
       NS_TRY(nvfp4::launch_amax_tiles(B, Dt::F32, xm, xm, slotB, nullptr, h, s));
       NS_TRY(nvfp4::launch_quant_tiles(B, Dt::F32, xm, xm, slotB, sgB, ws + L.qb_c, ws + L.qb_s,
                                        nullptr, nullptr, nullptr, s, nullptr, nullptr, h));
       nvfp4::GemmProblem g3{ws + L.qb_c, ws + L.qb_s, sgB, ws + L.qt_c, ws + L.qt_s, sgXc,
-                            xm, xn, xm, 0, 1.0f, a, X, X, nullptr};
+                            xm, xn, xm, 0, 1.0f, a, X, X, nullptr, 0};
       NS_TRY(nvfp4::launch_gemm(g3, L.p3, gpart, s));
       continue;
     }
@@ -146,21 +149,21 @@ ns_status ns_run(const void* G, ns_dtype gt, int64_t m, int64_t n, const float* 
                                      ws + L.qt_c, ws + L.qt_s, slotA, s));
     // A = qX qX^T (symmetric, K = xn)
     nvfp4::GemmProblem g1{ws + L.qx_c, ws + L.qx_s, sgX, ws + L.qx_c, ws + L.qx_s, sgX,
-                          xm, xm, xn, 1, 1.0f, 0.0f, nullptr, A, slotA};
+                          xm, xm, xn, 1, 1.0f, 0.0f, nullptr, A, slotA, 1};
     NS_TRY(nvfp4::launch_gemm(g1, L.p1, gpart, s));
     // qA = Q_1x16(A); A is exactly symmetric, so Q_16x1(A) = qA^T
     NS_TRY(nvfp4::launch_quant_rows(A, Dt::F32, xm, xm, slotA, sgA, ws + L.qa_c, ws + L.qa_s,
                                     slotB, s));
     // B = b A + c qA qA^T (symmetric, K = xm)
     nvfp4::GemmProblem g2{ws + L.qa_c, ws + L.qa_s, sgA, ws + L.qa_c, ws + L.qa_s, sgA,
-                          xm, xm, xm, 1, c, b, A, B, slotB};
+                          xm, xm, xm, 1, c, b, A, B, slotB, 1};
     NS_TRY(nvfp4::launch_gemm(g2, L.p2, gpart, s));
     // qB = Q_1x16(B)
     NS_TRY(nvfp4::launch_quant_rows(B, Dt::F32, xm, xm, slotB, sgB, ws + L.qb_c, ws + L.qb_s,
                                     slotX, s));
     // X' = a X + qB qX16 (K = xm), in place
     nvfp4::GemmProblem g3{ws + L.qb_c, ws + L.qb_s, sgB, ws + L.qt_c, ws + L.qt_s, sgX,
-                          xm, xn, xm, 0, 1.0f, a, X, X, slotX};
+                          xm, xn, xm, 0, 1.0f, a, X, X, slotX, 1};
     NS_TRY(nvfp4::launch_gemm(g3, L.p3, gpart, s));
   }
   NS_TRY(nvfp4::launch_write_out(X, xm, xn, tr, out, (Dt)ot, s));
@@ -190,7 +193,7 @@ ns_status validate_ns(const void* G, int gt, int64_t m, int64_t n, const float* 
 
 extern "C" {
 
-size_t nvfp4_quantize_workspace_bytes(int64_t, int64_t) { return kAlign; }
+size_t nvfp4_quantize_workspace_bytes(int64_t, int64_t) { return align_up(kSlotWords * sizeof(uint32_t)); }
 
 ns_status nvfp4_quantize(const void* x, ns_dtype xt, int64_t rows, int64_t cols, nvfp4_axis axis,
                          uint8_t* codes, uint8_t* scales, float* global_scale, void* ws,
@@ -202,7 +205,7 @@ ns_status nvfp4_quantize(const void* x, ns_dtype xt, int64_t rows, int64_t cols,
   if (!ws || ws_bytes < nvfp4_quantize_workspace_bytes(rows, cols)) return NS_ERR_WORKSPACE;
   hipStream_t s = as_stream(stream);
   uint32_t* slot = static_cast<uint32_t*>(ws);
-  zero_words_kernel<<<1, 64, 0, s>>>(slot, 1);
+  zero_words_kernel<<<1, 256, 0, s>>>(slot, kSlotWords);
   NS_TRY(hipGetLastError());
   NS_TRY(nvfp4::launch_amax(x, (Dt)xt, rows * cols, slot, s));
   if (axis == NVFP4_ROWS)
@@ -225,7 +228,7 @@ ns_status nvfp4_quantize_rht(const void* x, ns_dtype xt, int64_t rows, int64_t c
   hipStream_t s = as_stream(stream);
   uint32_t* slot = static_cast<uint32_t*>(ws);
   const nvfp4::RhtArg h{1u, (uint32_t)mask};
-  zero_words_kernel<<<1, 64, 0, s>>>(slot, 1);
+  zero_words_kernel<<<1, 256, 0, s>>>(slot, kSlotWords);
   NS_TRY(hipGetLastError());
   if (axis == NVFP4_ROWS) {
     NS_TRY(nvfp4::launch_amax_tiles(x, (Dt)xt, rows, cols, slot, nullptr, h, s));
@@ -278,7 +281,7 @@ ns_status nvfp4_gemm(const uint8_t* codes_p, const uint8_t* scales_p, const floa
   if (split_ok && ws_bytes < plan.ws_bytes) return NS_ERR_WORKSPACE;
   nvfp4::GemmProblem g{codes_p, scales_p, sg_p, codes_q, scales_q, sg_q, M, N, K,
                        symmetric ? 1 : 0, alpha, beta, beta != 0.0f ? addend : nullptr, out,
-                       amax_out};
+                       amax_out, 0};
   NS_TRY(nvfp4::launch_gemm(g, plan, static_cast<float*>(ws), as_stream(stream)));
   return NS_OK;
 }

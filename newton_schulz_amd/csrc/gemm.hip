@@ -269,7 +269,7 @@ __device__ __forceinline__ void epilogue(const GemmProblem& g, floatx16 (&acc)[C
         }
       }
     }
-  if (g.amax_out) amax_publish(amax, g.amax_out);
+  if (g.amax_out) amax_publish_wave(amax, g.amax_out, g.amax_parts != 0);
 }
 
 template <class C, bool SYM>
@@ -612,7 +612,7 @@ __global__ __launch_bounds__(GThreads, 2) void gemm_general_kernel(GemmProblem g
         const uint32_t a = abs_bits(v);
         amax = a > amax ? a : amax;
       }
-  if (g.amax_out) amax_publish(amax, g.amax_out);
+  if (g.amax_out) amax_publish_wave(amax, g.amax_out, g.amax_parts != 0);
 }
 
 // ---------------------------------------------------------------- plans ----

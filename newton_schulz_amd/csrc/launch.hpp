@@ -15,6 +15,11 @@ struct RhtArg {
   uint32_t on, mask;
 };
 
+// Words of one amax slot (kAmaxParts partials spaced one 128-byte line
+// apart; see nvfp4_device.hpp).  Zeroed by the caller before a producer
+// folds into it.
+constexpr int kAmaxSlotWords = 16 * 32;
+
 // ---- quantizer (quant.hip) -------------------------------------------------
 // max |x| over n elements into *slot (atomic max on the bit pattern; the
 // caller zeroes *slot first).  Non-finite values count as NaN.
@@ -63,6 +68,7 @@ struct GemmProblem {
   const float* addend;
   float* out;
   uint32_t* amax_out;
+  int amax_parts;   // amax_out is an amax slot of partials (1) or one word (0)
 };
 
 // Launch plan of one product: the fast path needs K % 128 == 0 and picks a

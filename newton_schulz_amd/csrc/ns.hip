@@ -78,12 +78,10 @@ __global__ __launch_bounds__(kThreads) void norm_finalize_kernel(const double* p
   double acc = 0.0;
   for (int i = threadIdx.x; i < kNormParts; i += kThreads) acc += part[i];
   double s = block_sum(acc);
-  if (threadIdx.x == 0) {
-    *inv = 1.0 / (sqrt(s) + 1e-7);
-    if (z0) *z0 = 0u;
-    if (z1) *z1 = 0u;
-    if (z2) *z2 = 0u;
-  }
+  if (threadIdx.x == 0) *inv = 1.0 / (sqrt(s) + 1e-7);
+  if (z0) amax_clear(z0);
+  if (z1) amax_clear(z1);
+  if (z2) amax_clear(z2);
 }
 
 // X tile 64 x 64 per workgroup; thread t owns X row t/4, columns
@@ -135,7 +133,7 @@ __global__ __launch_bounds__(kThreads) void normalize_kernel(const void* G, int6
 #pragma unroll
     for (int j = 0; j < 4; ++j) o[j] = make_float4(y[4 * j], y[4 * j + 1], y[4 * j + 2], y[4 * j + 3]);
   }
-  amax_publish(amax, amax_slot);
+  amax_publish_block(amax, amax_slot);
 }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {

@@ -35,20 +35,68 @@ __device__ __forceinline__ uint32_t abs_bits(uint32_t raw) {
   return b >= 0x7F800000u ? kNaNBits : b;
 }
 
-// Wave-reduce m and fold it into *slot with one atomic per wave, skipped when
-// the slot already holds at least m.  The slot only grows, so a stale read
-// can only cost an extra atomic, never a lost maximum; skipping keeps
-// thousands of waves from serialising on one address.
-__device__ __forceinline__ void amax_publish(uint32_t m, uint32_t* slot) {
+// Tensor maxima are gathered in "amax slots": kAmaxParts partial words, one
+// per 128-byte line.  Device-scope atomics on one address serialise (about
+// 10 ns each on MI355X), so each workgroup folds one block-wide maximum into
+// partial (workgroup index mod kAmaxParts) and readers take the maximum of
+// the partials.  Values are |x| bit patterns (ordered like the magnitudes;
+// NaN and infinity map to the NaN pattern, above every finite value).
+constexpr int kAmaxParts = 16;
+constexpr int kAmaxStride = 32;                        // words between partials
+constexpr int kAmaxWords = kAmaxParts * kAmaxStride;   // words per slot
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t m) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
-    uint32_t w = __shfl_xor(m, o, 64);
+    const uint32_t w = __shfl_xor(m, o, 64);
     m = w > m ? w : m;
   }
-  if ((threadIdx.x & 63) == 0) {
-    uint32_t cur = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (m > cur) atomicMax(slot, m);
+  return m;
+}
+
+// Block-wide maximum of m into `slot`: a partial of an amax slot
+// (parts = true) or a single word (parts = false).  Every thread of the
+// block must call it (it synchronises the block); at most 16 waves.
+__device__ __forceinline__ void amax_publish_block(uint32_t m, uint32_t* slot, bool parts = true) {
+  __shared__ uint32_t red[16];
+  m = wave_max_u32(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r = 0;
+    const int waves = (int)(blockDim.x + 63) >> 6;
+    for (int w = 0; w < waves; ++w) r = red[w] > r ? red[w] : r;
+    const unsigned b = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+    if (r != 0u) atomicMax(parts ? slot + (b % kAmaxParts) * kAmaxStride : slot, r);
   }
+}
+
+// Wave-wide maximum of m into `slot`, without a block barrier (for kernels
+// whose waves finish independently): lane 0 folds it into partial
+// (global wave index mod kAmaxParts), or into the single word.
+__device__ __forceinline__ void amax_publish_wave(uint32_t m, uint32_t* slot, bool parts = true) {
+  m = wave_max_u32(m);
+  if ((threadIdx.x & 63) == 0 && m != 0u) {
+    const unsigned b = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+    const unsigned w = b * ((blockDim.x + 63) >> 6) + (threadIdx.x >> 6);
+    atomicMax(parts ? slot + (w % kAmaxParts) * kAmaxStride : slot, m);
+  }
+}
+
+// Maximum over the partials of an amax slot.
+__device__ __forceinline__ uint32_t amax_read(const uint32_t* slot) {
+  uint32_t r = 0;
+#pragma unroll
+  for (int i = 0; i < kAmaxParts; ++i) {
+    const uint32_t v = slot[i * kAmaxStride];
+    r = v > r ? v : r;
+  }
+  return r;
+}
+
+// Zero an amax slot with the threads of one block.
+__device__ __forceinline__ void amax_clear(uint32_t* slot) {
+  for (int i = (int)threadIdx.x; i < kAmaxParts; i += (int)blockDim.x) slot[i * kAmaxStride] = 0u;
 }
 
 // s_g = RN_f32(amax / (6 * 448)); NaN stays NaN.

@@ -11,6 +11,8 @@
 
 namespace nvfp4 {
 
+static_assert(kAmaxSlotWords == kAmaxWords, "amax slot size");
+
 namespace {
 
 constexpr int kThreads = 256;
@@ -89,17 +91,7 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(const void* x, int64_t n
     fold(w0); fold(w1); fold(w2); fold(w3);
   }
   for (; i < nvec; i += stride) fold(p[i]);
-  m = wave_max(m);
-  __shared__ uint32_t red[kThreads / 64];
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t r = red[0];
-#pragma unroll
-    for (int w = 1; w < kThreads / 64; ++w) r = red[w] > r ? red[w] : r;
-    uint32_t cur = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (r > cur) atomicMax(slot, r);
-  }
+  amax_publish_block(m, slot);
 }
 
 // ------------------------------------------------------- row quantizer ----
@@ -115,10 +107,10 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
     uint8_t* codes, uint8_t* scales, uint32_t* zero_slot) {
   constexpr int EPL = T == Dt::F32 ? 4 : 8;   // elements per lane
   constexpr int G = 16 / EPL;                 // lanes per block
-  const float sg = global_scale_from_amax(*amax_slot);
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
-    if (sg_out) *sg_out = sg;
-    if (zero_slot) *zero_slot = 0u;
+  const float sg = global_scale_from_amax(amax_read(amax_slot));
+  if (blockIdx.x == 0) {
+    if (sg_out && threadIdx.x == 0) *sg_out = sg;
+    if (zero_slot) amax_clear(zero_slot);
   }
   const int64_t items = nelem / EPL, groups = items / G;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
@@ -181,12 +173,14 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(
     uint8_t* row_codes, uint8_t* row_scales, uint8_t* col_codes, uint8_t* col_scales,
     uint32_t* zero_slot, const uint32_t* amax_c, float* sg_out_c, RhtArg rht) {
   __shared__ uint32_t tile[64][65];
-  const float sg = global_scale_from_amax(*amax_slot);
-  const float sgc = amax_c ? global_scale_from_amax(*amax_c) : sg;
-  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
-    if (sg_out) *sg_out = sg;
-    if (sg_out_c) *sg_out_c = sgc;
-    if (zero_slot) *zero_slot = 0u;
+  const float sg = global_scale_from_amax(amax_read(amax_slot));
+  const float sgc = amax_c ? global_scale_from_amax(amax_read(amax_c)) : sg;
+  if (blockIdx.x == 0 && blockIdx.y == 0) {
+    if (threadIdx.x == 0) {
+      if (sg_out) *sg_out = sg;
+      if (sg_out_c) *sg_out_c = sgc;
+    }
+    if (zero_slot) amax_clear(zero_slot);
   }
   const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
   const int tr = threadIdx.x >> 2, tc = (threadIdx.x & 3) * 16;
@@ -257,7 +251,7 @@ __global__ __launch_bounds__(kThreads) void amax_tiles_kernel(
       const uint32_t a = abs_bits(v[i]);
       m = a > m ? a : m;
     }
-    amax_publish(m, slot_r);
+    amax_publish_block(m, slot_r);
   }
   if (slot_c) {
     __syncthreads();
@@ -274,7 +268,7 @@ __global__ __launch_bounds__(kThreads) void amax_tiles_kernel(
         m = a > m ? a : m;
       }
     }
-    amax_publish(m, slot_c);
+    amax_publish_block(m, slot_c);
   }
 }
 

@@ -130,6 +130,16 @@ def test_ns_rht_bf16_lowrank_with_clip():
     _compare_ns(got, G, coeffs, clip, masks, "bf16 lowrank 384x640 clip")
 
 
+def test_ns_rht_2048_full_size():
+    """The 2048^2 BF16 low-rank workload with its 8 x RMS clip, transformed."""
+    spec = synth.ns_workload("ns2048")
+    G, bits, clip = synth.ns_matrix(spec, 0)
+    coeffs = [CUBIC] * 5
+    masks = synth.rht_masks(5, seed=3)
+    got = host(ns.ns_orthogonalize_rht(to_dev_bf16(bits), coeffs, masks, clip))
+    _compare_ns(got, G, coeffs, clip, masks, "2048^2 lowrank cubic")
+
+
 def test_ns_rht_rejects_missing_masks():
     import ctypes
     fake = ctypes.c_void_p(0x1000)
