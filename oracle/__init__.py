@@ -11,6 +11,8 @@ Projections, Optimizers, and Attention" (arXiv 2607.04422):
   (x_hat = x_E2M1 * s * s_g, §2 "NVFP4 format"; RTN per §3.4).
 * ``rht``      — the random 16 x 16 Hadamard transform that §3.4 applies to
   every quantized operand along the contraction axis.
+* ``quantile`` — the p99 clip threshold as an order statistic of |G| (§3.4
+  p99 outlier clipping, App. F Table 8 quantile ratio 0.99).
 * ``ns``       — the Newton–Schulz iteration of the Root optimizer, exact
   (§2 "Root optimizer") and with NVFP4 operands (§3.4, the three-line NVFP4
   NS iteration, with or without the transform), plus the caller-side clip
@@ -27,7 +29,8 @@ round-trip of exactly representable tensors; idempotence; the per-block error
 bound; the FP64 GEMM against a pure-Python triple loop; the Hadamard matrix
 against its recursive construction, its orthogonality, the transform against
 its definition in plain loops, the FP32 butterfly against the FP64 product,
-and the cancellation of the transform in every NS product; exact NS against the
+and the cancellation of the transform in every NS product; the quantile
+against sorting and the library's inverted-CDF quantile; exact NS against the
 SVD closed form of its scalar map and, for the cubic, the polar factor; the
 quantized NS against the scalar map on matrices whose quantization is benign.
 The quantized NS on general inputs has no pin beyond the composition of these
