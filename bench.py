@@ -224,6 +224,20 @@ def main():
                       "what": "ns_orthogonalize_rht: the same step with H_16^r on every "
                               "quantized operand (extra amax passes over the transformed tensors)"}
 
+    # the same step with the clip taken on the device as the 0.99 quantile of
+    # |G| (three radix-selection passes over G before the normalisation)
+    qstep_ = lambda: ns.ns_orthogonalize_ex(Gd, coeffs, clip_quantile=0.99, out=out, workspace=ws,
+                                            stream=stream)
+    qms_ = time_events(qstep_, args.steps, args.warmup, stream)
+    qws_ = torch.empty(ns.ns_abs_quantile_workspace_bytes(), dtype=torch.uint8, device=dev)
+    qout_ = torch.empty(1, dtype=torch.float32, device=dev)
+    sel_ms = time_events(lambda: ns.ns_abs_quantile(Gd, 0.99, out=qout_, workspace=qws_, stream=stream),
+                         20, 3, stream)
+    line["ns_p99_clip"] = {"ms": round(qms_, 4), "value": round(flops / (qms_ * 1e-3) / 1e12, 2),
+                           "unit": "TFLOP/s", "quantile_ms": round(sel_ms, 4),
+                           "what": "ns_orthogonalize_ex with clip_quantile=0.99: the clip is the "
+                                   "0.99 quantile of |G| found on the device (radix selection)"}
+
     # BF16 torch NS of the same matrix, same GPU
     bms = bf16_ns_ms(torch, Gd, coeffs, stream)
     line["bf16_ns"] = {"ms": round(bms, 4), "speedup_nvfp4_vs_bf16": round(bms / ms, 3),

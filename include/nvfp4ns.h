@@ -175,6 +175,43 @@ ns_status ns_orthogonalize_rht(const void* G, ns_dtype gt, int64_t m, int64_t n,
                                const float* coeffs, int k, float clip, const uint16_t* masks,
                                void* out, ns_dtype ot, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * ns_abs_quantile — the q-quantile of |x| over `count` elements, the clip
+ * threshold of the NVFP4 Root path (§3.4 "p99 outlier clipping"; App. F
+ * Table 8 "Root quantile ratio 0.99"), read as an order statistic: the k-th
+ * smallest magnitude, k = ceil(q * count) computed in double and clamped to
+ * [1, count].  Magnitudes are ordered by their FP32 bit patterns with the
+ * sign cleared (BF16 widened exactly); NaN and infinity count as NaN, above
+ * every finite value, so a result that reaches them is NaN.
+ *   x      device, `count` FP32 or BF16 (xt) values, read only.
+ *   q      in (0, 1].
+ *   out    device, one float (written when the enqueued work runs).
+ *   ws     device scratch of ns_abs_quantile_workspace_bytes() (256 KiB).
+ * count must be a positive multiple of 16 below 2^31.
+ */
+size_t ns_abs_quantile_workspace_bytes(void);
+ns_status ns_abs_quantile(const void* x, ns_dtype xt, int64_t count, double q, float* out,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/* Options of ns_orthogonalize_ex. */
+typedef struct {
+  float clip;               /* as in ns_orthogonalize; ignored when clip_quantile > 0 */
+  double clip_quantile;     /* 0: use clip.  In (0, 1]: clip = the clip_quantile-quantile
+                               of |G| (as ns_abs_quantile), found on the device */
+  const uint16_t* rht_masks;/* NULL, or a HOST array of k masks (as ns_orthogonalize_rht) */
+} ns_options;
+
+/*
+ * ns_orthogonalize_ex — ns_orthogonalize with the clip threshold taken on
+ * the device as a quantile of |G| and/or the random Hadamard transform, as
+ * set in `opt` (HOST pointer, not NULL).  NS_ERR_ARG for a clip_quantile
+ * outside {0} U (0, 1].  Workspace ns_workspace_bytes(m, n); other
+ * arguments and errors as ns_orthogonalize.
+ */
+ns_status ns_orthogonalize_ex(const void* G, ns_dtype gt, int64_t m, int64_t n,
+                              const float* coeffs, int k, const ns_options* opt, void* out,
+                              ns_dtype ot, void* ws, size_t ws_bytes, void* stream);
+
 /* Workspace of ns_orthogonalize_grouped for `count` matrices (host arrays m, n). */
 size_t ns_grouped_workspace_bytes(int count, const int64_t* m, const int64_t* n);
 

@@ -8,7 +8,8 @@ module raises ImportError.
 Functions carry the C names:
     nvfp4_quantize, nvfp4_quantize_rht, nvfp4_dequantize,
     nvfp4_gemm_workspace_bytes, nvfp4_gemm, ns_workspace_bytes,
-    ns_orthogonalize, ns_orthogonalize_rht,
+    ns_orthogonalize, ns_orthogonalize_rht, ns_orthogonalize_ex,
+    ns_abs_quantile_workspace_bytes, ns_abs_quantile,
     ns_grouped_workspace_bytes, ns_orthogonalize_grouped
 """
 import ctypes
@@ -37,6 +38,13 @@ STATUS_NAMES = {0: "NS_OK", -1: "NS_ERR_ARG", -2: "NS_ERR_SHAPE",
 
 _i64, _sz, _vp, _f, _i = ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float, ctypes.c_int
 _u16 = ctypes.c_uint16
+_d = ctypes.c_double
+
+
+class NsOptions(ctypes.Structure):
+    """ns_options of the C ABI."""
+    _fields_ = [("clip", ctypes.c_float), ("clip_quantile", ctypes.c_double),
+                ("rht_masks", ctypes.POINTER(ctypes.c_uint16))]
 
 _SIGS = {
     "nvfp4_quantize_workspace_bytes": (_sz, [_i64, _i64]),
@@ -49,6 +57,9 @@ _SIGS = {
     "ns_workspace_bytes": (_sz, [_i64, _i64]),
     "ns_orthogonalize": (_i, [_vp, _i, _i64, _i64, _vp, _i, _f, _vp, _i, _vp, _sz, _vp]),
     "ns_orthogonalize_rht": (_i, [_vp, _i, _i64, _i64, _vp, _i, _f, _vp, _vp, _i, _vp, _sz, _vp]),
+    "ns_orthogonalize_ex": (_i, [_vp, _i, _i64, _i64, _vp, _i, _vp, _vp, _i, _vp, _sz, _vp]),
+    "ns_abs_quantile_workspace_bytes": (_sz, []),
+    "ns_abs_quantile": (_i, [_vp, _i, _i64, _d, _vp, _vp, _sz, _vp]),
     "ns_grouped_workspace_bytes": (_sz, [_i, _vp, _vp]),
     "ns_orthogonalize_grouped": (_i, [_i, _vp, _vp, _vp, _i, _vp, _i, _vp, _vp, _i, _vp, _sz, _vp]),
 }
@@ -250,6 +261,50 @@ def ns_orthogonalize_rht(G, coeffs, masks, clip=float("inf"), out_dtype=NS_F32, 
     _check(_lib.ns_orthogonalize_rht(_ptr(G), _dt(G), m, n, carr, k, float(clip), marr, _ptr(out),
                                      _dt(out), _ptr(workspace), workspace.numel(), _stream(stream)),
            "ns_orthogonalize_rht")
+    return out
+
+
+def ns_orthogonalize_ex(G, coeffs, clip=float("inf"), clip_quantile=0.0, rht_masks=None,
+                        out_dtype=NS_F32, out=None, workspace=None, stream=None):
+    """ns_orthogonalize with an on-device quantile clip (clip_quantile in
+    (0, 1]; 0 uses `clip`) and/or the random Hadamard transform (one
+    16-bit mask per step)."""
+    torch = _torch()
+    _need_cuda(G, out)
+    m, n = G.shape
+    if out is None:
+        out = torch.empty((m, n), dtype=_out_dtype(out_dtype), device=G.device)
+    if workspace is None:
+        workspace = torch.empty(ns_workspace_bytes(m, n), dtype=torch.uint8, device=G.device)
+    carr, k = _coeff_array(coeffs)
+    opt = NsOptions(float(clip), float(clip_quantile), None)
+    marr = None
+    if rht_masks is not None:
+        if len(rht_masks) != k:
+            raise ValueError("one Hadamard mask per step")
+        marr = (ctypes.c_uint16 * k)(*[int(v) & 0xFFFF for v in rht_masks])
+        opt.rht_masks = ctypes.cast(marr, ctypes.POINTER(ctypes.c_uint16))
+    _check(_lib.ns_orthogonalize_ex(_ptr(G), _dt(G), m, n, carr, k, ctypes.byref(opt), _ptr(out),
+                                    _dt(out), _ptr(workspace), workspace.numel(), _stream(stream)),
+           "ns_orthogonalize_ex")
+    return out
+
+
+def ns_abs_quantile_workspace_bytes():
+    return int(_lib.ns_abs_quantile_workspace_bytes())
+
+
+def ns_abs_quantile(x, q, out=None, workspace=None, stream=None):
+    """The q-quantile of |x| (k-th smallest magnitude, k = ceil(q N)) as a
+    one-element float32 device tensor."""
+    torch = _torch()
+    _need_cuda(x)
+    if out is None:
+        out = torch.empty(1, dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(ns_abs_quantile_workspace_bytes(), dtype=torch.uint8, device=x.device)
+    _check(_lib.ns_abs_quantile(_ptr(x), _dt(x), x.numel(), float(q), _ptr(out), _ptr(workspace),
+                                workspace.numel(), _stream(stream)), "ns_abs_quantile")
     return out
 
 

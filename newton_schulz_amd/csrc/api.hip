@@ -51,7 +51,7 @@ constexpr int kSlotWords = nvfp4::kAmaxSlotWords;
 
 // ---- workspace of one Newton–Schulz problem (iterate is xm x xn, xm <= xn)
 struct NsLayout {
-  size_t X, A, B, qx_c, qx_s, qt_c, qt_s, qa_c, qa_s, qb_c, qb_s, sg, slot, part, inv;
+  size_t X, A, B, qx_c, qx_s, qt_c, qt_s, qa_c, qa_s, qb_c, qb_s, sg, slot, part, inv, clip, sel;
   size_t gemm_part, total;
   nvfp4::GemmPlan p1, p2, p3;
 };
@@ -82,6 +82,8 @@ NsLayout ns_layout(int64_t m, int64_t n) {
   L.slot = take(4 * kSlotWords * sizeof(uint32_t));
   L.part = take(nvfp4::kNormParts * sizeof(double));
   L.inv = take(sizeof(double));
+  L.clip = take(sizeof(float));
+  L.sel = take(nvfp4::abs_quantile_workspace_bytes());
   L.gemm_part = take(part_bytes);
   L.total = o;
   return L;
@@ -92,9 +94,18 @@ NsLayout ns_layout(int64_t m, int64_t n) {
 // transform H^r: qX = Q_1x16(X H), qX16 = Q_16x1(H^T X) (own s_g),
 // qA = Q_1x16(A H) (= Q_16x1(H^T A)^T since A is symmetric), qB = Q_1x16(B H);
 // the maxima of the transformed tensors come from their own tiled pass.
+// 1-based rank of the q-quantile among n values: ceil(q n) in double,
+// clamped to [1, n].
+uint32_t quantile_rank(double q, int64_t n) {
+  double k = std::ceil(q * (double)n);
+  if (k < 1.0) k = 1.0;
+  if (k > (double)n) k = (double)n;
+  return (uint32_t)k;
+}
+
 ns_status ns_run(const void* G, ns_dtype gt, int64_t m, int64_t n, const float* coeffs, int k,
-                 float clip, const uint16_t* masks, void* out, ns_dtype ot, uint8_t* ws,
-                 hipStream_t s) {
+                 float clip, double clip_q, const uint16_t* masks, void* out, ns_dtype ot,
+                 uint8_t* ws, hipStream_t s) {
   const NsLayout L = ns_layout(m, n);
   const bool tr = m > n;
   const int64_t xm = tr ? n : m, xn = tr ? m : n;
@@ -111,9 +122,16 @@ ns_status ns_run(const void* G, ns_dtype gt, int64_t m, int64_t n, const float* 
 
   float* gpart = reinterpret_cast<float*>(ws + L.gemm_part);
 
-  NS_TRY(nvfp4::launch_norm_partials(G, (Dt)gt, m * n, clip, part, s));
+  // with clip_q > 0 the clip is the q-quantile of |G|, found on the device
+  float* clipd = nullptr;
+  if (clip_q > 0.0) {
+    clipd = reinterpret_cast<float*>(ws + L.clip);
+    NS_TRY(nvfp4::launch_abs_quantile(G, (Dt)gt, m * n, quantile_rank(clip_q, m * n), clipd,
+                                      ws + L.sel, s));
+  }
+  NS_TRY(nvfp4::launch_norm_partials(G, (Dt)gt, m * n, clip, clipd, part, s));
   NS_TRY(nvfp4::launch_norm_finalize(part, inv, slotX, slotA, slotB, s));
-  NS_TRY(nvfp4::launch_normalize(G, (Dt)gt, xm, xn, tr, clip, inv, X, slotX, s));
+  NS_TRY(nvfp4::launch_normalize(G, (Dt)gt, xm, xn, tr, clip, clipd, inv, X, slotX, s));
 
   for (int it = 0; it < k; ++it) {
     const float a = coeffs[3 * it], b = coeffs[3 * it + 1], c = coeffs[3 * it + 2];
@@ -297,7 +315,7 @@ ns_status ns_orthogonalize(const void* G, ns_dtype gt, int64_t m, int64_t n, con
   ns_status st = validate_ns(G, gt, m, n, coeffs, k, clip, out, ot);
   if (st != NS_OK) return st;
   if (!ws || ws_bytes < ns_workspace_bytes(m, n)) return NS_ERR_WORKSPACE;
-  return ns_run(G, gt, m, n, coeffs, k, clip, nullptr, out, ot, static_cast<uint8_t*>(ws),
+  return ns_run(G, gt, m, n, coeffs, k, clip, 0.0, nullptr, out, ot, static_cast<uint8_t*>(ws),
                 as_stream(stream));
 }
 
@@ -308,8 +326,35 @@ ns_status ns_orthogonalize_rht(const void* G, ns_dtype gt, int64_t m, int64_t n,
   ns_status st = validate_ns(G, gt, m, n, coeffs, k, clip, out, ot);
   if (st != NS_OK) return st;
   if (!ws || ws_bytes < ns_workspace_bytes(m, n)) return NS_ERR_WORKSPACE;
-  return ns_run(G, gt, m, n, coeffs, k, clip, masks, out, ot, static_cast<uint8_t*>(ws),
+  return ns_run(G, gt, m, n, coeffs, k, clip, 0.0, masks, out, ot, static_cast<uint8_t*>(ws),
                 as_stream(stream));
+}
+
+ns_status ns_orthogonalize_ex(const void* G, ns_dtype gt, int64_t m, int64_t n,
+                              const float* coeffs, int k, const ns_options* opt, void* out,
+                              ns_dtype ot, void* ws, size_t ws_bytes, void* stream) {
+  if (!opt) return NS_ERR_ARG;
+  const double q = opt->clip_quantile;
+  if (std::isnan(q) || q < 0.0 || q > 1.0) return NS_ERR_ARG;
+  // with a quantile the clip value is not used; validate as if clipping were off
+  const float clip = q > 0.0 ? INFINITY : opt->clip;
+  ns_status st = validate_ns(G, gt, m, n, coeffs, k, clip, out, ot);
+  if (st != NS_OK) return st;
+  if (!ws || ws_bytes < ns_workspace_bytes(m, n)) return NS_ERR_WORKSPACE;
+  return ns_run(G, gt, m, n, coeffs, k, clip, q, opt->rht_masks, out, ot,
+                static_cast<uint8_t*>(ws), as_stream(stream));
+}
+
+size_t ns_abs_quantile_workspace_bytes(void) { return align_up(nvfp4::abs_quantile_workspace_bytes()); }
+
+ns_status ns_abs_quantile(const void* x, ns_dtype xt, int64_t count, double q, float* out, void* ws,
+                          size_t ws_bytes, void* stream) {
+  if (!x || !out || !dtype_ok(xt) || std::isnan(q) || !(q > 0.0) || q > 1.0) return NS_ERR_ARG;
+  if (!dims_ok(count) || count >= kMaxElems) return NS_ERR_SHAPE;
+  if (!ws || ws_bytes < ns_abs_quantile_workspace_bytes()) return NS_ERR_WORKSPACE;
+  NS_TRY(nvfp4::launch_abs_quantile(x, (Dt)xt, count, quantile_rank(q, count), out, ws,
+                                    as_stream(stream)));
+  return NS_OK;
 }
 
 size_t ns_grouped_workspace_bytes(int count, const int64_t* m, const int64_t* n) {
@@ -336,7 +381,7 @@ ns_status ns_orthogonalize_grouped(int count, const void* const* G, const int64_
   if (!ws || ws_bytes < need) return NS_ERR_WORKSPACE;
   uint8_t* base = static_cast<uint8_t*>(ws);
   for (int i = 0; i < count; ++i) {
-    ns_status st = ns_run(G[i], gt, m[i], n[i], coeffs, k, clip[i], nullptr, out[i], ot, base,
+    ns_status st = ns_run(G[i], gt, m[i], n[i], coeffs, k, clip[i], 0.0, nullptr, out[i], ot, base,
                           as_stream(stream));
     if (st != NS_OK) return st;
     base += ns_workspace_bytes(m[i], n[i]);

@@ -85,18 +85,32 @@ struct GemmPlan {
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool symmetric, bool allow_split);
 hipError_t launch_gemm(const GemmProblem& g, const GemmPlan& p, float* partials, hipStream_t s);
 
+// ---- quantile of |x| (select.hip) ------------------------------------------
+// State of the radix selection: bits of the answer fixed so far and the rank
+// still sought among the keys that share them.
+struct SelectState {
+  uint32_t prefix, rank;
+};
+// Workspace of launch_abs_quantile, in bytes (independent of n).
+size_t abs_quantile_workspace_bytes();
+// *out = the rank-th smallest |x| (1-based, 1 <= rank <= n) over n elements,
+// magnitudes ordered by FP32 bits, non-finite values last (as NaN).
+hipError_t launch_abs_quantile(const void* x, Dt xt, int64_t n, uint32_t rank, float* out,
+                               void* ws, hipStream_t s);
+
 // ---- Newton–Schulz prologue / epilogue (ns.hip) ---------------------------
-// Partial sums of clamp(G)^2 into part[0..kNormParts).
+// Partial sums of clamp(G)^2 into part[0..kNormParts).  The clip is the
+// device value *clip_dev when that is given, else `clip`.
 constexpr int kNormParts = 1024;
-hipError_t launch_norm_partials(const void* G, Dt gt, int64_t n, float clip, double* part,
-                                hipStream_t s);
+hipError_t launch_norm_partials(const void* G, Dt gt, int64_t n, float clip, const float* clip_dev,
+                                double* part, hipStream_t s);
 // inv[0] = 1 / (sqrt(sum part) + eps); zeroes the listed slots.
 hipError_t launch_norm_finalize(const double* part, double* inv, uint32_t* zero0, uint32_t* zero1,
                                 uint32_t* zero2, hipStream_t s);
 // X[m][n] = clamp(G) * inv (G is m x n, or n x m read transposed), amax into slot.
 hipError_t launch_normalize(const void* G, Dt gt, int64_t m, int64_t n, bool transposed,
-                            float clip, const double* inv, float* X, uint32_t* amax_slot,
-                            hipStream_t s);
+                            float clip, const float* clip_dev, const double* inv, float* X,
+                            uint32_t* amax_slot, hipStream_t s);
 // out = X (m x n), or X^T written as n x m when transposed; f32 or bf16.
 hipError_t launch_write_out(const float* X, int64_t m, int64_t n, bool transposed, void* out,
                             Dt ot, hipStream_t s);

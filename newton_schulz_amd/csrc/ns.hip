@@ -56,7 +56,9 @@ __device__ __forceinline__ double block_sum(double v) {
 
 template <Dt T>
 __global__ __launch_bounds__(kThreads) void norm_partials_kernel(const void* G, int64_t nblk,
-                                                                  float clip, double* part) {
+                                                                  float clip, const float* clip_dev,
+                                                                  double* part) {
+  if (clip_dev) clip = *clip_dev;
   double acc = 0.0;
   for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < nblk;
        b += (int64_t)gridDim.x * kThreads) {
@@ -88,8 +90,10 @@ __global__ __launch_bounds__(kThreads) void norm_finalize_kernel(const double* p
 // 16*(t%4)..+15.  When transposed, G is xn x xm and its tile passes LDS.
 template <Dt T, bool TR>
 __global__ __launch_bounds__(kThreads) void normalize_kernel(const void* G, int64_t xm, int64_t xn,
-                                                              float clip, const double* invp,
-                                                              float* X, uint32_t* amax_slot) {
+                                                              float clip, const float* clip_dev,
+                                                              const double* invp, float* X,
+                                                              uint32_t* amax_slot) {
+  if (clip_dev) clip = *clip_dev;
   __shared__ float tile[64][65];
   const double inv = *invp;
   const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
@@ -195,13 +199,13 @@ __global__ __launch_bounds__(kThreads) void write_out_kernel(const float* X, int
 
 }  // namespace
 
-hipError_t launch_norm_partials(const void* G, Dt gt, int64_t n, float clip, double* part,
-                                hipStream_t s) {
+hipError_t launch_norm_partials(const void* G, Dt gt, int64_t n, float clip, const float* clip_dev,
+                                double* part, hipStream_t s) {
   const int64_t nblk = n / 16;
   if (gt == Dt::F32)
-    norm_partials_kernel<Dt::F32><<<kNormParts, kThreads, 0, s>>>(G, nblk, clip, part);
+    norm_partials_kernel<Dt::F32><<<kNormParts, kThreads, 0, s>>>(G, nblk, clip, clip_dev, part);
   else
-    norm_partials_kernel<Dt::BF16><<<kNormParts, kThreads, 0, s>>>(G, nblk, clip, part);
+    norm_partials_kernel<Dt::BF16><<<kNormParts, kThreads, 0, s>>>(G, nblk, clip, clip_dev, part);
   return hipGetLastError();
 }
 
@@ -212,15 +216,15 @@ hipError_t launch_norm_finalize(const double* part, double* inv, uint32_t* z0, u
 }
 
 hipError_t launch_normalize(const void* G, Dt gt, int64_t xm, int64_t xn, bool transposed,
-                            float clip, const double* inv, float* X, uint32_t* amax_slot,
-                            hipStream_t s) {
+                            float clip, const float* clip_dev, const double* inv, float* X,
+                            uint32_t* amax_slot, hipStream_t s) {
   dim3 grid((unsigned)((xn + 63) / 64), (unsigned)((xm + 63) / 64));
   if (gt == Dt::F32) {
-    if (transposed) normalize_kernel<Dt::F32, true><<<grid, kThreads, 0, s>>>(G, xm, xn, clip, inv, X, amax_slot);
-    else normalize_kernel<Dt::F32, false><<<grid, kThreads, 0, s>>>(G, xm, xn, clip, inv, X, amax_slot);
+    if (transposed) normalize_kernel<Dt::F32, true><<<grid, kThreads, 0, s>>>(G, xm, xn, clip, clip_dev, inv, X, amax_slot);
+    else normalize_kernel<Dt::F32, false><<<grid, kThreads, 0, s>>>(G, xm, xn, clip, clip_dev, inv, X, amax_slot);
   } else {
-    if (transposed) normalize_kernel<Dt::BF16, true><<<grid, kThreads, 0, s>>>(G, xm, xn, clip, inv, X, amax_slot);
-    else normalize_kernel<Dt::BF16, false><<<grid, kThreads, 0, s>>>(G, xm, xn, clip, inv, X, amax_slot);
+    if (transposed) normalize_kernel<Dt::BF16, true><<<grid, kThreads, 0, s>>>(G, xm, xn, clip, clip_dev, inv, X, amax_slot);
+    else normalize_kernel<Dt::BF16, false><<<grid, kThreads, 0, s>>>(G, xm, xn, clip, clip_dev, inv, X, amax_slot);
   }
   return hipGetLastError();
 }
