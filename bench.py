@@ -43,6 +43,8 @@ def parse():
     p.add_argument("--quant-warmup", type=int, default=20)
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     p.add_argument("--no-quant", action="store_true", help="skip the quantizer line")
+    p.add_argument("--no-grouped", action="store_true",
+                   help="skip the grouped batches (four 3072-wide blocks; the pages' d=4096/6144 blocks)")
     p.add_argument("--copy-probe", action="store_true",
                    help="finish with a plain 256 MiB device copy, the reference kernel that "
                         "scales the FETCH_SIZE / WRITE_SIZE counters of a profiled run")
@@ -129,6 +131,43 @@ def bf16_ns_ms(torch, G, coeffs, stream, reps=10):
             X = a * X + torch.mm(B, X)
         return X
     return time_events(run, reps, 3, stream)
+
+
+def grouped_line(ns, torch, synth, dev, stream, label, shapes, seed0, coeffs, clip_quantile,
+                 reps=3, warm=1):
+    """Grouped NS over a batch of BF16 gradients drawn on the device (the
+    lowrank value model), against BF16 torch NS of the same batch."""
+    from oracle.ns import ns_iteration_flops
+    Gs = [synth.device_lowrank_bf16(r, c, seed0 + i, dev) for i, (r, c) in enumerate(shapes)]
+    outs = [torch.empty(s, dtype=torch.float32, device=dev) for s in shapes]
+    ws = torch.empty(ns.ns_grouped_workspace_bytes(shapes), dtype=torch.uint8, device=dev)
+    if clip_quantile:
+        run = lambda: ns.ns_orthogonalize_grouped_ex(Gs, coeffs, clip_quantile=clip_quantile,
+                                                     outs=outs, workspace=ws, stream=stream)
+        clip_what = f"clip at the {clip_quantile} quantile of each |G| (on the device)"
+    else:
+        clips = [float(8.0 * torch.sqrt(torch.mean(g.double() ** 2))) for g in Gs]
+        run = lambda: ns.ns_orthogonalize_grouped(Gs, coeffs, clips, outs=outs, workspace=ws,
+                                                  stream=stream)
+        clip_what = "clip 8 x RMS(G) per matrix"
+    ms = time_events(run, reps, warm, stream)
+    flops = sum(len(coeffs) * ns_iteration_flops(r, c) for r, c in shapes)
+
+    def bf16_batch():
+        for g in Gs:
+            X = g.t() if g.shape[0] > g.shape[1] else g
+            X = X.float()
+            X = (X / (X.norm() + 1e-7)).to(torch.bfloat16)
+            for a, b, c in coeffs:
+                A = torch.mm(X, X.t())
+                B = b * A + c * torch.mm(A, A)
+                X = a * X + torch.mm(B, X)
+    bms = time_events(bf16_batch, reps, warm, stream)
+    del ws, outs, Gs
+    return {"workload": label, "matrices": len(shapes), "ms": round(ms, 3),
+            "value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+            "algorithmic_tflop": round(flops / 1e12, 3), "clip": clip_what,
+            "bf16_ms": round(bms, 3), "speedup_nvfp4_vs_bf16": round(bms / ms, 3)}
 
 
 def cpu_baseline(G, clip, coeffs, m, n):
@@ -242,6 +281,26 @@ def main():
     bms = bf16_ns_ms(torch, Gd, coeffs, stream)
     line["bf16_ns"] = {"ms": round(bms, 4), "speedup_nvfp4_vs_bf16": round(bms / ms, 3),
                        "what": "torch.mm in bf16 (hipBLASLt), full products, same 5 steps"}
+
+    if not args.no_grouped:
+        del ws
+        torch.cuda.empty_cache()
+        b4 = synth.ns_workload("ns4blocks")
+        line["grouped"] = [
+            grouped_line(ns, torch, synth, dev, stream,
+                         "four blocks at width 3072: Q,K,V,O 3072^2, up 3072x8192, down 8192x3072 "
+                         "(24 matrices), quintic x5", b4["shapes"], 5000, coeffs, 0.0),
+            grouped_line(ns, torch, synth, dev, stream,
+                         "the pages' four decoder blocks at d=4096 (d_ff 11008, 32 heads, 8 KV "
+                         "heads; 28 matrices), quintic x5", synth.pages_block_shapes(4096), 6000,
+                         coeffs, 0.99),
+            grouped_line(ns, torch, synth, dev, stream,
+                         "the pages' four decoder blocks at d=6144 (d_ff 13824, 48 heads, 8 KV "
+                         "heads; 28 matrices), quintic x5", synth.pages_block_shapes(6144), 7000,
+                         coeffs, 0.99),
+        ]
+        torch.cuda.empty_cache()
+        ws = None
 
     if not args.no_quant:
         del ws

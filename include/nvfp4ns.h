@@ -227,6 +227,18 @@ ns_status ns_orthogonalize_grouped(int count, const void* const* G, const int64_
                                    int k, const float* clip, void* const* out,
                                    ns_dtype ot, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * ns_orthogonalize_grouped_ex — ns_orthogonalize_grouped with the options of
+ * ns_orthogonalize_ex shared by every matrix: with opt->clip_quantile > 0
+ * each matrix is clipped at that quantile of its own |G| (clip may then be
+ * NULL), else at clip[i]; opt->rht_masks (k masks) applies to every matrix.
+ * Workspace ns_grouped_workspace_bytes().
+ */
+ns_status ns_orthogonalize_grouped_ex(int count, const void* const* G, const int64_t* m,
+                                      const int64_t* n, ns_dtype gt, const float* coeffs, int k,
+                                      const float* clip, const ns_options* opt, void* const* out,
+                                      ns_dtype ot, void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -368,6 +368,32 @@ size_t ns_grouped_workspace_bytes(int count, const int64_t* m, const int64_t* n)
   return total;
 }
 
+ns_status ns_orthogonalize_grouped_ex(int count, const void* const* G, const int64_t* m,
+                                      const int64_t* n, ns_dtype gt, const float* coeffs, int k,
+                                      const float* clip, const ns_options* opt, void* const* out,
+                                      ns_dtype ot, void* ws, size_t ws_bytes, void* stream) {
+  if (count <= 0 || !G || !m || !n || !out || !opt) return NS_ERR_ARG;
+  const double q = opt->clip_quantile;
+  if (std::isnan(q) || q < 0.0 || q > 1.0) return NS_ERR_ARG;
+  if (q == 0.0 && !clip) return NS_ERR_ARG;
+  for (int i = 0; i < count; ++i) {
+    const float ci = q > 0.0 ? INFINITY : clip[i];
+    ns_status st = validate_ns(G[i], gt, m[i], n[i], coeffs, k, ci, out[i], ot);
+    if (st != NS_OK) return st;
+  }
+  const size_t need = ns_grouped_workspace_bytes(count, m, n);
+  if (!ws || ws_bytes < need) return NS_ERR_WORKSPACE;
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  for (int i = 0; i < count; ++i) {
+    const float ci = q > 0.0 ? INFINITY : clip[i];
+    ns_status st = ns_run(G[i], gt, m[i], n[i], coeffs, k, ci, q, opt->rht_masks, out[i], ot, base,
+                          as_stream(stream));
+    if (st != NS_OK) return st;
+    base += ns_workspace_bytes(m[i], n[i]);
+  }
+  return NS_OK;
+}
+
 ns_status ns_orthogonalize_grouped(int count, const void* const* G, const int64_t* m,
                                    const int64_t* n, ns_dtype gt, const float* coeffs, int k,
                                    const float* clip, void* const* out, ns_dtype ot, void* ws,

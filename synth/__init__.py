@@ -112,6 +112,35 @@ def ns_workload(name):
     raise KeyError(name)
 
 
+def pages_block_shapes(d):
+    """Parameter shapes (out x in) of the pages' four decoder blocks at model
+    width d = 4096 or 6144 (Full-Stack FP4 §4.4: d_ff = 11008 / 13824,
+    32 / 48 query heads of width 128, 8 KV heads): per block Q, K, V, O, and
+    the gate, up and down projections of the gated MLP; 28 matrices."""
+    dff = {4096: 11008, 6144: 13824}[d]
+    kv = 8 * 128
+    block = [(d, d), (kv, d), (kv, d), (d, d), (dff, d), (dff, d), (d, dff)]
+    return block * 4
+
+
+def device_lowrank_bf16(rows, cols, seed, device, rank=32, noise=0.01):
+    """``lowrank_gradient``'s value model drawn on the GPU with torch's
+    seeded generator (for the large benchmark-only batches whose host
+    generation would take minutes), rounded to bfloat16."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    P = torch.randn((rows, rank), generator=g, device=device)
+    Q = torch.randn((cols, rank), generator=g, device=device)
+    S = P @ Q.t()
+    S /= S.norm()
+    x = S + noise * torch.randn((rows, cols), generator=g, device=device)
+    count = int(round(OUTLIER_FRACTION * rows * cols))
+    idx = torch.randperm(rows * cols, generator=g, device=device)[:count]
+    x.view(-1)[idx] *= OUTLIER_FACTOR
+    return x.to(torch.bfloat16)
+
+
 def ns_matrix(spec, i):
     """(values float32, bf16 bits or None, clip) of matrix i of a workload."""
     rows, cols = spec["shapes"][i]

@@ -103,3 +103,20 @@ def test_invalid_quantiles_are_rejected():
     with pytest.raises(ns.NSError) as e:
         ns.ns_orthogonalize_ex(G, [CUBIC], clip_quantile=2.0)
     assert e.value.status == ns.NS_ERR_ARG
+
+
+def test_grouped_ex_matches_single_calls():
+    shapes = [(128, 256), (256, 128), (96, 96)]
+    Gs = [to_dev_f32(synth.student_t(r, c, seed=20 + i)) for i, (r, c) in enumerate(shapes)]
+    coeffs = [CUBIC] * 3
+    masks = synth.rht_masks(3, seed=2)
+    outs = ns.ns_orthogonalize_grouped_ex(Gs, coeffs, clip_quantile=0.99, rht_masks=masks)
+    for g, o in zip(Gs, outs):
+        single = host(ns.ns_orthogonalize_ex(g, coeffs, clip_quantile=0.99, rht_masks=masks))
+        assert np.array_equal(host(o), single)
+    # without a quantile the per-matrix clips apply, as in ns_orthogonalize_grouped
+    clips = [0.05, 1.0, 0.02]
+    outs = ns.ns_orthogonalize_grouped_ex(Gs, coeffs, clips=clips)
+    ref = ns.ns_orthogonalize_grouped(Gs, coeffs, clips)
+    for a, b in zip(outs, ref):
+        assert np.array_equal(host(a), host(b))
