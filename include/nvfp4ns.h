@@ -125,10 +125,11 @@ ns_status nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales,
  *   addend may be NULL when beta == 0, and may equal out.
  *   amax_out (device uint32, may be NULL): atomically maxed with the bit
  *     pattern of |out| (non-finite values count as NaN); the caller zeroes it.
- *   ws: device scratch of nvfp4_gemm_workspace_bytes(); it lets symmetric
- *     products split K across workgroups (FP32 partials summed in a fixed
- *     order, so results do not depend on timing).  ws = NULL, ws_bytes = 0
- *     runs the product unsplit.  Calls sharing one ws must not overlap.
+ *   ws: device scratch of nvfp4_gemm_workspace_bytes(); it lets the tiles
+ *     left over after an equal number per CU be split along K across
+ *     workgroups (FP32 partials summed in a fixed order, so results do not
+ *     depend on timing).  ws = NULL, ws_bytes = 0 runs every tile whole.
+ *     Calls sharing one ws must not overlap.
  * M, N, K must be positive multiples of 16.
  */
 size_t nvfp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int symmetric);

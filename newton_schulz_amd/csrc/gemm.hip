@@ -25,9 +25,9 @@
 // access of a wave is one contiguous conflict-free kilobyte.
 //
 // Symmetric products compute only tiles that touch the upper triangle
-// (row <= col); each element there is written once and mirrored.  When the
-// tile count is small they are split along K into `splits` work units whose
-// FP32 partials a second kernel sums in split order (deterministic).
+// (row <= col); each element there is written once and mirrored.  Tiles
+// left over after one per CU are split along K into parts whose FP32
+// partials a second kernel sums in part order (deterministic); see FastArgs.
 #include "launch.hpp"
 #include "nvfp4_device.hpp"
 
@@ -81,13 +81,72 @@ struct Cfg {
   static constexpr int kLoadsPerWave = kCodeLoads + kScaleLoads;
 };
 
+// Schedule of one product (see plan_with): the tiles are cut into kXcds
+// contiguous runs, one per XCD (tiles sharing operand panels share an L2).
+// Within a run of n tiles, the first floor(n / cus) * cus are whole work
+// units -- the same number for every CU -- and each of the remaining
+// n mod cus tiles is split along K into `parts` units whose FP32 partials a
+// second kernel sums in a fixed order, so the leftover work spreads over
+// the CUs instead of doubling some of them.
 struct FastArgs {
   GemmProblem g;
-  int splits;
   int64_t TM, TN;       // tile grid
-  int64_t tiles, units;
+  int64_t tiles;
+  int cus;              // CUs per XCD
+  int parts;            // K-parts of a leftover tile (1: leftovers run whole)
   float* partials;
 };
+
+struct Unit {
+  int tile;             // tile index
+  int part;             // K-part of a split tile (0 for a whole tile)
+  int split;            // index among all split tiles, or -1 for a whole tile
+};
+
+// Scheduling arithmetic is 32-bit (tile counts stay far below 2^31) and
+// wave-uniform, so it stays in scalar registers.
+__device__ __forceinline__ void xcd_run(const FastArgs& a, int x, int& t0, int& n, int& whole) {
+  const int tiles = (int)a.tiles;
+  t0 = x * tiles / kXcds;
+  n = (x + 1) * tiles / kXcds - t0;
+  whole = a.parts > 1 ? n / a.cus * a.cus : n;
+}
+
+// Work unit of workgroup b (b % kXcds picks the XCD); false when none.
+__device__ __forceinline__ bool unit_of(const FastArgs& a, int b, Unit& u) {
+  const int x = b % kXcds, l = b / kXcds;
+  int t0, n, whole;
+  xcd_run(a, x, t0, n, whole);
+  if (l < whole) {
+    u.tile = t0 + l;
+    u.part = 0;
+    u.split = -1;
+    return true;
+  }
+  const int r = l - whole;
+  if (r >= (n - whole) * a.parts) return false;
+  int base = 0;                           // split tiles of the XCDs before x
+  for (int y = 0; y < x; ++y) {
+    int ty, ny, wy;
+    xcd_run(a, y, ty, ny, wy);
+    base += ny - wy;
+  }
+  u.tile = t0 + whole + r / a.parts;
+  u.part = r % a.parts;
+  u.split = base + r / a.parts;
+  return true;
+}
+
+// Tile of split tile number s (inverse of unit_of's numbering).
+__device__ __forceinline__ int split_tile(const FastArgs& a, int s) {
+  for (int x = 0; x < kXcds; ++x) {
+    int t0, n, whole;
+    xcd_run(a, x, t0, n, whole);
+    if (s < n - whole) return t0 + whole + s;
+    s -= n - whole;
+  }
+  return -1;
+}
 
 // Tile t of the grid: row-block I, col-block J.  Symmetric problems list only
 // tiles whose first row is <= their last column.
@@ -194,6 +253,89 @@ __device__ __forceinline__ void issue_stage(const GemmProblem& g, const StageSrc
   }
 }
 
+struct EpCtx {
+  float scale, beta;
+  int N;
+  int64_t m0, n0;       // tile origin
+  int dr0, dc0;         // this lane's first row / column inside the tile
+  bool fast;            // tile wholly inside the matrix and above the diagonal
+};
+
+template <class C, bool SYM>
+__device__ __forceinline__ EpCtx epilogue_ctx(const GemmProblem& g, int64_t m0, int64_t n0, int wm,
+                                              int wn, int lane) {
+  EpCtx e;
+  e.scale = g.alpha * (*g.sg_p) * (*g.sg_q);
+  e.beta = g.beta;
+  e.N = (int)g.N;
+  e.m0 = m0;
+  e.n0 = n0;
+  e.dr0 = wm * C::FM * 32 + 4 * (lane >> 5);
+  e.dc0 = wn * C::FN * 32 + (lane & 31);
+  const bool inside = m0 + C::BM <= g.M && n0 + C::BN <= g.N;
+  const bool upper = !SYM || (m0 + C::BM <= n0);        // every element has row < col
+  e.fast = inside && upper;
+  return e;
+}
+
+// The epilogue of one 32 x 32 block (i, j) of a wave's sub-tile, for the
+// reduce kernel (v holds the block's 16 values per lane in the MFMA output
+// layout); the same arithmetic as `epilogue` below, which keeps its own
+// copy because sharing this one raises the product kernel's register count.
+template <class C, bool SYM>
+__device__ __forceinline__ void epilogue_block(const GemmProblem& g, const EpCtx& e,
+                                               const floatx16& v16, int i, int j, uint32_t& amax) {
+  const int N = e.N;
+  // wave-uniform tile bases and 32-bit lane offsets (BM * N < 2^31)
+  float* otile = g.out + e.m0 * g.N + e.n0;
+  const float* atile = g.addend ? g.addend + e.m0 * g.N + e.n0 : nullptr;
+  float* mtile = g.out + e.n0 * g.N + e.m0;           // mirror: (col, row)
+  const int lo = e.dr0 * N + e.dc0, mo = e.dc0 * N + e.dr0;
+  auto valid = [&](int dr) {
+    if (e.fast) return true;
+    const int64_t row = e.m0 + e.dr0 + dr, col = e.n0 + e.dc0 + j * 32;
+    return row < g.M && col < g.N && (!SYM || row <= col);
+  };
+  float ad[16];
+  if (atile) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int dr = i * 32 + 8 * (r >> 2) + (r & 3);
+      ad[r] = valid(dr) ? atile[lo + dr * N + j * 32] : 0.0f;
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float v4[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int r = 4 * q + t;
+      const int dr = i * 32 + 8 * q + t;               // row offset from the lane's first row
+      float v = e.scale * v16[r];
+      if (atile) v = fmaf(e.beta, ad[r], v);
+      if (valid(dr)) {
+        otile[lo + dr * N + j * 32] = v;
+        const uint32_t ab = abs_bits(v);
+        amax = ab > amax ? ab : amax;
+      }
+      v4[t] = v;
+    }
+    if constexpr (SYM) {
+      // mirror: rows dr..dr+3 of column c become 4 consecutive floats
+      const int moff = mo + (j * 32) * N + i * 32 + 8 * q;
+      if (e.fast) {
+        *reinterpret_cast<float4*>(mtile + moff) = make_float4(v4[0], v4[1], v4[2], v4[3]);
+      } else {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int64_t row = e.m0 + e.dr0 + i * 32 + 8 * q + t, col = e.n0 + e.dc0 + j * 32;
+          if (row < g.M && col < g.N && row < col) mtile[moff + t] = v4[t];
+        }
+      }
+    }
+  }
+}
+
 // out = beta * addend + alpha * sgP * sgQ * acc for the tile at (m0, n0);
 // symmetric products write row <= col and mirror row < col.  amax of the
 // written values goes to amax_out.  Offsets inside a tile are 32-bit
@@ -272,19 +414,25 @@ __device__ __forceinline__ void epilogue(const GemmProblem& g, floatx16 (&acc)[C
   if (g.amax_out) amax_publish_wave(amax, g.amax_out, g.amax_parts != 0);
 }
 
+// FP32 partials of a K-part: per (block b = i*FN + j, quarter q) a run of
+// kThreads float4 (lane-major), so that a reader of one block and one wave
+// loads contiguous kilobytes.
+template <class C>
+__device__ __forceinline__ size_t partial_index(int b, int q, int thread) {
+  return ((size_t)(b * 4 + q) * C::kThreads + thread) * 4;
+}
+
 template <class C, bool SYM>
 __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_fast_kernel(FastArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::NST * C::kStage];
   const GemmProblem& g = a.g;
 
-  // ---- work unit -> (tile, split), XCD-aware: each XCD gets a contiguous run
-  const int64_t per_xcd = (a.units + kXcds - 1) / kXcds;
-  const int64_t u = (int64_t)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
-  if (u >= a.units) return;
-  const int64_t tile = u / a.splits;
-  const int split = (int)(u % a.splits);
+  // ---- work unit: a whole tile or a K-part of a leftover tile (unit_of)
+  Unit un;
+  if (!unit_of(a, (int)blockIdx.x, un)) return;
+  const int nparts = un.split < 0 ? 1 : a.parts;
   int64_t I, J;
-  tile_of<C::BM, C::BN, SYM>(tile, a.TM, a.TN, I, J);
+  tile_of<C::BM, C::BN, SYM>(un.tile, a.TM, a.TN, I, J);
   const int64_t m0 = I * C::BM, n0 = J * C::BN;
 
   const int lane = threadIdx.x & 63;
@@ -303,7 +451,7 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_fast_kernel(F
   init_sources<C>(g, m0, n0, wave, lane, src);
 
   const int64_t nk_all = g.K / C::BK;
-  const int64_t kc0 = nk_all * split / a.splits, kc1 = nk_all * (split + 1) / a.splits;
+  const int64_t kc0 = nk_all * un.part / nparts, kc1 = nk_all * (un.part + 1) / nparts;
 
 
   // prologue: stages kc0 .. kc0 + NST - 2 in flight
@@ -403,49 +551,57 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_fast_kernel(F
     }
   }
 
-  if (a.splits > 1) {
-    // split-K: store the FP32 partial; gemm_reduce_kernel sums the splits in
-    // order and runs the epilogue (a kernel boundary makes the partials
-    // visible without per-workgroup cache flushes)
-    float* part = a.partials + (size_t)u * C::kAcc * C::kThreads;
+  if (un.split >= 0) {
+    // K-part of a split tile: store the FP32 partial; gemm_reduce_kernel sums
+    // the parts in order and runs the epilogue (a kernel boundary makes the
+    // partials visible without per-workgroup cache flushes)
+    float* part = a.partials + ((size_t)un.split * a.parts + un.part) * C::kAcc * C::kThreads;
 #pragma unroll
     for (int i = 0; i < C::FM; ++i)
 #pragma unroll
       for (int j = 0; j < C::FN; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          part[((i * C::FN + j) * 16 + r) * C::kThreads + threadIdx.x] = acc[i][j][r];
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<float4*>(part + partial_index<C>(i * C::FN + j, q, threadIdx.x)) =
+              make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                          acc[i][j][4 * q + 3]);
     return;
   }
   epilogue<C, SYM>(g, acc, m0, n0, wm, wn, lane);
 }
 
-// Sum the split-K partials of one tile in split order, then the epilogue.
+// One wave per workgroup: block (i, j) of wave w's sub-tile of split tile
+// s, summed over the K-parts in part order, then that block's epilogue.
+// Workgroups: split tiles x waves x FM x FN, so the partials stream in
+// with many loads in flight.
 template <class C, bool SYM>
-__global__ __launch_bounds__(C::kThreads) void gemm_reduce_kernel(FastArgs a) {
-  const int64_t per_xcd = (a.tiles + kXcds - 1) / kXcds;
-  const int64_t tile = (int64_t)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
-  if (tile >= a.tiles) return;
+__global__ __launch_bounds__(64) void gemm_reduce_kernel(FastArgs a) {
+  constexpr int kBlocks = C::FM * C::FN;
+  const int bid = (int)blockIdx.x;
+  const int s = bid / (C::kWaves * kBlocks), rem = bid % (C::kWaves * kBlocks);
+  const int w = rem / kBlocks, b = rem % kBlocks, i = b / C::FN, j = b % C::FN;
+  const int tile = split_tile(a, s);
+  if (tile < 0) return;
   int64_t I, J;
   tile_of<C::BM, C::BN, SYM>(tile, a.TM, a.TN, I, J);
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave / C::WN, wn = wave % C::WN;
-  const float* base = a.partials + (size_t)tile * a.splits * C::kAcc * C::kThreads;
-  floatx16 acc[C::FM][C::FN];
+  const int thread = w * 64 + lane;                 // the lane's thread in the product kernel
+  const float* base = a.partials + (size_t)s * a.parts * C::kAcc * C::kThreads;
+  floatx16 v;
 #pragma unroll
-  for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-    for (int j = 0; j < C::FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int e = (i * C::FN + j) * 16 + r;
-        float v = base[(size_t)e * C::kThreads + threadIdx.x];
-        for (int sp = 1; sp < a.splits; ++sp)
-          v += base[((size_t)sp * C::kAcc + e) * C::kThreads + threadIdx.x];
-        acc[i][j][r] = v;
-      }
-  epilogue<C, SYM>(a.g, acc, I * C::BM, J * C::BN, wm, wn, lane);
+  for (int q = 0; q < 4; ++q) {
+    float4 t = *reinterpret_cast<const float4*>(base + partial_index<C>(b, q, thread));
+    for (int p = 1; p < a.parts; ++p) {
+      const float4 u = *reinterpret_cast<const float4*>(base + (size_t)p * C::kAcc * C::kThreads +
+                                                        partial_index<C>(b, q, thread));
+      t.x += u.x; t.y += u.y; t.z += u.z; t.w += u.w;
+    }
+    v[4 * q] = t.x; v[4 * q + 1] = t.y; v[4 * q + 2] = t.z; v[4 * q + 3] = t.w;
+  }
+  const EpCtx e = epilogue_ctx<C, SYM>(a.g, I * C::BM, J * C::BN, w / C::WN, w % C::WN, lane);
+  uint32_t amax = 0;
+  epilogue_block<C, SYM>(a.g, e, v, i, j, amax);
+  if (a.g.amax_out) amax_publish_wave(amax, a.g.amax_out, a.g.amax_parts != 0);
 }
 
 // ===========================================================================
@@ -634,19 +790,19 @@ using SmallCfg = Cfg<1, 2, 2, 2, NVFP4_FAST_NST, 128>;
 #define NVFP4_SMALL_MAX_K 4096  // ... when K is at most this
 #endif
 
-// Symmetric products are split along K only while the tiles alone would
-// leave CUs idle: the FP32 partials and the reduce pass cost more than the
-// extra parallelism returns once every CU has a tile.
-#ifndef NVFP4_TARGET_UNITS
-#define NVFP4_TARGET_UNITS 256   // MI355X compute units
+// Leftover tiles (see FastArgs) are split into at most cus / leftovers
+// parts, each of at least NVFP4_MIN_PART_STAGES K-stages, so that every CU
+// gets at most one part; products whose tiles divide evenly over the CUs of
+// each XCD run unsplit.
+#ifndef NVFP4_CUS_PER_XCD
+#define NVFP4_CUS_PER_XCD 32     // MI355X: 256 CUs in 8 XCDs
 #endif
-constexpr int64_t kTargetUnits = NVFP4_TARGET_UNITS;
-// a split must keep at least 4096 of K: shorter splits cost more in FP32
-// partial traffic and the reduce launch than the extra parallelism returns
-#ifndef NVFP4_MIN_K_SPLIT
-#define NVFP4_MIN_K_SPLIT 4096
+#ifndef NVFP4_MIN_PART_STAGES
+#define NVFP4_MIN_PART_STAGES 8  // 1024 of K per part at least
 #endif
-constexpr int64_t kMinKPerSplit = NVFP4_MIN_K_SPLIT;
+#ifndef NVFP4_MAX_PARTS
+#define NVFP4_MAX_PARTS 8
+#endif
 
 int64_t sym_tiles(int64_t TM, int64_t TN, int64_t BM, int64_t BN) {
   int64_t t = 0;
@@ -665,16 +821,39 @@ GemmPlan plan_with(int64_t M, int64_t N, int64_t K, bool symmetric, bool allow_s
   p.TM = (M + C::BM - 1) / C::BM;
   p.TN = (N + C::BN - 1) / C::BN;
   p.tiles = symmetric ? sym_tiles(p.TM, p.TN, C::BM, C::BN) : p.TM * p.TN;
-  int64_t splits = 1;
-  const int64_t stages = K / C::BK;
-  if (allow_split && symmetric) {
-    while (p.tiles * splits < kTargetUnits && (stages / (2 * splits)) * C::BK >= kMinKPerSplit)
-      splits *= 2;
+  const int cus = NVFP4_CUS_PER_XCD;
+  // leftover tiles of the busiest XCD run, and the units per XCD
+  int64_t left_max = 0, split_tiles = 0;
+  for (int x = 0; x < kXcds; ++x) {
+    const int64_t n = (int64_t)(x + 1) * p.tiles / kXcds - (int64_t)x * p.tiles / kXcds;
+    left_max = n % cus > left_max ? n % cus : left_max;
+    split_tiles += n % cus;
   }
-  p.splits = (int)splits;
-  p.units = p.tiles * splits;
-  if (splits > 1) {
-    const size_t part = (size_t)p.units * C::kAcc * C::kThreads * sizeof(float);
+  int parts = 1;
+  const int64_t stages = K / C::BK;
+  // split only where a leftover would double a CU's work (at most one whole
+  // tile per CU); with two or more the reduce pass costs more than it saves
+  // (measured: 3072^2 x 8192 with one whole tile per CU gains 22 us, 3072^2
+  // x 3072 with two loses 9 us)
+  const bool one_per_cu = p.tiles / kXcds < 2 * cus;
+  if (allow_split && left_max > 0 && one_per_cu) {
+    int64_t q = cus / left_max;
+    if (q > NVFP4_MAX_PARTS) q = NVFP4_MAX_PARTS;
+    if (q > stages / NVFP4_MIN_PART_STAGES) q = stages / NVFP4_MIN_PART_STAGES;
+    parts = q >= 2 ? (int)q : 1;
+  }
+  p.splits = parts;
+  int64_t per_xcd = 0;
+  for (int x = 0; x < kXcds; ++x) {
+    const int64_t n = (int64_t)(x + 1) * p.tiles / kXcds - (int64_t)x * p.tiles / kXcds;
+    const int64_t whole = parts > 1 ? n / cus * cus : n;
+    const int64_t u = whole + (n - whole) * parts;
+    per_xcd = u > per_xcd ? u : per_xcd;
+  }
+  p.units = per_xcd * kXcds;            // the grid
+  p.split_tiles = parts > 1 ? split_tiles : 0;
+  if (parts > 1) {
+    const size_t part = (size_t)p.split_tiles * parts * C::kAcc * C::kThreads * sizeof(float);
     p.partial_bytes = (part + 255) / 256 * 256;
   }
   p.ws_bytes = p.partial_bytes;
@@ -685,24 +864,23 @@ template <class C>
 hipError_t launch_with(const GemmProblem& g, const GemmPlan& p, float* partials, hipStream_t s) {
   FastArgs a;
   a.g = g;
-  a.splits = p.splits;
   a.TM = p.TM;
   a.TN = p.TN;
   a.tiles = p.tiles;
-  a.units = p.units;
+  a.cus = NVFP4_CUS_PER_XCD;
+  a.parts = p.splits;
   a.partials = p.splits > 1 ? partials : nullptr;
-  const int64_t grid = (p.units + kXcds - 1) / kXcds * kXcds;
   if (g.symmetric)
-    gemm_fast_kernel<C, true><<<dim3((unsigned)grid), C::kThreads, 0, s>>>(a);
+    gemm_fast_kernel<C, true><<<dim3((unsigned)p.units), C::kThreads, 0, s>>>(a);
   else
-    gemm_fast_kernel<C, false><<<dim3((unsigned)grid), C::kThreads, 0, s>>>(a);
+    gemm_fast_kernel<C, false><<<dim3((unsigned)p.units), C::kThreads, 0, s>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
-  const int64_t rgrid = (p.tiles + kXcds - 1) / kXcds * kXcds;
+  const unsigned rgrid = (unsigned)(p.split_tiles * C::kWaves * C::FM * C::FN);
   if (g.symmetric)
-    gemm_reduce_kernel<C, true><<<dim3((unsigned)rgrid), C::kThreads, 0, s>>>(a);
+    gemm_reduce_kernel<C, true><<<dim3(rgrid), 64, 0, s>>>(a);
   else
-    gemm_reduce_kernel<C, false><<<dim3((unsigned)rgrid), C::kThreads, 0, s>>>(a);
+    gemm_reduce_kernel<C, false><<<dim3(rgrid), 64, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -72,14 +72,16 @@ struct GemmProblem {
 };
 
 // Launch plan of one product: the fast path needs K % 128 == 0 and picks a
-// tile shape from the tile count; symmetric products on the fast path may
-// be split along K, which needs a workspace of ws_bytes for the FP32
+// tile shape from the tile count; tiles left over after an equal number per
+// CU may be split along K, which needs a workspace of ws_bytes for the FP32
 // partials.
 struct GemmPlan {
   bool fast;
   int cfg;                // tile shape of the fast path (0: 128 x 128, 1: 64 x 128)
-  int splits;
-  int64_t TM, TN, tiles, units;
+  int splits;             // K-parts of each leftover tile (1: none split)
+  int64_t TM, TN, tiles;
+  int64_t units;          // workgroups of the product kernel
+  int64_t split_tiles;    // tiles split into K-parts (0 when splits == 1)
   size_t partial_bytes, ws_bytes;
 };
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool symmetric, bool allow_split);

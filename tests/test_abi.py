@@ -65,11 +65,12 @@ def test_workspace_sizes_and_validation_on_host():
     # beta != 0 without an addend
     assert lib.nvfp4_gemm(fake, fake, fake, fake, fake, fake, 32, 32, 32, 0, 1.0, 2.0,
                           None, fake, None, None, 0, None) == ns.NS_ERR_ARG
-    # a symmetric 1024^2 x 16384 product has too few tiles to fill the GPU and
-    # splits K: it needs a workspace, and a too-small one is refused
-    wsg = lib.nvfp4_gemm_workspace_bytes(1024, 1024, 16384, 1)
+    # the 3072^2 x 8192 Gram product has 300 tiles for 8 XCDs of 32 CUs: the
+    # tiles left over after one per CU are split along K, which needs a
+    # workspace, and a too-small one is refused
+    wsg = lib.nvfp4_gemm_workspace_bytes(3072, 3072, 8192, 1)
     assert wsg > 0
-    assert lib.nvfp4_gemm(fake, fake, fake, fake, fake, fake, 1024, 1024, 16384, 1, 1.0, 0.0,
+    assert lib.nvfp4_gemm(fake, fake, fake, fake, fake, fake, 3072, 3072, 8192, 1, 1.0, 0.0,
                           None, other, None, fake, wsg - 1, None) == ns.NS_ERR_WORKSPACE
-    # 3072^2 x 8192 has a tile for every CU and runs unsplit
-    assert lib.nvfp4_gemm_workspace_bytes(3072, 3072, 8192, 1) == 0
+    # 3072 x 8192 x 3072 has 1536 tiles, six per CU: nothing is split
+    assert lib.nvfp4_gemm_workspace_bytes(3072, 8192, 3072, 0) == 0

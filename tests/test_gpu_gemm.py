@@ -140,8 +140,8 @@ def test_full_size_gemms_sampled():
 
 
 def test_symmetric_gemm_split_k():
-    """A symmetric product long enough in K to be split (two K halves whose
-    FP32 partials a second kernel sums in order)."""
+    """A symmetric product with fewer tiles than CUs: its tiles are split
+    along K into parts whose FP32 partials a second kernel sums in order."""
     M, K = 384, 8192
     assert ns.nvfp4_gemm_workspace_bytes(M, M, K, True) > 0       # split schedule
     rng = np.random.default_rng(8)
@@ -160,5 +160,26 @@ def test_symmetric_gemm_split_k():
     _check_amax(slot, got)
     # the same product unsplit (no workspace) agrees to accumulation order
     got1 = host(ns.nvfp4_gemm(qd, qd, M, M, K, symmetric=True, alpha=0.75, beta=-1.5,
+                              addend=to_dev_f32(add), split=False))
+    assert rel_fro(got1, got) <= 1e-6
+
+
+def test_general_gemm_leftover_tiles_split_k():
+    """A non-symmetric product whose tiles do not divide evenly over the CUs:
+    the leftover tiles run as K-parts (partials summed in order), the rest
+    whole; it matches the oracle and the unsplit run."""
+    M, NC, K = 384, 640, 4096
+    assert ns.nvfp4_gemm_workspace_bytes(M, NC, K, False) > 0
+    rng = np.random.default_rng(9)
+    P, Qm = rng.standard_normal((M, K)), rng.standard_normal((NC, K))
+    qp, qq = Q.quantize_rows(P), Q.quantize_rows(Qm)
+    want = N.gemm_nt(Q.dequantize_rows(qp), Q.dequantize_rows(qq))
+    add = rng.standard_normal((M, NC)).astype(np.float32)
+    slot = _amax_slot()
+    got = host(ns.nvfp4_gemm(dev_q(qp), dev_q(qq), M, NC, K, alpha=1.25, beta=0.5,
+                             addend=to_dev_f32(add), amax_out=slot))
+    assert rel_fro(got, 1.25 * want + 0.5 * add.astype(np.float64)) <= TOL
+    _check_amax(slot, got)
+    got1 = host(ns.nvfp4_gemm(dev_q(qp), dev_q(qq), M, NC, K, alpha=1.25, beta=0.5,
                               addend=to_dev_f32(add), split=False))
     assert rel_fro(got1, got) <= 1e-6
