@@ -152,7 +152,7 @@ size_t ns_workspace_bytes(int64_t m, int64_t n);
  *   G      [m][n] FP32 or BF16 (gt), read only.
  *   coeffs HOST array of k triples (a_i, b_i, c_i).
  *   clip   > 0; +inf disables clipping.  NaN passes through the clamp.
- *   out    [m][n] FP32 or BF16 (ot); must not overlap G.
+ *   out    [m][n] FP32 or BF16 (ot); must not overlap G or ws.
  *   ws     device scratch of ns_workspace_bytes(m, n).
  */
 ns_status ns_orthogonalize(const void* G, ns_dtype gt, int64_t m, int64_t n,

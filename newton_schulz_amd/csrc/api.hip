@@ -157,9 +157,12 @@ ns_status ns_run(const void* G, ns_dtype gt, int64_t m, int64_t n, const float* 
       NS_TRY(nvfp4::launch_amax_tiles(B, Dt::F32, xm, xm, slotB, nullptr, h, s));
       NS_TRY(nvfp4::launch_quant_tiles(B, Dt::F32, xm, xm, slotB, sgB, ws + L.qb_c, ws + L.qb_s,
                                        nullptr, nullptr, nullptr, s, nullptr, nullptr, h));
+      const bool direct = it == k - 1 && !tr && ot == NS_F32;
       nvfp4::GemmProblem g3{ws + L.qb_c, ws + L.qb_s, sgB, ws + L.qt_c, ws + L.qt_s, sgXc,
-                            xm, xn, xm, 0, 1.0f, a, X, X, nullptr, 0};
+                            xm, xn, xm, 0, 1.0f, a, X, direct ? static_cast<float*>(out) : X,
+                            nullptr, 0};
       NS_TRY(nvfp4::launch_gemm(g3, L.p3, gpart, s));
+      if (direct) return NS_OK;
       continue;
     }
     // qX = Q_1x16(X) and qX16 = Q_16x1(X) (stored as rows of X^T), one s_g
@@ -179,10 +182,14 @@ ns_status ns_run(const void* G, ns_dtype gt, int64_t m, int64_t n, const float* 
     // qB = Q_1x16(B)
     NS_TRY(nvfp4::launch_quant_rows(B, Dt::F32, xm, xm, slotB, sgB, ws + L.qb_c, ws + L.qb_s,
                                     slotX, s));
-    // X' = a X + qB qX16 (K = xm), in place
+    // X' = a X + qB qX16 (K = xm), in place; the last step of an FP32,
+    // untransposed call writes straight into `out` (no copy pass)
+    const bool direct = it == k - 1 && !tr && ot == NS_F32;
+    float* dst = direct ? static_cast<float*>(out) : X;
     nvfp4::GemmProblem g3{ws + L.qb_c, ws + L.qb_s, sgB, ws + L.qt_c, ws + L.qt_s, sgX,
-                          xm, xn, xm, 0, 1.0f, a, X, X, slotX, 1};
+                          xm, xn, xm, 0, 1.0f, a, X, dst, direct ? nullptr : slotX, 1};
     NS_TRY(nvfp4::launch_gemm(g3, L.p3, gpart, s));
+    if (direct) return NS_OK;
   }
   NS_TRY(nvfp4::launch_write_out(X, xm, xn, tr, out, (Dt)ot, s));
   return NS_OK;
@@ -315,6 +322,7 @@ ns_status ns_orthogonalize(const void* G, ns_dtype gt, int64_t m, int64_t n, con
   ns_status st = validate_ns(G, gt, m, n, coeffs, k, clip, out, ot);
   if (st != NS_OK) return st;
   if (!ws || ws_bytes < ns_workspace_bytes(m, n)) return NS_ERR_WORKSPACE;
+  if (overlaps(out, (size_t)(m * n) * dtype_size(ot), ws, ws_bytes)) return NS_ERR_ARG;
   return ns_run(G, gt, m, n, coeffs, k, clip, 0.0, nullptr, out, ot, static_cast<uint8_t*>(ws),
                 as_stream(stream));
 }
@@ -326,6 +334,7 @@ ns_status ns_orthogonalize_rht(const void* G, ns_dtype gt, int64_t m, int64_t n,
   ns_status st = validate_ns(G, gt, m, n, coeffs, k, clip, out, ot);
   if (st != NS_OK) return st;
   if (!ws || ws_bytes < ns_workspace_bytes(m, n)) return NS_ERR_WORKSPACE;
+  if (overlaps(out, (size_t)(m * n) * dtype_size(ot), ws, ws_bytes)) return NS_ERR_ARG;
   return ns_run(G, gt, m, n, coeffs, k, clip, 0.0, masks, out, ot, static_cast<uint8_t*>(ws),
                 as_stream(stream));
 }
@@ -341,6 +350,7 @@ ns_status ns_orthogonalize_ex(const void* G, ns_dtype gt, int64_t m, int64_t n,
   ns_status st = validate_ns(G, gt, m, n, coeffs, k, clip, out, ot);
   if (st != NS_OK) return st;
   if (!ws || ws_bytes < ns_workspace_bytes(m, n)) return NS_ERR_WORKSPACE;
+  if (overlaps(out, (size_t)(m * n) * dtype_size(ot), ws, ws_bytes)) return NS_ERR_ARG;
   return ns_run(G, gt, m, n, coeffs, k, clip, q, opt->rht_masks, out, ot,
                 static_cast<uint8_t*>(ws), as_stream(stream));
 }
@@ -383,6 +393,8 @@ ns_status ns_orthogonalize_grouped_ex(int count, const void* const* G, const int
   }
   const size_t need = ns_grouped_workspace_bytes(count, m, n);
   if (!ws || ws_bytes < need) return NS_ERR_WORKSPACE;
+  for (int i = 0; i < count; ++i)
+    if (overlaps(out[i], (size_t)(m[i] * n[i]) * dtype_size(ot), ws, ws_bytes)) return NS_ERR_ARG;
   uint8_t* base = static_cast<uint8_t*>(ws);
   for (int i = 0; i < count; ++i) {
     const float ci = q > 0.0 ? INFINITY : clip[i];
@@ -405,6 +417,8 @@ ns_status ns_orthogonalize_grouped(int count, const void* const* G, const int64_
   }
   const size_t need = ns_grouped_workspace_bytes(count, m, n);
   if (!ws || ws_bytes < need) return NS_ERR_WORKSPACE;
+  for (int i = 0; i < count; ++i)
+    if (overlaps(out[i], (size_t)(m[i] * n[i]) * dtype_size(ot), ws, ws_bytes)) return NS_ERR_ARG;
   uint8_t* base = static_cast<uint8_t*>(ws);
   for (int i = 0; i < count; ++i) {
     ns_status st = ns_run(G[i], gt, m[i], n[i], coeffs, k, clip[i], 0.0, nullptr, out[i], ot, base,

@@ -781,7 +781,10 @@ __global__ __launch_bounds__(GThreads, 2) void gemm_general_kernel(GemmProblem g
 #ifndef NVFP4_FAST_NST
 #define NVFP4_FAST_NST 2
 #endif
-using BigCfg = Cfg<2, 2, 2, 2, NVFP4_FAST_NST, 128>;
+#ifndef NVFP4_BIG_SHAPE
+#define NVFP4_BIG_SHAPE 2, 2, 2, 2
+#endif
+using BigCfg = Cfg<NVFP4_BIG_SHAPE, NVFP4_FAST_NST, 128>;
 using SmallCfg = Cfg<1, 2, 2, 2, NVFP4_FAST_NST, 128>;
 #ifndef NVFP4_SMALL_BELOW
 #define NVFP4_SMALL_BELOW 512   // big-tile count below which the small tiles run
