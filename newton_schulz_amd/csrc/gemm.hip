@@ -51,9 +51,12 @@ template <int WM_, int WN_, int FM_, int FN_, int NST_, int BK_>
 struct Cfg {
   static constexpr int WM = WM_, WN = WN_, FM = FM_, FN = FN_;
   static constexpr int NST = NST_;                    // LDS stages in flight
-  static constexpr int BK = BK_;                      // K elements per stage (64 or 128)
+  static constexpr int BK = BK_;                      // K elements per stage (64, 128 or 256)
   static constexpr int kHalves = BK / 64;             // 16-byte lane slices per row per stage
-  static_assert(BK == 64 || BK == 128, "BK must be 64 or 128");
+  static_assert(BK == 64 || BK == 128 || BK == 256, "BK must be 64, 128 or 256");
+  // BK = 256 loads whole 128-byte row lines (see row_chunk); the narrower
+  // stages load 32 rows x 16 bytes per instruction
+  static constexpr bool kLines = BK == 256;
   static constexpr int kWaves = WM * WN;
   static constexpr int kThreads = kWaves * 64;
   static constexpr int BM = WM * FM * 32, BN = WN * FN * 32;
@@ -61,7 +64,8 @@ struct Cfg {
   static constexpr int kGroups = GP + GQ;
   static constexpr int kRegions = kGroups * kHalves;  // 1 KB code regions per stage
   static constexpr int kCodeBytes = kRegions * 1024;
-  static constexpr int kScaleBytes = kGroups * 256;
+  static constexpr int kScaleGroupBytes = kLines ? 512 : 256;   // per 32-row group and stage
+  static constexpr int kScaleBytes = kGroups * kScaleGroupBytes;
   static constexpr int kStage = kCodeBytes + kScaleBytes;
   static constexpr int kAcc = FM * FN * 16;           // accumulators per lane
   // two resident workgroups per CU unless the accumulators alone need more
@@ -75,9 +79,13 @@ struct Cfg {
   // round-robin; when they do not divide evenly, a wave with one fewer
   // repeats its previous load (same bytes to the same LDS address) so that
   // every wave waits on the same count.
-  static_assert(kRegions >= kWaves && kGroups >= kWaves, "fewer regions than waves");
+  // Scale loads: one per group (4 bytes a lane), or with row lines one per
+  // pair of groups (16 bytes a lane, 64 rows).
+  static constexpr int kScaleRegions = kLines ? kGroups / 2 : kGroups;
+  static_assert(!kLines || GP % 2 == 0, "row-line scale loads pair groups of one operand");
+  static_assert(kRegions >= kWaves && kScaleRegions >= kWaves, "fewer regions than waves");
   static constexpr int kCodeLoads = (kRegions + kWaves - 1) / kWaves;
-  static constexpr int kScaleLoads = (kGroups + kWaves - 1) / kWaves;
+  static constexpr int kScaleLoads = (kScaleRegions + kWaves - 1) / kWaves;
   static constexpr int kLoadsPerWave = kCodeLoads + kScaleLoads;
 };
 
@@ -205,13 +213,50 @@ __device__ __forceinline__ int code_region(int wave, int q) {
 template <class C>
 __device__ __forceinline__ int scale_group(int wave, int q) {
   const int r = wave + q * C::kWaves;
-  return r < C::kGroups ? r : r - C::kWaves;
+  return r < C::kScaleRegions ? r : r - C::kWaves;
 }
+
+// Row-line stages (BK = 256): a 32-row group's stage is 32 rows x 128 bytes
+// (eight 16-byte chunks of 32 codes), stored in LDS row by row with chunk c
+// of row r at position c ^ row_swizzle(r).  A DMA instruction then reads 8
+// whole rows -- eight full 128-byte lines -- and the fragment reads below
+// (16 consecutive lanes = 16 rows, one chunk each) hit 16 distinct 16-byte
+// bank slots, as do any 8 consecutive lanes.
+__device__ __forceinline__ int row_swizzle(int r) { return (r ^ (r >> 3)) & 7; }
+
+// K map of a row-line stage: lane half h takes chunks 4h .. 4h+3; quarter
+// qs of the stage feeds its four MFMA steps from chunk 4h + qs, one word
+// (8 codes, two per byte) per step.  Scale block b of the stage covers
+// chunk b / 2, so the lane's 8 scale bytes are blocks 8h .. 8h+7.
 
 template <class C>
 __device__ __forceinline__ void init_sources(const GemmProblem& g, int64_t m0, int64_t n0, int wave,
                                              int lane, StageSrc<C>& src) {
   const int64_t kb = g.K / 2, sb = g.K / 16;
+  if constexpr (C::kLines) {
+#pragma unroll
+    for (int q = 0; q < C::kCodeLoads; ++q) {
+      // region r: rows 8*(r%4) .. +7 of group r/4, lane = row * 8 + position
+      const int r = code_region<C>(wave, q), grp = r / 4;
+      const int rr = 8 * (r % 4) + (lane >> 3);
+      const bool isP = grp < C::GP;
+      int64_t row = (isP ? m0 + 32 * grp : n0 + 32 * (grp - C::GP)) + rr;
+      const int64_t lim = isP ? g.M : g.N;
+      row = row < lim ? row : lim - 1;
+      src.code[q] = (uint32_t)(row * kb + 16 * ((lane & 7) ^ row_swizzle(rr)));
+    }
+#pragma unroll
+    for (int q = 0; q < C::kScaleLoads; ++q) {
+      // region r: groups 2r and 2r+1, one row (16 scale bytes) per lane
+      const int grp = 2 * scale_group<C>(wave, q) + (lane >> 5);
+      const bool isP = grp < C::GP;
+      int64_t row = (isP ? m0 + 32 * grp : n0 + 32 * (grp - C::GP)) + (lane & 31);
+      const int64_t lim = isP ? g.M : g.N;
+      row = row < lim ? row : lim - 1;
+      src.scale[q] = (uint32_t)(row * sb);
+    }
+    return;
+  }
 #pragma unroll
   for (int q = 0; q < C::kCodeLoads; ++q) {
     const int r = code_region<C>(wave, q), grp = r / C::kHalves, hs = r % C::kHalves;
@@ -247,9 +292,15 @@ __device__ __forceinline__ void issue_stage(const GemmProblem& g, const StageSrc
   }
 #pragma unroll
   for (int q = 0; q < C::kScaleLoads; ++q) {
-    const int grp = scale_group<C>(wave, q);
-    const uint8_t* op = (grp < C::GP ? g.scales_p : g.scales_q) + k0 / 16;
-    dma4(op, src.scale[q], base + (uint32_t)C::kCodeBytes + (uint32_t)grp * 256u);
+    const int sr = scale_group<C>(wave, q);
+    if constexpr (C::kLines) {
+      // groups 2sr (lanes 0-31) and 2sr+1 share one operand: GP is even
+      const uint8_t* op = (2 * sr < C::GP ? g.scales_p : g.scales_q) + k0 / 16;
+      dma16(op, src.scale[q], base + (uint32_t)C::kCodeBytes + (uint32_t)sr * 1024u);
+    } else {
+      const uint8_t* op = (sr < C::GP ? g.scales_p : g.scales_q) + k0 / 16;
+      dma4(op, src.scale[q], base + (uint32_t)C::kCodeBytes + (uint32_t)sr * 256u);
+    }
   }
 }
 
@@ -475,14 +526,31 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_fast_kernel(F
     const uint8_t* st = smem + ((kc - kc0) % C::NST) * C::kStage;
 
     // this lane's scale dword per fragment: blocks 4h..4h+3 of the stage
-    // (BK = 128) or the row's 4 blocks (BK = 64), as E4M3 bytes
-    uint32_t sp[C::FM], sq[C::FN];
+    // (BK = 128) or the row's 4 blocks (BK = 64), as E4M3 bytes; with row
+    // lines (BK = 256) two dwords, blocks 8h..8h+7
+    uint32_t sp[C::FM], sq[C::FN], sp1[C::FM], sq1[C::FN];
+    if constexpr (C::kLines) {
+      const int so = 16 * (lane & 31) + 8 * (lane >> 5);
 #pragma unroll
-    for (int i = 0; i < C::FM; ++i)
-      sp[i] = *reinterpret_cast<const uint32_t*>(st + C::kCodeBytes + (wm * C::FM + i) * 256 + 4 * lane);
+      for (int i = 0; i < C::FM; ++i) {
+        const uint2 w = *reinterpret_cast<const uint2*>(st + C::kCodeBytes + (wm * C::FM + i) * 512 + so);
+        sp[i] = w.x;
+        sp1[i] = w.y;
+      }
 #pragma unroll
-    for (int j = 0; j < C::FN; ++j)
-      sq[j] = *reinterpret_cast<const uint32_t*>(st + C::kCodeBytes + (C::GP + wn * C::FN + j) * 256 + 4 * lane);
+      for (int j = 0; j < C::FN; ++j) {
+        const uint2 w = *reinterpret_cast<const uint2*>(st + C::kCodeBytes + (C::GP + wn * C::FN + j) * 512 + so);
+        sq[j] = w.x;
+        sq1[j] = w.y;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i)
+        sp[i] = *reinterpret_cast<const uint32_t*>(st + C::kCodeBytes + (wm * C::FM + i) * 256 + 4 * lane);
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j)
+        sq[j] = *reinterpret_cast<const uint32_t*>(st + C::kCodeBytes + (C::GP + wn * C::FN + j) * 256 + 4 * lane);
+    }
     if constexpr (C::BK == 64) {
       // this lane half's two blocks into the low half-word
 #pragma unroll
@@ -495,15 +563,30 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_fast_kernel(F
     for (int hs = 0; hs < C::kHalves; ++hs) {
       uint4 cp[C::FM], cq[C::FN];
       half2_t spf[C::FM], sqf[C::FN];   // the half-stage's two block scales as f16
+      if constexpr (C::kLines) {
+        // chunk 4h + hs of row lane%32, at its swizzled position
+        const int lo = 128 * (lane & 31) + 16 * ((4 * (lane >> 5) + hs) ^ row_swizzle(lane & 31));
 #pragma unroll
-      for (int i = 0; i < C::FM; ++i) {
-        cp[i] = *reinterpret_cast<const uint4*>(st + ((wm * C::FM + i) * C::kHalves + hs) * 1024 + 16 * lane);
-        spf[i] = scale_pair2_f16(sp[i], hs);
-      }
+        for (int i = 0; i < C::FM; ++i) {
+          cp[i] = *reinterpret_cast<const uint4*>(st + (wm * C::FM + i) * 4096 + lo);
+          spf[i] = scale_pair2_f16(hs < 2 ? sp[i] : sp1[i], hs & 1);
+        }
 #pragma unroll
-      for (int j = 0; j < C::FN; ++j) {
-        cq[j] = *reinterpret_cast<const uint4*>(st + ((C::GP + wn * C::FN + j) * C::kHalves + hs) * 1024 + 16 * lane);
-        sqf[j] = scale_pair2_f16(sq[j], hs);
+        for (int j = 0; j < C::FN; ++j) {
+          cq[j] = *reinterpret_cast<const uint4*>(st + (C::GP + wn * C::FN + j) * 4096 + lo);
+          sqf[j] = scale_pair2_f16(hs < 2 ? sq[j] : sq1[j], hs & 1);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i) {
+          cp[i] = *reinterpret_cast<const uint4*>(st + ((wm * C::FM + i) * C::kHalves + hs) * 1024 + 16 * lane);
+          spf[i] = scale_pair2_f16(sp[i], hs);
+        }
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) {
+          cq[j] = *reinterpret_cast<const uint4*>(st + ((C::GP + wn * C::FN + j) * C::kHalves + hs) * 1024 + 16 * lane);
+          sqf[j] = scale_pair2_f16(sq[j], hs);
+        }
       }
       // software pipeline: step s + 1 is dequantized while step s multiplies
       half8_t av[C::FM], bv[C::FN];
@@ -775,17 +858,24 @@ __global__ __launch_bounds__(GThreads, 2) void gemm_general_kernel(GemmProblem g
 
 // Two tile shapes: 128 x 128 (four 64 x 64 waves), and 64 x 128 (two waves)
 // for products with short K whose 128 x 128 tiles would leave most of the
-// GPU's workgroup slots empty, such as qA qA^T at 3072^2 (300 tiles for 256
-// CUs).  Measured inside the iteration, the small tiles lose on long K (the
-// 3072^2 x 8192 Gram product: more operand re-reads) and win on short K.
+// GPU's workgroup slots empty.  With 128-wide stages the small tiles lose on
+// long K (more operand re-reads) and win on short K.
 #ifndef NVFP4_FAST_NST
 #define NVFP4_FAST_NST 2
 #endif
 #ifndef NVFP4_BIG_SHAPE
 #define NVFP4_BIG_SHAPE 2, 2, 2, 2
 #endif
-using BigCfg = Cfg<NVFP4_BIG_SHAPE, NVFP4_FAST_NST, 128>;
-using SmallCfg = Cfg<1, 2, 2, 2, NVFP4_FAST_NST, 128>;
+// K % 256 == 0 runs 128 x 128 tiles with 256-wide row-line stages: a DMA
+// instruction that reads whole 128-byte lines moves its kilobyte about four
+// times faster than one that gathers 32 bytes from each of 32 rows
+// (measured: 9.6 TB/s gathered vs 37 TB/s from L2 over all CUs), which
+// makes the short-K products fast on the big tiles too (qA qA^T at 3072^2:
+// 55 us vs 63 us on the 64 x 128 tiles).  Other multiples of 128 keep the
+// 128-wide stages and the tile choice below.
+using BigCfg = Cfg<NVFP4_BIG_SHAPE, NVFP4_FAST_NST, 256>;
+using BigCfg128 = Cfg<NVFP4_BIG_SHAPE, NVFP4_FAST_NST, 128>;
+using SmallCfg128 = Cfg<1, 2, 2, 2, NVFP4_FAST_NST, 128>;
 #ifndef NVFP4_SMALL_BELOW
 #define NVFP4_SMALL_BELOW 512   // big-tile count below which the small tiles run
 #endif
@@ -800,8 +890,8 @@ using SmallCfg = Cfg<1, 2, 2, 2, NVFP4_FAST_NST, 128>;
 #ifndef NVFP4_CUS_PER_XCD
 #define NVFP4_CUS_PER_XCD 32     // MI355X: 256 CUs in 8 XCDs
 #endif
-#ifndef NVFP4_MIN_PART_STAGES
-#define NVFP4_MIN_PART_STAGES 8  // 1024 of K per part at least
+#ifndef NVFP4_MIN_PART_K
+#define NVFP4_MIN_PART_K 1024    // K per part at least
 #endif
 #ifndef NVFP4_MAX_PARTS
 #define NVFP4_MAX_PARTS 8
@@ -842,7 +932,8 @@ GemmPlan plan_with(int64_t M, int64_t N, int64_t K, bool symmetric, bool allow_s
   if (allow_split && left_max > 0 && one_per_cu) {
     int64_t q = cus / left_max;
     if (q > NVFP4_MAX_PARTS) q = NVFP4_MAX_PARTS;
-    if (q > stages / NVFP4_MIN_PART_STAGES) q = stages / NVFP4_MIN_PART_STAGES;
+    if (q > K / NVFP4_MIN_PART_K) q = K / NVFP4_MIN_PART_K;
+    if (q > stages) q = stages;
     parts = q >= 2 ? (int)q : 1;
   }
   p.splits = parts;
@@ -896,9 +987,10 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool symmetric, bool allow_s
     p.splits = 1;
     return p;
   }
-  const GemmPlan big = plan_with<BigCfg>(M, N, K, symmetric, allow_split, 0);
+  if (K % 256 == 0) return plan_with<BigCfg>(M, N, K, symmetric, allow_split, 0);
+  const GemmPlan big = plan_with<BigCfg128>(M, N, K, symmetric, allow_split, 2);
   if (big.tiles >= NVFP4_SMALL_BELOW || K > NVFP4_SMALL_MAX_K) return big;
-  return plan_with<SmallCfg>(M, N, K, symmetric, allow_split, 1);
+  return plan_with<SmallCfg128>(M, N, K, symmetric, allow_split, 3);
 }
 
 hipError_t launch_gemm(const GemmProblem& g, const GemmPlan& p, float* partials, hipStream_t s) {
@@ -912,7 +1004,11 @@ hipError_t launch_gemm(const GemmProblem& g, const GemmPlan& p, float* partials,
     }
     return hipGetLastError();
   }
-  return p.cfg == 0 ? launch_with<BigCfg>(g, p, partials, s) : launch_with<SmallCfg>(g, p, partials, s);
+  switch (p.cfg) {
+    case 0: return launch_with<BigCfg>(g, p, partials, s);
+    case 2: return launch_with<BigCfg128>(g, p, partials, s);
+    default: return launch_with<SmallCfg128>(g, p, partials, s);
+  }
 }
 
 }  // namespace nvfp4

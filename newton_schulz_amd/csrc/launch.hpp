@@ -77,7 +77,8 @@ struct GemmProblem {
 // partials.
 struct GemmPlan {
   bool fast;
-  int cfg;                // tile shape of the fast path (0: 128 x 128, 1: 64 x 128)
+  int cfg;                // fast-path config: 128 x 128 tiles with 256-wide row-line
+                          // stages (0) or 128-wide ones (2), 64 x 128 tiles (3)
   int splits;             // K-parts of each leftover tile (1: none split)
   int64_t TM, TN, tiles;
   int64_t units;          // workgroups of the product kernel

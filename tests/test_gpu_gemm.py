@@ -77,7 +77,10 @@ def test_every_gemm_of_a_clipped_lowrank_run():
     _gemm_steps(trace_G, [QUINTIC, (1.5, -0.5, 0.0)], "lowrank 272x528")
 
 
-@pytest.mark.parametrize("MNK", [(144, 80, 272), (16, 16, 16), (128, 384, 4096), (200 - 8, 64, 48)])
+# K % 128 != 0 runs the general kernel, K % 256 == 128 the 128-wide stages,
+# K % 256 == 0 the row-line stages; the ragged M and N cut partial tiles
+@pytest.mark.parametrize("MNK", [(144, 80, 272), (16, 16, 16), (128, 384, 4096), (200 - 8, 64, 48),
+                                 (208, 144, 384), (208, 272, 1152), (208, 144, 512), (304, 528, 1280)])
 def test_general_gemm_ragged(MNK):
     M, Nn, K = MNK
     rng = np.random.default_rng(M + Nn + K)
@@ -93,7 +96,7 @@ def test_general_gemm_ragged(MNK):
     assert rel_fro(got2, 2.0 * add.astype(np.float32) - 0.5 * want) <= TOL
 
 
-@pytest.mark.parametrize("M,K", [(144, 272), (400, 96)])
+@pytest.mark.parametrize("M,K", [(144, 272), (400, 96), (208, 640), (336, 768), (528, 1536)])
 def test_symmetric_gemm_ragged(M, K):
     rng = np.random.default_rng(M)
     X = rng.standard_normal((M, K))
