@@ -105,6 +105,11 @@ struct FastArgs {
   float* partials;
 };
 
+template <bool B>
+struct BoolTag {
+  static constexpr bool value = B;
+};
+
 struct Unit {
   int tile;             // tile index
   int part;             // K-part of a split tile (0 for a whole tile)
@@ -393,15 +398,38 @@ __device__ __forceinline__ void epilogue_block(const GemmProblem& g, const EpCtx
 // (BM * N < 2^31 is checked at the API); tiles wholly inside the matrix
 // (and, if symmetric, wholly above the diagonal) skip the per-element tests.
 //
-// The addend may be the output itself, so the compiler must keep every
-// store after the loads it could alias; the 16 addend loads of each 32 x 32
-// sub-tile are therefore issued together before any of its stores: one
-// memory round trip per sub-tile instead of one per element.  This
-// is safe in place: each position is read only by the lane that writes it,
-// and mirrored stores land below the diagonal, which no tile reads.
+// The addend values of this lane's outputs (MFMA output layout), loaded by
+// the kernel while the tile's last K-stage still computes so that the
+// epilogue finds them in registers; positions outside the matrix (or below
+// the diagonal of a symmetric product) read as 0.
+template <class C, bool SYM>
+__device__ __forceinline__ void load_addend(const GemmProblem& g, int64_t m0, int64_t n0, int wm, int wn,
+                                            int lane, float (&ad)[C::FM][C::FN][16]) {
+  const int N = (int)g.N;
+  const int64_t r0 = m0 + wm * C::FM * 32 + 4 * (lane >> 5);
+  const int64_t c0 = n0 + wn * C::FN * 32 + (lane & 31);
+  const float* abase = g.addend + r0 * g.N + c0;
+  const bool fast = m0 + C::BM <= g.M && n0 + C::BN <= g.N && (!SYM || m0 + C::BM <= n0);
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int dr = i * 32 + 8 * (r >> 2) + (r & 3);
+        const int64_t row = r0 + dr, col = c0 + j * 32;
+        const bool ok = fast || (row < g.M && col < g.N && (!SYM || row <= col));
+        ad[i][j][r] = ok ? abase[dr * N + j * 32] : 0.0f;
+      }
+}
+
+// In place (addend == out) every position is read, by load_addend, before
+// the lane that owns it stores it, and mirrored stores land below the
+// diagonal, which no tile reads.
 template <class C, bool SYM>
 __device__ __forceinline__ void epilogue(const GemmProblem& g, floatx16 (&acc)[C::FM][C::FN],
-                                         int64_t m0, int64_t n0, int wm, int wn, int lane) {
+                                         const float (&ad)[C::FM][C::FN][16], int64_t m0, int64_t n0,
+                                         int wm, int wn, int lane) {
   const float scale = g.alpha * (*g.sg_p) * (*g.sg_q);
   const float beta = g.beta;
   const int h = lane >> 5, c32 = lane & 31;
@@ -409,7 +437,7 @@ __device__ __forceinline__ void epilogue(const GemmProblem& g, floatx16 (&acc)[C
   const int64_t r0 = m0 + wm * C::FM * 32 + 4 * h;     // first row of this lane
   const int64_t c0 = n0 + wn * C::FN * 32 + c32;       // first column of this lane
   float* obase = g.out + r0 * g.N + c0;
-  const float* abase = g.addend ? g.addend + r0 * g.N + c0 : nullptr;
+  const bool add = g.addend != nullptr;
   float* mbase = g.out + c0 * g.N + r0;                // mirror: (col, row)
   const bool inside = m0 + C::BM <= g.M && n0 + C::BN <= g.N;
   const bool upper = !SYM || (m0 + C::BM <= n0);       // every element has row < col
@@ -423,14 +451,6 @@ __device__ __forceinline__ void epilogue(const GemmProblem& g, floatx16 (&acc)[C
   for (int i = 0; i < C::FM; ++i)
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) {
-      float ad[16];
-      if (abase) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int dr = i * 32 + 8 * (r >> 2) + (r & 3);
-          ad[r] = valid(dr, j) ? abase[dr * N + j * 32] : 0.0f;
-        }
-      }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         float v4[4];
@@ -439,7 +459,7 @@ __device__ __forceinline__ void epilogue(const GemmProblem& g, floatx16 (&acc)[C
           const int r = 4 * q + t;
           const int dr = i * 32 + 8 * q + t;           // row offset from r0
           float v = scale * acc[i][j][r];
-          if (abase) v = fmaf(beta, ad[r], v);
+          if (add) v = fmaf(beta, ad[i][j][r], v);
           if (valid(dr, j)) {
             obase[dr * N + j * 32] = v;
             const uint32_t ab = abs_bits(v);
@@ -505,12 +525,16 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_fast_kernel(F
   const int64_t kc0 = nk_all * un.part / nparts, kc1 = nk_all * (un.part + 1) / nparts;
 
 
+  float ad[C::FM][C::FN][16];   // the addend, loaded during the last stage
+
   // prologue: stages kc0 .. kc0 + NST - 2 in flight
 #pragma unroll
   for (int p = 0; p < C::NST - 1; ++p)
     if (kc0 + p < kc1) issue_stage<C>(g, src, (kc0 + p) * C::BK, smem + p * C::kStage, wave);
 
-  for (int64_t kc = kc0; kc < kc1; ++kc) {
+  // one K-stage; the last (peeled, so that the addend registers are live
+  // only there) also fetches the epilogue's addend
+  auto stage = [&](int64_t kc, auto last) {
     // wait for this wave's loads of stage kc (later stages may stay in
     // flight), then for every wave's; the barrier also retires all reads of
     // the buffer the next issue overwrites
@@ -523,6 +547,10 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_fast_kernel(F
     if (kc + C::NST - 1 < kc1)
       issue_stage<C>(g, src, (kc + C::NST - 1) * C::BK,
                      smem + ((kc - kc0 + C::NST - 1) % C::NST) * C::kStage, wave);
+    // the last stage: fetch the epilogue's addend while it computes (no
+    // later stage waits on vmcnt, so these loads delay nothing)
+    if constexpr (decltype(last)::value)
+      if (un.split < 0 && g.addend) load_addend<C, SYM>(g, m0, n0, wm, wn, lane, ad);
     const uint8_t* st = smem + ((kc - kc0) % C::NST) * C::kStage;
 
     // this lane's scale dword per fragment: blocks 4h..4h+3 of the stage
@@ -632,7 +660,9 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_fast_kernel(F
         }
       }
     }
-  }
+  };
+  for (int64_t kc = kc0; kc < kc1 - 1; ++kc) stage(kc, BoolTag<false>{});
+  stage(kc1 - 1, BoolTag<true>{});
 
   if (un.split >= 0) {
     // K-part of a split tile: store the FP32 partial; gemm_reduce_kernel sums
@@ -650,7 +680,7 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_fast_kernel(F
                           acc[i][j][4 * q + 3]);
     return;
   }
-  epilogue<C, SYM>(g, acc, m0, n0, wm, wn, lane);
+  epilogue<C, SYM>(g, acc, ad, m0, n0, wm, wn, lane);
 }
 
 // One wave per workgroup: block (i, j) of wave w's sub-tile of split tile
