@@ -96,6 +96,11 @@ struct Cfg {
 // n mod cus tiles is split along K into `parts` units whose FP32 partials a
 // second kernel sums in a fixed order, so the leftover work spreads over
 // the CUs instead of doubling some of them.
+#ifndef NVFP4_MAX_PARTS
+#define NVFP4_MAX_PARTS 8
+#endif
+constexpr int kMaxParts = NVFP4_MAX_PARTS;   // K-parts of a split tile at most
+
 struct FastArgs {
   GemmProblem g;
   int64_t TM, TN;       // tile grid
@@ -334,17 +339,35 @@ __device__ __forceinline__ EpCtx epilogue_ctx(const GemmProblem& g, int64_t m0, 
   return e;
 }
 
+// The addend of one 32 x 32 block (i, j) of a wave's sub-tile in the MFMA
+// output layout (0 outside the matrix or below a symmetric diagonal).
+template <class C, bool SYM>
+__device__ __forceinline__ void load_addend_block(const GemmProblem& g, const EpCtx& e, int i, int j,
+                                                  float (&ad)[16]) {
+  const int N = e.N;
+  const float* atile = g.addend + e.m0 * g.N + e.n0;
+  const int lo = e.dr0 * N + e.dc0;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int dr = i * 32 + 8 * (r >> 2) + (r & 3);
+    const int64_t row = e.m0 + e.dr0 + dr, col = e.n0 + e.dc0 + j * 32;
+    const bool ok = e.fast || (row < g.M && col < g.N && (!SYM || row <= col));
+    ad[r] = ok ? atile[lo + dr * N + j * 32] : 0.0f;
+  }
+}
+
 // The epilogue of one 32 x 32 block (i, j) of a wave's sub-tile, for the
 // reduce kernel (v holds the block's 16 values per lane in the MFMA output
-// layout); the same arithmetic as `epilogue` below, which keeps its own
-// copy because sharing this one raises the product kernel's register count.
+// layout, ad its addend); the same arithmetic as `epilogue` below, which
+// keeps its own copy because sharing this one raises the product kernel's
+// register count.
 template <class C, bool SYM>
-__device__ __forceinline__ void epilogue_block(const GemmProblem& g, const EpCtx& e,
-                                               const floatx16& v16, int i, int j, uint32_t& amax) {
+__device__ __forceinline__ void epilogue_block(const GemmProblem& g, const EpCtx& e, const floatx16& v16,
+                                               const float (&ad)[16], int i, int j, uint32_t& amax) {
   const int N = e.N;
   // wave-uniform tile bases and 32-bit lane offsets (BM * N < 2^31)
   float* otile = g.out + e.m0 * g.N + e.n0;
-  const float* atile = g.addend ? g.addend + e.m0 * g.N + e.n0 : nullptr;
+  const bool atile = g.addend != nullptr;
   float* mtile = g.out + e.n0 * g.N + e.m0;           // mirror: (col, row)
   const int lo = e.dr0 * N + e.dc0, mo = e.dc0 * N + e.dr0;
   auto valid = [&](int dr) {
@@ -352,14 +375,6 @@ __device__ __forceinline__ void epilogue_block(const GemmProblem& g, const EpCtx
     const int64_t row = e.m0 + e.dr0 + dr, col = e.n0 + e.dc0 + j * 32;
     return row < g.M && col < g.N && (!SYM || row <= col);
   };
-  float ad[16];
-  if (atile) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int dr = i * 32 + 8 * (r >> 2) + (r & 3);
-      ad[r] = valid(dr) ? atile[lo + dr * N + j * 32] : 0.0f;
-    }
-  }
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     float v4[4];
@@ -700,20 +715,32 @@ __global__ __launch_bounds__(64) void gemm_reduce_kernel(FastArgs a) {
   const int lane = threadIdx.x & 63;
   const int thread = w * 64 + lane;                 // the lane's thread in the product kernel
   const float* base = a.partials + (size_t)s * a.parts * C::kAcc * C::kThreads;
+  const EpCtx e = epilogue_ctx<C, SYM>(a.g, I * C::BM, J * C::BN, w / C::WN, w % C::WN, lane);
+  // every load first (addend, then all parts), so that the block costs one
+  // memory round trip; then the sum in part order
+  float ad[16];
+  if (a.g.addend) load_addend_block<C, SYM>(a.g, e, i, j, ad);
+  float4 u[kMaxParts][4];
+#pragma unroll
+  for (int p = 0; p < kMaxParts; ++p)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (p < a.parts)
+        u[p][q] = *reinterpret_cast<const float4*>(base + (size_t)p * C::kAcc * C::kThreads +
+                                                   partial_index<C>(b, q, thread));
   floatx16 v;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    float4 t = *reinterpret_cast<const float4*>(base + partial_index<C>(b, q, thread));
-    for (int p = 1; p < a.parts; ++p) {
-      const float4 u = *reinterpret_cast<const float4*>(base + (size_t)p * C::kAcc * C::kThreads +
-                                                        partial_index<C>(b, q, thread));
-      t.x += u.x; t.y += u.y; t.z += u.z; t.w += u.w;
-    }
+    float4 t = u[0][q];
+#pragma unroll
+    for (int p = 1; p < kMaxParts; ++p)
+      if (p < a.parts) {
+        t.x += u[p][q].x; t.y += u[p][q].y; t.z += u[p][q].z; t.w += u[p][q].w;
+      }
     v[4 * q] = t.x; v[4 * q + 1] = t.y; v[4 * q + 2] = t.z; v[4 * q + 3] = t.w;
   }
-  const EpCtx e = epilogue_ctx<C, SYM>(a.g, I * C::BM, J * C::BN, w / C::WN, w % C::WN, lane);
   uint32_t amax = 0;
-  epilogue_block<C, SYM>(a.g, e, v, i, j, amax);
+  epilogue_block<C, SYM>(a.g, e, v, ad, i, j, amax);
   if (a.g.amax_out) amax_publish_wave(amax, a.g.amax_out, a.g.amax_parts != 0);
 }
 
@@ -922,9 +949,6 @@ using SmallCfg128 = Cfg<1, 2, 2, 2, NVFP4_FAST_NST, 128>;
 #endif
 #ifndef NVFP4_MIN_PART_K
 #define NVFP4_MIN_PART_K 1024    // K per part at least
-#endif
-#ifndef NVFP4_MAX_PARTS
-#define NVFP4_MAX_PARTS 8
 #endif
 
 int64_t sym_tiles(int64_t TM, int64_t TN, int64_t BM, int64_t BN) {
