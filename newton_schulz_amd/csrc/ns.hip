@@ -12,28 +12,20 @@ namespace nvfp4 {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kFlatGrid = 4096;   // workgroups of the flat passes at most
 
+// Four consecutive values (elements 4q .. 4q+3) as FP32 bit patterns.
+// Kernels give consecutive lanes consecutive q, so each load instruction of
+// a wave reads one contiguous run of memory: a gather of 16 bytes from each
+// of many cache lines costs the texture unit one line lookup per lane and
+// runs several times slower.
 template <Dt T>
-__device__ __forceinline__ void load16_raw(const void* base, int64_t idx, uint32_t (&v)[16]) {
+__device__ __forceinline__ uint4 load4(const void* base, int64_t q) {
   if constexpr (T == Dt::F32) {
-    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(base) + idx);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint4 w = p[j];
-      v[4 * j] = w.x; v[4 * j + 1] = w.y; v[4 * j + 2] = w.z; v[4 * j + 3] = w.w;
-    }
+    return reinterpret_cast<const uint4*>(base)[q];
   } else {
-    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + idx);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      uint4 w = p[j];
-      uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        v[8 * j + 2 * t] = ws[t] << 16;
-        v[8 * j + 2 * t + 1] = ws[t] & 0xFFFF0000u;
-      }
-    }
+    const uint2 w = reinterpret_cast<const uint2*>(base)[q];
+    return make_uint4(w.x << 16, w.x & 0xFFFF0000u, w.y << 16, w.y & 0xFFFF0000u);
   }
 }
 
@@ -55,22 +47,42 @@ __device__ __forceinline__ double block_sum(double v) {
 }
 
 template <Dt T>
-__global__ __launch_bounds__(kThreads) void norm_partials_kernel(const void* G, int64_t nblk,
-                                                                  float clip, const float* clip_dev,
-                                                                  double* part) {
+__global__ __launch_bounds__(kThreads) void norm_partials_kernel(const void* G, int64_t n, float clip,
+                                                                  const float* clip_dev, double* part) {
   if (clip_dev) clip = *clip_dev;
-  double acc = 0.0;
-  for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < nblk;
-       b += (int64_t)gridDim.x * kThreads) {
-    uint32_t v[16];
-    load16_raw<T>(G, b * 16, v);
+  // 16-byte units (4 FP32 or 8 BF16 values), consecutive lanes on
+  // consecutive units, four loads in flight; each thread keeps four FP64
+  // chains (one per 32-bit word of a unit) and adds them in a fixed order
+  constexpr int EPU = T == Dt::F32 ? 4 : 8;
+  constexpr int U = 4;
+  const int64_t nu = n / EPU, stride = (int64_t)gridDim.x * kThreads;
+  double ch[4] = {0.0, 0.0, 0.0, 0.0};
+  auto add = [&](uint4 w) {
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      double x = (double)clampf(__uint_as_float(v[i]), clip);
-      acc = fma(x, x, acc);
+    for (int t = 0; t < 4; ++t) {
+      if constexpr (T == Dt::F32) {
+        const double x = (double)clampf(__uint_as_float(ws[t]), clip);
+        ch[t] = fma(x, x, ch[t]);
+      } else {
+        const double x0 = (double)clampf(__uint_as_float(ws[t] << 16), clip);
+        ch[t] = fma(x0, x0, ch[t]);
+        const double x1 = (double)clampf(__uint_as_float(ws[t] & 0xFFFF0000u), clip);
+        ch[t] = fma(x1, x1, ch[t]);
+      }
     }
+  };
+  const uint4* p = static_cast<const uint4*>(G);
+  int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  for (; u + (U - 1) * stride < nu; u += U * stride) {
+    uint4 w[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) w[k] = p[u + k * stride];
+#pragma unroll
+    for (int k = 0; k < U; ++k) add(w[k]);
   }
-  double s = block_sum(acc);
+  for (; u < nu; u += stride) add(p[u]);
+  double s = block_sum((ch[0] + ch[1]) + (ch[2] + ch[3]));
   if (threadIdx.x == 0) part[blockIdx.x] = s;
 }
 
@@ -86,57 +98,94 @@ __global__ __launch_bounds__(kThreads) void norm_finalize_kernel(const double* p
   if (z2) amax_clear(z2);
 }
 
-// X tile 64 x 64 per workgroup; thread t owns X row t/4, columns
-// 16*(t%4)..+15.  When transposed, G is xn x xm and its tile passes LDS.
-template <Dt T, bool TR>
-__global__ __launch_bounds__(kThreads) void normalize_kernel(const void* G, int64_t xm, int64_t xn,
-                                                              float clip, const float* clip_dev,
-                                                              const double* invp, float* X,
-                                                              uint32_t* amax_slot) {
-  if (clip_dev) clip = *clip_dev;
-  __shared__ float tile[64][65];
-  const double inv = *invp;
-  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
-  const int tr = threadIdx.x >> 2, tc = (threadIdx.x & 3) * 16;
-  float x[16];
-  if constexpr (TR) {
-    // G row (c0 + tr), G columns (r0 + tc ..): X[r0 + tc + i][c0 + tr]
-    uint32_t v[16];
-    if (c0 + tr < xn && r0 + tc < xm) {
-      load16_raw<T>(G, (c0 + tr) * xm + r0 + tc, v);
-    } else {
+// 64 x 64 transposing tiles: a workgroup reads a tile of the source, whose
+// 64 rows hold 16 four-value units each, with lanes 16k .. 16k+15 on one
+// row's units (contiguous), keeps it in LDS as FP32, and writes the
+// transposed tile the same way: lanes 16k .. 16k+15 on the 16 units of one
+// destination row.  With the 65-float row pitch both LDS phases are free of
+// bank conflicts.
+constexpr int kTile = 64;
+using TileBuf = float[kTile][kTile + 1];
+
+// tile[r][c] = src[(row0 + r) * ld + col0 + c] for rows < nrows, cols < ncols
+template <Dt T>
+__device__ __forceinline__ void tile_load(const void* src, int64_t ld, int64_t row0, int64_t col0,
+                                          int64_t nrows, int64_t ncols, TileBuf& tile) {
+  const int u = threadIdx.x & 15;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) v[i] = 0u;
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) tile[tc + i][tr] = __uint_as_float(v[i]);
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 16; ++i) x[i] = tile[tr][tc + i];
-  } else {
-    uint32_t v[16];
-    if (r0 + tr < xm && c0 + tc < xn) {
-      load16_raw<T>(G, (r0 + tr) * xn + c0 + tc, v);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) v[i] = 0u;
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) x[i] = __uint_as_float(v[i]);
+  for (int pass = 0; pass < kTile / 16; ++pass) {
+    const int r = pass * 16 + (threadIdx.x >> 4);
+    uint4 w = make_uint4(0u, 0u, 0u, 0u);
+    if (row0 + r < nrows && col0 + 4 * u < ncols) w = load4<T>(src, ((row0 + r) * ld + col0) / 4 + u);
+    tile[r][4 * u] = __uint_as_float(w.x);
+    tile[r][4 * u + 1] = __uint_as_float(w.y);
+    tile[r][4 * u + 2] = __uint_as_float(w.z);
+    tile[r][4 * u + 3] = __uint_as_float(w.w);
   }
+}
+
+// X = normalised G^T: G is xn x xm, X is xm x xn.
+template <Dt T>
+__global__ __launch_bounds__(kThreads) void normalize_tr_kernel(const void* G, int64_t xm, int64_t xn,
+                                                                 float clip, const float* clip_dev,
+                                                                 const double* invp, float* X,
+                                                                 uint32_t* amax_slot) {
+  __shared__ TileBuf tile;
+  if (clip_dev) clip = *clip_dev;
+  const double inv = *invp;
+  const int64_t r0 = (int64_t)blockIdx.y * kTile, c0 = (int64_t)blockIdx.x * kTile;   // X tile
+  tile_load<T>(G, xm, c0, r0, xn, xm, tile);      // tile[X col][X row]
+  __syncthreads();
+  const int u = threadIdx.x & 15;
   uint32_t amax = 0;
-  if (r0 + tr < xm && c0 + tc < xn) {
-    float y[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      y[i] = (float)((double)clampf(x[i], clip) * inv);
-      uint32_t a = abs_bits(y[i]);
+  for (int pass = 0; pass < kTile / 16; ++pass) {
+    const int r = pass * 16 + (threadIdx.x >> 4);
+    if (r0 + r < xm && c0 + 4 * u < xn) {
+      float y[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        y[i] = (float)((double)clampf(tile[4 * u + i][r], clip) * inv);
+        const uint32_t a = abs_bits(y[i]);
+        amax = a > amax ? a : amax;
+      }
+      reinterpret_cast<float4*>(X + (r0 + r) * xn + c0)[u] = make_float4(y[0], y[1], y[2], y[3]);
+    }
+  }
+  amax_publish_block(amax, amax_slot);
+}
+
+// X = G (same layout): a flat pass over 4-value units, consecutive lanes on
+// consecutive units, four loads in flight per thread.
+template <Dt T>
+__global__ __launch_bounds__(kThreads) void normalize_flat_kernel(const void* G, int64_t nq, float clip,
+                                                                   const float* clip_dev, const double* invp,
+                                                                   float* X, uint32_t* amax_slot) {
+  constexpr int U = 4;
+  if (clip_dev) clip = *clip_dev;
+  const double inv = *invp;
+  uint32_t amax = 0;
+  auto emit = [&](int64_t q, uint4 w) {
+    const uint32_t v[4] = {w.x, w.y, w.z, w.w};
+    float y[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      y[i] = (float)((double)clampf(__uint_as_float(v[i]), clip) * inv);
+      const uint32_t a = abs_bits(y[i]);
       amax = a > amax ? a : amax;
     }
-    float4* o = reinterpret_cast<float4*>(X + (r0 + tr) * xn + c0 + tc);
+    reinterpret_cast<float4*>(X)[q] = make_float4(y[0], y[1], y[2], y[3]);
+  };
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  int64_t q = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  for (; q + (U - 1) * stride < nq; q += U * stride) {
+    uint4 w[U];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) o[j] = make_float4(y[4 * j], y[4 * j + 1], y[4 * j + 2], y[4 * j + 3]);
+    for (int u = 0; u < U; ++u) w[u] = load4<T>(G, q + u * stride);
+#pragma unroll
+    for (int u = 0; u < U; ++u) emit(q + u * stride, w[u]);
   }
+  for (; q < nq; q += stride) emit(q, load4<T>(G, q));
   amax_publish_block(amax, amax_slot);
 }
 
@@ -146,53 +195,43 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
 }
 
-// out = X (xm x xn) or X^T (xn x xm); 64 x 64 tiles of X.
-template <Dt O, bool TR>
-__global__ __launch_bounds__(kThreads) void write_out_kernel(const float* X, int64_t xm, int64_t xn,
-                                                              void* out) {
-  __shared__ float tile[64][65];
-  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
-  const int tr = threadIdx.x >> 2, tc = (threadIdx.x & 3) * 16;
-  float y[16];
-  int64_t orow, ocol, ocols;
-  bool ok;
-  if constexpr (TR) {
-    const bool in = r0 + tr < xm && c0 + tc < xn;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) tile[tr][tc + i] = in ? X[(r0 + tr) * xn + c0 + tc + i] : 0.0f;
-    __syncthreads();
-    // out row = X column c0 + tr, out columns = X rows r0 + tc ..
-#pragma unroll
-    for (int i = 0; i < 16; ++i) y[i] = tile[tc + i][tr];
-    orow = c0 + tr; ocol = r0 + tc; ocols = xm;
-    ok = orow < xn && ocol < xm;
-  } else {
-    ok = r0 + tr < xm && c0 + tc < xn;
-    if (ok) {
-      const float4* p = reinterpret_cast<const float4*>(X + (r0 + tr) * xn + c0 + tc);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float4 w = p[j];
-        y[4 * j] = w.x; y[4 * j + 1] = w.y; y[4 * j + 2] = w.z; y[4 * j + 3] = w.w;
-      }
-    }
-    orow = r0 + tr; ocol = c0 + tc; ocols = xn;
+__device__ __forceinline__ uint2 bf16x4(float a, float b, float c, float d) {
+  return make_uint2((uint32_t)f32_to_bf16_rne(a) | ((uint32_t)f32_to_bf16_rne(b) << 16),
+                    (uint32_t)f32_to_bf16_rne(c) | ((uint32_t)f32_to_bf16_rne(d) << 16));
+}
+
+// out = X in the output type (same layout): a flat pass over 4-value units.
+template <Dt O>
+__global__ __launch_bounds__(kThreads) void write_out_flat_kernel(const float* X, int64_t nq, void* out) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t q = (int64_t)blockIdx.x * kThreads + threadIdx.x; q < nq; q += stride) {
+    const float4 w = reinterpret_cast<const float4*>(X)[q];
+    if constexpr (O == Dt::F32)
+      reinterpret_cast<float4*>(out)[q] = w;
+    else
+      reinterpret_cast<uint2*>(out)[q] = bf16x4(w.x, w.y, w.z, w.w);
   }
-  if (!ok) return;
-  if constexpr (O == Dt::F32) {
-    float4* o = reinterpret_cast<float4*>(static_cast<float*>(out) + orow * ocols + ocol);
+}
+
+// out = X^T (xn x xm) through 64 x 64 tiles of X.
+template <Dt O>
+__global__ __launch_bounds__(kThreads) void write_out_tr_kernel(const float* X, int64_t xm, int64_t xn,
+                                                                 void* out) {
+  __shared__ TileBuf tile;
+  const int64_t r0 = (int64_t)blockIdx.y * kTile, c0 = (int64_t)blockIdx.x * kTile;   // X tile
+  tile_load<Dt::F32>(X, xn, r0, c0, xm, xn, tile);   // tile[X row][X col]
+  __syncthreads();
+  const int u = threadIdx.x & 15;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) o[j] = make_float4(y[4 * j], y[4 * j + 1], y[4 * j + 2], y[4 * j + 3]);
-  } else {
-    uint4* o = reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + orow * ocols + ocol);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      uint32_t w[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-        w[t] = (uint32_t)f32_to_bf16_rne(y[8 * j + 2 * t]) |
-               ((uint32_t)f32_to_bf16_rne(y[8 * j + 2 * t + 1]) << 16);
-      o[j] = make_uint4(w[0], w[1], w[2], w[3]);
+  for (int pass = 0; pass < kTile / 16; ++pass) {
+    const int c = pass * 16 + (threadIdx.x >> 4);      // out row c0 + c, columns r0 + 4u ..
+    if (c0 + c < xn && r0 + 4 * u < xm) {
+      const float a = tile[4 * u][c], b = tile[4 * u + 1][c], d = tile[4 * u + 2][c], e = tile[4 * u + 3][c];
+      const int64_t q = ((c0 + c) * xm + r0) / 4 + u;
+      if constexpr (O == Dt::F32)
+        reinterpret_cast<float4*>(out)[q] = make_float4(a, b, d, e);
+      else
+        reinterpret_cast<uint2*>(out)[q] = bf16x4(a, b, d, e);
     }
   }
 }
@@ -201,11 +240,10 @@ __global__ __launch_bounds__(kThreads) void write_out_kernel(const float* X, int
 
 hipError_t launch_norm_partials(const void* G, Dt gt, int64_t n, float clip, const float* clip_dev,
                                 double* part, hipStream_t s) {
-  const int64_t nblk = n / 16;
   if (gt == Dt::F32)
-    norm_partials_kernel<Dt::F32><<<kNormParts, kThreads, 0, s>>>(G, nblk, clip, clip_dev, part);
+    norm_partials_kernel<Dt::F32><<<kNormParts, kThreads, 0, s>>>(G, n, clip, clip_dev, part);
   else
-    norm_partials_kernel<Dt::BF16><<<kNormParts, kThreads, 0, s>>>(G, nblk, clip, clip_dev, part);
+    norm_partials_kernel<Dt::BF16><<<kNormParts, kThreads, 0, s>>>(G, n, clip, clip_dev, part);
   return hipGetLastError();
 }
 
@@ -218,27 +256,41 @@ hipError_t launch_norm_finalize(const double* part, double* inv, uint32_t* z0, u
 hipError_t launch_normalize(const void* G, Dt gt, int64_t xm, int64_t xn, bool transposed,
                             float clip, const float* clip_dev, const double* inv, float* X,
                             uint32_t* amax_slot, hipStream_t s) {
-  dim3 grid((unsigned)((xn + 63) / 64), (unsigned)((xm + 63) / 64));
-  if (gt == Dt::F32) {
-    if (transposed) normalize_kernel<Dt::F32, true><<<grid, kThreads, 0, s>>>(G, xm, xn, clip, clip_dev, inv, X, amax_slot);
-    else normalize_kernel<Dt::F32, false><<<grid, kThreads, 0, s>>>(G, xm, xn, clip, clip_dev, inv, X, amax_slot);
-  } else {
-    if (transposed) normalize_kernel<Dt::BF16, true><<<grid, kThreads, 0, s>>>(G, xm, xn, clip, clip_dev, inv, X, amax_slot);
-    else normalize_kernel<Dt::BF16, false><<<grid, kThreads, 0, s>>>(G, xm, xn, clip, clip_dev, inv, X, amax_slot);
+  if (!transposed) {
+    const int64_t nq = xm * xn / 4;
+    int64_t g = (nq + kThreads - 1) / kThreads;
+    g = g > kFlatGrid ? kFlatGrid : g;
+    if (gt == Dt::F32)
+      normalize_flat_kernel<Dt::F32><<<(unsigned)g, kThreads, 0, s>>>(G, nq, clip, clip_dev, inv, X, amax_slot);
+    else
+      normalize_flat_kernel<Dt::BF16><<<(unsigned)g, kThreads, 0, s>>>(G, nq, clip, clip_dev, inv, X, amax_slot);
+    return hipGetLastError();
   }
+  dim3 grid((unsigned)((xn + kTile - 1) / kTile), (unsigned)((xm + kTile - 1) / kTile));
+  if (gt == Dt::F32)
+    normalize_tr_kernel<Dt::F32><<<grid, kThreads, 0, s>>>(G, xm, xn, clip, clip_dev, inv, X, amax_slot);
+  else
+    normalize_tr_kernel<Dt::BF16><<<grid, kThreads, 0, s>>>(G, xm, xn, clip, clip_dev, inv, X, amax_slot);
   return hipGetLastError();
 }
 
 hipError_t launch_write_out(const float* X, int64_t xm, int64_t xn, bool transposed, void* out,
                             Dt ot, hipStream_t s) {
-  dim3 grid((unsigned)((xn + 63) / 64), (unsigned)((xm + 63) / 64));
-  if (ot == Dt::F32) {
-    if (transposed) write_out_kernel<Dt::F32, true><<<grid, kThreads, 0, s>>>(X, xm, xn, out);
-    else write_out_kernel<Dt::F32, false><<<grid, kThreads, 0, s>>>(X, xm, xn, out);
-  } else {
-    if (transposed) write_out_kernel<Dt::BF16, true><<<grid, kThreads, 0, s>>>(X, xm, xn, out);
-    else write_out_kernel<Dt::BF16, false><<<grid, kThreads, 0, s>>>(X, xm, xn, out);
+  if (!transposed) {
+    const int64_t nq = xm * xn / 4;
+    int64_t g = (nq + kThreads - 1) / kThreads;
+    g = g > kFlatGrid ? kFlatGrid : g;
+    if (ot == Dt::F32)
+      write_out_flat_kernel<Dt::F32><<<(unsigned)g, kThreads, 0, s>>>(X, nq, out);
+    else
+      write_out_flat_kernel<Dt::BF16><<<(unsigned)g, kThreads, 0, s>>>(X, nq, out);
+    return hipGetLastError();
   }
+  dim3 grid((unsigned)((xn + kTile - 1) / kTile), (unsigned)((xm + kTile - 1) / kTile));
+  if (ot == Dt::F32)
+    write_out_tr_kernel<Dt::F32><<<grid, kThreads, 0, s>>>(X, xm, xn, out);
+  else
+    write_out_tr_kernel<Dt::BF16><<<grid, kThreads, 0, s>>>(X, xm, xn, out);
   return hipGetLastError();
 }
 

@@ -67,6 +67,17 @@ def test_bf16_in_bf16_out_with_clip():
     _compare(got, G, coeffs, clip, "bf16 lowrank 384x640 clip")
 
 
+@pytest.mark.parametrize("shape", [(400, 144), (208, 80), (1040, 272)])
+def test_transposed_bf16_in_bf16_out(shape):
+    """m > n with BF16 in and out: the transposing normalize and write-out
+    kernels on ragged 64 x 64 tiles."""
+    G = synth.student_t(*shape, seed=shape[0])
+    bits, vals = synth.to_bf16(G)
+    coeffs = [CUBIC] * 3
+    got = _run(vals, bits, coeffs, 0.05, out_dtype=ns.NS_BF16)        # an active clip
+    _compare(got, vals, coeffs, 0.05, f"bf16 transposed {shape}")
+
+
 def test_ns2048_full_size():
     spec = synth.ns_workload("ns2048")
     G, bits, clip = synth.ns_matrix(spec, 0)
