@@ -14,21 +14,6 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kFlatGrid = 4096;   // workgroups of the flat passes at most
 
-// Four consecutive values (elements 4q .. 4q+3) as FP32 bit patterns.
-// Kernels give consecutive lanes consecutive q, so each load instruction of
-// a wave reads one contiguous run of memory: a gather of 16 bytes from each
-// of many cache lines costs the texture unit one line lookup per lane and
-// runs several times slower.
-template <Dt T>
-__device__ __forceinline__ uint4 load4(const void* base, int64_t q) {
-  if constexpr (T == Dt::F32) {
-    return reinterpret_cast<const uint4*>(base)[q];
-  } else {
-    const uint2 w = reinterpret_cast<const uint2*>(base)[q];
-    return make_uint4(w.x << 16, w.x & 0xFFFF0000u, w.y << 16, w.y & 0xFFFF0000u);
-  }
-}
-
 // clamp that lets NaN through
 __device__ __forceinline__ float clampf(float x, float c) {
   return x > c ? c : (x < -c ? -c : x);

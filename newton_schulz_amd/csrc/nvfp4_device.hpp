@@ -19,7 +19,24 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "launch.hpp"
+
 namespace nvfp4 {
+
+// Four consecutive values (elements 4q .. 4q+3) as FP32 bit patterns (BF16
+// widened exactly).  Kernels give consecutive lanes consecutive q, so each
+// load instruction of a wave reads one contiguous run of memory: a gather of
+// 16-byte pieces from many cache lines costs the texture unit one line
+// lookup per lane and runs several times slower.
+template <Dt T>
+__device__ __forceinline__ uint4 load4(const void* base, int64_t q) {
+  if constexpr (T == Dt::F32) {
+    return reinterpret_cast<const uint4*>(base)[q];
+  } else {
+    const uint2 w = reinterpret_cast<const uint2*>(base)[q];
+    return make_uint4(w.x << 16, w.x & 0xFFFF0000u, w.y << 16, w.y & 0xFFFF0000u);
+  }
+}
 
 constexpr uint32_t kNaNBits = 0x7FC00000u;
 
