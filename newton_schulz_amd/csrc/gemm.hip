@@ -42,6 +42,10 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 constexpr int kXcds = 8;   // MI355X: workgroups go round-robin to 8 XCDs
+#ifndef NVFP4_CUS_PER_XCD
+#define NVFP4_CUS_PER_XCD 32     // MI355X: 256 CUs in 8 XCDs
+#endif
+constexpr int kCus = NVFP4_CUS_PER_XCD;
 
 // ===========================================================================
 // Fast path: K % 128 == 0, DMA loads into fragment-major LDS.
@@ -105,7 +109,7 @@ struct FastArgs {
   GemmProblem g;
   int64_t TM, TN;       // tile grid
   int64_t tiles;
-  int cus;              // CUs per XCD
+  float rcp_tm;         // 1 / TM, for the column-major tile order
   int parts;            // K-parts of a leftover tile (1: leftovers run whole)
   float* partials;
 };
@@ -127,7 +131,7 @@ __device__ __forceinline__ void xcd_run(const FastArgs& a, int x, int& t0, int& 
   const int tiles = (int)a.tiles;
   t0 = x * tiles / kXcds;
   n = (x + 1) * tiles / kXcds - t0;
-  whole = a.parts > 1 ? n / a.cus * a.cus : n;
+  whole = a.parts > 1 ? n / kCus * kCus : n;
 }
 
 // Work unit of workgroup b (b % kXcds picks the XCD); false when none.
@@ -167,22 +171,29 @@ __device__ __forceinline__ int split_tile(const FastArgs& a, int s) {
 }
 
 // Tile t of the grid: row-block I, col-block J.  Symmetric problems list only
-// tiles whose first row is <= their last column.
+// tiles whose first row is <= their last column, row by row.  32-bit,
+// wave-uniform arithmetic without runtime divisions: every workgroup runs
+// this before its first load.
 template <int BM, int BN, bool SYM>
-__device__ __forceinline__ void tile_of(int64_t t, int64_t TM, int64_t TN, int64_t& I, int64_t& J) {
+__device__ __forceinline__ void tile_of(const FastArgs& a, int t, int64_t& I, int64_t& J) {
+  const int TM = (int)a.TM, TN = (int)a.TN;
   if constexpr (SYM) {
-    for (int64_t i = 0; i < TM; ++i) {
-      // first column block whose last column reaches row i*BM
-      const int64_t jmin = i * BM - BN + 1 <= 0 ? 0 : (i * BM) / BN;
-      if (jmin >= TN) continue;
-      const int64_t cnt = TN - jmin;
+    for (int i = 0; i < TM; ++i) {
+      const int jmin = (i * BM) / BN;   // first column block whose last column reaches row i*BM
+      const int cnt = TN - jmin;
+      if (cnt <= 0) continue;
       if (t < cnt) { I = i; J = jmin + t; return; }
       t -= cnt;
     }
     I = TM; J = 0;   // unreachable for t < tiles
   } else {
-    I = t % TM;      // column-major: an XCD's run of tiles shares Q columns
-    J = t / TM;
+    // column-major (an XCD's run of tiles shares Q columns): J = t / TM from
+    // the reciprocal, exact after one correction since t < 2^24
+    int j = (int)((float)t * a.rcp_tm);
+    int i = t - j * TM;
+    if (i < 0) { --j; i += TM; } else if (i >= TM) { ++j; i -= TM; }
+    I = i;
+    J = j;
   }
 }
 
@@ -518,7 +529,7 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_fast_kernel(F
   if (!unit_of(a, (int)blockIdx.x, un)) return;
   const int nparts = un.split < 0 ? 1 : a.parts;
   int64_t I, J;
-  tile_of<C::BM, C::BN, SYM>(un.tile, a.TM, a.TN, I, J);
+  tile_of<C::BM, C::BN, SYM>(a, un.tile, I, J);
   const int64_t m0 = I * C::BM, n0 = J * C::BN;
 
   const int lane = threadIdx.x & 63;
@@ -711,7 +722,7 @@ __global__ __launch_bounds__(64) void gemm_reduce_kernel(FastArgs a) {
   const int tile = split_tile(a, s);
   if (tile < 0) return;
   int64_t I, J;
-  tile_of<C::BM, C::BN, SYM>(tile, a.TM, a.TN, I, J);
+  tile_of<C::BM, C::BN, SYM>(a, tile, I, J);
   const int lane = threadIdx.x & 63;
   const int thread = w * 64 + lane;                 // the lane's thread in the product kernel
   const float* base = a.partials + (size_t)s * a.parts * C::kAcc * C::kThreads;
@@ -944,9 +955,6 @@ using SmallCfg128 = Cfg<1, 2, 2, 2, NVFP4_FAST_NST, 128>;
 // parts, each of at least NVFP4_MIN_PART_STAGES K-stages, so that every CU
 // gets at most one part; products whose tiles divide evenly over the CUs of
 // each XCD run unsplit.
-#ifndef NVFP4_CUS_PER_XCD
-#define NVFP4_CUS_PER_XCD 32     // MI355X: 256 CUs in 8 XCDs
-#endif
 #ifndef NVFP4_MIN_PART_K
 #define NVFP4_MIN_PART_K 1024    // K per part at least
 #endif
@@ -968,7 +976,7 @@ GemmPlan plan_with(int64_t M, int64_t N, int64_t K, bool symmetric, bool allow_s
   p.TM = (M + C::BM - 1) / C::BM;
   p.TN = (N + C::BN - 1) / C::BN;
   p.tiles = symmetric ? sym_tiles(p.TM, p.TN, C::BM, C::BN) : p.TM * p.TN;
-  const int cus = NVFP4_CUS_PER_XCD;
+  const int cus = kCus;
   // leftover tiles of the busiest XCD run, and the units per XCD
   int64_t left_max = 0, split_tiles = 0;
   for (int x = 0; x < kXcds; ++x) {
@@ -1015,7 +1023,7 @@ hipError_t launch_with(const GemmProblem& g, const GemmPlan& p, float* partials,
   a.TM = p.TM;
   a.TN = p.TN;
   a.tiles = p.tiles;
-  a.cus = NVFP4_CUS_PER_XCD;
+  a.rcp_tm = 1.0f / (float)p.TM;
   a.parts = p.splits;
   a.partials = p.splits > 1 ? partials : nullptr;
   if (g.symmetric)
