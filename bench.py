@@ -68,10 +68,13 @@ def time_events(fn, reps, warm, stream):
 
 def kernel_timings(ns, torch, dev, m, n, stream, reps=10):
     """The three products of an NS iteration launched through the C ABI on
-    the bench stream in the iteration's order, each operand quantized just
-    before its product as inside ns_orthogonalize, so caches hold what they
-    hold there.  Each product is bracketed by its own pair of HIP events;
-    returns {name: (average ms per launch, algorithmic flops per launch)}."""
+    the bench stream, each on operands quantized as inside
+    ns_orthogonalize.  Each product runs `reps` times back to back between
+    one pair of HIP events, after a spin kernel that keeps the GPU busy
+    while the host enqueues, so the interval holds the launches alone (a
+    pair of events around every single launch would add the events' own
+    processing, about 6 us, to each).  Returns {name: (average ms per
+    launch, algorithmic flops per launch)}."""
     from synth import gaussian
     X = torch.from_numpy((gaussian(m, n, seed=77) / np.sqrt(m * n)).astype(np.float32)).to(dev)
     A = torch.empty((m, m), dtype=torch.float32, device=dev)
@@ -79,28 +82,33 @@ def kernel_timings(ns, torch, dev, m, n, stream, reps=10):
     Xo = torch.empty_like(X)
     sym = m * (m + 1)
     flops = {"gemm_gram_xxT": sym * n, "gemm_gram_aaT": sym * m, "gemm_update_bx": 2 * m * m * n}
-    ev = {k: [] for k in flops}
-
-    def timed(name, fn):
+    qx = ns.nvfp4_quantize(X, ns.NVFP4_ROWS, stream=stream)
+    qt = ns.nvfp4_quantize(X, ns.NVFP4_COLS, stream=stream)
+    ws = {k: torch.empty(max(1, ns.nvfp4_gemm_workspace_bytes(*mnk)), dtype=torch.uint8, device=dev)
+          for k, mnk in (("g1", (m, m, n, True)), ("g2", (m, m, m, True)), ("g3", (m, n, m, False)))}
+    g1 = lambda: ns.nvfp4_gemm(qx, qx, m, m, n, symmetric=True, out=A, workspace=ws["g1"], stream=stream)
+    g1()
+    qa = ns.nvfp4_quantize(A, ns.NVFP4_ROWS, stream=stream)
+    g2 = lambda: ns.nvfp4_gemm(qa, qa, m, m, m, symmetric=True, alpha=2.0315, beta=-4.775, addend=A,
+                               out=Bm, workspace=ws["g2"], stream=stream)
+    g2()
+    qb = ns.nvfp4_quantize(Bm, ns.NVFP4_ROWS, stream=stream)
+    g3 = lambda: ns.nvfp4_gemm(qb, qt, m, n, m, alpha=1.0, beta=3.4445, addend=X, out=Xo,
+                               workspace=ws["g3"], stream=stream)
+    out = {}
+    for name, fn in (("gemm_gram_xxT", g1), ("gemm_gram_aaT", g2), ("gemm_update_bx", g3)):
+        fn()
+        fn()
+        with torch.cuda.stream(stream):
+            torch.cuda._sleep(20_000_000)
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         s.record(stream)
-        fn()
+        for _ in range(reps):
+            fn()
         e.record(stream)
-        ev[name].append((s, e))
-
-    for r in range(reps + 2):
-        qx = ns.nvfp4_quantize(X, ns.NVFP4_ROWS, stream=stream)
-        qt = ns.nvfp4_quantize(X, ns.NVFP4_COLS, stream=stream)
-        timed("gemm_gram_xxT", lambda: ns.nvfp4_gemm(qx, qx, m, m, n, symmetric=True, out=A, stream=stream))
-        qa = ns.nvfp4_quantize(A, ns.NVFP4_ROWS, stream=stream)
-        timed("gemm_gram_aaT", lambda: ns.nvfp4_gemm(qa, qa, m, m, m, symmetric=True, alpha=2.0315,
-                                                     beta=-4.775, addend=A, out=Bm, stream=stream))
-        qb = ns.nvfp4_quantize(Bm, ns.NVFP4_ROWS, stream=stream)
-        timed("gemm_update_bx", lambda: ns.nvfp4_gemm(qb, qt, m, n, m, alpha=1.0, beta=3.4445,
-                                                      addend=X, out=Xo, stream=stream))
+        out[name] = (s, e)
     torch.cuda.synchronize()
-    # the first two rounds are warm-up
-    return {k: (sum(s.elapsed_time(e) for s, e in v[2:]) / reps, flops[k]) for k, v in ev.items()}
+    return {k: (s.elapsed_time(e) / reps, flops[k]) for k, (s, e) in out.items()}
 
 
 def source_digest():
@@ -117,8 +125,8 @@ def source_digest():
 # HBM bytes per launch of the dominant kernel (X = a X + qB qX16^T at
 # 3072 x 8192), from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE, each scaled by
 # what the counter reads for a plain copy of known size; see profiles/.
-DOMINANT_TRAFFIC = {"src_sha256": "deb9f8ebb0b4b338f735cb29bbb7997324e7fe55f5c03cc28afa92723df68533",
-                    "bytes_per_launch": 396745830}
+DOMINANT_TRAFFIC = {"src_sha256": "1ae3b7b479041aa9480f094db87ab192ea65e6413b0f7b28c5ac39bdab267ca1",
+                    "bytes_per_launch": 440024017}
 
 
 def bf16_ns_ms(torch, G, coeffs, stream, reps=10):
