@@ -31,9 +31,6 @@
 #include "launch.hpp"
 #include "nvfp4_device.hpp"
 
-#ifndef NVFP4_SCHED
-#define NVFP4_SCHED 0
-#endif
 
 namespace nvfp4 {
 namespace {
@@ -55,9 +52,9 @@ template <int WM_, int WN_, int FM_, int FN_, int NST_, int BK_>
 struct Cfg {
   static constexpr int WM = WM_, WN = WN_, FM = FM_, FN = FN_;
   static constexpr int NST = NST_;                    // LDS stages in flight
-  static constexpr int BK = BK_;                      // K elements per stage (64, 128 or 256)
+  static constexpr int BK = BK_;                      // K elements per stage (128 or 256)
   static constexpr int kHalves = BK / 64;             // 16-byte lane slices per row per stage
-  static_assert(BK == 64 || BK == 128 || BK == 256, "BK must be 64, 128 or 256");
+  static_assert(BK == 128 || BK == 256, "BK must be 128 or 256");
   // BK = 256 loads whole 128-byte row lines (see row_chunk); the narrower
   // stages load 32 rows x 16 bytes per instruction
   static constexpr bool kLines = BK == 256;
@@ -295,9 +292,8 @@ __device__ __forceinline__ void init_sources(const GemmProblem& g, int64_t m0, i
     int64_t row = (isP ? m0 + 32 * grp : n0 + 32 * (grp - C::GP)) + (lane & 31);
     const int64_t lim = isP ? g.M : g.N;
     row = row < lim ? row : lim - 1;
-    // BK = 128: 8 scale bytes per row and stage, lane half h loads its 4;
-    // BK = 64: 4 bytes per row, both halves load them and pick their 2
-    src.scale[q] = (uint32_t)(row * sb + (C::BK == 128 ? 4 * (lane >> 5) : 0));
+    // 8 scale bytes per row and stage, lane half h loads its 4
+    src.scale[q] = (uint32_t)(row * sb + 4 * (lane >> 5));
   }
 }
 
@@ -580,8 +576,8 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_fast_kernel(F
     const uint8_t* st = smem + ((kc - kc0) % C::NST) * C::kStage;
 
     // this lane's scale dword per fragment: blocks 4h..4h+3 of the stage
-    // (BK = 128) or the row's 4 blocks (BK = 64), as E4M3 bytes; with row
-    // lines (BK = 256) two dwords, blocks 8h..8h+7
+    // (BK = 128), as E4M3 bytes; with row lines (BK = 256) two dwords,
+    // blocks 8h..8h+7
     uint32_t sp[C::FM], sq[C::FN], sp1[C::FM], sq1[C::FN];
     if constexpr (C::kLines) {
       const int so = 16 * (lane & 31) + 8 * (lane >> 5);
@@ -604,13 +600,6 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_fast_kernel(F
 #pragma unroll
       for (int j = 0; j < C::FN; ++j)
         sq[j] = *reinterpret_cast<const uint32_t*>(st + C::kCodeBytes + (C::GP + wn * C::FN + j) * 256 + 4 * lane);
-    }
-    if constexpr (C::BK == 64) {
-      // this lane half's two blocks into the low half-word
-#pragma unroll
-      for (int i = 0; i < C::FM; ++i) sp[i] >>= 16 * (lane >> 5);
-#pragma unroll
-      for (int j = 0; j < C::FN; ++j) sq[j] >>= 16 * (lane >> 5);
     }
 
 #pragma unroll
@@ -668,16 +657,6 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_fast_kernel(F
 #pragma unroll
           for (int j = 0; j < C::FN; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
-#if NVFP4_SCHED
-        if (s < 3) {
-          // interleave: after each MFMA, a share of the next step's dequant
-#pragma unroll
-          for (int t = 0; t < C::FM * C::FN; ++t) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, NVFP4_SCHED, 0);
-          }
-        }
-#endif
         if (s < 3) {
 #pragma unroll
           for (int i = 0; i < C::FM; ++i) av[i] = an[i];
