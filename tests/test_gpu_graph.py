@@ -1,0 +1,63 @@
+"""The NS step captured into a HIP graph: every launch of the path is a
+kernel (no memset or allocation inside the call), so a captured call replays
+to the eager result bit for bit.  Each replay is checked, with eager work on
+the same workspace between replays."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+
+pytestmark = pytest.mark.gpu
+
+import newton_schulz_amd as ns  # noqa: E402
+from gpu_util import host, to_dev_bf16  # noqa: E402
+
+CUBIC = (1.5, -0.5, 0.0)
+
+
+def _capture(fn):
+    """Warm up on a side stream, then capture fn() into a graph."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fn()
+    torch.cuda.synchronize()
+    return graph
+
+
+@pytest.mark.parametrize("variant", ["plain", "p99 clip + transform"])
+def test_graph_replays_match_eager(variant):
+    G = synth.student_t(384, 640, seed=31)
+    bits, _ = synth.to_bf16(G)
+    Gd = to_dev_bf16(bits)
+    other = to_dev_bf16(synth.to_bf16(synth.gaussian(384, 640, seed=32))[0])
+    coeffs = [CUBIC] * 4
+    ws = torch.empty(ns.ns_workspace_bytes(384, 640), dtype=torch.uint8, device=Gd.device)
+    out = torch.empty((384, 640), dtype=torch.float32, device=Gd.device)
+    if variant == "plain":
+        call = lambda g: ns.ns_orthogonalize(g, coeffs, 0.05, out=out, workspace=ws)
+    else:
+        masks = synth.rht_masks(len(coeffs), seed=3)
+        call = lambda g: ns.ns_orthogonalize_ex(g, coeffs, clip_quantile=0.99, rht_masks=masks,
+                                                out=out, workspace=ws)
+    call(Gd)
+    want = host(out).copy()
+    call(other)
+    want_other = host(out).copy()
+    graph = _capture(lambda: call(Gd))
+    for r in range(3):
+        out.fill_(float("nan"))
+        call(other)                               # eager work on the same workspace
+        assert np.array_equal(host(out), want_other)
+        out.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        got = host(out)
+        print(f"[graph] {variant} replay {r}: equal={np.array_equal(got, want)}", flush=True)
+        assert np.array_equal(got, want), (variant, r)
