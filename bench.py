@@ -125,7 +125,7 @@ def source_digest():
 # HBM bytes per launch of the dominant kernel (X = a X + qB qX16^T at
 # 3072 x 8192), from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE, each scaled by
 # what the counter reads for a plain copy of known size; see profiles/.
-DOMINANT_TRAFFIC = {"src_sha256": "e66aca073b0e19e7f4b077c0a4e4e0f1ec8b80f8a72272b3b7d5ab4b0d736f5d",
+DOMINANT_TRAFFIC = {"src_sha256": "51d28fba42a04b19e8ce6c952d0a7cc00f886c17bfcc3aa824e6d7cfa17bd8d1",
                     "bytes_per_launch": 440024017}
 
 

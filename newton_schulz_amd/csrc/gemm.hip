@@ -14,15 +14,22 @@
 // epilogue.
 //
 // K order inside an MFMA: a product sums over K, so any permutation of K
-// applied to both operands leaves it unchanged.  For each 128-wide K stage,
-// lane l (row l%32 of its 32-row group, half h = l/32) owns bytes
-// [32h, 32h+32) of the row's 64 code bytes; MFMA step s of half-stage hs
-// uses its word s of bytes [32h + 16hs, +16).  Both operands use this map.
+// applied to both operands leaves it unchanged; both operands use the same
+// map.  Stages are 256 wide when K % 256 == 0, else 128 wide.
 //
-// LDS is laid out fragment-major: for each 32-row group and half-stage a
-// 1 KB region holds lane l's 16 bytes at 16*l, exactly what both the DMA
-// load of lane l writes and the fragment read of lane l reads, so every LDS
-// access of a wave is one contiguous conflict-free kilobyte.
+// 256-wide stages (row lines): a 32-row group's stage is 32 rows x 128 code
+// bytes, loaded eight whole rows (eight 128-byte lines) per DMA instruction
+// and kept in LDS row by row with a chunk swizzle (row_swizzle below); lane l
+// (row l%32, half h = l/32) consumes 16-byte chunks 4h .. 4h+3 of its row,
+// one per quarter-stage, one word per MFMA step.
+//
+// 128-wide stages: lane l owns bytes [32h, 32h+32) of the row's 64 code
+// bytes; MFMA step s of half-stage hs uses its word s of bytes
+// [32h + 16hs, +16).  LDS is fragment-major: for each 32-row group and
+// half-stage a 1 KB region holds lane l's 16 bytes at 16*l, exactly what
+// both the DMA load of lane l writes and the fragment read of lane l reads.
+// A DMA instruction then gathers 32 bytes from each of 32 rows, which moves
+// data about four times slower than reading whole lines.
 //
 // Symmetric products compute only tiles that touch the upper triangle
 // (row <= col); each element there is written once and mirrored.  Tiles
@@ -55,7 +62,7 @@ struct Cfg {
   static constexpr int BK = BK_;                      // K elements per stage (128 or 256)
   static constexpr int kHalves = BK / 64;             // 16-byte lane slices per row per stage
   static_assert(BK == 128 || BK == 256, "BK must be 128 or 256");
-  // BK = 256 loads whole 128-byte row lines (see row_chunk); the narrower
+  // BK = 256 loads whole 128-byte row lines (see row_swizzle); the narrower
   // stages load 32 rows x 16 bytes per instruction
   static constexpr bool kLines = BK == 256;
   static constexpr int kWaves = WM * WN;
