@@ -221,7 +221,14 @@ size_t ns_grouped_workspace_bytes(int count, const int64_t* m, const int64_t* n)
  * matrices with one coefficient schedule, as one batch of launches.
  *   G, out  HOST arrays of `count` device pointers.
  *   m, n    HOST arrays of shapes.   clip  HOST array of per-matrix clips.
- *   ws      device scratch of ns_grouped_workspace_bytes().
+ *   ws      device scratch of ns_grouped_workspace_bytes() (one part per
+ *           matrix).
+ * The matrices run concurrently on up to four library-owned streams of the
+ * current device (default priority, created on the first grouped call and
+ * kept until the process ends), forked from `stream` through an event and
+ * joined back into it: the call is ordered on `stream` like any other and
+ * can be captured into a graph.  Each result equals its single call's bit
+ * for bit.  Calls that overlap on one device share the streams.
  */
 ns_status ns_orthogonalize_grouped(int count, const void* const* G, const int64_t* m,
                                    const int64_t* n, ns_dtype gt, const float* coeffs,
@@ -233,7 +240,8 @@ ns_status ns_orthogonalize_grouped(int count, const void* const* G, const int64_
  * ns_orthogonalize_ex shared by every matrix: with opt->clip_quantile > 0
  * each matrix is clipped at that quantile of its own |G| (clip may then be
  * NULL), else at clip[i]; opt->rht_masks (k masks) applies to every matrix.
- * Workspace ns_grouped_workspace_bytes().
+ * Workspace ns_grouped_workspace_bytes(); concurrency and ordering as for
+ * ns_orthogonalize_grouped.
  */
 ns_status ns_orthogonalize_grouped_ex(int count, const void* const* G, const int64_t* m,
                                       const int64_t* n, ns_dtype gt, const float* coeffs, int k,

@@ -7,7 +7,10 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
+#include <algorithm>
 #include <cstring>
+#include <mutex>
+#include <vector>
 
 #include "../../include/nvfp4ns.h"
 #include "launch.hpp"
@@ -25,6 +28,37 @@ constexpr int64_t kMaxElems = (int64_t)1 << 31;
 inline bool dtype_ok(int d) { return d == NS_F32 || d == NS_BF16; }
 inline size_t dtype_size(ns_dtype d) { return d == NS_F32 ? 4 : 2; }
 inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+// ---- concurrent problems of a grouped call --------------------------------
+// The problems of a grouped call are independent (each has its own part of
+// the workspace), so they run on kGroupStreams internal streams: the caller's
+// stream forks into them through an event and joins them back, so the call
+// stays ordered on the caller's stream and can be captured into a graph.
+// Small problems then fill the GPU together, and one problem's tail kernels
+// overlap another's.  The streams (default priority) are created once per
+// device and kept until the process ends.
+constexpr int kGroupStreams = 4;
+constexpr int kMaxDevices = 64;
+
+hipError_t group_streams(hipStream_t (&out)[kGroupStreams]) {
+  static std::mutex mu;
+  static hipStream_t streams[kMaxDevices][kGroupStreams];
+  static bool made[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!made[dev]) {
+    for (int i = 0; i < kGroupStreams; ++i) {
+      e = hipStreamCreateWithFlags(&streams[dev][i], hipStreamNonBlocking);
+      if (e != hipSuccess) return e;
+    }
+    made[dev] = true;
+  }
+  for (int i = 0; i < kGroupStreams; ++i) out[i] = streams[dev][i];
+  return hipSuccess;
+}
 
 // A failed launch returns NS_ERR_HIP; with NVFP4NS_DEBUG set in the
 // environment the HIP error and the failing call are also printed.
@@ -367,6 +401,73 @@ ns_status ns_abs_quantile(const void* x, ns_dtype xt, int64_t count, double q, f
   return NS_OK;
 }
 
+}  // extern "C" (reopened below)
+
+namespace {
+
+// Runs run(i, stream) for problems 0 .. count-1 on the group streams, forked
+// from and joined back into `caller`: largest problem first (flops of one
+// step), each to the stream with the least work so far.  Every stream used is
+// joined back, also after an error.
+template <class F>
+ns_status run_grouped(int count, const int64_t* m, const int64_t* n, hipStream_t caller, F&& run) {
+  hipStream_t ss[kGroupStreams];
+  NS_TRY(group_streams(ss));
+  const int used = count < kGroupStreams ? count : kGroupStreams;
+  hipEvent_t ev[kGroupStreams + 1] = {};      // ev[0] forks, ev[1 + j] joins stream j
+  for (int j = 0; j <= used; ++j) {
+    const hipError_t e = hipEventCreateWithFlags(&ev[j], hipEventDisableTiming);
+    if (e != hipSuccess) {
+      for (int t = 0; t < j; ++t) (void)hipEventDestroy(ev[t]);
+      return hip_failed(e, "hipEventCreateWithFlags", __LINE__);
+    }
+  }
+  auto cost = [&](int i) {
+    const double a = (double)m[i], b = (double)n[i];
+    return a * b * (a < b ? a : b);
+  };
+  std::vector<int> order((size_t)count);
+  for (int i = 0; i < count; ++i) order[(size_t)i] = i;
+  std::stable_sort(order.begin(), order.end(), [&](int x, int y) { return cost(x) > cost(y); });
+  ns_status st = NS_OK;
+  hipError_t e = hipEventRecord(ev[0], caller);
+  for (int j = 0; j < used && e == hipSuccess; ++j) e = hipStreamWaitEvent(ss[j], ev[0], 0);
+  if (e == hipSuccess) {
+    double load[kGroupStreams] = {};
+    for (int i : order) {
+      int j = 0;
+      for (int t = 1; t < used; ++t) j = load[t] < load[j] ? t : j;
+      st = run(i, ss[j]);
+      if (st != NS_OK) break;
+      load[j] += cost(i);
+    }
+    for (int j = 0; j < used; ++j) {
+      hipError_t ej = hipEventRecord(ev[1 + j], ss[j]);
+      if (ej == hipSuccess) ej = hipStreamWaitEvent(caller, ev[1 + j], 0);
+      if (e == hipSuccess) e = ej;
+    }
+  }
+  for (int j = 0; j <= used; ++j) (void)hipEventDestroy(ev[j]);
+  if (st != NS_OK) return st;
+  if (e != hipSuccess) return hip_failed(e, "group fork/join", __LINE__);
+  return NS_OK;
+}
+
+// Byte offset of problem i's workspace in a grouped call.
+std::vector<size_t> group_offsets(int count, const int64_t* m, const int64_t* n) {
+  std::vector<size_t> off((size_t)count);
+  size_t o = 0;
+  for (int i = 0; i < count; ++i) {
+    off[(size_t)i] = o;
+    o += ns_workspace_bytes(m[i], n[i]);
+  }
+  return off;
+}
+
+}  // namespace
+
+extern "C" {
+
 size_t ns_grouped_workspace_bytes(int count, const int64_t* m, const int64_t* n) {
   if (count <= 0 || !m || !n) return 0;
   size_t total = 0;
@@ -396,14 +497,12 @@ ns_status ns_orthogonalize_grouped_ex(int count, const void* const* G, const int
   for (int i = 0; i < count; ++i)
     if (overlaps(out[i], (size_t)(m[i] * n[i]) * dtype_size(ot), ws, ws_bytes)) return NS_ERR_ARG;
   uint8_t* base = static_cast<uint8_t*>(ws);
-  for (int i = 0; i < count; ++i) {
+  const std::vector<size_t> off = group_offsets(count, m, n);
+  return run_grouped(count, m, n, as_stream(stream), [&](int i, hipStream_t s) {
     const float ci = q > 0.0 ? INFINITY : clip[i];
-    ns_status st = ns_run(G[i], gt, m[i], n[i], coeffs, k, ci, q, opt->rht_masks, out[i], ot, base,
-                          as_stream(stream));
-    if (st != NS_OK) return st;
-    base += ns_workspace_bytes(m[i], n[i]);
-  }
-  return NS_OK;
+    return ns_run(G[i], gt, m[i], n[i], coeffs, k, ci, q, opt->rht_masks, out[i], ot,
+                  base + off[(size_t)i], s);
+  });
 }
 
 ns_status ns_orthogonalize_grouped(int count, const void* const* G, const int64_t* m,
@@ -420,13 +519,11 @@ ns_status ns_orthogonalize_grouped(int count, const void* const* G, const int64_
   for (int i = 0; i < count; ++i)
     if (overlaps(out[i], (size_t)(m[i] * n[i]) * dtype_size(ot), ws, ws_bytes)) return NS_ERR_ARG;
   uint8_t* base = static_cast<uint8_t*>(ws);
-  for (int i = 0; i < count; ++i) {
-    ns_status st = ns_run(G[i], gt, m[i], n[i], coeffs, k, clip[i], 0.0, nullptr, out[i], ot, base,
-                          as_stream(stream));
-    if (st != NS_OK) return st;
-    base += ns_workspace_bytes(m[i], n[i]);
-  }
-  return NS_OK;
+  const std::vector<size_t> off = group_offsets(count, m, n);
+  return run_grouped(count, m, n, as_stream(stream), [&](int i, hipStream_t s) {
+    return ns_run(G[i], gt, m[i], n[i], coeffs, k, clip[i], 0.0, nullptr, out[i], ot,
+                  base + off[(size_t)i], s);
+  });
 }
 
 }  // extern "C"

@@ -61,3 +61,29 @@ def test_graph_replays_match_eager(variant):
         got = host(out)
         print(f"[graph] {variant} replay {r}: equal={np.array_equal(got, want)}", flush=True)
         assert np.array_equal(got, want), (variant, r)
+
+
+def test_grouped_call_captures_across_its_streams():
+    """A grouped call forks onto internal streams and joins them back into
+    the caller's stream; captured, it replays to the eager results."""
+    shapes = [(256, 512), (512, 256), (128, 128), (384, 640), (64, 192)]
+    Gs = [to_dev_bf16(synth.to_bf16(synth.student_t(r, c, seed=40 + i))[0])
+          for i, (r, c) in enumerate(shapes)]
+    coeffs = [CUBIC] * 3
+    clips = [0.05] * len(shapes)
+    outs = [torch.empty(s, dtype=torch.float32, device=Gs[0].device) for s in shapes]
+    ws = torch.empty(ns.ns_grouped_workspace_bytes(shapes), dtype=torch.uint8, device=Gs[0].device)
+    call = lambda: ns.ns_orthogonalize_grouped(Gs, coeffs, clips, outs=outs, workspace=ws)
+    call()
+    want = [host(o).copy() for o in outs]
+    for g, w, c in zip(Gs, want, clips):                  # each equals its single call
+        assert np.array_equal(host(ns.ns_orthogonalize(g, coeffs, c)), w)
+    graph = _capture(call)
+    for r in range(3):
+        for o in outs:
+            o.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, (o, w) in enumerate(zip(outs, want)):
+            assert np.array_equal(host(o), w), (r, i)
+    print("[graph] grouped: 3 replays equal", flush=True)
