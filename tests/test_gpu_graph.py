@@ -31,15 +31,18 @@ def _capture(fn):
     return graph
 
 
-@pytest.mark.parametrize("variant", ["plain", "p99 clip + transform"])
-def test_graph_replays_match_eager(variant):
-    G = synth.student_t(384, 640, seed=31)
+# 384 x 8192: the Gram product's leftover tiles are split along K, so its
+# K-parts and their reduce run on a side stream forked from the call's stream
+@pytest.mark.parametrize("variant,shape", [("plain", (384, 640)), ("plain", (384, 8192)),
+                                           ("p99 clip + transform", (384, 640))])
+def test_graph_replays_match_eager(variant, shape):
+    G = synth.student_t(*shape, seed=31)
     bits, _ = synth.to_bf16(G)
     Gd = to_dev_bf16(bits)
-    other = to_dev_bf16(synth.to_bf16(synth.gaussian(384, 640, seed=32))[0])
+    other = to_dev_bf16(synth.to_bf16(synth.gaussian(*shape, seed=32))[0])
     coeffs = [CUBIC] * 4
-    ws = torch.empty(ns.ns_workspace_bytes(384, 640), dtype=torch.uint8, device=Gd.device)
-    out = torch.empty((384, 640), dtype=torch.float32, device=Gd.device)
+    ws = torch.empty(ns.ns_workspace_bytes(*shape), dtype=torch.uint8, device=Gd.device)
+    out = torch.empty(shape, dtype=torch.float32, device=Gd.device)
     if variant == "plain":
         call = lambda g: ns.ns_orthogonalize(g, coeffs, 0.05, out=out, workspace=ws)
     else:
@@ -59,8 +62,8 @@ def test_graph_replays_match_eager(variant):
         graph.replay()
         torch.cuda.synchronize()
         got = host(out)
-        print(f"[graph] {variant} replay {r}: equal={np.array_equal(got, want)}", flush=True)
-        assert np.array_equal(got, want), (variant, r)
+        print(f"[graph] {variant} {shape} replay {r}: equal={np.array_equal(got, want)}", flush=True)
+        assert np.array_equal(got, want), (variant, shape, r)
 
 
 def test_grouped_call_captures_across_its_streams():
