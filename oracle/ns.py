@@ -81,11 +81,12 @@ def ns_exact(G, coeffs, clip=np.inf, eps=EPS):
     return X.T if transposed else X
 
 
-def ns_nvfp4(G, coeffs, clip=np.inf, eps=EPS, trace=None, rht_masks=None):
+def ns_nvfp4(G, coeffs, clip=np.inf, eps=EPS, trace=None, rht_masks=None, adaptive46=False):
     """Newton–Schulz with NVFP4 operands for every product (§3.4 iteration).
 
     ``rht_masks``: None, or one 16-bit sign mask per step for the random
-    Hadamard transform of that step.  ``trace``, if a list, receives one
+    Hadamard transform of that step.  ``adaptive46``: every quantization
+    picks M = 4 or 6 per block (oracle/nvfp4.py).  ``trace``, if a list, receives one
     dict per step with the quantized operands and the float64 intermediates
     (X before the step, A, B, X after).
     """
@@ -96,22 +97,22 @@ def ns_nvfp4(G, coeffs, clip=np.inf, eps=EPS, trace=None, rht_masks=None):
     for it, (a, b, c) in enumerate(coeffs):
         if rht_masks is None:
             amax_x = tensor_amax(X)
-            qX = quantize_rows(X, amax=amax_x)       # Q_1x16(X)
-            qX16 = quantize_cols(X, amax=amax_x)     # Q_16x1(X), stored as X^T rows
+            qX = quantize_rows(X, amax=amax_x, adaptive46=adaptive46)       # Q_1x16(X)
+            qX16 = quantize_cols(X, amax=amax_x, adaptive46=adaptive46)     # Q_16x1(X), stored as X^T rows
         else:
             h = rht_masks[it]
-            qX = quantize_rows(rht_rows(X, h))       # Q_1x16(X H)
-            qX16 = quantize_cols(rht_cols(X, h))     # Q_16x1(H^T X)
+            qX = quantize_rows(rht_rows(X, h), adaptive46=adaptive46)       # Q_1x16(X H)
+            qX16 = quantize_cols(rht_cols(X, h), adaptive46=adaptive46)     # Q_16x1(H^T X)
         dX = dequantize_rows(qX)
         A = gemm_nt(dX, dX)                          # qX qX^T
         if rht_masks is None:
-            qA = quantize_rows(A)                    # Q_1x16(A)
-            qA16 = quantize_cols(A)                  # Q_16x1(A)
+            qA = quantize_rows(A, adaptive46=adaptive46)                    # Q_1x16(A)
+            qA16 = quantize_cols(A, adaptive46=adaptive46)                  # Q_16x1(A)
         else:
-            qA = quantize_rows(rht_rows(A, h))       # Q_1x16(A H)
-            qA16 = quantize_cols(rht_cols(A, h))     # Q_16x1(H^T A)
+            qA = quantize_rows(rht_rows(A, h), adaptive46=adaptive46)       # Q_1x16(A H)
+            qA16 = quantize_cols(rht_cols(A, h), adaptive46=adaptive46)     # Q_16x1(H^T A)
         B = b * A + c * (dequantize_rows(qA) @ dequantize_cols(qA16))
-        qB = quantize_rows(B if rht_masks is None else rht_rows(B, h))   # Q_1x16(B [H])
+        qB = quantize_rows(B if rht_masks is None else rht_rows(B, h), adaptive46=adaptive46)   # Q_1x16(B [H])
         Xn = a * X + dequantize_rows(qB) @ dequantize_cols(qX16)
         if trace is not None:
             trace.append(dict(X=X, qX=qX, qX16=qX16, A=A, qA=qA, qA16=qA16,

@@ -18,6 +18,19 @@ Readings (the page prints the decode rule only):
   values keep it).  Codes are packed two per byte, element 2i in the low
   nibble.  Scales are one byte per block, row-major [rows][cols/16].
 * Q_16x1(T) is Q_1x16(T^T) and is stored in the layout of T^T.
+
+Adaptive 4/6 block scaling (§3.4 says the Root quantizations use RTN and
+adaptive 4/6 scaling; §5 names it adaptive M=4/M=6 block scaling after Four
+Over Six [7], whose rule is not on the pages).  Readings, with ``adaptive46``:
+* every block is encoded twice, with its maximum mapped to M = 6 (the rule
+  above) and to M = 4 (s = RNE_E4M3FN(amax_b / (4 * s_g)), saturating at 448);
+  the element codes follow from each scale by the same RTN rule;
+* the block keeps the candidate with the smaller squared error
+  sum (x - x_hat)^2, each difference, square and running sum rounded in
+  float64 in element order (0..15); M = 6 wins ties;
+* s_g is unchanged (amax / 2688), so a block whose M = 4 scale saturates
+  simply loses the comparison.  The decode rule is unchanged: the scale byte
+  alone says how a block decodes.
 """
 from dataclasses import dataclass
 from fractions import Fraction
@@ -76,12 +89,36 @@ def global_scale(amax):
     return _round_fraction_to_f32(Fraction(float(amax)) / AMAX_TO_SG)
 
 
-def quantize_rows(t, amax=None):
+def _encode_blocks(mag, amax_b, sg64, m_max):
+    """Scale codes [rows, nblk] and magnitude codes [rows, cols] with the block
+    maximum mapped to m_max (6, or 4 for the adaptive candidate), and the
+    per-element unit s * s_g (float64, exact)."""
+    scale_codes = e4m3fn_encode_quotient(amax_b, m_max * sg64)
+    s = e4m3fn_decode(scale_codes)                        # exact float64
+    den = np.repeat(s * sg64, BLOCK, axis=1)              # exact (<= 28 bits)
+    mag_codes = e2m1_encode_quotient(mag, np.where(den > 0, den, 1.0))
+    return scale_codes, np.where(den > 0, mag_codes, 0), den
+
+
+def block_sq_error(x, neg, mag_codes, den):
+    """Per block: sum over its 16 elements, in element order, of
+    (x - x_hat)^2, every operation rounded in float64."""
+    rows, cols = x.shape
+    v = e2m1_decode(mag_codes) * den                       # exact magnitudes
+    d = (x - np.where(neg == 1, -v, v)).reshape(rows, cols // BLOCK, BLOCK)
+    e = np.zeros((rows, cols // BLOCK))
+    for i in range(BLOCK):
+        e = e + d[:, :, i] * d[:, :, i]
+    return e
+
+
+def quantize_rows(t, amax=None, adaptive46=False):
     """Q_1x16(t): blocks of 16 consecutive elements along each row.
 
     ``amax`` overrides the tensor maximum (used when ``t`` is a slice of a
     larger tensor whose maximum is known, or to share one s_g between the
-    two layouts of the same tensor).
+    two layouts of the same tensor).  ``adaptive46`` selects M = 4 or 6 per
+    block (module docstring).
     """
     t = np.asarray(t)
     if t.ndim != 2 or t.shape[1] % BLOCK:
@@ -105,24 +142,26 @@ def quantize_rows(t, amax=None):
         mag_codes = np.zeros((rows, cols), dtype=np.int64)
     else:
         amax_b = blocks.max(axis=2)
-        scale_codes = e4m3fn_encode_quotient(amax_b, 6.0 * sg64)
-        s = e4m3fn_decode(scale_codes)                    # exact float64
-        den = np.repeat(s * sg64, BLOCK, axis=1)          # exact (<= 28 bits)
-        mag_codes = e2m1_encode_quotient(mag, np.where(den > 0, den, 1.0))
-        mag_codes = np.where(den > 0, mag_codes, 0)
+        scale_codes, mag_codes, den = _encode_blocks(mag, amax_b, sg64, 6.0)
+        if adaptive46:
+            sc4, mc4, den4 = _encode_blocks(mag, amax_b, sg64, 4.0)
+            pick4 = block_sq_error(x, neg, mc4, den4) < block_sq_error(x, neg, mag_codes, den)
+            scale_codes = np.where(pick4, sc4, scale_codes)
+            mag_codes = np.where(np.repeat(pick4, BLOCK, axis=1), mc4, mag_codes)
 
     codes4 = (neg << 3) | mag_codes
     packed = (codes4[:, 0::2] | (codes4[:, 1::2] << 4)).astype(np.uint8)
     return NVFP4Tensor(packed, scale_codes.astype(np.uint8), s_g, rows, cols)
 
 
-def quantize_cols(t, amax=None):
+def quantize_cols(t, amax=None, adaptive46=False):
     """Q_16x1(t) = Q_1x16(t^T): blocks of 16 down each column of t.
 
     The result is stored in the layout of t^T (cols rows of rows/2 bytes).
     """
     t = np.asarray(t)
-    return quantize_rows(t.T, amax=tensor_amax(t) if amax is None else amax)
+    return quantize_rows(t.T, amax=tensor_amax(t) if amax is None else amax,
+                         adaptive46=adaptive46)
 
 
 def dequantize_rows(q):

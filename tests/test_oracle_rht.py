@@ -84,9 +84,9 @@ def test_fp32_butterfly_within_rounding_of_fp64(mask):
 def _identity_quantizers(monkeypatch):
     # quantize / dequantize as exact identities (the 16x1 layout stores the
     # transpose), leaving only the transforms and the products
-    monkeypatch.setattr(N, "quantize_rows", lambda t, amax=None: np.array(t, np.float64))
+    monkeypatch.setattr(N, "quantize_rows", lambda t, amax=None, adaptive46=False: np.array(t, np.float64))
     monkeypatch.setattr(N, "dequantize_rows", lambda q: q)
-    monkeypatch.setattr(N, "quantize_cols", lambda t, amax=None: np.array(t, np.float64).T)
+    monkeypatch.setattr(N, "quantize_cols", lambda t, amax=None, adaptive46=False: np.array(t, np.float64).T)
     monkeypatch.setattr(N, "dequantize_cols", lambda q: q.T)
 
 
