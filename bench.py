@@ -125,7 +125,7 @@ def source_digest():
 # HBM bytes per launch of the dominant kernel (X = a X + qB qX16^T at
 # 3072 x 8192), from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE, each scaled by
 # what the counter reads for a plain copy of known size; see profiles/.
-DOMINANT_TRAFFIC = {"src_sha256": "51d28fba42a04b19e8ce6c952d0a7cc00f886c17bfcc3aa824e6d7cfa17bd8d1",
+DOMINANT_TRAFFIC = {"src_sha256": "039a38d7679554ed29b95dea038010b371f7b058d01be35a800a78d467ab3683",
                     "bytes_per_launch": 440024017}
 
 
@@ -284,6 +284,16 @@ def main():
                            "unit": "TFLOP/s", "quantile_ms": round(sel_ms, 4),
                            "what": "ns_orthogonalize_ex with clip_quantile=0.99: the clip is the "
                                    "0.99 quantile of |G| found on the device (radix selection)"}
+
+    # the same step with adaptive 4/6 block scaling on every quantization
+    # (each block keeps the better of its M = 6 and M = 4 encodings)
+    astep_ = lambda: ns.ns_orthogonalize_ex(Gd, coeffs, clip=clip, adaptive46=True, out=out,
+                                            workspace=ws, stream=stream)
+    ams_ = time_events(astep_, args.steps, args.warmup, stream)
+    line["ns_46"] = {"ms": round(ams_, 4), "value": round(flops / (ams_ * 1e-3) / 1e12, 2),
+                     "unit": "TFLOP/s",
+                     "what": "ns_orthogonalize_ex with adaptive46: every quantization picks M = 4 "
+                             "or 6 per block by squared error (two encodings per block)"}
 
     # BF16 torch NS of the same matrix, same GPU
     bms = bf16_ns_ms(torch, Gd, coeffs, stream)

@@ -101,6 +101,21 @@ ns_status nvfp4_quantize_rht(const void* x, ns_dtype xt, int64_t rows, int64_t c
                              float* global_scale, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * nvfp4_quantize_46 — nvfp4_quantize with adaptive 4/6 block scaling, the
+ * quantization the Root iteration uses (Full-Stack FP4 §3.4: RTN with
+ * adaptive 4/6 scaling; §5: adaptive M = 4 / M = 6 block scaling of Four
+ * Over Six).  Each block is encoded twice, with its maximum mapped to 6
+ * (s = RNE_E4M3FN(amax_b / (6 s_g)), as nvfp4_quantize) and to 4
+ * (s = RNE_E4M3FN(amax_b / (4 s_g)), saturating at 448), and keeps the
+ * encoding whose squared error sum (x - q s s_g)^2 -- each operation rounded
+ * in double, elements in order -- is smaller; M = 6 on ties.  s_g, the
+ * layouts, the decode rule and the errors are those of nvfp4_quantize.
+ */
+ns_status nvfp4_quantize_46(const void* x, ns_dtype xt, int64_t rows, int64_t cols,
+                            nvfp4_axis axis, uint8_t* codes, uint8_t* scales,
+                            float* global_scale, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * nvfp4_dequantize — x_hat = x_E2M1 * s * s_g (§2 "NVFP4 format").
  * Inputs as written by nvfp4_quantize for the same rows, cols and axis;
  * out is [rows][cols] in the ORIGINAL orientation (an NVFP4_COLS tensor is
@@ -200,12 +215,14 @@ typedef struct {
   double clip_quantile;     /* 0: use clip.  In (0, 1]: clip = the clip_quantile-quantile
                                of |G| (as ns_abs_quantile), found on the device */
   const uint16_t* rht_masks;/* NULL, or a HOST array of k masks (as ns_orthogonalize_rht) */
+  int adaptive46;           /* nonzero: every quantization of the iteration uses adaptive
+                               4/6 block scaling (as nvfp4_quantize_46) */
 } ns_options;
 
 /*
  * ns_orthogonalize_ex — ns_orthogonalize with the clip threshold taken on
- * the device as a quantile of |G| and/or the random Hadamard transform, as
- * set in `opt` (HOST pointer, not NULL).  NS_ERR_ARG for a clip_quantile
+ * the device as a quantile of |G|, the random Hadamard transform and/or
+ * adaptive 4/6 block scaling, as set in `opt` (HOST pointer, not NULL).  NS_ERR_ARG for a clip_quantile
  * outside {0} U (0, 1].  Workspace ns_workspace_bytes(m, n); other
  * arguments and errors as ns_orthogonalize.
  */

@@ -44,12 +44,13 @@ _d = ctypes.c_double
 class NsOptions(ctypes.Structure):
     """ns_options of the C ABI."""
     _fields_ = [("clip", ctypes.c_float), ("clip_quantile", ctypes.c_double),
-                ("rht_masks", ctypes.POINTER(ctypes.c_uint16))]
+                ("rht_masks", ctypes.POINTER(ctypes.c_uint16)), ("adaptive46", ctypes.c_int)]
 
 _SIGS = {
     "nvfp4_quantize_workspace_bytes": (_sz, [_i64, _i64]),
     "nvfp4_quantize": (_i, [_vp, _i, _i64, _i64, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
     "nvfp4_quantize_rht": (_i, [_vp, _i, _i64, _i64, _i, _u16, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "nvfp4_quantize_46": (_i, [_vp, _i, _i64, _i64, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
     "nvfp4_dequantize": (_i, [_vp, _vp, _vp, _i64, _i64, _i, _vp, _i, _vp]),
     "nvfp4_gemm_workspace_bytes": (_sz, [_i64, _i64, _i64, _i]),
     "nvfp4_gemm": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i, _f, _f, _vp, _vp, _vp,
@@ -122,11 +123,12 @@ def _need_cuda(*ts):
 # ------------------------------------------------------------- quantizer --
 
 def nvfp4_quantize(x, axis=NVFP4_ROWS, codes=None, scales=None, global_scale=None,
-                   workspace=None, stream=None):
+                   workspace=None, stream=None, adaptive46=False):
     """NVFP4 quantization of a 2-D float32/bfloat16 device tensor.
 
     Returns (codes uint8 [r][c/2], scales uint8 [r][c/16], s_g float32 [1]),
-    in the layout of x (NVFP4_ROWS) or of x^T (NVFP4_COLS).
+    in the layout of x (NVFP4_ROWS) or of x^T (NVFP4_COLS).  adaptive46=True
+    calls nvfp4_quantize_46 (adaptive 4/6 block scaling).
     """
     torch = _torch()
     _need_cuda(x)
@@ -142,9 +144,10 @@ def nvfp4_quantize(x, axis=NVFP4_ROWS, codes=None, scales=None, global_scale=Non
     wsb = _lib.nvfp4_quantize_workspace_bytes(rows, cols)
     if workspace is None:
         workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
-    _check(_lib.nvfp4_quantize(_ptr(x), _dt(x), rows, cols, axis, _ptr(codes), _ptr(scales),
-                               _ptr(global_scale), _ptr(workspace), workspace.numel(),
-                               _stream(stream)), "nvfp4_quantize")
+    fn, name = ((_lib.nvfp4_quantize_46, "nvfp4_quantize_46") if adaptive46
+                else (_lib.nvfp4_quantize, "nvfp4_quantize"))
+    _check(fn(_ptr(x), _dt(x), rows, cols, axis, _ptr(codes), _ptr(scales), _ptr(global_scale),
+              _ptr(workspace), workspace.numel(), _stream(stream)), name)
     return codes, scales, global_scale
 
 
@@ -267,10 +270,10 @@ def ns_orthogonalize_rht(G, coeffs, masks, clip=float("inf"), out_dtype=NS_F32, 
 
 
 def ns_orthogonalize_ex(G, coeffs, clip=float("inf"), clip_quantile=0.0, rht_masks=None,
-                        out_dtype=NS_F32, out=None, workspace=None, stream=None):
+                        out_dtype=NS_F32, out=None, workspace=None, stream=None, adaptive46=False):
     """ns_orthogonalize with an on-device quantile clip (clip_quantile in
-    (0, 1]; 0 uses `clip`) and/or the random Hadamard transform (one
-    16-bit mask per step)."""
+    (0, 1]; 0 uses `clip`), the random Hadamard transform (one 16-bit mask
+    per step) and/or adaptive 4/6 block scaling on every quantization."""
     torch = _torch()
     _need_cuda(G, out)
     m, n = G.shape
@@ -279,7 +282,7 @@ def ns_orthogonalize_ex(G, coeffs, clip=float("inf"), clip_quantile=0.0, rht_mas
     if workspace is None:
         workspace = torch.empty(ns_workspace_bytes(m, n), dtype=torch.uint8, device=G.device)
     carr, k = _coeff_array(coeffs)
-    opt = NsOptions(float(clip), float(clip_quantile), None)
+    opt = NsOptions(float(clip), float(clip_quantile), None, 1 if adaptive46 else 0)
     marr = None
     if rht_masks is not None:
         if len(rht_masks) != k:
@@ -345,9 +348,11 @@ def ns_orthogonalize_grouped(Gs, coeffs, clips, out_dtype=NS_F32, outs=None, wor
 
 
 def ns_orthogonalize_grouped_ex(Gs, coeffs, clips=None, clip_quantile=0.0, rht_masks=None,
-                                out_dtype=NS_F32, outs=None, workspace=None, stream=None):
-    """ns_orthogonalize_grouped with a per-matrix quantile clip and/or the
-    random Hadamard transform (options shared by every matrix)."""
+                                out_dtype=NS_F32, outs=None, workspace=None, stream=None,
+                                adaptive46=False):
+    """ns_orthogonalize_grouped with a per-matrix quantile clip, the random
+    Hadamard transform and/or adaptive 4/6 scaling (options shared by every
+    matrix)."""
     torch = _torch()
     cnt = len(Gs)
     _need_cuda(*Gs)
@@ -366,7 +371,7 @@ def ns_orthogonalize_grouped_ex(Gs, coeffs, clips=None, clip_quantile=0.0, rht_m
     ns_ = (ctypes.c_int64 * cnt)(*[s[1] for s in shapes])
     cl = (ctypes.c_float * cnt)(*[float(c) for c in clips]) if clips is not None else None
     carr, k = _coeff_array(coeffs)
-    opt = NsOptions(float("inf"), float(clip_quantile), None)
+    opt = NsOptions(float("inf"), float(clip_quantile), None, 1 if adaptive46 else 0)
     marr = None
     if rht_masks is not None:
         if len(rht_masks) != k:

@@ -138,8 +138,9 @@ uint32_t quantile_rank(double q, int64_t n) {
 }
 
 ns_status ns_run(const void* G, ns_dtype gt, int64_t m, int64_t n, const float* coeffs, int k,
-                 float clip, double clip_q, const uint16_t* masks, void* out, ns_dtype ot,
-                 uint8_t* ws, hipStream_t s) {
+                 float clip, double clip_q, const uint16_t* masks, bool a46, void* out,
+                 ns_dtype ot, uint8_t* ws, hipStream_t s) {
+  const uint32_t o46 = a46 ? 1u : 0u;   // adaptive 4/6 on every quantization
   const NsLayout L = ns_layout(m, n);
   const bool tr = m > n;
   const int64_t xm = tr ? n : m, xn = tr ? m : n;
@@ -170,7 +171,7 @@ ns_status ns_run(const void* G, ns_dtype gt, int64_t m, int64_t n, const float* 
   for (int it = 0; it < k; ++it) {
     const float a = coeffs[3 * it], b = coeffs[3 * it + 1], c = coeffs[3 * it + 2];
     if (masks) {
-      const nvfp4::RhtArg h{1u, (uint32_t)masks[it]};
+      const nvfp4::RhtArg h{1u, (uint32_t)masks[it], o46};
       zero_words_kernel<<<1, 256, 0, s>>>(slot, 4 * kSlotWords);
       NS_TRY(hipGetLastError());
       // qX = Q_1x16(X H), qX16 = Q_16x1(H^T X), each with its own s_g
@@ -201,21 +202,32 @@ ns_status ns_run(const void* G, ns_dtype gt, int64_t m, int64_t n, const float* 
     }
     // qX = Q_1x16(X) and qX16 = Q_16x1(X) (stored as rows of X^T), one s_g
     NS_TRY(nvfp4::launch_quant_tiles(X, Dt::F32, xm, xn, slotX, sgX, ws + L.qx_c, ws + L.qx_s,
-                                     ws + L.qt_c, ws + L.qt_s, slotA, s));
+                                     ws + L.qt_c, ws + L.qt_s, slotA, s, nullptr, nullptr,
+                                     nvfp4::RhtArg{0u, 0u, o46}));
     // A = qX qX^T (symmetric, K = xn)
     nvfp4::GemmProblem g1{ws + L.qx_c, ws + L.qx_s, sgX, ws + L.qx_c, ws + L.qx_s, sgX,
                           xm, xm, xn, 1, 1.0f, 0.0f, nullptr, A, slotA, 1};
     NS_TRY(nvfp4::launch_gemm(g1, L.p1, gpart, s));
     // qA = Q_1x16(A); A is exactly symmetric, so Q_16x1(A) = qA^T
-    NS_TRY(nvfp4::launch_quant_rows(A, Dt::F32, xm, xm, slotA, sgA, ws + L.qa_c, ws + L.qa_s,
-                                    slotB, s));
+    if (a46)   // one thread per block: the tiled quantizer, rows only
+      NS_TRY(nvfp4::launch_quant_tiles(A, Dt::F32, xm, xm, slotA, sgA, ws + L.qa_c, ws + L.qa_s,
+                                       nullptr, nullptr, slotB, s, nullptr, nullptr,
+                                       nvfp4::RhtArg{0u, 0u, 1u}));
+    else
+      NS_TRY(nvfp4::launch_quant_rows(A, Dt::F32, xm, xm, slotA, sgA, ws + L.qa_c, ws + L.qa_s,
+                                      slotB, s));
     // B = b A + c qA qA^T (symmetric, K = xm)
     nvfp4::GemmProblem g2{ws + L.qa_c, ws + L.qa_s, sgA, ws + L.qa_c, ws + L.qa_s, sgA,
                           xm, xm, xm, 1, c, b, A, B, slotB, 1};
     NS_TRY(nvfp4::launch_gemm(g2, L.p2, gpart, s));
     // qB = Q_1x16(B)
-    NS_TRY(nvfp4::launch_quant_rows(B, Dt::F32, xm, xm, slotB, sgB, ws + L.qb_c, ws + L.qb_s,
-                                    slotX, s));
+    if (a46)
+      NS_TRY(nvfp4::launch_quant_tiles(B, Dt::F32, xm, xm, slotB, sgB, ws + L.qb_c, ws + L.qb_s,
+                                       nullptr, nullptr, slotX, s, nullptr, nullptr,
+                                       nvfp4::RhtArg{0u, 0u, 1u}));
+    else
+      NS_TRY(nvfp4::launch_quant_rows(B, Dt::F32, xm, xm, slotB, sgB, ws + L.qb_c, ws + L.qb_s,
+                                      slotX, s));
     // X' = a X + qB qX16 (K = xm), in place; the last step of an FP32,
     // untransposed call writes straight into `out` (no copy pass)
     const bool direct = it == k - 1 && !tr && ot == NS_F32;
@@ -286,7 +298,7 @@ ns_status nvfp4_quantize_rht(const void* x, ns_dtype xt, int64_t rows, int64_t c
   if (!ws || ws_bytes < nvfp4_quantize_workspace_bytes(rows, cols)) return NS_ERR_WORKSPACE;
   hipStream_t s = as_stream(stream);
   uint32_t* slot = static_cast<uint32_t*>(ws);
-  const nvfp4::RhtArg h{1u, (uint32_t)mask};
+  const nvfp4::RhtArg h{1u, (uint32_t)mask, 0u};
   zero_words_kernel<<<1, 256, 0, s>>>(slot, kSlotWords);
   NS_TRY(hipGetLastError());
   if (axis == NVFP4_ROWS) {
@@ -298,6 +310,29 @@ ns_status nvfp4_quantize_rht(const void* x, ns_dtype xt, int64_t rows, int64_t c
     NS_TRY(nvfp4::launch_quant_tiles(x, (Dt)xt, rows, cols, slot, global_scale, nullptr, nullptr,
                                      codes, scales, nullptr, s, nullptr, nullptr, h));
   }
+  return NS_OK;
+}
+
+ns_status nvfp4_quantize_46(const void* x, ns_dtype xt, int64_t rows, int64_t cols, nvfp4_axis axis,
+                            uint8_t* codes, uint8_t* scales, float* global_scale, void* ws,
+                            size_t ws_bytes, void* stream) {
+  if (!x || !codes || !scales || !global_scale || !dtype_ok(xt) ||
+      (axis != NVFP4_ROWS && axis != NVFP4_COLS))
+    return NS_ERR_ARG;
+  if (!dims_ok(rows) || !dims_ok(cols)) return NS_ERR_SHAPE;
+  if (!ws || ws_bytes < nvfp4_quantize_workspace_bytes(rows, cols)) return NS_ERR_WORKSPACE;
+  hipStream_t s = as_stream(stream);
+  uint32_t* slot = static_cast<uint32_t*>(ws);
+  const nvfp4::RhtArg o{0u, 0u, 1u};
+  zero_words_kernel<<<1, 256, 0, s>>>(slot, kSlotWords);
+  NS_TRY(hipGetLastError());
+  NS_TRY(nvfp4::launch_amax(x, (Dt)xt, rows * cols, slot, s));
+  if (axis == NVFP4_ROWS)
+    NS_TRY(nvfp4::launch_quant_tiles(x, (Dt)xt, rows, cols, slot, global_scale, codes, scales,
+                                     nullptr, nullptr, nullptr, s, nullptr, nullptr, o));
+  else
+    NS_TRY(nvfp4::launch_quant_tiles(x, (Dt)xt, rows, cols, slot, global_scale, nullptr, nullptr,
+                                     codes, scales, nullptr, s, nullptr, nullptr, o));
   return NS_OK;
 }
 
@@ -357,7 +392,7 @@ ns_status ns_orthogonalize(const void* G, ns_dtype gt, int64_t m, int64_t n, con
   if (st != NS_OK) return st;
   if (!ws || ws_bytes < ns_workspace_bytes(m, n)) return NS_ERR_WORKSPACE;
   if (overlaps(out, (size_t)(m * n) * dtype_size(ot), ws, ws_bytes)) return NS_ERR_ARG;
-  return ns_run(G, gt, m, n, coeffs, k, clip, 0.0, nullptr, out, ot, static_cast<uint8_t*>(ws),
+  return ns_run(G, gt, m, n, coeffs, k, clip, 0.0, nullptr, false, out, ot, static_cast<uint8_t*>(ws),
                 as_stream(stream));
 }
 
@@ -369,7 +404,7 @@ ns_status ns_orthogonalize_rht(const void* G, ns_dtype gt, int64_t m, int64_t n,
   if (st != NS_OK) return st;
   if (!ws || ws_bytes < ns_workspace_bytes(m, n)) return NS_ERR_WORKSPACE;
   if (overlaps(out, (size_t)(m * n) * dtype_size(ot), ws, ws_bytes)) return NS_ERR_ARG;
-  return ns_run(G, gt, m, n, coeffs, k, clip, 0.0, masks, out, ot, static_cast<uint8_t*>(ws),
+  return ns_run(G, gt, m, n, coeffs, k, clip, 0.0, masks, false, out, ot, static_cast<uint8_t*>(ws),
                 as_stream(stream));
 }
 
@@ -385,7 +420,7 @@ ns_status ns_orthogonalize_ex(const void* G, ns_dtype gt, int64_t m, int64_t n,
   if (st != NS_OK) return st;
   if (!ws || ws_bytes < ns_workspace_bytes(m, n)) return NS_ERR_WORKSPACE;
   if (overlaps(out, (size_t)(m * n) * dtype_size(ot), ws, ws_bytes)) return NS_ERR_ARG;
-  return ns_run(G, gt, m, n, coeffs, k, clip, q, opt->rht_masks, out, ot,
+  return ns_run(G, gt, m, n, coeffs, k, clip, q, opt->rht_masks, opt->adaptive46 != 0, out, ot,
                 static_cast<uint8_t*>(ws), as_stream(stream));
 }
 
@@ -500,7 +535,7 @@ ns_status ns_orthogonalize_grouped_ex(int count, const void* const* G, const int
   const std::vector<size_t> off = group_offsets(count, m, n);
   return run_grouped(count, m, n, as_stream(stream), [&](int i, hipStream_t s) {
     const float ci = q > 0.0 ? INFINITY : clip[i];
-    return ns_run(G[i], gt, m[i], n[i], coeffs, k, ci, q, opt->rht_masks, out[i], ot,
+    return ns_run(G[i], gt, m[i], n[i], coeffs, k, ci, q, opt->rht_masks, opt->adaptive46 != 0, out[i], ot,
                   base + off[(size_t)i], s);
   });
 }
@@ -521,7 +556,7 @@ ns_status ns_orthogonalize_grouped(int count, const void* const* G, const int64_
   uint8_t* base = static_cast<uint8_t*>(ws);
   const std::vector<size_t> off = group_offsets(count, m, n);
   return run_grouped(count, m, n, as_stream(stream), [&](int i, hipStream_t s) {
-    return ns_run(G[i], gt, m[i], n[i], coeffs, k, clip[i], 0.0, nullptr, out[i], ot,
+    return ns_run(G[i], gt, m[i], n[i], coeffs, k, clip[i], 0.0, nullptr, false, out[i], ot,
                   base + off[(size_t)i], s);
   });
 }

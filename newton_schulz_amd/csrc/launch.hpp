@@ -8,11 +8,12 @@ namespace nvfp4 {
 
 enum class Dt : int { F32 = 0, BF16 = 1 };
 
-// Random Hadamard transform option of the tiled quantizer kernels: when `on`,
-// every 16-block is multiplied by H^r = diag(s) H_16 / 4 before it is used,
-// s_j = -1 where bit j of `mask` is set.
+// Per-block options of the tiled quantizer kernels.  With `on` every 16-block
+// is multiplied by H^r = diag(s) H_16 / 4 before it is used, s_j = -1 where
+// bit j of `mask` is set.  With `adaptive46` every block keeps the better of
+// its M = 6 and M = 4 encodings (encode_block16_46 in nvfp4_device.hpp).
 struct RhtArg {
-  uint32_t on, mask;
+  uint32_t on, mask, adaptive46;
 };
 
 // Words of one amax slot (kAmaxParts partials spaced one 128-byte line
@@ -36,14 +37,15 @@ hipError_t launch_quant_rows(const void* x, Dt xt, int64_t rows, int64_t cols,
 // Q_1x16 and/or Q_16x1 of a rows x cols matrix through 64x64 LDS tiles, one
 // read of x for both layouts.  Either output pair may be null.  The column
 // layout takes its s_g from amax_c / sg_out_c when given (else the row
-// ones); with rht.on every block is transformed first.
+// ones); with rht.on every block is transformed first, with rht.adaptive46
+// every block takes the better of its 4/6 encodings.
 hipError_t launch_quant_tiles(const void* x, Dt xt, int64_t rows, int64_t cols,
                               const uint32_t* amax_slot, float* sg_out,
                               uint8_t* row_codes, uint8_t* row_scales,
                               uint8_t* col_codes, uint8_t* col_scales,
                               uint32_t* zero_slot, hipStream_t s,
                               const uint32_t* amax_c = nullptr, float* sg_out_c = nullptr,
-                              RhtArg rht = RhtArg{0u, 0u});
+                              RhtArg rht = RhtArg{0u, 0u, 0u});
 // Maxima of |x H^r| over the row blocks into slot_r and of |H^r^T x| over the
 // column blocks into slot_c (either may be null); the caller zeroes them.
 hipError_t launch_amax_tiles(const void* x, Dt xt, int64_t rows, int64_t cols, uint32_t* slot_r,

@@ -212,17 +212,23 @@ __device__ __forceinline__ uint32_t e4m3_rne_sat_f32(float x) {
 // exact one; widened by 2^-19 either way it brackets it, and when both ends
 // round to the same byte (rounding is monotone) that byte is exact.
 // Otherwise, or for extreme s_g, the exact double quotient decides.
-__device__ __forceinline__ uint32_t block_scale_byte(uint32_t amax_b_bits, float sg) {
+// Scale byte with the block maximum mapped to M (6, or 4 for the adaptive
+// 4/6 candidate): RNE_E4M3FN(amax_b / (M s_g)), saturating at 448.
+template <int M>
+__device__ __forceinline__ uint32_t block_scale_byte_m(uint32_t amax_b_bits, float sg) {
   if (sg != sg) return 0x7Fu;               // NaN tensor
   if (sg == 0.0f) return 0u;
   if (sg > 0x1p-100f && sg < 0x1p100f) {
-    const float q = __uint_as_float(amax_b_bits) * __builtin_amdgcn_rcpf(6.0f * sg);
+    const float q = __uint_as_float(amax_b_bits) * __builtin_amdgcn_rcpf((float)M * sg);
     const uint32_t lo = e4m3_rne_sat_f32(q * (1.0f - 0x1p-19f));
     const uint32_t hi = e4m3_rne_sat_f32(q * (1.0f + 0x1p-19f));
     if (lo == hi) return lo;
   }
-  const double q = (double)__uint_as_float(amax_b_bits) / (6.0 * (double)sg);
+  const double q = (double)__uint_as_float(amax_b_bits) / ((double)M * (double)sg);
   return e4m3_rne_sat(q);
+}
+__device__ __forceinline__ uint32_t block_scale_byte(uint32_t amax_b_bits, float sg) {
+  return block_scale_byte_m<6>(amax_b_bits, sg);
 }
 
 // Exact encode of 16 values by thresholds (the reference rule above).
@@ -249,15 +255,8 @@ __device__ __forceinline__ void encode_block16_exact(const uint32_t (&v)[16], fl
 // exact RNE of the quotient.  A block where any element's two codes differ
 // (a tie or a near-tie), or whose s*s_g is outside [2^-120, 2^120], is
 // encoded by the exact threshold rule instead.
-__device__ __forceinline__ void encode_block16(const uint32_t (&v)[16], float sg,
-                                               uint32_t& lo, uint32_t& hi, uint32_t& scale) {
-  uint32_t amax_b = 0;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const uint32_t a = v[i] & 0x7FFFFFFFu;
-    amax_b = a > amax_b ? a : amax_b;
-  }
-  scale = block_scale_byte(amax_b, sg);
+__device__ __forceinline__ void encode_codes16(const uint32_t (&v)[16], float sg, uint32_t scale,
+                                              uint32_t& lo, uint32_t& hi) {
   const float s = (scale == 0x7Fu) ? 0.0f : __builtin_amdgcn_cvt_f32_fp8((int)scale, 0);
   const float unit = s * sg;
   if (unit > 0x1p-120f && unit < 0x1p120f) {
@@ -285,6 +284,65 @@ __device__ __forceinline__ void encode_block16(const uint32_t (&v)[16], float sg
     }
   }
   encode_block16_exact(v, sg, scale, lo, hi);
+}
+
+__device__ __forceinline__ uint32_t block_amax_bits(const uint32_t (&v)[16]) {
+  uint32_t amax_b = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t a = v[i] & 0x7FFFFFFFu;
+    amax_b = a > amax_b ? a : amax_b;
+  }
+  return amax_b;
+}
+
+__device__ __forceinline__ void encode_block16(const uint32_t (&v)[16], float sg,
+                                               uint32_t& lo, uint32_t& hi, uint32_t& scale) {
+  scale = block_scale_byte(block_amax_bits(v), sg);
+  encode_codes16(v, sg, scale, lo, hi);
+}
+
+// Squared error of a block's encoding: the sum over its 16 elements, in
+// element order, of (x - q s s_g)^2, each difference, square and sum rounded
+// in double (no fused multiply-add, so that the comparison below is the one
+// the plain definition makes).  q s s_g is exact in double.
+__device__ __forceinline__ double block_sq_error(const uint32_t (&v)[16], float sg, uint32_t scale,
+                                                 uint32_t lo, uint32_t hi) {
+#pragma clang fp contract(off)
+  const double unit = e4m3_value(scale) * (double)sg;
+  double e = 0.0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t c = ((i < 8 ? lo : hi) >> (4 * (i & 7))) & 0xFu;
+    const uint32_t ex = (c >> 1) & 3u, mb = c & 1u;
+    const double mag = ex == 0 ? 0.5 * (double)mb : ldexp(1.0 + 0.5 * (double)mb, (int)ex - 1);
+    const double val = (c & 8u) ? -(mag * unit) : mag * unit;
+    const double d = (double)__uint_as_float(v[i]) - val;
+    e = e + d * d;
+  }
+  return e;
+}
+
+// Adaptive 4/6 block scaling (the Root quantizations of Full-Stack FP4,
+// §3.4; adaptive M = 4 / M = 6 block scaling of Four Over Six): the block is
+// encoded with its maximum mapped to 6 and to 4 and keeps the encoding with
+// the smaller squared error; M = 6 on ties (and when s_g is NaN or zero, or
+// both candidates share a scale).  s_g is that of plain NVFP4.
+__device__ __forceinline__ void encode_block16_46(const uint32_t (&v)[16], float sg,
+                                                  uint32_t& lo, uint32_t& hi, uint32_t& scale) {
+  const uint32_t amax_b = block_amax_bits(v);
+  scale = block_scale_byte_m<6>(amax_b, sg);
+  encode_codes16(v, sg, scale, lo, hi);
+  if (!(sg > 0.0f) || scale == 0x7Fu) return;
+  const uint32_t s4 = block_scale_byte_m<4>(amax_b, sg);
+  if (s4 == scale) return;
+  uint32_t lo4, hi4;
+  encode_codes16(v, sg, s4, lo4, hi4);
+  if (block_sq_error(v, sg, s4, lo4, hi4) < block_sq_error(v, sg, scale, lo, hi)) {
+    lo = lo4;
+    hi = hi4;
+    scale = s4;
+  }
 }
 
 // Codes of the EPL (4 or 8) elements one lane holds of a block whose scale

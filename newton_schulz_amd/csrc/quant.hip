@@ -204,7 +204,8 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(
     if (in) {
       if (rht.on) rht16(v, rht.mask);
       uint32_t lo, hi, sc;
-      encode_block16(v, sg, lo, hi, sc);
+      if (rht.adaptive46) encode_block16_46(v, sg, lo, hi, sc);
+      else encode_block16(v, sg, lo, hi, sc);
       const int64_t e = (r0 + tr) * cols + c0 + tc;
       reinterpret_cast<uint2*>(row_codes)[e / 16] = make_uint2(lo, hi);
       row_scales[e / 16] = (uint8_t)sc;
@@ -219,7 +220,8 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(
       for (int i = 0; i < 16; ++i) w[i] = tile[16 * b + i][j];
       if (rht.on) rht16(w, rht.mask);
       uint32_t lo, hi, sc;
-      encode_block16(w, sgc, lo, hi, sc);
+      if (rht.adaptive46) encode_block16_46(w, sgc, lo, hi, sc);
+      else encode_block16(w, sgc, lo, hi, sc);
       const int64_t e = (c0 + j) * rows + r0 + 16 * b;   // element of the transpose
       reinterpret_cast<uint2*>(col_codes)[e / 16] = make_uint2(lo, hi);
       col_scales[e / 16] = (uint8_t)sc;
