@@ -125,7 +125,7 @@ def source_digest():
 # HBM bytes per launch of the dominant kernel (X = a X + qB qX16^T at
 # 3072 x 8192), from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE, each scaled by
 # what the counter reads for a plain copy of known size; see profiles/.
-DOMINANT_TRAFFIC = {"src_sha256": "039a38d7679554ed29b95dea038010b371f7b058d01be35a800a78d467ab3683",
+DOMINANT_TRAFFIC = {"src_sha256": "168b878a290c5880036ed8cf7e941f62fa09303bd01848b1ed18c3cbeef23ade",
                     "bytes_per_launch": 440024017}
 
 

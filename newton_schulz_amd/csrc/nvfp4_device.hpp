@@ -302,6 +302,23 @@ __device__ __forceinline__ void encode_block16(const uint32_t (&v)[16], float sg
   encode_codes16(v, sg, scale, lo, hi);
 }
 
+// Signed E2M1 values of a block's 16 codes (element 2i in the low nibble of
+// byte i of lo:hi), exact in FP32: the hardware conversion at unit scale.
+__device__ __forceinline__ void decode_codes16(uint32_t lo, uint32_t hi, float (&q)[16]) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const f32x2 p[8] = {
+      __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(lo, 1.0f, 0),
+      __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(lo, 1.0f, 1),
+      __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(lo, 1.0f, 2),
+      __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(lo, 1.0f, 3),
+      __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(hi, 1.0f, 0),
+      __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(hi, 1.0f, 1),
+      __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(hi, 1.0f, 2),
+      __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(hi, 1.0f, 3)};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) q[i] = p[i >> 1][i & 1];
+}
+
 // Squared error of a block's encoding: the sum over its 16 elements, in
 // element order, of (x - q s s_g)^2, each difference, square and sum rounded
 // in double (no fused multiply-add, so that the comparison below is the one
@@ -310,17 +327,52 @@ __device__ __forceinline__ double block_sq_error(const uint32_t (&v)[16], float 
                                                  uint32_t lo, uint32_t hi) {
 #pragma clang fp contract(off)
   const double unit = e4m3_value(scale) * (double)sg;
+  float q[16];
+  decode_codes16(lo, hi, q);
   double e = 0.0;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const uint32_t c = ((i < 8 ? lo : hi) >> (4 * (i & 7))) & 0xFu;
-    const uint32_t ex = (c >> 1) & 3u, mb = c & 1u;
-    const double mag = ex == 0 ? 0.5 * (double)mb : ldexp(1.0 + 0.5 * (double)mb, (int)ex - 1);
-    const double val = (c & 8u) ? -(mag * unit) : mag * unit;
-    const double d = (double)__uint_as_float(v[i]) - val;
+    const double d = (double)__uint_as_float(v[i]) - (double)q[i] * unit;   // exact product
     e = e + d * d;
   }
   return e;
+}
+
+// The same sum in FP32, for screening: q s is exact in FP32 (at most six
+// significant bits), so each difference x - (q s) s_g is rounded once (fma),
+// and each square is added with one rounding.  The result is within
+// 18.1 * 2^-24 of the exact sum relatively, plus 2^-121 absolutely for
+// results in FP32's subnormal range, unless it overflowed.
+__device__ __forceinline__ float block_sq_error_f32(const uint32_t (&v)[16], float sg,
+                                                    uint32_t scale, uint32_t lo, uint32_t hi) {
+  const float s = __builtin_amdgcn_cvt_f32_fp8((int)scale, 0);
+  float q[16];
+  decode_codes16(lo, hi, q);
+  float e = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float d = __builtin_fmaf(q[i] * s, -sg, __uint_as_float(v[i]));
+    e = __builtin_fmaf(d, d, e);
+  }
+  return e;
+}
+
+// Whether the M = 4 encoding (s4, lo4, hi4) has the strictly smaller squared
+// error, as block_sq_error decides it.  The FP32 sums decide whenever they
+// differ by more than their error bounds (relative 2^-18 is above
+// 18.1 * 2^-24 with room for the rounding of the bounds themselves, and
+// 2^-120 covers the subnormal range); otherwise the double sums decide.
+__device__ __forceinline__ bool four_is_better(const uint32_t (&v)[16], float sg, uint32_t s6,
+                                               uint32_t lo6, uint32_t hi6, uint32_t s4,
+                                               uint32_t lo4, uint32_t hi4) {
+  const float e6 = block_sq_error_f32(v, sg, s6, lo6, hi6);
+  const float e4 = block_sq_error_f32(v, sg, s4, lo4, hi4);
+  constexpr float kRel = 0x1p-18f, kAbs = 0x1p-120f, kMax = 0x1.fffffep127f;
+  if (e4 <= kMax && e6 <= kMax) {
+    if (e4 * (1.0f + kRel) + kAbs < e6 * (1.0f - kRel) - kAbs) return true;
+    if (e4 * (1.0f - kRel) - kAbs > e6 * (1.0f + kRel) + kAbs) return false;
+  }
+  return block_sq_error(v, sg, s4, lo4, hi4) < block_sq_error(v, sg, s6, lo6, hi6);
 }
 
 // Adaptive 4/6 block scaling (the Root quantizations of Full-Stack FP4,
@@ -338,7 +390,7 @@ __device__ __forceinline__ void encode_block16_46(const uint32_t (&v)[16], float
   if (s4 == scale) return;
   uint32_t lo4, hi4;
   encode_codes16(v, sg, s4, lo4, hi4);
-  if (block_sq_error(v, sg, s4, lo4, hi4) < block_sq_error(v, sg, scale, lo, hi)) {
+  if (four_is_better(v, sg, scale, lo, hi, s4, lo4, hi4)) {
     lo = lo4;
     hi = hi4;
     scale = s4;

@@ -31,6 +31,12 @@ def _inputs():
     z[:16] = 0.0
     z[16:32, ::3] = -0.0
     yield "zero rows and signed zeros 48x48", z
+    # s_g = 1 (one block of 2688) and blocks of values that both candidates
+    # often encode exactly: equal errors, decided by the double sums, keep 6
+    e = rng.choice([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0, 8.0, 12.0], (64, 96))
+    e *= rng.choice([-1.0, 1.0], e.shape)
+    e[0, :16] = 2688.0
+    yield "exactly representable values 64x96", e
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
