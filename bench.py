@@ -203,8 +203,8 @@ def cpu_baseline(G, clip, coeffs, m, n):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(see DESIGN.md for how the path would shard).", file=sys.stderr)
+        print("bench.py measures one GPU only: the NS path runs on a single GPU and has "
+              "no multi-GPU mode; run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     import torch
     import newton_schulz_amd as ns

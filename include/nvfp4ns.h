@@ -17,8 +17,9 @@
  *   - Matrices are dense row-major with no padding.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Every call
  *     only enqueues work on it and returns; nothing synchronises.  The
- *     caller owns all memory; the library allocates nothing and keeps no
- *     state between calls.
+ *     caller owns all memory; the library allocates no device memory and
+ *     keeps no data between calls (the grouped calls keep only their
+ *     streams, see ns_orthogonalize_grouped).
  *   - Arguments are validated before anything is enqueued; a negative
  *     status means nothing was launched.  NS_ERR_HIP means a launch failed.
  *   - Data-dependent cases are defined, never errors: a NaN or infinity in
@@ -61,8 +62,8 @@ typedef enum { NS_F32 = 0, NS_BF16 = 1 } ns_dtype;
  * scale bytes). */
 typedef enum { NVFP4_ROWS = 0, NVFP4_COLS = 1 } nvfp4_axis;
 
-/* Workspace of nvfp4_quantize and nvfp4_quantize_rht, in bytes (the partial
- * tensor maxima: 2 KiB, independent of the shape). */
+/* Workspace of nvfp4_quantize, nvfp4_quantize_rht and nvfp4_quantize_46, in
+ * bytes (the partial tensor maxima: 2 KiB, independent of the shape). */
 size_t nvfp4_quantize_workspace_bytes(int64_t rows, int64_t cols);
 
 /*
@@ -222,9 +223,9 @@ typedef struct {
 /*
  * ns_orthogonalize_ex — ns_orthogonalize with the clip threshold taken on
  * the device as a quantile of |G|, the random Hadamard transform and/or
- * adaptive 4/6 block scaling, as set in `opt` (HOST pointer, not NULL).  NS_ERR_ARG for a clip_quantile
- * outside {0} U (0, 1].  Workspace ns_workspace_bytes(m, n); other
- * arguments and errors as ns_orthogonalize.
+ * adaptive 4/6 block scaling, as set in `opt` (HOST pointer, not NULL).
+ * NS_ERR_ARG for a clip_quantile outside {0} U (0, 1].  Workspace
+ * ns_workspace_bytes(m, n); other arguments and errors as ns_orthogonalize.
  */
 ns_status ns_orthogonalize_ex(const void* G, ns_dtype gt, int64_t m, int64_t n,
                               const float* coeffs, int k, const ns_options* opt, void* out,
@@ -256,7 +257,8 @@ ns_status ns_orthogonalize_grouped(int count, const void* const* G, const int64_
  * ns_orthogonalize_grouped_ex — ns_orthogonalize_grouped with the options of
  * ns_orthogonalize_ex shared by every matrix: with opt->clip_quantile > 0
  * each matrix is clipped at that quantile of its own |G| (clip may then be
- * NULL), else at clip[i]; opt->rht_masks (k masks) applies to every matrix.
+ * NULL), else at clip[i]; opt->rht_masks (k masks) and opt->adaptive46
+ * apply to every matrix.
  * Workspace ns_grouped_workspace_bytes(); concurrency and ordering as for
  * ns_orthogonalize_grouped.
  */

@@ -206,14 +206,14 @@ __device__ __forceinline__ uint32_t e4m3_rne_sat_f32(float x) {
   return ((b + 0x7FFFFu + ((b >> 20) & 1u)) >> 20) - ((127u - 7u) << 3);
 }
 
-// Scale byte of a block with maximum |x| = amax_b (as float bits) under s_g:
-// RNE_E4M3(amax_b / (6 s_g)) of the exact quotient.  Fast path: the float
-// quotient through the hardware reciprocal is within 2^-22 relative of the
-// exact one; widened by 2^-19 either way it brackets it, and when both ends
-// round to the same byte (rounding is monotone) that byte is exact.
-// Otherwise, or for extreme s_g, the exact double quotient decides.
-// Scale byte with the block maximum mapped to M (6, or 4 for the adaptive
-// 4/6 candidate): RNE_E4M3FN(amax_b / (M s_g)), saturating at 448.
+// Scale byte of a block with maximum |x| = amax_b (as float bits) under s_g,
+// the block maximum mapped to M (6; 4 for the adaptive 4/6 candidate):
+// RNE_E4M3FN(amax_b / (M s_g)) of the exact quotient, saturating at 448.
+// Fast path: the float quotient through the hardware reciprocal is within
+// 2^-22 relative of the exact one; widened by 2^-19 either way it brackets
+// it, and when both ends round to the same byte (rounding is monotone) that
+// byte is exact.  Otherwise, or for extreme s_g, the exact double quotient
+// decides.
 template <int M>
 __device__ __forceinline__ uint32_t block_scale_byte_m(uint32_t amax_b_bits, float sg) {
   if (sg != sg) return 0x7Fu;               // NaN tensor

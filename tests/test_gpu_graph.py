@@ -34,7 +34,8 @@ def _capture(fn):
 # 384 x 8192: the Gram product's leftover tiles are split along K, so its
 # K-parts and their reduce run on a side stream forked from the call's stream
 @pytest.mark.parametrize("variant,shape", [("plain", (384, 640)), ("plain", (384, 8192)),
-                                           ("p99 clip + transform", (384, 640))])
+                                           ("p99 clip + transform", (384, 640)),
+                                           ("adaptive 4/6", (384, 640))])
 def test_graph_replays_match_eager(variant, shape):
     G = synth.student_t(*shape, seed=31)
     bits, _ = synth.to_bf16(G)
@@ -45,6 +46,9 @@ def test_graph_replays_match_eager(variant, shape):
     out = torch.empty(shape, dtype=torch.float32, device=Gd.device)
     if variant == "plain":
         call = lambda g: ns.ns_orthogonalize(g, coeffs, 0.05, out=out, workspace=ws)
+    elif variant == "adaptive 4/6":
+        call = lambda g: ns.ns_orthogonalize_ex(g, coeffs, clip=0.05, adaptive46=True,
+                                                out=out, workspace=ws)
     else:
         masks = synth.rht_masks(len(coeffs), seed=3)
         call = lambda g: ns.ns_orthogonalize_ex(g, coeffs, clip_quantile=0.99, rht_masks=masks,
