@@ -15,6 +15,12 @@
  *     per-matrix arrays' elements are DEVICE pointers; coeffs, m, n, clip
  *     and the pointer arrays themselves are HOST memory.
  *   - Matrices are dense row-major with no padding.
+ *   - Device arrays must be 16-byte aligned, and single device floats or
+ *     words (global_scale, sg_p, sg_q, amax_out, ns_abs_quantile's out)
+ *     4-byte aligned; hipMalloc and torch allocations are.  What a call
+ *     writes (outputs and workspace) must not overlap what it reads or
+ *     another of its outputs, except that nvfp4_gemm's addend may be out
+ *     itself.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Every call
  *     only enqueues work on it and returns; nothing synchronises.  The
  *     caller owns all memory; the library allocates no device memory and
@@ -47,7 +53,8 @@ extern "C" {
 
 typedef enum {
   NS_OK = 0,
-  NS_ERR_ARG = -1,        /* null pointer, bad enum, k <= 0, clip NaN or <= 0, aliasing */
+  NS_ERR_ARG = -1,        /* null pointer, bad enum, k <= 0, clip NaN or <= 0, a
+                             misaligned pointer, overlapping arrays */
   NS_ERR_SHAPE = -2,      /* a dimension <= 0 or not a multiple of 16, or a matrix of
                              2^31 or more elements in ns_orthogonalize / nvfp4_gemm */
   NS_ERR_WORKSPACE = -3,  /* ws is NULL or ws_bytes is below the required size */

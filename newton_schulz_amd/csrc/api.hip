@@ -9,6 +9,7 @@
 #include <cstdlib>
 #include <algorithm>
 #include <cstring>
+#include <initializer_list>
 #include <mutex>
 #include <vector>
 
@@ -28,6 +29,28 @@ constexpr int64_t kMaxElems = (int64_t)1 << 31;
 inline bool dtype_ok(int d) { return d == NS_F32 || d == NS_BF16; }
 inline size_t dtype_size(ns_dtype d) { return d == NS_F32 ? 4 : 2; }
 inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+// Device arrays must be 16-byte aligned (the kernels move 16-byte vectors);
+// single floats and words 4-byte aligned.
+inline bool al(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+// A byte range of device memory; null or empty ranges overlap nothing.
+struct Span {
+  const void* p;
+  size_t n;
+};
+// Whether the written range `o` shares a byte with any of `others`.
+bool hits(Span o, std::initializer_list<Span> others) {
+  if (!o.p || o.n == 0) return false;
+  for (const Span& t : others)
+    if (t.p && t.n && overlaps(o.p, o.n, t.p, t.n)) return true;
+  return false;
+}
 
 // ---- concurrent problems of a grouped call --------------------------------
 // The problems of a grouped call are independent (each has its own part of
@@ -241,11 +264,6 @@ ns_status ns_run(const void* G, ns_dtype gt, int64_t m, int64_t n, const float* 
   return NS_OK;
 }
 
-bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
-  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
-  return x < y + nb && y < x + na;
-}
-
 ns_status validate_ns(const void* G, int gt, int64_t m, int64_t n, const float* coeffs, int k,
                       float clip, const void* out, int ot) {
   if (!G || !out || !coeffs || k <= 0 || !dtype_ok(gt) || !dtype_ok(ot)) return NS_ERR_ARG;
@@ -254,8 +272,39 @@ ns_status validate_ns(const void* G, int gt, int64_t m, int64_t n, const float* 
   if (m * n >= kMaxElems) return NS_ERR_SHAPE;
   for (int i = 0; i < 3 * k; ++i)
     if (!std::isfinite(coeffs[i])) return NS_ERR_ARG;
+  if (!al(G, 16) || !al(out, 16)) return NS_ERR_ARG;
   if (overlaps(G, (size_t)(m * n) * dtype_size((ns_dtype)gt), out,
                (size_t)(m * n) * dtype_size((ns_dtype)ot)))
+    return NS_ERR_ARG;
+  return NS_OK;
+}
+
+// The workspace of one NS problem: 16-byte aligned, clear of G and out.
+ns_status check_ns_ws(const void* G, int gt, int64_t m, int64_t n, const void* out, int ot,
+                      const void* ws, size_t ws_bytes) {
+  if (!al(ws, 16)) return NS_ERR_ARG;
+  const size_t e = (size_t)(m * n);
+  if (hits(Span{ws, ws_bytes}, {Span{G, e * dtype_size((ns_dtype)gt)},
+                                Span{out, e * dtype_size((ns_dtype)ot)}}))
+    return NS_ERR_ARG;
+  return NS_OK;
+}
+
+// Arguments shared by the three quantizer entry points.
+ns_status validate_quant(const void* x, int xt, int64_t rows, int64_t cols, int axis,
+                         const void* codes, const void* scales, const void* global_scale,
+                         const void* ws, size_t ws_bytes) {
+  if (!x || !codes || !scales || !global_scale || !dtype_ok(xt) ||
+      (axis != NVFP4_ROWS && axis != NVFP4_COLS))
+    return NS_ERR_ARG;
+  if (!dims_ok(rows) || !dims_ok(cols)) return NS_ERR_SHAPE;
+  if (!ws || ws_bytes < align_up(kSlotWords * sizeof(uint32_t))) return NS_ERR_WORKSPACE;
+  if (!al(x, 16) || !al(codes, 16) || !al(scales, 16) || !al(ws, 16) || !al(global_scale, 4))
+    return NS_ERR_ARG;
+  const size_t e = (size_t)(rows * cols);
+  const Span X{x, e * dtype_size((ns_dtype)xt)}, C{codes, e / 2}, S{scales, e / 16},
+      Gs{global_scale, sizeof(float)}, W{ws, ws_bytes};
+  if (hits(C, {X, S, Gs, W}) || hits(S, {X, Gs, W}) || hits(Gs, {X, W}) || hits(W, {X}))
     return NS_ERR_ARG;
   return NS_OK;
 }
@@ -269,11 +318,9 @@ size_t nvfp4_quantize_workspace_bytes(int64_t, int64_t) { return align_up(kSlotW
 ns_status nvfp4_quantize(const void* x, ns_dtype xt, int64_t rows, int64_t cols, nvfp4_axis axis,
                          uint8_t* codes, uint8_t* scales, float* global_scale, void* ws,
                          size_t ws_bytes, void* stream) {
-  if (!x || !codes || !scales || !global_scale || !dtype_ok(xt) ||
-      (axis != NVFP4_ROWS && axis != NVFP4_COLS))
-    return NS_ERR_ARG;
-  if (!dims_ok(rows) || !dims_ok(cols)) return NS_ERR_SHAPE;
-  if (!ws || ws_bytes < nvfp4_quantize_workspace_bytes(rows, cols)) return NS_ERR_WORKSPACE;
+  const ns_status st =
+      validate_quant(x, xt, rows, cols, axis, codes, scales, global_scale, ws, ws_bytes);
+  if (st != NS_OK) return st;
   hipStream_t s = as_stream(stream);
   uint32_t* slot = static_cast<uint32_t*>(ws);
   zero_words_kernel<<<1, 256, 0, s>>>(slot, kSlotWords);
@@ -291,11 +338,9 @@ ns_status nvfp4_quantize(const void* x, ns_dtype xt, int64_t rows, int64_t cols,
 ns_status nvfp4_quantize_rht(const void* x, ns_dtype xt, int64_t rows, int64_t cols,
                              nvfp4_axis axis, uint16_t mask, uint8_t* codes, uint8_t* scales,
                              float* global_scale, void* ws, size_t ws_bytes, void* stream) {
-  if (!x || !codes || !scales || !global_scale || !dtype_ok(xt) ||
-      (axis != NVFP4_ROWS && axis != NVFP4_COLS))
-    return NS_ERR_ARG;
-  if (!dims_ok(rows) || !dims_ok(cols)) return NS_ERR_SHAPE;
-  if (!ws || ws_bytes < nvfp4_quantize_workspace_bytes(rows, cols)) return NS_ERR_WORKSPACE;
+  const ns_status st =
+      validate_quant(x, xt, rows, cols, axis, codes, scales, global_scale, ws, ws_bytes);
+  if (st != NS_OK) return st;
   hipStream_t s = as_stream(stream);
   uint32_t* slot = static_cast<uint32_t*>(ws);
   const nvfp4::RhtArg h{1u, (uint32_t)mask, 0u};
@@ -316,11 +361,9 @@ ns_status nvfp4_quantize_rht(const void* x, ns_dtype xt, int64_t rows, int64_t c
 ns_status nvfp4_quantize_46(const void* x, ns_dtype xt, int64_t rows, int64_t cols, nvfp4_axis axis,
                             uint8_t* codes, uint8_t* scales, float* global_scale, void* ws,
                             size_t ws_bytes, void* stream) {
-  if (!x || !codes || !scales || !global_scale || !dtype_ok(xt) ||
-      (axis != NVFP4_ROWS && axis != NVFP4_COLS))
-    return NS_ERR_ARG;
-  if (!dims_ok(rows) || !dims_ok(cols)) return NS_ERR_SHAPE;
-  if (!ws || ws_bytes < nvfp4_quantize_workspace_bytes(rows, cols)) return NS_ERR_WORKSPACE;
+  const ns_status st =
+      validate_quant(x, xt, rows, cols, axis, codes, scales, global_scale, ws, ws_bytes);
+  if (st != NS_OK) return st;
   hipStream_t s = as_stream(stream);
   uint32_t* slot = static_cast<uint32_t*>(ws);
   const nvfp4::RhtArg o{0u, 0u, 1u};
@@ -343,6 +386,11 @@ ns_status nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const fl
       (axis != NVFP4_ROWS && axis != NVFP4_COLS))
     return NS_ERR_ARG;
   if (!dims_ok(rows) || !dims_ok(cols)) return NS_ERR_SHAPE;
+  if (!al(codes, 16) || !al(scales, 16) || !al(out, 16) || !al(global_scale, 4)) return NS_ERR_ARG;
+  const size_t e = (size_t)(rows * cols);
+  if (hits(Span{out, e * dtype_size(ot)},
+           {Span{codes, e / 2}, Span{scales, e / 16}, Span{global_scale, sizeof(float)}}))
+    return NS_ERR_ARG;
   hipStream_t s = as_stream(stream);
   if (axis == NVFP4_ROWS)
     NS_TRY(nvfp4::launch_dequant_rows(codes, scales, global_scale, rows, cols, out, (Dt)ot, s));
@@ -373,6 +421,18 @@ ns_status nvfp4_gemm(const uint8_t* codes_p, const uint8_t* scales_p, const floa
   const bool split_ok = ws != nullptr;
   nvfp4::GemmPlan plan = nvfp4::plan_gemm(M, N, K, symmetric != 0, split_ok);
   if (split_ok && ws_bytes < plan.ws_bytes) return NS_ERR_WORKSPACE;
+  if (!al(codes_p, 16) || !al(scales_p, 16) || !al(codes_q, 16) || !al(scales_q, 16) ||
+      !al(out, 16) || !al(sg_p, 4) || !al(sg_q, 4) || !al(addend, 16) || !al(ws, 16) ||
+      !al(amax_out, 4))
+    return NS_ERR_ARG;
+  const size_t mk = (size_t)(M * K), nk = (size_t)(N * K), mn = (size_t)(M * N) * sizeof(float);
+  const Span P{codes_p, mk / 2}, PS{scales_p, mk / 16}, Q{codes_q, nk / 2}, QS{scales_q, nk / 16},
+      SP{sg_p, sizeof(float)}, SQ{sg_q, sizeof(float)}, O{out, mn},
+      Ad{beta != 0.0f && addend != out ? addend : nullptr, mn}, Am{amax_out, sizeof(uint32_t)},
+      W{ws, split_ok ? ws_bytes : 0};
+  if (hits(O, {P, PS, Q, QS, SP, SQ, Ad, Am, W}) || hits(Am, {P, PS, Q, QS, SP, SQ, Ad, W}) ||
+      hits(W, {P, PS, Q, QS, SP, SQ, Ad}))
+    return NS_ERR_ARG;
   nvfp4::GemmProblem g{codes_p, scales_p, sg_p, codes_q, scales_q, sg_q, M, N, K,
                        symmetric ? 1 : 0, alpha, beta, beta != 0.0f ? addend : nullptr, out,
                        amax_out, 0};
@@ -391,7 +451,8 @@ ns_status ns_orthogonalize(const void* G, ns_dtype gt, int64_t m, int64_t n, con
   ns_status st = validate_ns(G, gt, m, n, coeffs, k, clip, out, ot);
   if (st != NS_OK) return st;
   if (!ws || ws_bytes < ns_workspace_bytes(m, n)) return NS_ERR_WORKSPACE;
-  if (overlaps(out, (size_t)(m * n) * dtype_size(ot), ws, ws_bytes)) return NS_ERR_ARG;
+  st = check_ns_ws(G, gt, m, n, out, ot, ws, ws_bytes);
+  if (st != NS_OK) return st;
   return ns_run(G, gt, m, n, coeffs, k, clip, 0.0, nullptr, false, out, ot, static_cast<uint8_t*>(ws),
                 as_stream(stream));
 }
@@ -403,7 +464,8 @@ ns_status ns_orthogonalize_rht(const void* G, ns_dtype gt, int64_t m, int64_t n,
   ns_status st = validate_ns(G, gt, m, n, coeffs, k, clip, out, ot);
   if (st != NS_OK) return st;
   if (!ws || ws_bytes < ns_workspace_bytes(m, n)) return NS_ERR_WORKSPACE;
-  if (overlaps(out, (size_t)(m * n) * dtype_size(ot), ws, ws_bytes)) return NS_ERR_ARG;
+  st = check_ns_ws(G, gt, m, n, out, ot, ws, ws_bytes);
+  if (st != NS_OK) return st;
   return ns_run(G, gt, m, n, coeffs, k, clip, 0.0, masks, false, out, ot, static_cast<uint8_t*>(ws),
                 as_stream(stream));
 }
@@ -419,7 +481,8 @@ ns_status ns_orthogonalize_ex(const void* G, ns_dtype gt, int64_t m, int64_t n,
   ns_status st = validate_ns(G, gt, m, n, coeffs, k, clip, out, ot);
   if (st != NS_OK) return st;
   if (!ws || ws_bytes < ns_workspace_bytes(m, n)) return NS_ERR_WORKSPACE;
-  if (overlaps(out, (size_t)(m * n) * dtype_size(ot), ws, ws_bytes)) return NS_ERR_ARG;
+  st = check_ns_ws(G, gt, m, n, out, ot, ws, ws_bytes);
+  if (st != NS_OK) return st;
   return ns_run(G, gt, m, n, coeffs, k, clip, q, opt->rht_masks, opt->adaptive46 != 0, out, ot,
                 static_cast<uint8_t*>(ws), as_stream(stream));
 }
@@ -431,6 +494,9 @@ ns_status ns_abs_quantile(const void* x, ns_dtype xt, int64_t count, double q, f
   if (!x || !out || !dtype_ok(xt) || std::isnan(q) || !(q > 0.0) || q > 1.0) return NS_ERR_ARG;
   if (!dims_ok(count) || count >= kMaxElems) return NS_ERR_SHAPE;
   if (!ws || ws_bytes < ns_abs_quantile_workspace_bytes()) return NS_ERR_WORKSPACE;
+  if (!al(x, 16) || !al(ws, 16) || !al(out, 4)) return NS_ERR_ARG;
+  const Span X{x, (size_t)count * dtype_size(xt)}, W{ws, ws_bytes};
+  if (hits(Span{out, sizeof(float)}, {X, W}) || hits(W, {X})) return NS_ERR_ARG;
   NS_TRY(nvfp4::launch_abs_quantile(x, (Dt)xt, count, quantile_rank(q, count), out, ws,
                                     as_stream(stream)));
   return NS_OK;
@@ -488,6 +554,26 @@ ns_status run_grouped(int count, const int64_t* m, const int64_t* n, hipStream_t
   return NS_OK;
 }
 
+// The problems of a grouped call run concurrently: no output may touch
+// another problem's input or output, and the workspace touches none of them.
+ns_status check_group(int count, const void* const* G, const int64_t* m, const int64_t* n,
+                      ns_dtype gt, void* const* out, ns_dtype ot, const void* ws, size_t ws_bytes) {
+  if (!al(ws, 16)) return NS_ERR_ARG;
+  const Span W{ws, ws_bytes};
+  for (int i = 0; i < count; ++i) {
+    const size_t e = (size_t)(m[i] * n[i]);
+    const Span Gi{G[i], e * dtype_size(gt)}, Oi{out[i], e * dtype_size(ot)};
+    if (hits(W, {Gi, Oi})) return NS_ERR_ARG;
+    for (int j = 0; j < count; ++j) {
+      if (j == i) continue;
+      const size_t f = (size_t)(m[j] * n[j]);
+      if (hits(Oi, {Span{G[j], f * dtype_size(gt)}, Span{out[j], f * dtype_size(ot)}}))
+        return NS_ERR_ARG;
+    }
+  }
+  return NS_OK;
+}
+
 // Byte offset of problem i's workspace in a grouped call.
 std::vector<size_t> group_offsets(int count, const int64_t* m, const int64_t* n) {
   std::vector<size_t> off((size_t)count);
@@ -529,8 +615,10 @@ ns_status ns_orthogonalize_grouped_ex(int count, const void* const* G, const int
   }
   const size_t need = ns_grouped_workspace_bytes(count, m, n);
   if (!ws || ws_bytes < need) return NS_ERR_WORKSPACE;
-  for (int i = 0; i < count; ++i)
-    if (overlaps(out[i], (size_t)(m[i] * n[i]) * dtype_size(ot), ws, ws_bytes)) return NS_ERR_ARG;
+  {
+    const ns_status st = check_group(count, G, m, n, gt, out, ot, ws, ws_bytes);
+    if (st != NS_OK) return st;
+  }
   uint8_t* base = static_cast<uint8_t*>(ws);
   const std::vector<size_t> off = group_offsets(count, m, n);
   return run_grouped(count, m, n, as_stream(stream), [&](int i, hipStream_t s) {
@@ -551,8 +639,10 @@ ns_status ns_orthogonalize_grouped(int count, const void* const* G, const int64_
   }
   const size_t need = ns_grouped_workspace_bytes(count, m, n);
   if (!ws || ws_bytes < need) return NS_ERR_WORKSPACE;
-  for (int i = 0; i < count; ++i)
-    if (overlaps(out[i], (size_t)(m[i] * n[i]) * dtype_size(ot), ws, ws_bytes)) return NS_ERR_ARG;
+  {
+    const ns_status st = check_group(count, G, m, n, gt, out, ot, ws, ws_bytes);
+    if (st != NS_OK) return st;
+  }
   uint8_t* base = static_cast<uint8_t*>(ws);
   const std::vector<size_t> off = group_offsets(count, m, n);
   return run_grouped(count, m, n, as_stream(stream), [&](int i, hipStream_t s) {

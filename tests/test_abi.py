@@ -74,3 +74,68 @@ def test_workspace_sizes_and_validation_on_host():
                           None, other, None, fake, wsg - 1, None) == ns.NS_ERR_WORKSPACE
     # 3072 x 8192 x 3072 has 1536 tiles, six per CU: nothing is split
     assert lib.nvfp4_gemm_workspace_bytes(3072, 8192, 3072, 0) == 0
+
+
+# Distinct fake device addresses, 1 TiB apart (never dereferenced: each call
+# below fails validation before anything is enqueued).
+def _addr(i, off=0):
+    return ctypes.c_void_p((i + 1) * (1 << 40) + off)
+
+
+def test_alignment_and_overlap_are_refused_on_host():
+    ns = pytest.importorskip("newton_schulz_amd")
+    lib = ns._lib
+    qws = lib.nvfp4_quantize_workspace_bytes(64, 64)
+    x, codes, scales, sg, ws = (_addr(i) for i in range(5))
+    # misaligned input / codes / tensor scale
+    assert lib.nvfp4_quantize(_addr(0, 4), 0, 64, 64, 0, codes, scales, sg, ws, qws, None) == ns.NS_ERR_ARG
+    assert lib.nvfp4_quantize(x, 0, 64, 64, 0, _addr(1, 8), scales, sg, ws, qws, None) == ns.NS_ERR_ARG
+    assert lib.nvfp4_quantize_46(x, 0, 64, 64, 1, codes, scales, _addr(3, 2), ws, qws, None) == ns.NS_ERR_ARG
+    # codes inside the input, scales inside the codes, workspace inside the input
+    assert lib.nvfp4_quantize(x, 0, 64, 64, 0, _addr(0, 256), scales, sg, ws, qws, None) == ns.NS_ERR_ARG
+    assert lib.nvfp4_quantize_rht(x, 0, 64, 64, 0, 0x1234, codes, _addr(1, 64), sg, ws, qws,
+                                  None) == ns.NS_ERR_ARG
+    assert lib.nvfp4_quantize(x, 0, 64, 64, 0, codes, scales, sg, _addr(0, 1024), qws, None) == ns.NS_ERR_ARG
+    # dequantize into its own codes
+    assert lib.nvfp4_dequantize(codes, scales, sg, 64, 64, 0, _addr(1, 512), 0, None) == ns.NS_ERR_ARG
+    # GEMM: output over an operand, amax word inside the output, misaligned addend
+    P, PS, Q, QS, SP, SQ, O = (_addr(i) for i in range(7))
+    assert lib.nvfp4_gemm(P, PS, SP, Q, QS, SQ, 64, 64, 256, 0, 1.0, 0.0, None, _addr(2, 4096),
+                          None, None, 0, None) == ns.NS_ERR_ARG
+    assert lib.nvfp4_gemm(P, PS, SP, Q, QS, SQ, 64, 64, 256, 0, 1.0, 0.0, None, O, _addr(6, 64),
+                          None, 0, None) == ns.NS_ERR_ARG
+    assert lib.nvfp4_gemm(P, PS, SP, Q, QS, SQ, 64, 64, 256, 0, 1.0, 1.0, _addr(7, 8), O,
+                          None, None, 0, None) == ns.NS_ERR_ARG
+    # addend partly over the output (equal is allowed, a shifted one is not)
+    assert lib.nvfp4_gemm(P, PS, SP, Q, QS, SQ, 64, 64, 256, 0, 1.0, 1.0, _addr(6, 256), O,
+                          None, None, 0, None) == ns.NS_ERR_ARG
+    # NS: misaligned G, workspace over G
+    coeffs = (ctypes.c_float * 3)(3.4445, -4.775, 2.0315)
+    nws = lib.ns_workspace_bytes(64, 128)
+    assert lib.ns_orthogonalize(_addr(0, 2), 1, 64, 128, coeffs, 1, 1.0, _addr(1), 0, _addr(2), nws,
+                                None) == ns.NS_ERR_ARG
+    assert lib.ns_orthogonalize(_addr(0), 1, 64, 128, coeffs, 1, 1.0, _addr(1), 0, _addr(0, 4096), nws,
+                                None) == ns.NS_ERR_ARG
+    # quantile: misaligned output word
+    aws = lib.ns_abs_quantile_workspace_bytes()
+    assert lib.ns_abs_quantile(_addr(0), 0, 1024, ctypes.c_double(0.99), _addr(1, 1), _addr(2), aws,
+                               None) == ns.NS_ERR_ARG
+
+
+def test_grouped_outputs_must_not_touch_other_problems():
+    ns = pytest.importorskip("newton_schulz_amd")
+    lib = ns._lib
+    coeffs = (ctypes.c_float * 3)(3.4445, -4.775, 2.0315)
+    m = (ctypes.c_int64 * 2)(64, 64)
+    n = (ctypes.c_int64 * 2)(128, 128)
+    clip = (ctypes.c_float * 2)(1.0, 1.0)
+    wsb = lib.ns_grouped_workspace_bytes(2, m, n)
+    G = (ctypes.c_void_p * 2)(_addr(0).value, _addr(1).value)
+    # problem 0 writes over problem 1's input
+    out = (ctypes.c_void_p * 2)(_addr(1).value, _addr(3).value)
+    assert lib.ns_orthogonalize_grouped(2, G, m, n, 1, coeffs, 1, clip, out, 0, _addr(4), wsb,
+                                        None) == ns.NS_ERR_ARG
+    # both problems write the same output
+    out = (ctypes.c_void_p * 2)(_addr(2).value, _addr(2).value)
+    assert lib.ns_orthogonalize_grouped(2, G, m, n, 1, coeffs, 1, clip, out, 0, _addr(4), wsb,
+                                        None) == ns.NS_ERR_ARG
