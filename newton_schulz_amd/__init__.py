@@ -90,9 +90,11 @@ def _torch():
     return torch
 
 
-def _stream(stream):
+def _stream(stream, device=None):
+    """The stream to enqueue on: `stream`, else the current stream of the
+    tensors' device."""
     torch = _torch()
-    s = stream if stream is not None else torch.cuda.current_stream()
+    s = stream if stream is not None else torch.cuda.current_stream(device)
     return ctypes.c_void_p(s.cuda_stream)
 
 
@@ -115,9 +117,33 @@ def _ptr(t):
 
 
 def _need_cuda(*ts):
+    ts = [t for t in ts if t is not None]
     for t in ts:
-        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+        if not t.is_cuda or not t.is_contiguous():
             raise ValueError("tensors must be contiguous device tensors")
+    if any(t.device != ts[0].device for t in ts):
+        raise ValueError("tensors must be on one device")
+
+
+def _need(t, name, dtypes, numel):
+    """A caller-supplied tensor: one of `dtypes` and at least `numel`
+    elements, so that no kernel reads or writes past its end."""
+    if t is None:
+        return
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected one of {dtypes}")
+    if t.numel() < numel:
+        raise ValueError(f"{name}: {t.numel()} elements, at least {numel} needed")
+
+
+def _need_shape(t, name, shape):
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _floats():
+    torch = _torch()
+    return (torch.float32, torch.bfloat16)
 
 
 # ------------------------------------------------------------- quantizer --
@@ -144,11 +170,22 @@ def nvfp4_quantize(x, axis=NVFP4_ROWS, codes=None, scales=None, global_scale=Non
     wsb = _lib.nvfp4_quantize_workspace_bytes(rows, cols)
     if workspace is None:
         workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    _need_quant_outputs(x, rows, cols, codes, scales, global_scale, workspace)
     fn, name = ((_lib.nvfp4_quantize_46, "nvfp4_quantize_46") if adaptive46
                 else (_lib.nvfp4_quantize, "nvfp4_quantize"))
-    _check(fn(_ptr(x), _dt(x), rows, cols, axis, _ptr(codes), _ptr(scales), _ptr(global_scale),
-              _ptr(workspace), workspace.numel(), _stream(stream)), name)
+    with torch.cuda.device(dev):
+        _check(fn(_ptr(x), _dt(x), rows, cols, axis, _ptr(codes), _ptr(scales), _ptr(global_scale),
+                  _ptr(workspace), workspace.numel(), _stream(stream, dev)), name)
     return codes, scales, global_scale
+
+
+def _need_quant_outputs(x, rows, cols, codes, scales, global_scale, workspace):
+    torch = _torch()
+    _need_cuda(x, codes, scales, global_scale, workspace)
+    _need(codes, "codes", (torch.uint8,), rows * cols // 2)
+    _need(scales, "scales", (torch.uint8,), rows * cols // 16)
+    _need(global_scale, "global_scale", (torch.float32,), 1)
+    _need(workspace, "workspace", (torch.uint8,), 0)
 
 
 def nvfp4_quantize_rht(x, mask, axis=NVFP4_ROWS, codes=None, scales=None, global_scale=None,
@@ -170,9 +207,12 @@ def nvfp4_quantize_rht(x, mask, axis=NVFP4_ROWS, codes=None, scales=None, global
     wsb = _lib.nvfp4_quantize_workspace_bytes(rows, cols)
     if workspace is None:
         workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
-    _check(_lib.nvfp4_quantize_rht(_ptr(x), _dt(x), rows, cols, axis, int(mask) & 0xFFFF,
-                                   _ptr(codes), _ptr(scales), _ptr(global_scale), _ptr(workspace),
-                                   workspace.numel(), _stream(stream)), "nvfp4_quantize_rht")
+    _need_quant_outputs(x, rows, cols, codes, scales, global_scale, workspace)
+    with torch.cuda.device(dev):
+        _check(_lib.nvfp4_quantize_rht(_ptr(x), _dt(x), rows, cols, axis, int(mask) & 0xFFFF,
+                                       _ptr(codes), _ptr(scales), _ptr(global_scale),
+                                       _ptr(workspace), workspace.numel(), _stream(stream, dev)),
+               "nvfp4_quantize_rht")
     return codes, scales, global_scale
 
 
@@ -180,11 +220,17 @@ def nvfp4_dequantize(codes, scales, global_scale, rows, cols, axis=NVFP4_ROWS,
                      out_dtype=NS_F32, out=None, stream=None):
     """x_hat = x_E2M1 * s * s_g, in the original rows x cols orientation."""
     torch = _torch()
-    _need_cuda(codes, scales, global_scale)
+    _need_cuda(codes, scales, global_scale, out)
     if out is None:
         out = torch.empty((rows, cols), dtype=_out_dtype(out_dtype), device=codes.device)
-    _check(_lib.nvfp4_dequantize(_ptr(codes), _ptr(scales), _ptr(global_scale), rows, cols, axis,
-                                 _ptr(out), out_dtype, _stream(stream)), "nvfp4_dequantize")
+    _need(codes, "codes", (torch.uint8,), rows * cols // 2)
+    _need(scales, "scales", (torch.uint8,), rows * cols // 16)
+    _need(global_scale, "global_scale", (torch.float32,), 1)
+    _need(out, "out", (_out_dtype(out_dtype),), rows * cols)
+    with torch.cuda.device(codes.device):
+        _check(_lib.nvfp4_dequantize(_ptr(codes), _ptr(scales), _ptr(global_scale), rows, cols,
+                                     axis, _ptr(out), out_dtype, _stream(stream, codes.device)),
+               "nvfp4_dequantize")
     return out
 
 
@@ -212,11 +258,26 @@ def nvfp4_gemm(p, q, M, N, K, symmetric=False, alpha=1.0, beta=0.0, addend=None,
     if workspace is None and split:
         nb = nvfp4_gemm_workspace_bytes(M, N, K, symmetric)
         workspace = torch.empty(max(nb, 1), dtype=torch.uint8, device=pc.device)
+    _need_cuda(pc, workspace)
+    u8 = (torch.uint8,)
+    _need(pc, "p codes", u8, M * K // 2)
+    _need(ps, "p scales", u8, M * K // 16)
+    _need(qc, "q codes", u8, N * K // 2)
+    _need(qs, "q scales", u8, N * K // 16)
+    _need(pg, "p s_g", (torch.float32,), 1)
+    _need(qg, "q s_g", (torch.float32,), 1)
+    _need(out, "out", (torch.float32,), M * N)
+    if float(beta) != 0.0:
+        _need(addend, "addend", (torch.float32,), M * N)
+    _need(amax_out, "amax_out", (torch.int32, torch.uint32), 1)
+    _need(workspace, "workspace", u8, 0)
     wsp, wsn = (_ptr(workspace), workspace.numel()) if workspace is not None else (_ptr(None), 0)
-    _check(_lib.nvfp4_gemm(_ptr(pc), _ptr(ps), _ptr(pg), _ptr(qc), _ptr(qs), _ptr(qg),
-                           M, N, K, 1 if symmetric else 0, float(alpha), float(beta),
-                           _ptr(addend), _ptr(out), _ptr(amax_out), wsp, wsn, _stream(stream)),
-           "nvfp4_gemm")
+    with torch.cuda.device(pc.device):
+        _check(_lib.nvfp4_gemm(_ptr(pc), _ptr(ps), _ptr(pg), _ptr(qc), _ptr(qs), _ptr(qg),
+                               M, N, K, 1 if symmetric else 0, float(alpha), float(beta),
+                               _ptr(addend), _ptr(out), _ptr(amax_out), wsp, wsn,
+                               _stream(stream, pc.device)),
+               "nvfp4_gemm")
     return out
 
 
@@ -224,6 +285,14 @@ def nvfp4_gemm(p, q, M, N, K, symmetric=False, alpha=1.0, beta=0.0, addend=None,
 
 def ns_workspace_bytes(m, n):
     return int(_lib.ns_workspace_bytes(m, n))
+
+
+def _need_ns(G, out, workspace):
+    torch = _torch()
+    _need_cuda(G, out, workspace)
+    _need_shape(out, "out", G.shape)
+    _need(out, "out", _floats(), G.numel())
+    _need(workspace, "workspace", (torch.uint8,), 0)
 
 
 def _coeff_array(coeffs):
@@ -241,10 +310,12 @@ def ns_orthogonalize(G, coeffs, clip=float("inf"), out_dtype=NS_F32, out=None, w
         out = torch.empty((m, n), dtype=_out_dtype(out_dtype), device=G.device)
     if workspace is None:
         workspace = torch.empty(ns_workspace_bytes(m, n), dtype=torch.uint8, device=G.device)
+    _need_ns(G, out, workspace)
     carr, k = _coeff_array(coeffs)
-    _check(_lib.ns_orthogonalize(_ptr(G), _dt(G), m, n, carr, k, float(clip), _ptr(out),
-                                 _dt(out), _ptr(workspace), workspace.numel(), _stream(stream)),
-           "ns_orthogonalize")
+    with torch.cuda.device(G.device):
+        _check(_lib.ns_orthogonalize(_ptr(G), _dt(G), m, n, carr, k, float(clip), _ptr(out),
+                                     _dt(out), _ptr(workspace), workspace.numel(),
+                                     _stream(stream, G.device)), "ns_orthogonalize")
     return out
 
 
@@ -259,13 +330,15 @@ def ns_orthogonalize_rht(G, coeffs, masks, clip=float("inf"), out_dtype=NS_F32, 
         out = torch.empty((m, n), dtype=_out_dtype(out_dtype), device=G.device)
     if workspace is None:
         workspace = torch.empty(ns_workspace_bytes(m, n), dtype=torch.uint8, device=G.device)
+    _need_ns(G, out, workspace)
     carr, k = _coeff_array(coeffs)
     if len(masks) != k:
         raise ValueError("one Hadamard mask per step")
     marr = (ctypes.c_uint16 * k)(*[int(v) & 0xFFFF for v in masks])
-    _check(_lib.ns_orthogonalize_rht(_ptr(G), _dt(G), m, n, carr, k, float(clip), marr, _ptr(out),
-                                     _dt(out), _ptr(workspace), workspace.numel(), _stream(stream)),
-           "ns_orthogonalize_rht")
+    with torch.cuda.device(G.device):
+        _check(_lib.ns_orthogonalize_rht(_ptr(G), _dt(G), m, n, carr, k, float(clip), marr,
+                                         _ptr(out), _dt(out), _ptr(workspace), workspace.numel(),
+                                         _stream(stream, G.device)), "ns_orthogonalize_rht")
     return out
 
 
@@ -281,6 +354,7 @@ def ns_orthogonalize_ex(G, coeffs, clip=float("inf"), clip_quantile=0.0, rht_mas
         out = torch.empty((m, n), dtype=_out_dtype(out_dtype), device=G.device)
     if workspace is None:
         workspace = torch.empty(ns_workspace_bytes(m, n), dtype=torch.uint8, device=G.device)
+    _need_ns(G, out, workspace)
     carr, k = _coeff_array(coeffs)
     opt = NsOptions(float(clip), float(clip_quantile), None, 1 if adaptive46 else 0)
     marr = None
@@ -289,9 +363,10 @@ def ns_orthogonalize_ex(G, coeffs, clip=float("inf"), clip_quantile=0.0, rht_mas
             raise ValueError("one Hadamard mask per step")
         marr = (ctypes.c_uint16 * k)(*[int(v) & 0xFFFF for v in rht_masks])
         opt.rht_masks = ctypes.cast(marr, ctypes.POINTER(ctypes.c_uint16))
-    _check(_lib.ns_orthogonalize_ex(_ptr(G), _dt(G), m, n, carr, k, ctypes.byref(opt), _ptr(out),
-                                    _dt(out), _ptr(workspace), workspace.numel(), _stream(stream)),
-           "ns_orthogonalize_ex")
+    with torch.cuda.device(G.device):
+        _check(_lib.ns_orthogonalize_ex(_ptr(G), _dt(G), m, n, carr, k, ctypes.byref(opt),
+                                        _ptr(out), _dt(out), _ptr(workspace), workspace.numel(),
+                                        _stream(stream, G.device)), "ns_orthogonalize_ex")
     return out
 
 
@@ -308,8 +383,13 @@ def ns_abs_quantile(x, q, out=None, workspace=None, stream=None):
         out = torch.empty(1, dtype=torch.float32, device=x.device)
     if workspace is None:
         workspace = torch.empty(ns_abs_quantile_workspace_bytes(), dtype=torch.uint8, device=x.device)
-    _check(_lib.ns_abs_quantile(_ptr(x), _dt(x), x.numel(), float(q), _ptr(out), _ptr(workspace),
-                                workspace.numel(), _stream(stream)), "ns_abs_quantile")
+    _need_cuda(x, out, workspace)
+    _need(out, "out", (torch.float32,), 1)
+    _need(workspace, "workspace", (torch.uint8,), 0)
+    with torch.cuda.device(x.device):
+        _check(_lib.ns_abs_quantile(_ptr(x), _dt(x), x.numel(), float(q), _ptr(out),
+                                    _ptr(workspace), workspace.numel(), _stream(stream, x.device)),
+               "ns_abs_quantile")
     return out
 
 
@@ -335,16 +415,33 @@ def ns_orthogonalize_grouped(Gs, coeffs, clips, out_dtype=NS_F32, outs=None, wor
     if workspace is None:
         workspace = torch.empty(ns_grouped_workspace_bytes(shapes), dtype=torch.uint8,
                                 device=Gs[0].device)
+    _need_group(Gs, outs, workspace)
+    if len(clips) != cnt:
+        raise ValueError("one clip per matrix")
     gp = (ctypes.c_void_p * cnt)(*[g.data_ptr() for g in Gs])
     op = (ctypes.c_void_p * cnt)(*[o.data_ptr() for o in outs])
     ms = (ctypes.c_int64 * cnt)(*[s[0] for s in shapes])
     ns = (ctypes.c_int64 * cnt)(*[s[1] for s in shapes])
     cl = (ctypes.c_float * cnt)(*[float(c) for c in clips])
     carr, k = _coeff_array(coeffs)
-    _check(_lib.ns_orthogonalize_grouped(cnt, gp, ms, ns, dt, carr, k, cl, op, _dt(outs[0]),
-                                         _ptr(workspace), workspace.numel(), _stream(stream)),
-           "ns_orthogonalize_grouped")
+    dev = Gs[0].device
+    with torch.cuda.device(dev):
+        _check(_lib.ns_orthogonalize_grouped(cnt, gp, ms, ns, dt, carr, k, cl, op, _dt(outs[0]),
+                                             _ptr(workspace), workspace.numel(),
+                                             _stream(stream, dev)), "ns_orthogonalize_grouped")
     return outs
+
+
+def _need_group(Gs, outs, workspace):
+    torch = _torch()
+    if len(Gs) == 0 or len(outs) != len(Gs):
+        raise ValueError("one output per matrix, at least one matrix")
+    _need_cuda(*Gs, *outs, workspace)
+    for i, (g, o) in enumerate(zip(Gs, outs)):
+        _need_shape(o, f"outs[{i}]", g.shape)
+        _need(o, f"outs[{i}]", (outs[0].dtype,), g.numel())
+    _need(outs[0], "outs[0]", _floats(), 0)
+    _need(workspace, "workspace", (torch.uint8,), 0)
 
 
 def ns_orthogonalize_grouped_ex(Gs, coeffs, clips=None, clip_quantile=0.0, rht_masks=None,
@@ -365,6 +462,9 @@ def ns_orthogonalize_grouped_ex(Gs, coeffs, clips=None, clip_quantile=0.0, rht_m
     if workspace is None:
         workspace = torch.empty(ns_grouped_workspace_bytes(shapes), dtype=torch.uint8,
                                 device=Gs[0].device)
+    _need_group(Gs, outs, workspace)
+    if clips is not None and len(clips) != cnt:
+        raise ValueError("one clip per matrix")
     gp = (ctypes.c_void_p * cnt)(*[g.data_ptr() for g in Gs])
     op = (ctypes.c_void_p * cnt)(*[o.data_ptr() for o in outs])
     ms = (ctypes.c_int64 * cnt)(*[s[0] for s in shapes])
@@ -378,7 +478,11 @@ def ns_orthogonalize_grouped_ex(Gs, coeffs, clips=None, clip_quantile=0.0, rht_m
             raise ValueError("one Hadamard mask per step")
         marr = (ctypes.c_uint16 * k)(*[int(v) & 0xFFFF for v in rht_masks])
         opt.rht_masks = ctypes.cast(marr, ctypes.POINTER(ctypes.c_uint16))
-    _check(_lib.ns_orthogonalize_grouped_ex(cnt, gp, ms, ns_, dt, carr, k, cl, ctypes.byref(opt), op,
-                                            _dt(outs[0]), _ptr(workspace), workspace.numel(),
-                                            _stream(stream)), "ns_orthogonalize_grouped_ex")
+    dev = Gs[0].device
+    with torch.cuda.device(dev):
+        _check(_lib.ns_orthogonalize_grouped_ex(cnt, gp, ms, ns_, dt, carr, k, cl,
+                                                ctypes.byref(opt), op, _dt(outs[0]),
+                                                _ptr(workspace), workspace.numel(),
+                                                _stream(stream, dev)),
+               "ns_orthogonalize_grouped_ex")
     return outs
