@@ -102,3 +102,16 @@ def test_ns_with_adaptive46_and_transform():
     masks = synth.rht_masks(3, seed=12)
     got = host(ns.ns_orthogonalize_ex(to_dev_f32(G), coeffs, rht_masks=masks, adaptive46=True))
     _compare(got, G, coeffs, "f32 gaussian 384x768 + H", rht_masks=masks)
+
+
+def test_grouped_with_adaptive46_equals_single_calls():
+    shapes = [(128, 256), (256, 128), (64, 192)]
+    Gs = [to_dev_bf16(synth.to_bf16(synth.student_t(r, c, seed=60 + i))[0])
+          for i, (r, c) in enumerate(shapes)]
+    coeffs = [CUBIC] * 3
+    outs = ns.ns_orthogonalize_grouped_ex(Gs, coeffs, clips=[0.1] * len(shapes), adaptive46=True)
+    for i, (g, o) in enumerate(zip(Gs, outs)):
+        single = host(ns.ns_orthogonalize_ex(g, coeffs, clip=0.1, adaptive46=True))
+        print(f"[ns-46] grouped {shapes[i]} equal to single: {np.array_equal(host(o), single)}",
+              flush=True)
+        assert np.array_equal(host(o), single), shapes[i]
