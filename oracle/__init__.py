@@ -29,8 +29,10 @@ round-trip of exactly representable tensors; idempotence; the per-block error
 bound; the FP64 GEMM against a pure-Python triple loop; the Hadamard matrix
 against its recursive construction, its orthogonality, the transform against
 its definition in plain loops, the FP32 butterfly against the FP64 product,
-and the cancellation of the transform in every NS product; the quantile
-against sorting and the library's inverted-CDF quantile; exact NS against the
+and the cancellation of the transform in every NS product; adaptive 4/6
+block choices against a brute-force rebuild of both candidates over every
+scale byte and code; the quantile against sorting and the library's
+inverted-CDF quantile; exact NS against the
 SVD closed form of its scalar map and, for the cubic, the polar factor; the
 quantized NS against the scalar map on matrices whose quantization is benign.
 The quantized NS on general inputs has no pin beyond the composition of these
