@@ -125,7 +125,7 @@ def source_digest():
 # HBM bytes per launch of the dominant kernel (X = a X + qB qX16^T at
 # 3072 x 8192), from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE, each scaled by
 # what the counter reads for a plain copy of known size; see profiles/.
-DOMINANT_TRAFFIC = {"src_sha256": "e95bf8d599a224372d6cebf9712d34136bd06449a51e46f6cf4535d76aafbd13",
+DOMINANT_TRAFFIC = {"src_sha256": "710595bb7d8b6f9a67073f13966efa3057cd046228de7823023b54d040861f62",
                     "bytes_per_launch": 440303861}
 
 

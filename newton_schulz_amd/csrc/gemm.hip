@@ -835,8 +835,10 @@ __global__ __launch_bounds__(GThreads, 2) void gemm_general_kernel(GemmProblem g
     ti = r;
     tj = r + rem;
   } else {
-    ti = blockIdx.y;
-    tj = blockIdx.x;
+    // one-dimensional grid, row-major over tiles (no 65535 cap on tile rows)
+    const uint32_t tn = (uint32_t)((g.N + GBN - 1) / GBN);
+    ti = blockIdx.x / tn;
+    tj = blockIdx.x % tn;
   }
   const int64_t m0 = ti * GBM, n0 = tj * GBN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -1047,8 +1049,9 @@ hipError_t launch_gemm(const GemmProblem& g, const GemmPlan& p, float* partials,
       const int64_t nt = (g.M + GBM - 1) / GBM;
       gemm_general_kernel<true><<<dim3((unsigned)(nt * (nt + 1) / 2)), GThreads, 0, s>>>(g);
     } else {
-      dim3 grid((unsigned)((g.N + GBN - 1) / GBN), (unsigned)((g.M + GBM - 1) / GBM));
-      gemm_general_kernel<false><<<grid, GThreads, 0, s>>>(g);
+      const int64_t tiles = ((g.N + GBN - 1) / GBN) * ((g.M + GBM - 1) / GBM);
+      if (tiles > INT32_MAX) return hipErrorInvalidValue;
+      gemm_general_kernel<false><<<dim3((unsigned)tiles), GThreads, 0, s>>>(g);
     }
     return hipGetLastError();
   }

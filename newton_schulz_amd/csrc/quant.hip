@@ -4,6 +4,8 @@
 // and §3.4: a per-tensor maximum (first pass, HBM-bound read), then per
 // 16-block an E4M3 scale and sixteen E2M1 codes (second pass).  The exact
 // rounding rules live in nvfp4_device.hpp.
+#include <climits>
+#include <cstdint>
 #include <type_traits>
 
 #include "launch.hpp"
@@ -55,6 +57,25 @@ __device__ __forceinline__ void load16(const void* base, int64_t idx, uint32_t (
       }
     }
   }
+}
+
+// 64x64 tiles on a one-dimensional grid (a second grid dimension would cap
+// the rows at 65535 tiles): workgroup b takes tile row b / tiles_x and tile
+// column b % tiles_x, row-major, the order a two-dimensional grid runs in.
+__device__ __forceinline__ int64_t tile_row0(uint32_t tiles_x) {
+  return (int64_t)(blockIdx.x / tiles_x) * 64;
+}
+__device__ __forceinline__ int64_t tile_col0(uint32_t tiles_x) {
+  return (int64_t)(blockIdx.x % tiles_x) * 64;
+}
+// Tiles per row and the grid of a rows x cols tensor; false if the tile
+// count does not fit a grid.
+inline bool tile_grid(int64_t rows, int64_t cols, uint32_t& tiles_x, uint32_t& grid) {
+  const int64_t tx = (cols + 63) / 64, tiles = tx * ((rows + 63) / 64);
+  if (tiles <= 0 || tiles > INT32_MAX) return false;
+  tiles_x = (uint32_t)tx;
+  grid = (uint32_t)tiles;
+  return true;
 }
 
 __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
@@ -173,20 +194,21 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
 
 template <Dt T, bool ROWS, bool COLS>
 __global__ __launch_bounds__(kThreads) void quant_tile_kernel(
-    const void* x, int64_t rows, int64_t cols, const uint32_t* amax_slot, float* sg_out,
-    uint8_t* row_codes, uint8_t* row_scales, uint8_t* col_codes, uint8_t* col_scales,
-    uint32_t* zero_slot, const uint32_t* amax_c, float* sg_out_c, RhtArg rht) {
+    const void* x, int64_t rows, int64_t cols, uint32_t tiles_x, const uint32_t* amax_slot,
+    float* sg_out, uint8_t* row_codes, uint8_t* row_scales, uint8_t* col_codes,
+    uint8_t* col_scales, uint32_t* zero_slot, const uint32_t* amax_c, float* sg_out_c,
+    RhtArg rht) {
   __shared__ uint32_t tile[64][65];
   const float sg = global_scale_from_amax(amax_read(amax_slot));
   const float sgc = amax_c ? global_scale_from_amax(amax_read(amax_c)) : sg;
-  if (blockIdx.x == 0 && blockIdx.y == 0) {
+  if (blockIdx.x == 0) {
     if (threadIdx.x == 0) {
       if (sg_out) *sg_out = sg;
       if (sg_out_c) *sg_out_c = sgc;
     }
     if (zero_slot) amax_clear(zero_slot);
   }
-  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+  const int64_t r0 = tile_row0(tiles_x), c0 = tile_col0(tiles_x);
   const int tr = threadIdx.x >> 2, tc = (threadIdx.x & 3) * 16;
   const bool in = (r0 + tr < rows) && (c0 + tc < cols);
   uint32_t v[16];
@@ -233,9 +255,10 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(
 // column blocks (H^r^T x, into slot_c), same tiling as quant_tile_kernel.
 template <Dt T>
 __global__ __launch_bounds__(kThreads) void amax_tiles_kernel(
-    const void* x, int64_t rows, int64_t cols, uint32_t* slot_r, uint32_t* slot_c, RhtArg rht) {
+    const void* x, int64_t rows, int64_t cols, uint32_t tiles_x, uint32_t* slot_r,
+    uint32_t* slot_c, RhtArg rht) {
   __shared__ uint32_t tile[64][65];
-  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+  const int64_t r0 = tile_row0(tiles_x), c0 = tile_col0(tiles_x);
   const int tr = threadIdx.x >> 2, tc = (threadIdx.x & 3) * 16;
   const bool in = (r0 + tr < rows) && (c0 + tc < cols);
   uint32_t v[16];
@@ -398,10 +421,10 @@ __global__ __launch_bounds__(kThreads) void dequant_rows_kernel(
 template <Dt O>
 __global__ __launch_bounds__(kThreads) void dequant_cols_kernel(
     const uint8_t* codes, const uint8_t* scales, const float* sgp, int64_t rows, int64_t cols,
-    void* out) {
+    uint32_t tiles_x, void* out) {
   __shared__ float tile[64][65];
   const float sg = *sgp;
-  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+  const int64_t r0 = tile_row0(tiles_x), c0 = tile_col0(tiles_x);
   {
     const int j = threadIdx.x >> 2, b = threadIdx.x & 3;   // column j, row block b
     float u[16];
@@ -463,13 +486,14 @@ hipError_t launch_quant_tiles(const void* x, Dt xt, int64_t rows, int64_t cols,
                               uint8_t* row_scales, uint8_t* col_codes, uint8_t* col_scales,
                               uint32_t* zero_slot, hipStream_t s, const uint32_t* amax_c,
                               float* sg_out_c, RhtArg rht) {
-  dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 63) / 64));
+  uint32_t tiles_x, grid;
+  if (!tile_grid(rows, cols, tiles_x, grid)) return hipErrorInvalidValue;
   const bool R = row_codes != nullptr, C = col_codes != nullptr;
 #define NVFP4_QT(T, RR, CC)                                                                   \
-  quant_tile_kernel<T, RR, CC><<<grid, kThreads, 0, s>>>(x, rows, cols, amax_slot, sg_out,    \
-                                                         row_codes, row_scales, col_codes,    \
-                                                         col_scales, zero_slot, amax_c,       \
-                                                         sg_out_c, rht)
+  quant_tile_kernel<T, RR, CC><<<grid, kThreads, 0, s>>>(x, rows, cols, tiles_x, amax_slot,   \
+                                                         sg_out, row_codes, row_scales,       \
+                                                         col_codes, col_scales, zero_slot,    \
+                                                         amax_c, sg_out_c, rht)
   if (xt == Dt::F32) {
     if (R && C) NVFP4_QT(Dt::F32, true, true);
     else if (R) NVFP4_QT(Dt::F32, true, false);
@@ -485,11 +509,12 @@ hipError_t launch_quant_tiles(const void* x, Dt xt, int64_t rows, int64_t cols,
 
 hipError_t launch_amax_tiles(const void* x, Dt xt, int64_t rows, int64_t cols, uint32_t* slot_r,
                              uint32_t* slot_c, RhtArg rht, hipStream_t s) {
-  dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 63) / 64));
+  uint32_t tiles_x, grid;
+  if (!tile_grid(rows, cols, tiles_x, grid)) return hipErrorInvalidValue;
   if (xt == Dt::F32)
-    amax_tiles_kernel<Dt::F32><<<grid, kThreads, 0, s>>>(x, rows, cols, slot_r, slot_c, rht);
+    amax_tiles_kernel<Dt::F32><<<grid, kThreads, 0, s>>>(x, rows, cols, tiles_x, slot_r, slot_c, rht);
   else
-    amax_tiles_kernel<Dt::BF16><<<grid, kThreads, 0, s>>>(x, rows, cols, slot_r, slot_c, rht);
+    amax_tiles_kernel<Dt::BF16><<<grid, kThreads, 0, s>>>(x, rows, cols, tiles_x, slot_r, slot_c, rht);
   return hipGetLastError();
 }
 
@@ -507,11 +532,12 @@ hipError_t launch_dequant_rows(const uint8_t* codes, const uint8_t* scales, cons
 
 hipError_t launch_dequant_cols(const uint8_t* codes, const uint8_t* scales, const float* sg,
                                int64_t rows, int64_t cols, void* out, Dt ot, hipStream_t s) {
-  dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 63) / 64));
+  uint32_t tiles_x, grid;
+  if (!tile_grid(rows, cols, tiles_x, grid)) return hipErrorInvalidValue;
   if (ot == Dt::F32)
-    dequant_cols_kernel<Dt::F32><<<grid, kThreads, 0, s>>>(codes, scales, sg, rows, cols, out);
+    dequant_cols_kernel<Dt::F32><<<grid, kThreads, 0, s>>>(codes, scales, sg, rows, cols, tiles_x, out);
   else
-    dequant_cols_kernel<Dt::BF16><<<grid, kThreads, 0, s>>>(codes, scales, sg, rows, cols, out);
+    dequant_cols_kernel<Dt::BF16><<<grid, kThreads, 0, s>>>(codes, scales, sg, rows, cols, tiles_x, out);
   return hipGetLastError();
 }
 
