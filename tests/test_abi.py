@@ -139,3 +139,24 @@ def test_grouped_outputs_must_not_touch_other_problems():
     out = (ctypes.c_void_p * 2)(_addr(2).value, _addr(2).value)
     assert lib.ns_orthogonalize_grouped(2, G, m, n, 1, coeffs, 1, clip, out, 0, _addr(4), wsb,
                                         None) == ns.NS_ERR_ARG
+
+
+def test_empty_shapes_are_refused_on_host():
+    """Zero-sized matrices have no NVFP4 blocks: every entry point answers
+    NS_ERR_SHAPE without enqueuing anything."""
+    ns = pytest.importorskip("newton_schulz_amd")
+    lib = ns._lib
+    coeffs = (ctypes.c_float * 3)(3.4445, -4.775, 2.0315)
+    a, b, c, d, e = (_addr(i) for i in range(5))
+    assert lib.ns_workspace_bytes(0, 64) == 0
+    assert lib.ns_orthogonalize(a, 0, 0, 64, coeffs, 1, 1.0, b, 0, c, 1 << 20, None) == ns.NS_ERR_SHAPE
+    assert lib.ns_orthogonalize(a, 0, 64, 0, coeffs, 1, 1.0, b, 0, c, 1 << 20, None) == ns.NS_ERR_SHAPE
+    assert lib.nvfp4_quantize(a, 0, 0, 16, 0, b, c, d, e, 4096, None) == ns.NS_ERR_SHAPE
+    assert lib.nvfp4_dequantize(a, b, c, 16, 0, 0, d, 0, None) == ns.NS_ERR_SHAPE
+    assert lib.nvfp4_gemm(a, b, c, a, b, c, 0, 0, 32, 1, 1.0, 0.0, None, d, None, None, 0,
+                          None) == ns.NS_ERR_SHAPE
+    assert lib.nvfp4_gemm_workspace_bytes(16, 16, 0, 0) == 0
+    assert lib.ns_abs_quantile(a, 0, 0, ctypes.c_double(0.5), b, c, 1 << 20, None) == ns.NS_ERR_SHAPE
+    m = (ctypes.c_int64 * 1)(0)
+    n = (ctypes.c_int64 * 1)(64)
+    assert lib.ns_grouped_workspace_bytes(1, m, n) == 0
