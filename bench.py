@@ -272,7 +272,7 @@ def main():
                               "quantized operand (extra amax passes over the transformed tensors)"}
 
     # the same step with the clip taken on the device as the 0.99 quantile of
-    # |G| (three radix-selection passes over G before the normalisation)
+    # |G| (radix-selection passes over G before the normalisation: two for BF16)
     qstep_ = lambda: ns.ns_orthogonalize_ex(Gd, coeffs, clip_quantile=0.99, out=out, workspace=ws,
                                             stream=stream)
     qms_ = time_events(qstep_, args.steps, args.warmup, stream)

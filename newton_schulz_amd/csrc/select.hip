@@ -6,7 +6,9 @@
 // Magnitudes are ordered by their FP32 bit patterns with the sign cleared
 // (non-finite values as the NaN pattern, above every finite one), so the
 // k-th smallest is found by radix selection on 31-bit keys: three passes
-// over the input fix bits 30..20, 19..9 and 8..0 of the answer.  Each pass
+// over the input fix bits 30..20, 19..9 and 8..0 of the answer.  BF16 keys
+// (widened exactly) have their low 16 bits zero, so for them two passes,
+// bits 30..20 and 19..16, fix every bit that can be set.  Each pass
 // builds per-workgroup LDS histograms of the keys that match the prefix
 // found so far and folds them into a global histogram whose bins sit one
 // 128-byte line apart (atomics on distinct lines proceed in parallel); a
@@ -27,7 +29,8 @@ constexpr int kScanThreads = 1024;   // scan: two bins per thread
 struct Pass {
   int shift, bits;
 };
-constexpr Pass kPasses[3] = {{20, 11}, {9, 11}, {0, 9}};
+constexpr Pass kPassesF32[3] = {{20, 11}, {9, 11}, {0, 9}};
+constexpr Pass kPassesBF16[2] = {{20, 11}, {16, 4}};
 
 __device__ __forceinline__ uint32_t magnitude_key(uint32_t f32_bits) {
   const uint32_t b = f32_bits & 0x7FFFFFFFu;
@@ -134,13 +137,16 @@ hipError_t launch_abs_quantile(const void* x, Dt xt, int64_t n, uint32_t rank, f
   const int64_t nvec = xt == Dt::F32 ? n / 4 : n / 8;
   int64_t grid = (nvec + kThreads * 4 - 1) / (kThreads * 4);
   grid = grid < 1 ? 1 : (grid > kHistBlocks ? kHistBlocks : grid);
-  for (int p = 0; p < 3; ++p) {
-    const Pass ps = kPasses[p];
-    if (xt == Dt::F32)
+  const bool f32 = xt == Dt::F32;
+  const int npass = f32 ? 3 : 2;
+  for (int p = 0; p < npass; ++p) {
+    const Pass ps = f32 ? kPassesF32[p] : kPassesBF16[p];
+    if (f32)
       radix_hist_kernel<Dt::F32><<<(unsigned)grid, kThreads, 0, s>>>(x, n, st, ps.shift, ps.bits, ghist);
     else
       radix_hist_kernel<Dt::BF16><<<(unsigned)grid, kThreads, 0, s>>>(x, n, st, ps.shift, ps.bits, ghist);
-    radix_select_kernel<<<1, kScanThreads, 0, s>>>(st, ghist, ps.shift, ps.bits, p == 2 ? out : nullptr);
+    radix_select_kernel<<<1, kScanThreads, 0, s>>>(st, ghist, ps.shift, ps.bits,
+                                                   p == npass - 1 ? out : nullptr);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

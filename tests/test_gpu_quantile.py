@@ -48,6 +48,13 @@ def test_quantile_ties_zeros_and_nonfinite():
     y[:30] = np.nan
     y[30:60] = -np.inf
     _check(y, to_dev_f32(y), "1.5% non-finite")            # q >= 0.99 reaches NaN
+    # the same inputs in BF16 (whose keys are selected in two radix passes)
+    for label, arr in (("integer ties", x), ("all zero", z), ("1.5% non-finite", y)):
+        bits, vals = synth.to_bf16(arr)
+        _check(vals, to_dev_bf16(bits), f"bf16 {label}")
+    # BF16 magnitudes that differ only in the bits the second pass fixes
+    bits, vals = synth.to_bf16(np.linspace(1.0, 1.0625, 4096, dtype=np.float32))
+    _check(vals, to_dev_bf16(bits), "bf16 one binade")
 
 
 def test_quantile_full_size_gradient():
