@@ -125,7 +125,7 @@ def source_digest():
 # HBM bytes per launch of the dominant kernel (X = a X + qB qX16^T at
 # 3072 x 8192), from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE, each scaled by
 # what the counter reads for a plain copy of known size; see profiles/.
-DOMINANT_TRAFFIC = {"src_sha256": "710595bb7d8b6f9a67073f13966efa3057cd046228de7823023b54d040861f62",
+DOMINANT_TRAFFIC = {"src_sha256": "7f435038b0e46fb324bdd8dd88fe3bd6c95cbcccf18dff94fd4c41c48c7614f4",
                     "bytes_per_launch": 440303861}
 
 

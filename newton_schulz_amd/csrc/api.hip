@@ -119,9 +119,9 @@ NsLayout ns_layout(int64_t m, int64_t n) {
   L.p1 = nvfp4::plan_gemm((int64_t)xm, (int64_t)xm, (int64_t)xn, true, true);
   L.p2 = nvfp4::plan_gemm((int64_t)xm, (int64_t)xm, (int64_t)xm, true, true);
   L.p3 = nvfp4::plan_gemm((int64_t)xm, (int64_t)xn, (int64_t)xm, false, true);
-  size_t part_bytes = 0;
+  size_t part_bytes = 0;   // the products run one after another on one GEMM workspace
   for (const nvfp4::GemmPlan* p : {&L.p1, &L.p2, &L.p3})
-    part_bytes = p->partial_bytes > part_bytes ? p->partial_bytes : part_bytes;
+    part_bytes = p->ws_bytes > part_bytes ? p->ws_bytes : part_bytes;
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes); return at; };
   L.X = take(xm * xn * 4);
@@ -178,7 +178,10 @@ ns_status ns_run(const void* G, ns_dtype gt, int64_t m, int64_t n, const float* 
            *slotXc = slot + 3 * kSlotWords;
   float *sgX = sg, *sgA = sg + 1, *sgB = sg + 2, *sgXc = sg + 3;
 
-  float* gpart = reinterpret_cast<float*>(ws + L.gemm_part);
+  // GEMM workspace; its split-tile counters are zeroed once per call (by
+  // the norm pass below) and every product leaves them zero
+  uint8_t* gws = ws + L.gemm_part;
+  const bool any_split = L.total > L.gemm_part;
 
   // with clip_q > 0 the clip is the q-quantile of |G|, found on the device
   float* clipd = nullptr;
@@ -188,7 +191,9 @@ ns_status ns_run(const void* G, ns_dtype gt, int64_t m, int64_t n, const float* 
                                       ws + L.sel, s));
   }
   NS_TRY(nvfp4::launch_norm_partials(G, (Dt)gt, m * n, clip, clipd, part, s));
-  NS_TRY(nvfp4::launch_norm_finalize(part, inv, slotX, slotA, slotB, s));
+  NS_TRY(nvfp4::launch_norm_finalize(part, inv, slotX, slotA, slotB,
+                                     any_split ? reinterpret_cast<uint32_t*>(gws) : nullptr,
+                                     (int)(nvfp4::kGemmCounterBytes / sizeof(uint32_t)), s));
   NS_TRY(nvfp4::launch_normalize(G, (Dt)gt, xm, xn, tr, clip, clipd, inv, X, slotX, s));
 
   for (int it = 0; it < k; ++it) {
@@ -203,14 +208,14 @@ ns_status ns_run(const void* G, ns_dtype gt, int64_t m, int64_t n, const float* 
                                        ws + L.qt_c, ws + L.qt_s, nullptr, s, slotXc, sgXc, h));
       nvfp4::GemmProblem g1{ws + L.qx_c, ws + L.qx_s, sgX, ws + L.qx_c, ws + L.qx_s, sgX,
                             xm, xm, xn, 1, 1.0f, 0.0f, nullptr, A, nullptr, 0};
-      NS_TRY(nvfp4::launch_gemm(g1, L.p1, gpart, s));
+      NS_TRY(nvfp4::launch_gemm(g1, L.p1, gws, false, s));
       // qA = Q_1x16(A H)
       NS_TRY(nvfp4::launch_amax_tiles(A, Dt::F32, xm, xm, slotA, nullptr, h, s));
       NS_TRY(nvfp4::launch_quant_tiles(A, Dt::F32, xm, xm, slotA, sgA, ws + L.qa_c, ws + L.qa_s,
                                        nullptr, nullptr, nullptr, s, nullptr, nullptr, h));
       nvfp4::GemmProblem g2{ws + L.qa_c, ws + L.qa_s, sgA, ws + L.qa_c, ws + L.qa_s, sgA,
                             xm, xm, xm, 1, c, b, A, B, nullptr, 0};
-      NS_TRY(nvfp4::launch_gemm(g2, L.p2, gpart, s));
+      NS_TRY(nvfp4::launch_gemm(g2, L.p2, gws, false, s));
       // qB = Q_1x16(B H)
       NS_TRY(nvfp4::launch_amax_tiles(B, Dt::F32, xm, xm, slotB, nullptr, h, s));
       NS_TRY(nvfp4::launch_quant_tiles(B, Dt::F32, xm, xm, slotB, sgB, ws + L.qb_c, ws + L.qb_s,
@@ -219,7 +224,7 @@ ns_status ns_run(const void* G, ns_dtype gt, int64_t m, int64_t n, const float* 
       nvfp4::GemmProblem g3{ws + L.qb_c, ws + L.qb_s, sgB, ws + L.qt_c, ws + L.qt_s, sgXc,
                             xm, xn, xm, 0, 1.0f, a, X, direct ? static_cast<float*>(out) : X,
                             nullptr, 0};
-      NS_TRY(nvfp4::launch_gemm(g3, L.p3, gpart, s));
+      NS_TRY(nvfp4::launch_gemm(g3, L.p3, gws, false, s));
       if (direct) return NS_OK;
       continue;
     }
@@ -230,7 +235,7 @@ ns_status ns_run(const void* G, ns_dtype gt, int64_t m, int64_t n, const float* 
     // A = qX qX^T (symmetric, K = xn)
     nvfp4::GemmProblem g1{ws + L.qx_c, ws + L.qx_s, sgX, ws + L.qx_c, ws + L.qx_s, sgX,
                           xm, xm, xn, 1, 1.0f, 0.0f, nullptr, A, slotA, 1};
-    NS_TRY(nvfp4::launch_gemm(g1, L.p1, gpart, s));
+    NS_TRY(nvfp4::launch_gemm(g1, L.p1, gws, false, s));
     // qA = Q_1x16(A); A is exactly symmetric, so Q_16x1(A) = qA^T
     if (a46)   // one thread per block: the tiled quantizer, rows only
       NS_TRY(nvfp4::launch_quant_tiles(A, Dt::F32, xm, xm, slotA, sgA, ws + L.qa_c, ws + L.qa_s,
@@ -242,7 +247,7 @@ ns_status ns_run(const void* G, ns_dtype gt, int64_t m, int64_t n, const float* 
     // B = b A + c qA qA^T (symmetric, K = xm)
     nvfp4::GemmProblem g2{ws + L.qa_c, ws + L.qa_s, sgA, ws + L.qa_c, ws + L.qa_s, sgA,
                           xm, xm, xm, 1, c, b, A, B, slotB, 1};
-    NS_TRY(nvfp4::launch_gemm(g2, L.p2, gpart, s));
+    NS_TRY(nvfp4::launch_gemm(g2, L.p2, gws, false, s));
     // qB = Q_1x16(B)
     if (a46)
       NS_TRY(nvfp4::launch_quant_tiles(B, Dt::F32, xm, xm, slotB, sgB, ws + L.qb_c, ws + L.qb_s,
@@ -257,7 +262,7 @@ ns_status ns_run(const void* G, ns_dtype gt, int64_t m, int64_t n, const float* 
     float* dst = direct ? static_cast<float*>(out) : X;
     nvfp4::GemmProblem g3{ws + L.qb_c, ws + L.qb_s, sgB, ws + L.qt_c, ws + L.qt_s, sgX,
                           xm, xn, xm, 0, 1.0f, a, X, dst, direct ? nullptr : slotX, 1};
-    NS_TRY(nvfp4::launch_gemm(g3, L.p3, gpart, s));
+    NS_TRY(nvfp4::launch_gemm(g3, L.p3, gws, false, s));
     if (direct) return NS_OK;
   }
   NS_TRY(nvfp4::launch_write_out(X, xm, xn, tr, out, (Dt)ot, s));
@@ -436,7 +441,7 @@ ns_status nvfp4_gemm(const uint8_t* codes_p, const uint8_t* scales_p, const floa
   nvfp4::GemmProblem g{codes_p, scales_p, sg_p, codes_q, scales_q, sg_q, M, N, K,
                        symmetric ? 1 : 0, alpha, beta, beta != 0.0f ? addend : nullptr, out,
                        amax_out, 0};
-  NS_TRY(nvfp4::launch_gemm(g, plan, static_cast<float*>(ws), as_stream(stream)));
+  NS_TRY(nvfp4::launch_gemm(g, plan, ws, true, as_stream(stream)));
   return NS_OK;
 }
 

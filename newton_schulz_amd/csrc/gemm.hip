@@ -34,7 +34,9 @@
 // Symmetric products compute only tiles that touch the upper triangle
 // (row <= col); each element there is written once and mirrored.  Tiles
 // left over after one per CU are split along K into parts whose FP32
-// partials a second kernel sums in part order (deterministic); see FastArgs.
+// partials are summed in part order (deterministic): by the part that
+// finishes last, inside the product kernel, when the whole tiles are long
+// enough to hide that work, else by a second kernel; see FastArgs.
 #include "launch.hpp"
 #include "nvfp4_device.hpp"
 
@@ -116,7 +118,18 @@ struct FastArgs {
   float rcp_tm;         // 1 / TM, for the column-major tile order
   int parts;            // K-parts of a leftover tile (1: leftovers run whole)
   float* partials;
+  uint32_t* counters;   // per split tile, K-parts finished; null: a second kernel sums
 };
+
+// The last K-part of a split tile sums the parts inside the product kernel
+// when a whole tile runs at least this many K-stages (the summing and the
+// tile's epilogue then finish while the whole tiles still compute); with
+// fewer, the CU that sums slows the whole tile beside it by more than the
+// second kernel costs (measured: 3072^2 x 8192 gains 9 us, 3072^2 x 3072
+// loses 8 us).
+#ifndef NVFP4_FIXUP_MIN_STAGES
+#define NVFP4_FIXUP_MIN_STAGES 24
+#endif
 
 template <bool B>
 struct BoolTag {
@@ -522,9 +535,13 @@ __device__ __forceinline__ size_t partial_index(int b, int q, int thread) {
   return ((size_t)(b * 4 + q) * C::kThreads + thread) * 4;
 }
 
-template <class C, bool SYM>
+// FIXUP: the last K-part of a split tile sums the parts (a.counters set);
+// otherwise gemm_reduce_kernel does.  Two instantiations, so that products
+// without split tiles keep the plain kernel's code.
+template <class C, bool SYM, bool FIXUP>
 __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_fast_kernel(FastArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::NST * C::kStage];
+  __shared__ uint32_t last_part;
   const GemmProblem& g = a.g;
 
   // ---- work unit: a whole tile or a K-part of a leftover tile (unit_of)
@@ -677,20 +694,97 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_fast_kernel(F
   stage(kc1 - 1, BoolTag<true>{});
 
   if (un.split >= 0) {
-    // K-part of a split tile: store the FP32 partial; gemm_reduce_kernel sums
-    // the parts in order and runs the epilogue (a kernel boundary makes the
-    // partials visible without per-workgroup cache flushes)
     float* part = a.partials + ((size_t)un.split * a.parts + un.part) * C::kAcc * C::kThreads;
+    if constexpr (!FIXUP) {
+      // gemm_reduce_kernel sums the parts in order and runs the epilogue (a
+      // kernel boundary makes the partials visible without cache flushes)
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            *reinterpret_cast<float4*>(part + partial_index<C>(i * C::FN + j, q, threadIdx.x)) =
+                make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                            acc[i][j][4 * q + 3]);
+      return;
+    } else {
+    // Summed here by the part that finishes last.  The partials move with
+    // the sc1 cache policy -- coherent at device scope: a store completes at
+    // the point all XCDs read through and a load reads from there, never a
+    // stale line of the reader's L2 -- so no L2 writeback or invalidation is
+    // needed.  Each part's stores complete (vmcnt 0) before it counts itself
+    // done with a device-scope atomic; the part that sees every other one
+    // done loads their partials after that.
+    constexpr int kSc1 = 16;                          // cache-policy bit sc1
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const uint32_t part_bytes = (uint32_t)(C::kAcc * C::kThreads * 4);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        a.partials + (size_t)un.split * a.parts * C::kAcc * C::kThreads, (short)0,
+        (int)(part_bytes * (uint32_t)a.parts), 0x00020000);
 #pragma unroll
     for (int i = 0; i < C::FM; ++i)
 #pragma unroll
       for (int j = 0; j < C::FN; ++j)
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          *reinterpret_cast<float4*>(part + partial_index<C>(i * C::FN + j, q, threadIdx.x)) =
-              make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                          acc[i][j][4 * q + 3]);
-    return;
+        for (int q = 0; q < 4; ++q) {
+          const u32x4 w = {__float_as_uint(acc[i][j][4 * q]), __float_as_uint(acc[i][j][4 * q + 1]),
+                           __float_as_uint(acc[i][j][4 * q + 2]), __float_as_uint(acc[i][j][4 * q + 3])};
+          __builtin_amdgcn_raw_buffer_store_b128(
+              w, rs, (int)(un.part * part_bytes + 4 * partial_index<C>(i * C::FN + j, q, threadIdx.x)),
+              0, kSc1);
+        }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();                                  // every wave's partial is stored
+    if (threadIdx.x == 0) {
+      const uint32_t done = __hip_atomic_fetch_add(a.counters + un.split, 1u, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+      const bool last = done == (uint32_t)(a.parts - 1);
+      // every other part has counted itself: leave the counter zero for the
+      // next launch
+      if (last) __hip_atomic_store(a.counters + un.split, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      last_part = last ? 1u : 0u;
+    }
+    __syncthreads();
+    if (last_part == 0u) return;
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) {
+        // two quarters of the block at a time: the other parts' values
+        // first (one memory round trip), then the sum in part order, the
+        // order gemm_reduce_kernel uses
+        floatx16 sum = acc[i][j];
+#pragma unroll
+        for (int qq = 0; qq < 4; qq += 2) {
+          u32x4 u[kMaxParts][2];
+#pragma unroll
+          for (int p = 0; p < kMaxParts; ++p)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+              if (p < a.parts && p != un.part)
+                u[p][h] = __builtin_amdgcn_raw_buffer_load_b128(
+                    rs, (int)(p * part_bytes + 4 * partial_index<C>(i * C::FN + j, qq + h, threadIdx.x)),
+                    0, kSc1);
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const int r = 4 * (qq + h) + t;
+              float x = 0.0f;
+#pragma unroll
+              for (int p = 0; p < kMaxParts; ++p) {
+                if (p >= a.parts) break;
+                const float v = p == un.part ? acc[i][j][r] : __uint_as_float(u[p][h][t]);
+                x = p == 0 ? v : x + v;
+              }
+              sum[r] = x;
+            }
+        }
+        acc[i][j] = sum;
+      }
+    if (g.addend) load_addend<C, SYM>(g, m0, n0, wm, wn, lane, ad);
+    }
   }
   epilogue<C, SYM>(g, acc, ad, m0, n0, wm, wn, lane);
 }
@@ -996,16 +1090,23 @@ GemmPlan plan_with(int64_t M, int64_t N, int64_t K, bool symmetric, bool allow_s
   }
   p.units = per_xcd * kXcds;            // the grid
   p.split_tiles = parts > 1 ? split_tiles : 0;
+  p.fixup = parts > 1 && stages >= NVFP4_FIXUP_MIN_STAGES &&
+            (size_t)p.split_tiles * sizeof(uint32_t) <= kGemmCounterBytes;
   if (parts > 1) {
     const size_t part = (size_t)p.split_tiles * parts * C::kAcc * C::kThreads * sizeof(float);
     p.partial_bytes = (part + 255) / 256 * 256;
+    p.ws_bytes = kGemmCounterBytes + p.partial_bytes;
   }
-  p.ws_bytes = p.partial_bytes;
   return p;
 }
 
+__global__ void zero_counters_kernel(uint32_t* c, int n) {
+  for (int i = (int)threadIdx.x; i < n; i += (int)blockDim.x) c[i] = 0u;
+}
+
 template <class C>
-hipError_t launch_with(const GemmProblem& g, const GemmPlan& p, float* partials, hipStream_t s) {
+hipError_t launch_with(const GemmProblem& g, const GemmPlan& p, void* ws, bool zero_counters,
+                       hipStream_t s) {
   FastArgs a;
   a.g = g;
   a.TM = p.TM;
@@ -1013,13 +1114,25 @@ hipError_t launch_with(const GemmProblem& g, const GemmPlan& p, float* partials,
   a.tiles = p.tiles;
   a.rcp_tm = 1.0f / (float)p.TM;
   a.parts = p.splits;
-  a.partials = p.splits > 1 ? partials : nullptr;
-  if (g.symmetric)
-    gemm_fast_kernel<C, true><<<dim3((unsigned)p.units), C::kThreads, 0, s>>>(a);
+  a.partials = p.splits > 1 ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + kGemmCounterBytes)
+                            : nullptr;
+  a.counters = p.fixup ? static_cast<uint32_t*>(ws) : nullptr;
+  if (p.fixup && zero_counters) {
+    zero_counters_kernel<<<1, 256, 0, s>>>(a.counters, (int)p.split_tiles);
+    const hipError_t ez = hipGetLastError();
+    if (ez != hipSuccess) return ez;
+  }
+  const dim3 grid((unsigned)p.units);
+  if (g.symmetric && p.fixup)
+    gemm_fast_kernel<C, true, true><<<grid, C::kThreads, 0, s>>>(a);
+  else if (g.symmetric)
+    gemm_fast_kernel<C, true, false><<<grid, C::kThreads, 0, s>>>(a);
+  else if (p.fixup)
+    gemm_fast_kernel<C, false, true><<<grid, C::kThreads, 0, s>>>(a);
   else
-    gemm_fast_kernel<C, false><<<dim3((unsigned)p.units), C::kThreads, 0, s>>>(a);
+    gemm_fast_kernel<C, false, false><<<grid, C::kThreads, 0, s>>>(a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.splits == 1) return e;
+  if (e != hipSuccess || p.splits == 1 || p.fixup) return e;
   const unsigned rgrid = (unsigned)(p.split_tiles * C::kWaves * C::FM * C::FN);
   if (g.symmetric)
     gemm_reduce_kernel<C, true><<<dim3(rgrid), 64, 0, s>>>(a);
@@ -1043,7 +1156,8 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool symmetric, bool allow_s
   return plan_with<SmallCfg128>(M, N, K, symmetric, allow_split, 3);
 }
 
-hipError_t launch_gemm(const GemmProblem& g, const GemmPlan& p, float* partials, hipStream_t s) {
+hipError_t launch_gemm(const GemmProblem& g, const GemmPlan& p, void* ws, bool zero_counters,
+                       hipStream_t s) {
   if (!p.fast) {
     if (g.symmetric) {
       const int64_t nt = (g.M + GBM - 1) / GBM;
@@ -1056,9 +1170,9 @@ hipError_t launch_gemm(const GemmProblem& g, const GemmPlan& p, float* partials,
     return hipGetLastError();
   }
   switch (p.cfg) {
-    case 0: return launch_with<BigCfg>(g, p, partials, s);
-    case 2: return launch_with<BigCfg128>(g, p, partials, s);
-    default: return launch_with<SmallCfg128>(g, p, partials, s);
+    case 0: return launch_with<BigCfg>(g, p, ws, zero_counters, s);
+    case 2: return launch_with<BigCfg128>(g, p, ws, zero_counters, s);
+    default: return launch_with<SmallCfg128>(g, p, ws, zero_counters, s);
   }
 }
 

@@ -75,20 +75,28 @@ struct GemmProblem {
 
 // Launch plan of one product: the fast path needs K % 128 == 0 and picks a
 // tile shape from the tile count; tiles left over after an equal number per
-// CU may be split along K, which needs a workspace of ws_bytes for the FP32
-// partials.
+// CU may be split along K, which needs a workspace of ws_bytes: a counter
+// region of kGemmCounterBytes (one word per split tile) followed by the FP32
+// partials.  With `fixup` the K-part that finishes last sums the partials
+// inside the product kernel; otherwise a second kernel does.
+constexpr size_t kGemmCounterBytes = 1024;
 struct GemmPlan {
   bool fast;
   int cfg;                // fast-path config: 128 x 128 tiles with 256-wide row-line
                           // stages (0) or 128-wide ones (2), 64 x 128 tiles (3)
   int splits;             // K-parts of each leftover tile (1: none split)
+  bool fixup;             // split tiles summed by their last K-part (no second kernel)
   int64_t TM, TN, tiles;
   int64_t units;          // workgroups of the product kernel
   int64_t split_tiles;    // tiles split into K-parts (0 when splits == 1)
   size_t partial_bytes, ws_bytes;
 };
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool symmetric, bool allow_split);
-hipError_t launch_gemm(const GemmProblem& g, const GemmPlan& p, float* partials, hipStream_t s);
+// ws: the plan's workspace.  The counters must be zero when the product
+// starts; every launch leaves them zero.  zero_counters clears them first
+// (a small kernel) for callers that cannot guarantee that.
+hipError_t launch_gemm(const GemmProblem& g, const GemmPlan& p, void* ws, bool zero_counters,
+                       hipStream_t s);
 
 // ---- quantile of |x| (select.hip) ------------------------------------------
 // State of the radix selection: bits of the answer fixed so far and the rank
@@ -109,9 +117,10 @@ hipError_t launch_abs_quantile(const void* x, Dt xt, int64_t n, uint32_t rank, f
 constexpr int kNormParts = 1024;
 hipError_t launch_norm_partials(const void* G, Dt gt, int64_t n, float clip, const float* clip_dev,
                                 double* part, hipStream_t s);
-// inv[0] = 1 / (sqrt(sum part) + eps); zeroes the listed slots.
+// inv[0] = 1 / (sqrt(sum part) + eps); zeroes the listed slots and the
+// n_words words at `words` (may be null).
 hipError_t launch_norm_finalize(const double* part, double* inv, uint32_t* zero0, uint32_t* zero1,
-                                uint32_t* zero2, hipStream_t s);
+                                uint32_t* zero2, uint32_t* words, int n_words, hipStream_t s);
 // X[m][n] = clamp(G) * inv (G is m x n, or n x m read transposed), amax into slot.
 hipError_t launch_normalize(const void* G, Dt gt, int64_t m, int64_t n, bool transposed,
                             float clip, const float* clip_dev, const double* inv, float* X,

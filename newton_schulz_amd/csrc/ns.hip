@@ -73,7 +73,8 @@ __global__ __launch_bounds__(kThreads) void norm_partials_kernel(const void* G, 
 
 __global__ __launch_bounds__(kThreads) void norm_finalize_kernel(const double* part, double* inv,
                                                                   uint32_t* z0, uint32_t* z1,
-                                                                  uint32_t* z2) {
+                                                                  uint32_t* z2, uint32_t* words,
+                                                                  int n_words) {
   double acc = 0.0;
   for (int i = threadIdx.x; i < kNormParts; i += kThreads) acc += part[i];
   double s = block_sum(acc);
@@ -81,6 +82,7 @@ __global__ __launch_bounds__(kThreads) void norm_finalize_kernel(const double* p
   if (z0) amax_clear(z0);
   if (z1) amax_clear(z1);
   if (z2) amax_clear(z2);
+  for (int i = threadIdx.x; i < n_words; i += kThreads) words[i] = 0u;
 }
 
 // 64 x 64 transposing tiles: a workgroup reads a tile of the source, whose
@@ -233,8 +235,8 @@ hipError_t launch_norm_partials(const void* G, Dt gt, int64_t n, float clip, con
 }
 
 hipError_t launch_norm_finalize(const double* part, double* inv, uint32_t* z0, uint32_t* z1,
-                                uint32_t* z2, hipStream_t s) {
-  norm_finalize_kernel<<<1, kThreads, 0, s>>>(part, inv, z0, z1, z2);
+                                uint32_t* z2, uint32_t* words, int n_words, hipStream_t s) {
+  norm_finalize_kernel<<<1, kThreads, 0, s>>>(part, inv, z0, z1, z2, words, words ? n_words : 0);
   return hipGetLastError();
 }
 

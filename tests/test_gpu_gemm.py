@@ -144,7 +144,8 @@ def test_full_size_gemms_sampled():
 
 def test_symmetric_gemm_split_k():
     """A symmetric product with fewer tiles than CUs: its tiles are split
-    along K into parts whose FP32 partials a second kernel sums in order."""
+    along K into eight parts whose FP32 partials the last part to finish
+    sums in part order inside the product kernel."""
     M, K = 384, 8192
     assert ns.nvfp4_gemm_workspace_bytes(M, M, K, True) > 0       # split schedule
     rng = np.random.default_rng(8)
@@ -165,6 +166,31 @@ def test_symmetric_gemm_split_k():
     got1 = host(ns.nvfp4_gemm(qd, qd, M, M, K, symmetric=True, alpha=0.75, beta=-1.5,
                               addend=to_dev_f32(add), split=False))
     assert rel_fro(got1, got) <= 1e-6
+
+
+def test_split_k_sums_are_deterministic():
+    """3072^2 x 8192 Gram product (the NS step's first product): 44 leftover
+    tiles in five K-parts each, summed by the last part inside the product
+    kernel.  Which part finishes last varies from launch to launch; the sum
+    order does not, so every launch gives the same bits; they also match the
+    oracle on sampled entries."""
+    m, n = 3072, 8192
+    x = synth.gaussian(m, n, seed=23) / np.sqrt(m * n)
+    q = Q.quantize_rows(x)
+    qd = dev_q(q)
+    ws = torch.empty(ns.nvfp4_gemm_workspace_bytes(m, m, n, True), dtype=torch.uint8, device=DEV)
+    out = torch.empty((m, m), dtype=torch.float32, device=DEV)
+    first = host(ns.nvfp4_gemm(qd, qd, m, m, n, symmetric=True, out=out, workspace=ws)).copy()
+    for r in range(12):
+        out.fill_(float("nan"))
+        got = host(ns.nvfp4_gemm(qd, qd, m, m, n, symmetric=True, out=out, workspace=ws))
+        assert np.array_equal(got, first), r
+    print("[gemm] 3072^2 x 8192 split-K: 13 launches bit-identical", flush=True)
+    rng = np.random.default_rng(3)
+    ii, jj = rng.integers(0, m, 256), rng.integers(0, m, 256)
+    dq = Q.dequantize_rows(q)
+    want = np.sum(dq[ii] * dq[jj], axis=1)
+    assert np.linalg.norm(first[ii, jj] - want) <= TOL * np.linalg.norm(want)
 
 
 def test_general_gemm_leftover_tiles_split_k():
