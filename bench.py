@@ -125,7 +125,7 @@ def source_digest():
 # HBM bytes per launch of the dominant kernel (X = a X + qB qX16^T at
 # 3072 x 8192), from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE, each scaled by
 # what the counter reads for a plain copy of known size; see profiles/.
-DOMINANT_TRAFFIC = {"src_sha256": "7f435038b0e46fb324bdd8dd88fe3bd6c95cbcccf18dff94fd4c41c48c7614f4",
+DOMINANT_TRAFFIC = {"src_sha256": "186675f7e74c6ec1db599be6ef0ab33590f0ac902f9a7662c93da504fc152179",
                     "bytes_per_launch": 440303861}
 
 

@@ -103,9 +103,10 @@ struct Cfg {
 // contiguous runs, one per XCD (tiles sharing operand panels share an L2).
 // Within a run of n tiles, the first floor(n / cus) * cus are whole work
 // units -- the same number for every CU -- and each of the remaining
-// n mod cus tiles is split along K into `parts` units whose FP32 partials a
-// second kernel sums in a fixed order, so the leftover work spreads over
-// the CUs instead of doubling some of them.
+// n mod cus tiles is split along K into `parts` units whose FP32 partials
+// are summed in a fixed order (by the last part to finish or by a second
+// kernel, see FastArgs), so the leftover work spreads over the CUs instead
+// of doubling some of them.
 #ifndef NVFP4_MAX_PARTS
 #define NVFP4_MAX_PARTS 8
 #endif
