@@ -108,7 +108,8 @@ constexpr int kSlotWords = nvfp4::kAmaxSlotWords;
 
 // ---- workspace of one Newton–Schulz problem (iterate is xm x xn, xm <= xn)
 struct NsLayout {
-  size_t X, A, B, qx_c, qx_s, qt_c, qt_s, qa_c, qa_s, qb_c, qb_s, sg, slot, part, inv, clip, sel;
+  size_t X, A, B, qx_c, qx_s, qt_c, qt_s, qa_c, qa_s, qb_c, qb_s, sg, slot, part, part_amax, inv,
+      clip, sel;
   size_t gemm_part, total;
   nvfp4::GemmPlan p1, p2, p3;
 };
@@ -138,6 +139,7 @@ NsLayout ns_layout(int64_t m, int64_t n) {
   L.sg = take(4 * sizeof(float));
   L.slot = take(4 * kSlotWords * sizeof(uint32_t));
   L.part = take(nvfp4::kNormParts * sizeof(double));
+  L.part_amax = take(nvfp4::kNormParts * sizeof(uint32_t));
   L.inv = take(sizeof(double));
   L.clip = take(sizeof(float));
   L.sel = take(nvfp4::abs_quantile_workspace_bytes());
@@ -173,6 +175,7 @@ ns_status ns_run(const void* G, ns_dtype gt, int64_t m, int64_t n, const float* 
   float* sg = reinterpret_cast<float*>(ws + L.sg);
   uint32_t* slot = reinterpret_cast<uint32_t*>(ws + L.slot);
   double* part = reinterpret_cast<double*>(ws + L.part);
+  uint32_t* part_amax = reinterpret_cast<uint32_t*>(ws + L.part_amax);
   double* inv = reinterpret_cast<double*>(ws + L.inv);
   uint32_t *slotX = slot, *slotA = slot + kSlotWords, *slotB = slot + 2 * kSlotWords,
            *slotXc = slot + 3 * kSlotWords;
@@ -190,11 +193,14 @@ ns_status ns_run(const void* G, ns_dtype gt, int64_t m, int64_t n, const float* 
     NS_TRY(nvfp4::launch_abs_quantile(G, (Dt)gt, m * n, quantile_rank(clip_q, m * n), clipd,
                                       ws + L.sel, s));
   }
-  NS_TRY(nvfp4::launch_norm_partials(G, (Dt)gt, m * n, clip, clipd, part, s));
-  NS_TRY(nvfp4::launch_norm_finalize(part, inv, slotX, slotA, slotB,
+  NS_TRY(nvfp4::launch_norm_partials(G, (Dt)gt, m * n, clip, clipd, part, part_amax, s));
+  NS_TRY(nvfp4::launch_norm_finalize(part, part_amax, inv, slotX, slotA, slotB,
                                      any_split ? reinterpret_cast<uint32_t*>(gws) : nullptr,
                                      (int)(nvfp4::kGemmCounterBytes / sizeof(uint32_t)), s));
-  NS_TRY(nvfp4::launch_normalize(G, (Dt)gt, xm, xn, tr, clip, clipd, inv, X, slotX, s));
+  // untransformed and untransposed: the first quantization pass also
+  // normalises G into X (max |X| is already in slotX)
+  const bool fused = !masks && !tr;
+  if (!fused) NS_TRY(nvfp4::launch_normalize(G, (Dt)gt, xm, xn, tr, clip, clipd, inv, X, slotX, s));
 
   for (int it = 0; it < k; ++it) {
     const float a = coeffs[3 * it], b = coeffs[3 * it + 1], c = coeffs[3 * it + 2];
@@ -229,9 +235,14 @@ ns_status ns_run(const void* G, ns_dtype gt, int64_t m, int64_t n, const float* 
       continue;
     }
     // qX = Q_1x16(X) and qX16 = Q_16x1(X) (stored as rows of X^T), one s_g
-    NS_TRY(nvfp4::launch_quant_tiles(X, Dt::F32, xm, xn, slotX, sgX, ws + L.qx_c, ws + L.qx_s,
-                                     ws + L.qt_c, ws + L.qt_s, slotA, s, nullptr, nullptr,
-                                     nvfp4::RhtArg{0u, 0u, o46}));
+    if (fused && it == 0)
+      NS_TRY(nvfp4::launch_normalize_quant_tiles(G, (Dt)gt, xm, xn, clip, clipd, inv, X, slotX, sgX,
+                                                 ws + L.qx_c, ws + L.qx_s, ws + L.qt_c,
+                                                 ws + L.qt_s, slotA, a46, s));
+    else
+      NS_TRY(nvfp4::launch_quant_tiles(X, Dt::F32, xm, xn, slotX, sgX, ws + L.qx_c, ws + L.qx_s,
+                                       ws + L.qt_c, ws + L.qt_s, slotA, s, nullptr, nullptr,
+                                       nvfp4::RhtArg{0u, 0u, o46}));
     // A = qX qX^T (symmetric, K = xn)
     nvfp4::GemmProblem g1{ws + L.qx_c, ws + L.qx_s, sgX, ws + L.qx_c, ws + L.qx_s, sgX,
                           xm, xm, xn, 1, 1.0f, 0.0f, nullptr, A, slotA, 1};

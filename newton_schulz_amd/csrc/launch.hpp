@@ -46,6 +46,16 @@ hipError_t launch_quant_tiles(const void* x, Dt xt, int64_t rows, int64_t cols,
                               uint32_t* zero_slot, hipStream_t s,
                               const uint32_t* amax_c = nullptr, float* sg_out_c = nullptr,
                               RhtArg rht = RhtArg{0u, 0u, 0u});
+// The first NS quantization fused with the normalisation: X = clamp(G) * inv
+// (G is rows x cols, the X layout), written to X and quantized in both
+// layouts in the same pass.  amax_slot must already hold max |X| (from
+// launch_norm_finalize); the other arguments as launch_quant_tiles.
+hipError_t launch_normalize_quant_tiles(const void* G, Dt gt, int64_t rows, int64_t cols, float clip,
+                                        const float* clip_dev, const double* inv, float* X,
+                                        const uint32_t* amax_slot, float* sg_out,
+                                        uint8_t* row_codes, uint8_t* row_scales,
+                                        uint8_t* col_codes, uint8_t* col_scales,
+                                        uint32_t* zero_slot, bool adaptive46, hipStream_t s);
 // Maxima of |x H^r| over the row blocks into slot_r and of |H^r^T x| over the
 // column blocks into slot_c (either may be null); the caller zeroes them.
 hipError_t launch_amax_tiles(const void* x, Dt xt, int64_t rows, int64_t cols, uint32_t* slot_r,
@@ -112,15 +122,19 @@ hipError_t launch_abs_quantile(const void* x, Dt xt, int64_t n, uint32_t rank, f
                                void* ws, hipStream_t s);
 
 // ---- Newton–Schulz prologue / epilogue (ns.hip) ---------------------------
-// Partial sums of clamp(G)^2 into part[0..kNormParts).  The clip is the
-// device value *clip_dev when that is given, else `clip`.
+// Partial sums of clamp(G)^2 into part[0..kNormParts) and partial maxima of
+// |clamp(G)| (as bit patterns, non-finite as NaN) into part_amax.  The clip
+// is the device value *clip_dev when that is given, else `clip`.
 constexpr int kNormParts = 1024;
 hipError_t launch_norm_partials(const void* G, Dt gt, int64_t n, float clip, const float* clip_dev,
-                                double* part, hipStream_t s);
+                                double* part, uint32_t* part_amax, hipStream_t s);
 // inv[0] = 1 / (sqrt(sum part) + eps); zeroes the listed slots and the
-// n_words words at `words` (may be null).
-hipError_t launch_norm_finalize(const double* part, double* inv, uint32_t* zero0, uint32_t* zero1,
-                                uint32_t* zero2, uint32_t* words, int n_words, hipStream_t s);
+// n_words words at `words` (may be null), then stores max |X_0| =
+// RN_f32(max |clamp(G)| * inv) -- rounding is monotone, so this is the
+// maximum of the normalised elements -- into the slot zero0.
+hipError_t launch_norm_finalize(const double* part, const uint32_t* part_amax, double* inv,
+                                uint32_t* zero0, uint32_t* zero1, uint32_t* zero2, uint32_t* words,
+                                int n_words, hipStream_t s);
 // X[m][n] = clamp(G) * inv (G is m x n, or n x m read transposed), amax into slot.
 hipError_t launch_normalize(const void* G, Dt gt, int64_t m, int64_t n, bool transposed,
                             float clip, const float* clip_dev, const double* inv, float* X,

@@ -31,9 +31,21 @@ __device__ __forceinline__ double block_sum(double v) {
   return r;
 }
 
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v) {
+  __shared__ uint32_t red[kThreads / 64];
+  v = wave_max_u32(v);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  uint32_t r = 0;
+  if (threadIdx.x == 0)
+    for (int w = 0; w < kThreads / 64; ++w) r = red[w] > r ? red[w] : r;
+  return r;
+}
+
 template <Dt T>
 __global__ __launch_bounds__(kThreads) void norm_partials_kernel(const void* G, int64_t n, float clip,
-                                                                  const float* clip_dev, double* part) {
+                                                                  const float* clip_dev, double* part,
+                                                                  uint32_t* part_amax) {
   if (clip_dev) clip = *clip_dev;
   // 16-byte units (4 FP32 or 8 BF16 values), consecutive lanes on
   // consecutive units, four loads in flight; each thread keeps four FP64
@@ -42,18 +54,27 @@ __global__ __launch_bounds__(kThreads) void norm_partials_kernel(const void* G, 
   constexpr int U = 4;
   const int64_t nu = n / EPU, stride = (int64_t)gridDim.x * kThreads;
   double ch[4] = {0.0, 0.0, 0.0, 0.0};
+  uint32_t amax = 0;
   auto add = [&](uint4 w) {
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       if constexpr (T == Dt::F32) {
-        const double x = (double)clampf(__uint_as_float(ws[t]), clip);
+        const float c = clampf(__uint_as_float(ws[t]), clip);
+        const double x = (double)c;
         ch[t] = fma(x, x, ch[t]);
+        const uint32_t a = abs_bits(c);
+        amax = a > amax ? a : amax;
       } else {
-        const double x0 = (double)clampf(__uint_as_float(ws[t] << 16), clip);
+        const float c0 = clampf(__uint_as_float(ws[t] << 16), clip);
+        const double x0 = (double)c0;
         ch[t] = fma(x0, x0, ch[t]);
-        const double x1 = (double)clampf(__uint_as_float(ws[t] & 0xFFFF0000u), clip);
+        const float c1 = clampf(__uint_as_float(ws[t] & 0xFFFF0000u), clip);
+        const double x1 = (double)c1;
         ch[t] = fma(x1, x1, ch[t]);
+        const uint32_t a0 = abs_bits(c0), a1 = abs_bits(c1);
+        amax = a0 > amax ? a0 : amax;
+        amax = a1 > amax ? a1 : amax;
       }
     }
   };
@@ -68,21 +89,40 @@ __global__ __launch_bounds__(kThreads) void norm_partials_kernel(const void* G, 
   }
   for (; u < nu; u += stride) add(p[u]);
   double s = block_sum((ch[0] + ch[1]) + (ch[2] + ch[3]));
-  if (threadIdx.x == 0) part[blockIdx.x] = s;
+  __syncthreads();
+  const uint32_t m = block_max_u32(amax);
+  if (threadIdx.x == 0) {
+    part[blockIdx.x] = s;
+    part_amax[blockIdx.x] = m;
+  }
 }
 
-__global__ __launch_bounds__(kThreads) void norm_finalize_kernel(const double* part, double* inv,
-                                                                  uint32_t* z0, uint32_t* z1,
-                                                                  uint32_t* z2, uint32_t* words,
-                                                                  int n_words) {
+__global__ __launch_bounds__(kThreads) void norm_finalize_kernel(const double* part,
+                                                                  const uint32_t* part_amax,
+                                                                  double* inv, uint32_t* z0,
+                                                                  uint32_t* z1, uint32_t* z2,
+                                                                  uint32_t* words, int n_words) {
   double acc = 0.0;
-  for (int i = threadIdx.x; i < kNormParts; i += kThreads) acc += part[i];
+  uint32_t am = 0;
+  for (int i = threadIdx.x; i < kNormParts; i += kThreads) {
+    acc += part[i];
+    am = part_amax[i] > am ? part_amax[i] : am;
+  }
   double s = block_sum(acc);
-  if (threadIdx.x == 0) *inv = 1.0 / (sqrt(s) + 1e-7);
+  __syncthreads();
+  am = block_max_u32(am);
   if (z0) amax_clear(z0);
   if (z1) amax_clear(z1);
   if (z2) amax_clear(z2);
   for (int i = threadIdx.x; i < n_words; i += kThreads) words[i] = 0u;
+  if (threadIdx.x == 0) {
+    const double iv = 1.0 / (sqrt(s) + 1e-7);
+    *inv = iv;
+    // max |X_0|: the normalisation of the largest |clamp(G)| (monotone
+    // rounding); a non-finite maximum stays NaN.  Thread 0 cleared partial 0
+    // of z0 above, in program order before this store.
+    if (z0) z0[0] = am >= 0x7F800000u ? kNaNBits : abs_bits((float)((double)__uint_as_float(am) * iv));
+  }
 }
 
 // 64 x 64 transposing tiles: a workgroup reads a tile of the source, whose
@@ -226,17 +266,19 @@ __global__ __launch_bounds__(kThreads) void write_out_tr_kernel(const float* X, 
 }  // namespace
 
 hipError_t launch_norm_partials(const void* G, Dt gt, int64_t n, float clip, const float* clip_dev,
-                                double* part, hipStream_t s) {
+                                double* part, uint32_t* part_amax, hipStream_t s) {
   if (gt == Dt::F32)
-    norm_partials_kernel<Dt::F32><<<kNormParts, kThreads, 0, s>>>(G, n, clip, clip_dev, part);
+    norm_partials_kernel<Dt::F32><<<kNormParts, kThreads, 0, s>>>(G, n, clip, clip_dev, part, part_amax);
   else
-    norm_partials_kernel<Dt::BF16><<<kNormParts, kThreads, 0, s>>>(G, n, clip, clip_dev, part);
+    norm_partials_kernel<Dt::BF16><<<kNormParts, kThreads, 0, s>>>(G, n, clip, clip_dev, part, part_amax);
   return hipGetLastError();
 }
 
-hipError_t launch_norm_finalize(const double* part, double* inv, uint32_t* z0, uint32_t* z1,
-                                uint32_t* z2, uint32_t* words, int n_words, hipStream_t s) {
-  norm_finalize_kernel<<<1, kThreads, 0, s>>>(part, inv, z0, z1, z2, words, words ? n_words : 0);
+hipError_t launch_norm_finalize(const double* part, const uint32_t* part_amax, double* inv,
+                                uint32_t* z0, uint32_t* z1, uint32_t* z2, uint32_t* words,
+                                int n_words, hipStream_t s) {
+  norm_finalize_kernel<<<1, kThreads, 0, s>>>(part, part_amax, inv, z0, z1, z2, words,
+                                              words ? n_words : 0);
   return hipGetLastError();
 }
 

@@ -192,12 +192,28 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
 // by its random Hadamard transform (rht16), and the column layout may take
 // its own tensor scale (amax_c, sg_out_c) since X H and H^T X differ.
 
-template <Dt T, bool ROWS, bool COLS>
+// With NORM the input is G and each loaded value is first normalised,
+// y = RN_f32(clamp(g, -clip, clip) * inv) -- the value the NS normalisation
+// writes -- and X = y is stored beside the codes.
+struct NormArg {
+  float clip;
+  const float* clip_dev;   // device clip, used when not null
+  const double* inv;       // 1 / (||clamp(G)||_F + eps)
+  float* X;
+};
+
+// clamp that lets NaN through
+__device__ __forceinline__ float clamp_nan(float x, float c) {
+  return x > c ? c : (x < -c ? -c : x);
+}
+
+template <Dt T, bool ROWS, bool COLS, bool NORM = false>
 __global__ __launch_bounds__(kThreads) void quant_tile_kernel(
     const void* x, int64_t rows, int64_t cols, uint32_t tiles_x, const uint32_t* amax_slot,
     float* sg_out, uint8_t* row_codes, uint8_t* row_scales, uint8_t* col_codes,
     uint8_t* col_scales, uint32_t* zero_slot, const uint32_t* amax_c, float* sg_out_c,
-    RhtArg rht) {
+    RhtArg rht, NormArg nrm) {
+  static_assert(!NORM || COLS, "the normalised X is written from the LDS tile");
   __shared__ uint32_t tile[64][65];
   const float sg = global_scale_from_amax(amax_read(amax_slot));
   const float sgc = amax_c ? global_scale_from_amax(amax_read(amax_c)) : sg;
@@ -214,6 +230,13 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(
   uint32_t v[16];
   if (in) {
     load16<T>(x, (r0 + tr) * cols + c0 + tc, v);
+    if constexpr (NORM) {
+      const float clip = nrm.clip_dev ? *nrm.clip_dev : nrm.clip;
+      const double inv = *nrm.inv;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        v[i] = __float_as_uint((float)((double)clamp_nan(__uint_as_float(v[i]), clip) * inv));
+    }
   } else {
 #pragma unroll
     for (int i = 0; i < 16; ++i) v[i] = 0u;
@@ -235,6 +258,19 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(
   }
   if constexpr (COLS) {
     __syncthreads();
+    if constexpr (NORM) {
+      // X from the LDS tile: 16 lanes per 256-byte row, so each store
+      // instruction writes whole lines
+      const int u = threadIdx.x & 15;
+#pragma unroll
+      for (int pass = 0; pass < 4; ++pass) {
+        const int r = pass * 16 + (threadIdx.x >> 4);
+        if (r0 + r < rows && c0 + 4 * u < cols)
+          reinterpret_cast<float4*>(nrm.X + (r0 + r) * cols + c0)[u] =
+              make_float4(__uint_as_float(tile[r][4 * u]), __uint_as_float(tile[r][4 * u + 1]),
+                          __uint_as_float(tile[r][4 * u + 2]), __uint_as_float(tile[r][4 * u + 3]));
+      }
+    }
     const int j = threadIdx.x >> 2, b = threadIdx.x & 3;
     if (c0 + j < cols && r0 + 16 * b < rows) {
       uint32_t w[16];
@@ -493,7 +529,7 @@ hipError_t launch_quant_tiles(const void* x, Dt xt, int64_t rows, int64_t cols,
   quant_tile_kernel<T, RR, CC><<<grid, kThreads, 0, s>>>(x, rows, cols, tiles_x, amax_slot,   \
                                                          sg_out, row_codes, row_scales,       \
                                                          col_codes, col_scales, zero_slot,    \
-                                                         amax_c, sg_out_c, rht)
+                                                         amax_c, sg_out_c, rht, NormArg{})
   if (xt == Dt::F32) {
     if (R && C) NVFP4_QT(Dt::F32, true, true);
     else if (R) NVFP4_QT(Dt::F32, true, false);
@@ -504,6 +540,27 @@ hipError_t launch_quant_tiles(const void* x, Dt xt, int64_t rows, int64_t cols,
     else NVFP4_QT(Dt::BF16, false, true);
   }
 #undef NVFP4_QT
+  return hipGetLastError();
+}
+
+hipError_t launch_normalize_quant_tiles(const void* G, Dt gt, int64_t rows, int64_t cols, float clip,
+                                        const float* clip_dev, const double* inv, float* X,
+                                        const uint32_t* amax_slot, float* sg_out,
+                                        uint8_t* row_codes, uint8_t* row_scales,
+                                        uint8_t* col_codes, uint8_t* col_scales,
+                                        uint32_t* zero_slot, bool adaptive46, hipStream_t s) {
+  uint32_t tiles_x, grid;
+  if (!tile_grid(rows, cols, tiles_x, grid)) return hipErrorInvalidValue;
+  const RhtArg o{0u, 0u, adaptive46 ? 1u : 0u};
+  const NormArg nrm{clip, clip_dev, inv, X};
+  if (gt == Dt::F32)
+    quant_tile_kernel<Dt::F32, true, true, true><<<grid, kThreads, 0, s>>>(
+        G, rows, cols, tiles_x, amax_slot, sg_out, row_codes, row_scales, col_codes, col_scales,
+        zero_slot, nullptr, nullptr, o, nrm);
+  else
+    quant_tile_kernel<Dt::BF16, true, true, true><<<grid, kThreads, 0, s>>>(
+        G, rows, cols, tiles_x, amax_slot, sg_out, row_codes, row_scales, col_codes, col_scales,
+        zero_slot, nullptr, nullptr, o, nrm);
   return hipGetLastError();
 }
 
