@@ -168,6 +168,35 @@ def test_symmetric_gemm_split_k():
     assert rel_fro(got1, got) <= 1e-6
 
 
+@pytest.mark.parametrize("M,NC,sym", [(400, 400, True), (400, 272, False)])
+def test_split_k_in_kernel_sum_ragged(M, NC, sym):
+    """K = 8192 (32 K-stages): leftover tiles are summed by their last K-part
+    inside the product kernel; ragged edge tiles, an addend and the fused
+    amax on that path."""
+    K = 8192
+    assert ns.nvfp4_gemm_workspace_bytes(M, NC, K, sym) > 0
+    rng = np.random.default_rng(M + NC)
+    P = rng.standard_normal((M, K))
+    qp = Q.quantize_rows(P)
+    if sym:
+        qq = qp
+        add = rng.standard_normal((M, M))
+        add = (add + add.T).astype(np.float32)
+    else:
+        qq = Q.quantize_rows(rng.standard_normal((NC, K)))
+        add = rng.standard_normal((M, NC)).astype(np.float32)
+    want = N.gemm_nt(Q.dequantize_rows(qp), Q.dequantize_rows(qq))
+    pd = dev_q(qp)
+    qd = pd if sym else dev_q(qq)
+    slot = _amax_slot()
+    got = host(ns.nvfp4_gemm(pd, qd, M, NC, K, symmetric=sym, alpha=0.5, beta=2.0,
+                             addend=to_dev_f32(add), amax_out=slot))
+    assert rel_fro(got, 0.5 * want + 2.0 * add.astype(np.float64)) <= TOL
+    if sym:
+        assert np.array_equal(got, got.T)
+    _check_amax(slot, got)
+
+
 def test_split_k_sums_are_deterministic():
     """3072^2 x 8192 Gram product (the NS step's first product): 44 leftover
     tiles in five K-parts each, summed by the last part inside the product
