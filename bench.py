@@ -125,7 +125,7 @@ def source_digest():
 # HBM bytes per launch of the dominant kernel (X = a X + qB qX16^T at
 # 3072 x 8192), from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE, each scaled by
 # what the counter reads for a plain copy of known size; see profiles/.
-DOMINANT_TRAFFIC = {"src_sha256": "186675f7e74c6ec1db599be6ef0ab33590f0ac902f9a7662c93da504fc152179",
+DOMINANT_TRAFFIC = {"src_sha256": "8ff2245d2a1b57b82273eec7f842a661ee9a45fa1b12cabdecf03297c1bbf1cc",
                     "bytes_per_launch": 440303861}
 
 

@@ -695,8 +695,8 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_fast_kernel(F
   stage(kc1 - 1, BoolTag<true>{});
 
   if (un.split >= 0) {
-    float* part = a.partials + ((size_t)un.split * a.parts + un.part) * C::kAcc * C::kThreads;
     if constexpr (!FIXUP) {
+      float* part = a.partials + ((size_t)un.split * a.parts + un.part) * C::kAcc * C::kThreads;
       // gemm_reduce_kernel sums the parts in order and runs the epilogue (a
       // kernel boundary makes the partials visible without cache flushes)
 #pragma unroll
@@ -710,81 +710,81 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_fast_kernel(F
                             acc[i][j][4 * q + 3]);
       return;
     } else {
-    // Summed here by the part that finishes last.  The partials move with
-    // the sc1 cache policy -- coherent at device scope: a store completes at
-    // the point all XCDs read through and a load reads from there, never a
-    // stale line of the reader's L2 -- so no L2 writeback or invalidation is
-    // needed.  Each part's stores complete (vmcnt 0) before it counts itself
-    // done with a device-scope atomic; the part that sees every other one
-    // done loads their partials after that.
-    constexpr int kSc1 = 16;                          // cache-policy bit sc1
-    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-    const uint32_t part_bytes = (uint32_t)(C::kAcc * C::kThreads * 4);
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        a.partials + (size_t)un.split * a.parts * C::kAcc * C::kThreads, (short)0,
-        (int)(part_bytes * (uint32_t)a.parts), 0x00020000);
+      // Summed here by the part that finishes last.  The partials move with
+      // the sc1 cache policy -- coherent at device scope: a store completes at
+      // the point all XCDs read through and a load reads from there, never a
+      // stale line of the reader's L2 -- so no L2 writeback or invalidation is
+      // needed.  Each part's stores complete (vmcnt 0) before it counts itself
+      // done with a device-scope atomic; the part that sees every other one
+      // done loads their partials after that.
+      constexpr int kSc1 = 16;                          // cache-policy bit sc1
+      typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+      const uint32_t part_bytes = (uint32_t)(C::kAcc * C::kThreads * 4);
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          a.partials + (size_t)un.split * a.parts * C::kAcc * C::kThreads, (short)0,
+          (int)(part_bytes * (uint32_t)a.parts), 0x00020000);   // raw buffer, 32-bit data format
 #pragma unroll
-    for (int i = 0; i < C::FM; ++i)
+      for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-      for (int j = 0; j < C::FN; ++j)
+        for (int j = 0; j < C::FN; ++j)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const u32x4 w = {__float_as_uint(acc[i][j][4 * q]), __float_as_uint(acc[i][j][4 * q + 1]),
-                           __float_as_uint(acc[i][j][4 * q + 2]), __float_as_uint(acc[i][j][4 * q + 3])};
-          __builtin_amdgcn_raw_buffer_store_b128(
-              w, rs, (int)(un.part * part_bytes + 4 * partial_index<C>(i * C::FN + j, q, threadIdx.x)),
-              0, kSc1);
-        }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();                                  // every wave's partial is stored
-    if (threadIdx.x == 0) {
-      const uint32_t done = __hip_atomic_fetch_add(a.counters + un.split, 1u, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT);
-      const bool last = done == (uint32_t)(a.parts - 1);
-      // every other part has counted itself: leave the counter zero for the
-      // next launch
-      if (last) __hip_atomic_store(a.counters + un.split, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      last_part = last ? 1u : 0u;
-    }
-    __syncthreads();
-    if (last_part == 0u) return;
+          for (int q = 0; q < 4; ++q) {
+            const u32x4 w = {__float_as_uint(acc[i][j][4 * q]), __float_as_uint(acc[i][j][4 * q + 1]),
+                             __float_as_uint(acc[i][j][4 * q + 2]), __float_as_uint(acc[i][j][4 * q + 3])};
+            __builtin_amdgcn_raw_buffer_store_b128(
+                w, rs, (int)(un.part * part_bytes + 4 * partial_index<C>(i * C::FN + j, q, threadIdx.x)),
+                0, kSc1);
+          }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();                                  // every wave's partial is stored
+      if (threadIdx.x == 0) {
+        const uint32_t done = __hip_atomic_fetch_add(a.counters + un.split, 1u, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+        const bool last = done == (uint32_t)(a.parts - 1);
+        // every other part has counted itself: leave the counter zero for the
+        // next launch
+        if (last) __hip_atomic_store(a.counters + un.split, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last_part = last ? 1u : 0u;
+      }
+      __syncthreads();
+      if (last_part == 0u) return;
 #pragma unroll
-    for (int i = 0; i < C::FM; ++i)
+      for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-      for (int j = 0; j < C::FN; ++j) {
-        // two quarters of the block at a time: the other parts' values
-        // first (one memory round trip), then the sum in part order, the
-        // order gemm_reduce_kernel uses
-        floatx16 sum = acc[i][j];
+        for (int j = 0; j < C::FN; ++j) {
+          // two quarters of the block at a time: the other parts' values
+          // first (one memory round trip), then the sum in part order, the
+          // order gemm_reduce_kernel uses
+          floatx16 sum = acc[i][j];
 #pragma unroll
-        for (int qq = 0; qq < 4; qq += 2) {
-          u32x4 u[kMaxParts][2];
+          for (int qq = 0; qq < 4; qq += 2) {
+            u32x4 u[kMaxParts][2];
 #pragma unroll
-          for (int p = 0; p < kMaxParts; ++p)
+            for (int p = 0; p < kMaxParts; ++p)
+#pragma unroll
+              for (int h = 0; h < 2; ++h)
+                if (p < a.parts && p != un.part)
+                  u[p][h] = __builtin_amdgcn_raw_buffer_load_b128(
+                      rs, (int)(p * part_bytes + 4 * partial_index<C>(i * C::FN + j, qq + h, threadIdx.x)),
+                      0, kSc1);
 #pragma unroll
             for (int h = 0; h < 2; ++h)
-              if (p < a.parts && p != un.part)
-                u[p][h] = __builtin_amdgcn_raw_buffer_load_b128(
-                    rs, (int)(p * part_bytes + 4 * partial_index<C>(i * C::FN + j, qq + h, threadIdx.x)),
-                    0, kSc1);
 #pragma unroll
-          for (int h = 0; h < 2; ++h)
+              for (int t = 0; t < 4; ++t) {
+                const int r = 4 * (qq + h) + t;
+                float x = 0.0f;
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              const int r = 4 * (qq + h) + t;
-              float x = 0.0f;
-#pragma unroll
-              for (int p = 0; p < kMaxParts; ++p) {
-                if (p >= a.parts) break;
-                const float v = p == un.part ? acc[i][j][r] : __uint_as_float(u[p][h][t]);
-                x = p == 0 ? v : x + v;
+                for (int p = 0; p < kMaxParts; ++p) {
+                  if (p >= a.parts) break;
+                  const float v = p == un.part ? acc[i][j][r] : __uint_as_float(u[p][h][t]);
+                  x = p == 0 ? v : x + v;
+                }
+                sum[r] = x;
               }
-              sum[r] = x;
-            }
+          }
+          acc[i][j] = sum;
         }
-        acc[i][j] = sum;
-      }
-    if (g.addend) load_addend<C, SYM>(g, m0, n0, wm, wn, lane, ad);
+      if (g.addend) load_addend<C, SYM>(g, m0, n0, wm, wn, lane, ad);
     }
   }
   epilogue<C, SYM>(g, acc, ad, m0, n0, wm, wn, lane);
