@@ -123,13 +123,13 @@ struct FastArgs {
 };
 
 // The last K-part of a split tile sums the parts inside the product kernel
-// when a whole tile runs at least this many K-stages (the summing and the
-// tile's epilogue then finish while the whole tiles still compute); with
-// fewer, the CU that sums slows the whole tile beside it by more than the
-// second kernel costs (measured: 3072^2 x 8192 gains 9 us, 3072^2 x 3072
-// loses 8 us).
+// when a whole tile runs at least this many K-stages; the summing then
+// overlaps the whole tiles' K-loops.  With fewer stages the summing CU
+// slows the whole tile beside it by about what the second kernel costs
+// (measured, against the reduce kernel: 3072^2 x 8192 (32 stages) gains
+// 11 us, 3072^2 x 3072 (12 stages) 3 us).
 #ifndef NVFP4_FIXUP_MIN_STAGES
-#define NVFP4_FIXUP_MIN_STAGES 24
+#define NVFP4_FIXUP_MIN_STAGES 12
 #endif
 
 template <bool B>
@@ -748,42 +748,43 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_fast_kernel(F
       }
       __syncthreads();
       if (last_part == 0u) return;
+      // part by part in part order: a part's whole partial (16 loads in
+      // flight) is added to the running sum; this part's own values come
+      // from registers.  sum = p0, then sum += p1, += p2, ... as
+      // gemm_reduce_kernel adds them.
+      floatx16 sum[C::FM][C::FN];
+      for (int p = 0; p < a.parts; ++p) {
+        floatx16 v[C::FM][C::FN];
+        if (p == un.part) {
+#pragma unroll
+          for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j) v[i][j] = acc[i][j];
+        } else {
+#pragma unroll
+          for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(
+                    rs, (int)(p * part_bytes + 4 * partial_index<C>(i * C::FN + j, q, threadIdx.x)),
+                    0, kSc1);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) v[i][j][4 * q + t] = __uint_as_float(w[t]);
+              }
+        }
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+          for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sum[i][j][r] = p == 0 ? v[i][j][r] : sum[i][j][r] + v[i][j][r];
+      }
 #pragma unroll
       for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-        for (int j = 0; j < C::FN; ++j) {
-          // two quarters of the block at a time: the other parts' values
-          // first (one memory round trip), then the sum in part order, the
-          // order gemm_reduce_kernel uses
-          floatx16 sum = acc[i][j];
-#pragma unroll
-          for (int qq = 0; qq < 4; qq += 2) {
-            u32x4 u[kMaxParts][2];
-#pragma unroll
-            for (int p = 0; p < kMaxParts; ++p)
-#pragma unroll
-              for (int h = 0; h < 2; ++h)
-                if (p < a.parts && p != un.part)
-                  u[p][h] = __builtin_amdgcn_raw_buffer_load_b128(
-                      rs, (int)(p * part_bytes + 4 * partial_index<C>(i * C::FN + j, qq + h, threadIdx.x)),
-                      0, kSc1);
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-              for (int t = 0; t < 4; ++t) {
-                const int r = 4 * (qq + h) + t;
-                float x = 0.0f;
-#pragma unroll
-                for (int p = 0; p < kMaxParts; ++p) {
-                  if (p >= a.parts) break;
-                  const float v = p == un.part ? acc[i][j][r] : __uint_as_float(u[p][h][t]);
-                  x = p == 0 ? v : x + v;
-                }
-                sum[r] = x;
-              }
-          }
-          acc[i][j] = sum;
-        }
+        for (int j = 0; j < C::FN; ++j) acc[i][j] = sum[i][j];
       if (g.addend) load_addend<C, SYM>(g, m0, n0, wm, wn, lane, ad);
     }
   }

@@ -197,6 +197,31 @@ def test_split_k_in_kernel_sum_ragged(M, NC, sym):
     _check_amax(slot, got)
 
 
+@pytest.mark.parametrize("M,NC,sym", [(384, 384, True), (384, 640, False)])
+def test_split_k_reduce_kernel_path(M, NC, sym):
+    """K = 2048 (8 K-stages): too short for the in-kernel sum, the K-parts'
+    partials go through gemm_reduce_kernel."""
+    K = 2048
+    assert ns.nvfp4_gemm_workspace_bytes(M, NC, K, sym) > 0
+    rng = np.random.default_rng(M + NC + 1)
+    qp = Q.quantize_rows(rng.standard_normal((M, K)))
+    qq = qp if sym else Q.quantize_rows(rng.standard_normal((NC, K)))
+    add = rng.standard_normal((M, NC))
+    if sym:
+        add = add + add.T
+    add = add.astype(np.float32)
+    want = N.gemm_nt(Q.dequantize_rows(qp), Q.dequantize_rows(qq))
+    pd = dev_q(qp)
+    qd = pd if sym else dev_q(qq)
+    slot = _amax_slot()
+    got = host(ns.nvfp4_gemm(pd, qd, M, NC, K, symmetric=sym, alpha=-1.0, beta=0.25,
+                             addend=to_dev_f32(add), amax_out=slot))
+    assert rel_fro(got, -want + 0.25 * add.astype(np.float64)) <= TOL
+    if sym:
+        assert np.array_equal(got, got.T)
+    _check_amax(slot, got)
+
+
 def test_split_k_sums_are_deterministic():
     """3072^2 x 8192 Gram product (the NS step's first product): 44 leftover
     tiles in five K-parts each, summed by the last part inside the product
@@ -224,8 +249,9 @@ def test_split_k_sums_are_deterministic():
 
 def test_general_gemm_leftover_tiles_split_k():
     """A non-symmetric product whose tiles do not divide evenly over the CUs:
-    the leftover tiles run as K-parts (partials summed in order), the rest
-    whole; it matches the oracle and the unsplit run."""
+    the leftover tiles run as K-parts (partials summed in order by the last
+    part, 16 K-stages), the rest whole; it matches the oracle and the
+    unsplit run."""
     M, NC, K = 384, 640, 4096
     assert ns.nvfp4_gemm_workspace_bytes(M, NC, K, False) > 0
     rng = np.random.default_rng(9)
