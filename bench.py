@@ -125,7 +125,7 @@ def source_digest():
 # HBM bytes per launch of the dominant kernel (X = a X + qB qX16^T at
 # 3072 x 8192), from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE, each scaled by
 # what the counter reads for a plain copy of known size; see profiles/.
-DOMINANT_TRAFFIC = {"src_sha256": "809419f2c689d6f01d20fb78644f914ff787bd4aa7f8846aa94ad0b0f0b37ef1",
+DOMINANT_TRAFFIC = {"src_sha256": "363d1c41511f59121901871fb4283f57ea55485230a150b1c2893897923e7e5c",
                     "bytes_per_launch": 440303861}
 
 

@@ -243,30 +243,24 @@ ns_status ns_run(const void* G, ns_dtype gt, int64_t m, int64_t n, const float* 
       NS_TRY(nvfp4::launch_quant_tiles(X, Dt::F32, xm, xn, slotX, sgX, ws + L.qx_c, ws + L.qx_s,
                                        ws + L.qt_c, ws + L.qt_s, slotA, s, nullptr, nullptr,
                                        nvfp4::RhtArg{0u, 0u, o46}));
-    // A = qX qX^T (symmetric, K = xn)
+    // A = qX qX^T (symmetric, K = xn); only its upper triangle is stored
+    // (and the diagonal tiles whole), which is all that its quantizer and
+    // the addend of the next product read
     nvfp4::GemmProblem g1{ws + L.qx_c, ws + L.qx_s, sgX, ws + L.qx_c, ws + L.qx_s, sgX,
-                          xm, xm, xn, 1, 1.0f, 0.0f, nullptr, A, slotA, 1};
+                          xm, xm, xn, 1, 1.0f, 0.0f, nullptr, A, slotA, 1, 1};
     NS_TRY(nvfp4::launch_gemm(g1, L.p1, gws, false, s));
-    // qA = Q_1x16(A); A is exactly symmetric, so Q_16x1(A) = qA^T
-    if (a46)   // one thread per block: the tiled quantizer, rows only
-      NS_TRY(nvfp4::launch_quant_tiles(A, Dt::F32, xm, xm, slotA, sgA, ws + L.qa_c, ws + L.qa_s,
-                                       nullptr, nullptr, slotB, s, nullptr, nullptr,
-                                       nvfp4::RhtArg{0u, 0u, 1u}));
-    else
-      NS_TRY(nvfp4::launch_quant_rows(A, Dt::F32, xm, xm, slotA, sgA, ws + L.qa_c, ws + L.qa_s,
-                                      slotB, s));
-    // B = b A + c qA qA^T (symmetric, K = xm)
+    // qA = Q_1x16(A) from the tiles on and above the diagonal (A is exactly
+    // symmetric: the rows of a lower tile are the columns of an upper one,
+    // and Q_16x1(A) = qA^T)
+    NS_TRY(nvfp4::launch_quant_sym_tiles(A, xm, slotA, sgA, ws + L.qa_c, ws + L.qa_s, slotB, a46,
+                                         s));
+    // B = b A + c qA qA^T (symmetric, K = xm), upper triangle as for A
     nvfp4::GemmProblem g2{ws + L.qa_c, ws + L.qa_s, sgA, ws + L.qa_c, ws + L.qa_s, sgA,
-                          xm, xm, xm, 1, c, b, A, B, slotB, 1};
+                          xm, xm, xm, 1, c, b, A, B, slotB, 1, 1};
     NS_TRY(nvfp4::launch_gemm(g2, L.p2, gws, false, s));
-    // qB = Q_1x16(B)
-    if (a46)
-      NS_TRY(nvfp4::launch_quant_tiles(B, Dt::F32, xm, xm, slotB, sgB, ws + L.qb_c, ws + L.qb_s,
-                                       nullptr, nullptr, slotX, s, nullptr, nullptr,
-                                       nvfp4::RhtArg{0u, 0u, 1u}));
-    else
-      NS_TRY(nvfp4::launch_quant_rows(B, Dt::F32, xm, xm, slotB, sgB, ws + L.qb_c, ws + L.qb_s,
-                                      slotX, s));
+    // qB = Q_1x16(B), likewise
+    NS_TRY(nvfp4::launch_quant_sym_tiles(B, xm, slotB, sgB, ws + L.qb_c, ws + L.qb_s, slotX, a46,
+                                         s));
     // X' = a X + qB qX16 (K = xm), in place; the last step of an FP32,
     // untransposed call writes straight into `out` (no copy pass)
     const bool direct = it == k - 1 && !tr && ot == NS_F32;

@@ -348,6 +348,7 @@ struct EpCtx {
   int64_t m0, n0;       // tile origin
   int dr0, dc0;         // this lane's first row / column inside the tile
   bool fast;            // tile wholly inside the matrix and above the diagonal
+  bool mirror;          // symmetric: store the transpose below the diagonal
 };
 
 template <class C, bool SYM>
@@ -364,6 +365,7 @@ __device__ __forceinline__ EpCtx epilogue_ctx(const GemmProblem& g, int64_t m0, 
   const bool inside = m0 + C::BM <= g.M && n0 + C::BN <= g.N;
   const bool upper = !SYM || (m0 + C::BM <= n0);        // every element has row < col
   e.fast = inside && upper;
+  e.mirror = !(g.upper_only && m0 + C::BM <= n0);
   return e;
 }
 
@@ -421,8 +423,11 @@ __device__ __forceinline__ void epilogue_block(const GemmProblem& g, const EpCtx
     }
     if constexpr (SYM) {
       // mirror: rows dr..dr+3 of column c become 4 consecutive floats
+      // (none for a tile above the diagonal of an upper_only product)
       const int moff = mo + (j * 32) * N + i * 32 + 8 * q;
-      if (e.fast) {
+      if (!e.mirror) {
+        // lower triangle not stored
+      } else if (e.fast) {
         *reinterpret_cast<float4*>(mtile + moff) = make_float4(v4[0], v4[1], v4[2], v4[3]);
       } else {
 #pragma unroll
@@ -436,7 +441,8 @@ __device__ __forceinline__ void epilogue_block(const GemmProblem& g, const EpCtx
 }
 
 // out = beta * addend + alpha * sgP * sgQ * acc for the tile at (m0, n0);
-// symmetric products write row <= col and mirror row < col.  amax of the
+// symmetric products write row <= col and mirror row < col (with
+// upper_only, only inside the tiles that touch the diagonal).  amax of the
 // written values goes to amax_out.  Offsets inside a tile are 32-bit
 // (BM * N < 2^31 is checked at the API); tiles wholly inside the matrix
 // (and, if symmetric, wholly above the diagonal) skip the per-element tests.
@@ -484,6 +490,7 @@ __device__ __forceinline__ void epilogue(const GemmProblem& g, floatx16 (&acc)[C
   float* mbase = g.out + c0 * g.N + r0;                // mirror: (col, row)
   const bool inside = m0 + C::BM <= g.M && n0 + C::BN <= g.N;
   const bool upper = !SYM || (m0 + C::BM <= n0);       // every element has row < col
+  const bool mirror = !(upper && g.upper_only);
   auto valid = [&](int dr, int j) {
     if (inside && upper) return true;
     const int64_t row = r0 + dr, col = c0 + j * 32;
@@ -513,7 +520,9 @@ __device__ __forceinline__ void epilogue(const GemmProblem& g, floatx16 (&acc)[C
         if constexpr (SYM) {
           // mirror: rows r0+dr..+3 of column c become 4 consecutive floats
           const int moff = (j * 32) * N + i * 32 + 8 * q;
-          if (inside && upper) {
+          if (!mirror) {
+            // upper_only: lower triangle not stored
+          } else if (inside && upper) {
             *reinterpret_cast<float4*>(mbase + moff) = make_float4(v4[0], v4[1], v4[2], v4[3]);
           } else {
 #pragma unroll

@@ -34,6 +34,13 @@ hipError_t launch_quant_rows(const void* x, Dt xt, int64_t rows, int64_t cols,
                              uint8_t* codes, uint8_t* scales, uint32_t* zero_slot,
                              hipStream_t s);
 
+// Q_1x16 of a symmetric m x m FP32 matrix of which only the tiles on or
+// above the diagonal (64 x 64) are read: the column blocks of tile (I, J)
+// are the row blocks of tile (J, I).
+hipError_t launch_quant_sym_tiles(const float* x, int64_t m, const uint32_t* amax_slot,
+                                  float* sg_out, uint8_t* codes, uint8_t* scales,
+                                  uint32_t* zero_slot, bool adaptive46, hipStream_t s);
+
 // Q_1x16 and/or Q_16x1 of a rows x cols matrix through 64x64 LDS tiles, one
 // read of x for both layouts.  Either output pair may be null.  The column
 // layout takes its s_g from amax_c / sg_out_c when given (else the row
@@ -81,6 +88,8 @@ struct GemmProblem {
   float* out;
   uint32_t* amax_out;
   int amax_parts;   // amax_out is an amax slot of partials (1) or one word (0)
+  int upper_only;   // symmetric: tiles wholly above the diagonal skip their
+                   // mirror (only row <= col and the diagonal tiles are stored)
 };
 
 // Launch plan of one product: the fast path needs K % 128 == 0 and picks a

@@ -195,6 +195,13 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
 // With NORM the input is G and each loaded value is first normalised,
 // y = RN_f32(clamp(g, -clip, clip) * inv) -- the value the NS normalisation
 // writes -- and X = y is stored beside the codes.
+// With `sym` the input is a symmetric square matrix of which only the tiles
+// on or above the diagonal are read (the GEMM left the rest unwritten):
+// tile (I, J), I < J, encodes its rows into the row layout at (I, J) and its
+// columns into the row layout at (J, I), which holds the same blocks since
+// tile (J, I) is the transpose of tile (I, J); col_codes and col_scales are
+// then the row buffers themselves, and a diagonal tile encodes its rows only.
+
 struct NormArg {
   float clip;
   const float* clip_dev;   // device clip, used when not null
@@ -212,7 +219,7 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(
     const void* x, int64_t rows, int64_t cols, uint32_t tiles_x, const uint32_t* amax_slot,
     float* sg_out, uint8_t* row_codes, uint8_t* row_scales, uint8_t* col_codes,
     uint8_t* col_scales, uint32_t* zero_slot, const uint32_t* amax_c, float* sg_out_c,
-    RhtArg rht, NormArg nrm) {
+    RhtArg rht, NormArg nrm, uint32_t sym) {
   static_assert(!NORM || COLS, "the normalised X is written from the LDS tile");
   __shared__ uint32_t tile[64][65];
   const float sg = global_scale_from_amax(amax_read(amax_slot));
@@ -225,6 +232,7 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(
     if (zero_slot) amax_clear(zero_slot);
   }
   const int64_t r0 = tile_row0(tiles_x), c0 = tile_col0(tiles_x);
+  if (sym && r0 > c0) return;   // below the diagonal: done by tile (J, I)
   const int tr = threadIdx.x >> 2, tc = (threadIdx.x & 3) * 16;
   const bool in = (r0 + tr < rows) && (c0 + tc < cols);
   uint32_t v[16];
@@ -272,7 +280,7 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(
       }
     }
     const int j = threadIdx.x >> 2, b = threadIdx.x & 3;
-    if (c0 + j < cols && r0 + 16 * b < rows) {
+    if (c0 + j < cols && r0 + 16 * b < rows && !(sym && r0 == c0)) {
       uint32_t w[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) w[i] = tile[16 * b + i][j];
@@ -529,7 +537,7 @@ hipError_t launch_quant_tiles(const void* x, Dt xt, int64_t rows, int64_t cols,
   quant_tile_kernel<T, RR, CC><<<grid, kThreads, 0, s>>>(x, rows, cols, tiles_x, amax_slot,   \
                                                          sg_out, row_codes, row_scales,       \
                                                          col_codes, col_scales, zero_slot,    \
-                                                         amax_c, sg_out_c, rht, NormArg{})
+                                                         amax_c, sg_out_c, rht, NormArg{}, 0u)
   if (xt == Dt::F32) {
     if (R && C) NVFP4_QT(Dt::F32, true, true);
     else if (R) NVFP4_QT(Dt::F32, true, false);
@@ -540,6 +548,17 @@ hipError_t launch_quant_tiles(const void* x, Dt xt, int64_t rows, int64_t cols,
     else NVFP4_QT(Dt::BF16, false, true);
   }
 #undef NVFP4_QT
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_sym_tiles(const float* x, int64_t m, const uint32_t* amax_slot,
+                                  float* sg_out, uint8_t* codes, uint8_t* scales,
+                                  uint32_t* zero_slot, bool adaptive46, hipStream_t s) {
+  uint32_t tiles_x, grid;
+  if (!tile_grid(m, m, tiles_x, grid)) return hipErrorInvalidValue;
+  quant_tile_kernel<Dt::F32, true, true><<<grid, kThreads, 0, s>>>(
+      x, m, m, tiles_x, amax_slot, sg_out, codes, scales, codes, scales, zero_slot, nullptr,
+      nullptr, RhtArg{0u, 0u, adaptive46 ? 1u : 0u}, NormArg{}, 1u);
   return hipGetLastError();
 }
 
@@ -556,11 +575,11 @@ hipError_t launch_normalize_quant_tiles(const void* G, Dt gt, int64_t rows, int6
   if (gt == Dt::F32)
     quant_tile_kernel<Dt::F32, true, true, true><<<grid, kThreads, 0, s>>>(
         G, rows, cols, tiles_x, amax_slot, sg_out, row_codes, row_scales, col_codes, col_scales,
-        zero_slot, nullptr, nullptr, o, nrm);
+        zero_slot, nullptr, nullptr, o, nrm, 0u);
   else
     quant_tile_kernel<Dt::BF16, true, true, true><<<grid, kThreads, 0, s>>>(
         G, rows, cols, tiles_x, amax_slot, sg_out, row_codes, row_scales, col_codes, col_scales,
-        zero_slot, nullptr, nullptr, o, nrm);
+        zero_slot, nullptr, nullptr, o, nrm, 0u);
   return hipGetLastError();
 }
 
