@@ -44,7 +44,7 @@ from .formats import (E2M1_MAGNITUDES, e2m1_decode, e4m3fn_decode,
 from .nvfp4 import (tensor_amax, global_scale, quantize_rows, quantize_cols,
                     dequantize_rows, dequantize_cols, round_to_bf16,
                     NVFP4Tensor)
-from .ns import (clip_and_normalize, gemm_nt, ns_exact, ns_nvfp4,
+from .ns import (clip_and_normalize, gemm_nt, ns_exact, ns_nvfp4, ns_nvfp4_step,
                  ns_iteration_flops)
 
 __all__ = [
@@ -52,6 +52,6 @@ __all__ = [
     "e4m3fn_encode_quotient", "e2m1_encode_quotient",
     "tensor_amax", "global_scale", "quantize_rows", "quantize_cols",
     "dequantize_rows", "dequantize_cols", "round_to_bf16", "NVFP4Tensor",
-    "clip_and_normalize", "gemm_nt", "ns_exact", "ns_nvfp4",
+    "clip_and_normalize", "gemm_nt", "ns_exact", "ns_nvfp4", "ns_nvfp4_step",
     "ns_iteration_flops",
 ]

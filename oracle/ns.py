@@ -81,44 +81,64 @@ def ns_exact(G, coeffs, clip=np.inf, eps=EPS):
     return X.T if transposed else X
 
 
+def ns_nvfp4_step(X, a, b, c, rht_mask=None, adaptive46=False, trace=None):
+    """One NVFP4 Newton–Schulz step (the three-line iteration of §3.4) from
+    the iterate X (m x n, m <= n, any float dtype, widened exactly to
+    float64), returning X' as float64:
+
+        qX = Q_1x16(X [H]),   qX16 = Q_16x1([H^T] X),   A = qX qX^T
+        qA = Q_1x16(A [H]),   qA16 = Q_16x1([H^T] A),   B = b A + c qA qA16
+        qB = Q_1x16(B [H]),                             X' = a X + qB qX16
+
+    ``rht_mask``: None, or the 16-bit sign mask of this step's random
+    Hadamard transform H.  ``adaptive46``: every quantization picks M = 4 or
+    6 per block (oracle/nvfp4.py).  ``trace``, if a list, receives a dict
+    with the quantized operands and the float64 intermediates.
+    """
+    X = np.asarray(X, dtype=np.float64)
+    if rht_mask is None:
+        amax_x = tensor_amax(X)
+        qX = quantize_rows(X, amax=amax_x, adaptive46=adaptive46)       # Q_1x16(X)
+        qX16 = quantize_cols(X, amax=amax_x, adaptive46=adaptive46)     # Q_16x1(X), stored as X^T rows
+    else:
+        qX = quantize_rows(rht_rows(X, rht_mask), adaptive46=adaptive46)      # Q_1x16(X H)
+        qX16 = quantize_cols(rht_cols(X, rht_mask), adaptive46=adaptive46)    # Q_16x1(H^T X)
+    dX = dequantize_rows(qX)
+    A = gemm_nt(dX, dX)                          # qX qX^T
+    if rht_mask is None:
+        qA = quantize_rows(A, adaptive46=adaptive46)                    # Q_1x16(A)
+        qA16 = quantize_cols(A, adaptive46=adaptive46)                  # Q_16x1(A)
+    else:
+        qA = quantize_rows(rht_rows(A, rht_mask), adaptive46=adaptive46)      # Q_1x16(A H)
+        qA16 = quantize_cols(rht_cols(A, rht_mask), adaptive46=adaptive46)    # Q_16x1(H^T A)
+    B = b * A + c * (dequantize_rows(qA) @ dequantize_cols(qA16))
+    qB = quantize_rows(B if rht_mask is None else rht_rows(B, rht_mask),
+                       adaptive46=adaptive46)                           # Q_1x16(B [H])
+    Xn = a * X + dequantize_rows(qB) @ dequantize_cols(qX16)
+    if trace is not None:
+        trace.append(dict(X=X, qX=qX, qX16=qX16, A=A, qA=qA, qA16=qA16,
+                          B=B, qB=qB, X_next=Xn, coeffs=(a, b, c), rht_mask=rht_mask))
+    return Xn
+
+
 def ns_nvfp4(G, coeffs, clip=np.inf, eps=EPS, trace=None, rht_masks=None, adaptive46=False):
-    """Newton–Schulz with NVFP4 operands for every product (§3.4 iteration).
+    """Newton–Schulz with NVFP4 operands for every product (§3.4 iteration):
+    orientation, clip and normalisation, then ``ns_nvfp4_step`` once per
+    coefficient triple.
 
     ``rht_masks``: None, or one 16-bit sign mask per step for the random
     Hadamard transform of that step.  ``adaptive46``: every quantization
-    picks M = 4 or 6 per block (oracle/nvfp4.py).  ``trace``, if a list, receives one
-    dict per step with the quantized operands and the float64 intermediates
-    (X before the step, A, B, X after).
+    picks M = 4 or 6 per block (oracle/nvfp4.py).  ``trace``, if a list,
+    receives one dict per step with the quantized operands and the float64
+    intermediates (X before the step, A, B, X after).
     """
     Gt, transposed = _orient(G)
     X = clip_and_normalize(Gt, clip, eps)
     if rht_masks is not None and len(rht_masks) != len(coeffs):
         raise ValueError("one Hadamard mask per step")
     for it, (a, b, c) in enumerate(coeffs):
-        if rht_masks is None:
-            amax_x = tensor_amax(X)
-            qX = quantize_rows(X, amax=amax_x, adaptive46=adaptive46)       # Q_1x16(X)
-            qX16 = quantize_cols(X, amax=amax_x, adaptive46=adaptive46)     # Q_16x1(X), stored as X^T rows
-        else:
-            h = rht_masks[it]
-            qX = quantize_rows(rht_rows(X, h), adaptive46=adaptive46)       # Q_1x16(X H)
-            qX16 = quantize_cols(rht_cols(X, h), adaptive46=adaptive46)     # Q_16x1(H^T X)
-        dX = dequantize_rows(qX)
-        A = gemm_nt(dX, dX)                          # qX qX^T
-        if rht_masks is None:
-            qA = quantize_rows(A, adaptive46=adaptive46)                    # Q_1x16(A)
-            qA16 = quantize_cols(A, adaptive46=adaptive46)                  # Q_16x1(A)
-        else:
-            qA = quantize_rows(rht_rows(A, h), adaptive46=adaptive46)       # Q_1x16(A H)
-            qA16 = quantize_cols(rht_cols(A, h), adaptive46=adaptive46)     # Q_16x1(H^T A)
-        B = b * A + c * (dequantize_rows(qA) @ dequantize_cols(qA16))
-        qB = quantize_rows(B if rht_masks is None else rht_rows(B, h), adaptive46=adaptive46)   # Q_1x16(B [H])
-        Xn = a * X + dequantize_rows(qB) @ dequantize_cols(qX16)
-        if trace is not None:
-            trace.append(dict(X=X, qX=qX, qX16=qX16, A=A, qA=qA, qA16=qA16,
-                              B=B, qB=qB, X_next=Xn, coeffs=(a, b, c),
-                              rht_mask=None if rht_masks is None else rht_masks[it]))
-        X = Xn
+        X = ns_nvfp4_step(X, a, b, c, rht_mask=None if rht_masks is None else rht_masks[it],
+                          adaptive46=adaptive46, trace=trace)
     return X.T if transposed else X
 
 

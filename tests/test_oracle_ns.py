@@ -157,3 +157,52 @@ def test_iteration_flops():
     # config 4 shape: m = 3072, n = 8192 -> 260.95 GFLOP per step
     assert abs(N.ns_iteration_flops(3072, 8192) - 260.95e9) < 0.01e9
     assert N.ns_iteration_flops(8192, 3072) == N.ns_iteration_flops(3072, 8192)
+
+
+def test_step_composes_to_the_loop():
+    # ns_nvfp4 is orientation + clip + normalisation followed by one
+    # ns_nvfp4_step per coefficient triple, bit for bit, in both orientations
+    rng = np.random.default_rng(7)
+    for shape in [(32, 48), (48, 32)]:
+        G = rng.standard_normal(shape)
+        coeffs = [QUINTIC, (3.0, -3.2, 1.2), CUBIC]
+        want = N.ns_nvfp4(G, coeffs, clip=1.5)
+        X = N.clip_and_normalize(G if shape[0] <= shape[1] else G.T, clip=1.5)
+        for a, b, c in coeffs:
+            X = N.ns_nvfp4_step(X, a, b, c)
+        got = X if shape[0] <= shape[1] else X.T
+        assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("abc", [QUINTIC, (3.0, -3.2, 1.2), (0.5, 2.0, -1.25), (1.0, 0.0, 0.75)])
+def test_step_follows_scalar_map_term_by_term(abc):
+    # On an equal-magnitude matrix with orthogonal rows every quantization is
+    # exact (up to the single rounding of s_g), so one step gives
+    # (a + b s^2 + c s^4) X; the schedules exercise each term's coefficient
+    # and sign separately (a dropped or swapped term breaks the equality).
+    rng = np.random.default_rng(8)
+    M = _equal_magnitude_rows(16, 64, rng)
+    for s in (0.125, 0.7, 1.3):
+        X = M * (s / np.sqrt(64.0))           # singular values all equal to s
+        a, b, c = abc
+        got = N.ns_nvfp4_step(X, a, b, c)
+        want = (a + b * s ** 2 + c * s ** 4) * X
+        assert np.linalg.norm(got - want) <= 1e-5 * max(np.linalg.norm(want), 1e-30)
+
+
+def test_step_trace_holds_the_operands_it_used():
+    rng = np.random.default_rng(9)
+    X = rng.standard_normal((32, 64)) * 0.05
+    tr = []
+    Xn = N.ns_nvfp4_step(X, *QUINTIC, trace=tr)
+    t = tr[0]
+    a, b, c = QUINTIC
+    # each product recomputed from the traced quantized operands
+    dX = Q.dequantize_rows(t["qX"])
+    assert np.array_equal(t["A"], dX @ dX.T)
+    assert np.allclose(t["B"], b * t["A"] + c * Q.dequantize_rows(t["qA"]) @ Q.dequantize_cols(t["qA16"]),
+                       rtol=0, atol=1e-15)
+    assert np.allclose(Xn, a * X + Q.dequantize_rows(t["qB"]) @ Q.dequantize_cols(t["qX16"]),
+                       rtol=0, atol=1e-15)
+    # the 16x1 operand of A is the transpose of its 1x16 operand (A symmetric)
+    assert np.array_equal(t["qA"].codes, t["qA16"].codes)
