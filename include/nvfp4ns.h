@@ -167,6 +167,39 @@ ns_status nvfp4_gemm(const uint8_t* codes_p, const uint8_t* scales_p, const floa
 size_t ns_workspace_bytes(int64_t m, int64_t n);
 
 /*
+ * ns_workspace_map — where ns_orthogonalize (and its _rht / _ex variants)
+ * keeps the iteration's operands inside its workspace, as byte offsets from
+ * ws.  An inspection aid (tests, debugging); the kernels need nothing from
+ * the caller beyond ns_workspace_bytes().  The iterate is xm x xn with
+ * xm = min(m, n), xn = max(m, n) (G^T when m > n).
+ *   x                  FP32 X [xm][xn]
+ *   a, b               FP32 A and B [xm][xm]; without the transform only the
+ *                      elements with row <= col are written (A and B are
+ *                      symmetric), with it the whole matrix
+ *   qx_codes/_scales   Q_1x16(X [H]): [xm][xn/2] codes, [xm][xn/16] scales
+ *   qt_codes/_scales   Q_16x1([H^T] X) stored as rows of X^T: [xn][xm/2], [xn][xm/16]
+ *   qa_codes/_scales   Q_1x16(A [H]): [xm][xm/2], [xm][xm/16]
+ *   qb_codes/_scales   Q_1x16(B [H]): likewise
+ *   global_scales      4 floats: s_g of qX, qA, qB, and of qX16 under the
+ *                      transform (without it qX16 uses s_g of qX)
+ * After a call of k steps these hold the last step's values: its input
+ * iterate X_{k-1} in x when the call is untransposed with FP32 output (the
+ * last product writes `out` directly), else X_k; the last step's A, B and
+ * every quantized operand of that step.
+ * Returns NS_ERR_SHAPE for shapes ns_orthogonalize rejects, NS_ERR_ARG for
+ * map == NULL.
+ */
+typedef struct {
+  int64_t xm, xn;
+  size_t x, a, b;
+  size_t qx_codes, qx_scales, qt_codes, qt_scales;
+  size_t qa_codes, qa_scales, qb_codes, qb_scales;
+  size_t global_scales;
+  size_t total;             /* == ns_workspace_bytes(m, n) */
+} ns_workspace_map;
+ns_status ns_workspace_layout(int64_t m, int64_t n, ns_workspace_map* map);
+
+/*
  * ns_orthogonalize — k NVFP4 Newton–Schulz steps (§2 "Root optimizer",
  * §3.4 NVFP4 NS iteration) on one matrix:
  *   X_0 = clamp(G, -clip, clip) / (||clamp(G)||_F + 1e-7)     (on G^T if m > n)

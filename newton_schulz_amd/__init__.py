@@ -7,7 +7,7 @@ module raises ImportError.
 
 Functions carry the C names:
     nvfp4_quantize, nvfp4_quantize_rht, nvfp4_dequantize,
-    nvfp4_gemm_workspace_bytes, nvfp4_gemm, ns_workspace_bytes,
+    nvfp4_gemm_workspace_bytes, nvfp4_gemm, ns_workspace_bytes, ns_workspace_layout,
     ns_orthogonalize, ns_orthogonalize_rht, ns_orthogonalize_ex,
     ns_abs_quantile_workspace_bytes, ns_abs_quantile,
     ns_grouped_workspace_bytes, ns_orthogonalize_grouped, ns_orthogonalize_grouped_ex
@@ -46,6 +46,17 @@ class NsOptions(ctypes.Structure):
     _fields_ = [("clip", ctypes.c_float), ("clip_quantile", ctypes.c_double),
                 ("rht_masks", ctypes.POINTER(ctypes.c_uint16)), ("adaptive46", ctypes.c_int)]
 
+class NsWorkspaceMap(ctypes.Structure):
+    """ns_workspace_map of the C ABI (byte offsets into an NS workspace)."""
+    _fields_ = [("xm", ctypes.c_int64), ("xn", ctypes.c_int64),
+                ("x", ctypes.c_size_t), ("a", ctypes.c_size_t), ("b", ctypes.c_size_t),
+                ("qx_codes", ctypes.c_size_t), ("qx_scales", ctypes.c_size_t),
+                ("qt_codes", ctypes.c_size_t), ("qt_scales", ctypes.c_size_t),
+                ("qa_codes", ctypes.c_size_t), ("qa_scales", ctypes.c_size_t),
+                ("qb_codes", ctypes.c_size_t), ("qb_scales", ctypes.c_size_t),
+                ("global_scales", ctypes.c_size_t), ("total", ctypes.c_size_t)]
+
+
 _SIGS = {
     "nvfp4_quantize_workspace_bytes": (_sz, [_i64, _i64]),
     "nvfp4_quantize": (_i, [_vp, _i, _i64, _i64, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -56,6 +67,7 @@ _SIGS = {
     "nvfp4_gemm": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i, _f, _f, _vp, _vp, _vp,
                         _vp, _sz, _vp]),
     "ns_workspace_bytes": (_sz, [_i64, _i64]),
+    "ns_workspace_layout": (_i, [_i64, _i64, _vp]),
     "ns_orthogonalize": (_i, [_vp, _i, _i64, _i64, _vp, _i, _f, _vp, _i, _vp, _sz, _vp]),
     "ns_orthogonalize_rht": (_i, [_vp, _i, _i64, _i64, _vp, _i, _f, _vp, _vp, _i, _vp, _sz, _vp]),
     "ns_orthogonalize_ex": (_i, [_vp, _i, _i64, _i64, _vp, _i, _vp, _vp, _i, _vp, _sz, _vp]),
@@ -285,6 +297,36 @@ def nvfp4_gemm(p, q, M, N, K, symmetric=False, alpha=1.0, beta=0.0, addend=None,
 
 def ns_workspace_bytes(m, n):
     return int(_lib.ns_workspace_bytes(m, n))
+
+
+def ns_workspace_layout(m, n):
+    """ns_workspace_layout: dict of the byte offsets (and xm, xn, total) of
+    the iteration's operands inside an ns_orthogonalize workspace."""
+    mp = NsWorkspaceMap()
+    _check(_lib.ns_workspace_layout(m, n, ctypes.byref(mp)), "ns_workspace_layout")
+    return {name: int(getattr(mp, name)) for name, _ in NsWorkspaceMap._fields_}
+
+
+def ns_workspace_views(ws, m, n):
+    """Views of the operands inside an NS workspace (uint8 device tensor):
+    X, A, B as float32 matrices, the four NVFP4 operands as (codes, scales)
+    uint8 matrices, and the four tensor scales as float32[4]."""
+    torch = _torch()
+    L = ns_workspace_layout(m, n)
+    xm, xn = L["xm"], L["xn"]
+
+    def f32(off, r, c):
+        return ws[off:off + 4 * r * c].view(torch.float32).view(r, c)
+
+    def u8(off, r, c):
+        return ws[off:off + r * c].view(r, c)
+
+    return {"X": f32(L["x"], xm, xn), "A": f32(L["a"], xm, xm), "B": f32(L["b"], xm, xm),
+            "qX": (u8(L["qx_codes"], xm, xn // 2), u8(L["qx_scales"], xm, xn // 16)),
+            "qX16": (u8(L["qt_codes"], xn, xm // 2), u8(L["qt_scales"], xn, xm // 16)),
+            "qA": (u8(L["qa_codes"], xm, xm // 2), u8(L["qa_scales"], xm, xm // 16)),
+            "qB": (u8(L["qb_codes"], xm, xm // 2), u8(L["qb_scales"], xm, xm // 16)),
+            "sg": ws[L["global_scales"]:L["global_scales"] + 16].view(torch.float32)}
 
 
 def _need_ns(G, out, workspace):

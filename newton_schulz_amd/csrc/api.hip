@@ -455,6 +455,28 @@ size_t ns_workspace_bytes(int64_t m, int64_t n) {
   return ns_layout(m, n).total;
 }
 
+ns_status ns_workspace_layout(int64_t m, int64_t n, ns_workspace_map* map) {
+  if (!map) return NS_ERR_ARG;
+  if (!dims_ok(m) || !dims_ok(n) || m * n >= kMaxElems) return NS_ERR_SHAPE;
+  const NsLayout L = ns_layout(m, n);
+  map->xm = m < n ? m : n;
+  map->xn = m < n ? n : m;
+  map->x = L.X;
+  map->a = L.A;
+  map->b = L.B;
+  map->qx_codes = L.qx_c;
+  map->qx_scales = L.qx_s;
+  map->qt_codes = L.qt_c;
+  map->qt_scales = L.qt_s;
+  map->qa_codes = L.qa_c;
+  map->qa_scales = L.qa_s;
+  map->qb_codes = L.qb_c;
+  map->qb_scales = L.qb_s;
+  map->global_scales = L.sg;
+  map->total = L.total;
+  return NS_OK;
+}
+
 ns_status ns_orthogonalize(const void* G, ns_dtype gt, int64_t m, int64_t n, const float* coeffs,
                            int k, float clip, void* out, ns_dtype ot, void* ws, size_t ws_bytes,
                            void* stream) {

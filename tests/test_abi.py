@@ -160,3 +160,28 @@ def test_empty_shapes_are_refused_on_host():
     m = (ctypes.c_int64 * 1)(0)
     n = (ctypes.c_int64 * 1)(64)
     assert lib.ns_grouped_workspace_bytes(1, m, n) == 0
+
+
+def test_workspace_layout_on_host():
+    ns = pytest.importorskip("newton_schulz_amd")
+    for m, n in [(3072, 8192), (8192, 3072), (144, 400), (16, 16)]:
+        L = ns.ns_workspace_layout(m, n)
+        xm, xn = min(m, n), max(m, n)
+        assert (L["xm"], L["xn"]) == (xm, xn)
+        assert L["total"] == ns.ns_workspace_bytes(m, n)
+        # each operand's byte range, in layout order, inside the workspace
+        spans = [("x", 4 * xm * xn), ("a", 4 * xm * xm), ("b", 4 * xm * xm),
+                 ("qx_codes", xm * xn // 2), ("qx_scales", xm * xn // 16),
+                 ("qt_codes", xm * xn // 2), ("qt_scales", xm * xn // 16),
+                 ("qa_codes", xm * xm // 2), ("qa_scales", xm * xm // 16),
+                 ("qb_codes", xm * xm // 2), ("qb_scales", xm * xm // 16),
+                 ("global_scales", 16)]
+        end = 0
+        for name, size in spans:
+            assert L[name] >= end and L[name] % 256 == 0, (m, n, name)
+            end = L[name] + size
+        assert end <= L["total"]
+    with pytest.raises(ns.NSError) as e:
+        ns.ns_workspace_layout(30, 32)
+    assert e.value.status == ns.NS_ERR_SHAPE
+    assert ns._lib.ns_workspace_layout(32, 32, None) == ns.NS_ERR_ARG

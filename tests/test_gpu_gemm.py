@@ -267,3 +267,38 @@ def test_general_gemm_leftover_tiles_split_k():
     got1 = host(ns.nvfp4_gemm(dev_q(qp), dev_q(qq), M, NC, K, alpha=1.25, beta=0.5,
                               addend=to_dev_f32(add), split=False))
     assert rel_fro(got1, got) <= 1e-6
+
+
+def test_full_size_gram_update_sampled():
+    """B = b A + c qA qA^T at the benchmark's size (3072^2, K = 3072) with the
+    quintic's b and c: the launch the NS step makes, whose leftover tiles are
+    split into K-parts summed by their last part inside the product kernel.
+    512 sampled entries against float64 dot products of dequantized rows;
+    the result is exactly symmetric and three launches agree bit for bit."""
+    m = 3072
+    b, c = -4.775, 2.0315
+    assert ns.nvfp4_gemm_workspace_bytes(m, m, m, True) > 0        # split schedule
+    rng = np.random.default_rng(12)
+    Xs = rng.standard_normal((m, 1024)) / 32.0
+    A = (Xs @ Xs.T).astype(np.float32)          # a Gram matrix: large diagonal
+    A = np.triu(A) + np.triu(A, 1).T
+    qa = Q.quantize_rows(A)
+    qd = dev_q(qa)
+    Ad = to_dev_f32(A)
+    ws = torch.empty(ns.nvfp4_gemm_workspace_bytes(m, m, m, True), dtype=torch.uint8, device=DEV)
+    slot = _amax_slot()
+    got = host(ns.nvfp4_gemm(qd, qd, m, m, m, symmetric=True, alpha=c, beta=b, addend=Ad,
+                             amax_out=slot, workspace=ws)).copy()
+    assert np.array_equal(got, got.T)
+    _check_amax(slot, got)
+    for _ in range(2):
+        again = host(ns.nvfp4_gemm(qd, qd, m, m, m, symmetric=True, alpha=c, beta=b, addend=Ad,
+                                   workspace=ws))
+        assert np.array_equal(again, got)
+    ii, jj = rng.integers(0, m, 512), rng.integers(0, m, 512)
+    da_i = Q.dequantize_rows(Q.NVFP4Tensor(qa.codes[ii], qa.scales[ii], qa.global_scale, 512, m))
+    da_j = Q.dequantize_rows(Q.NVFP4Tensor(qa.codes[jj], qa.scales[jj], qa.global_scale, 512, m))
+    want = b * A[ii, jj].astype(np.float64) + c * np.sum(da_i * da_j, axis=1)
+    err = np.linalg.norm(got[ii, jj] - want) / np.linalg.norm(want)
+    print(f"[gemm] 3072^2 x 3072 quintic update: sampled rel {err:.3g}", flush=True)
+    assert err <= TOL
