@@ -45,6 +45,8 @@ def parse():
     p.add_argument("--no-quant", action="store_true", help="skip the quantizer line")
     p.add_argument("--no-grouped", action="store_true",
                    help="skip the grouped batches (four 3072-wide blocks; the pages' d=4096/6144 blocks)")
+    p.add_argument("--quant-only", action="store_true",
+                   help="run only the standalone quantizer leg (for profiling its kernels)")
     p.add_argument("--copy-probe", action="store_true",
                    help="finish with a plain 256 MiB device copy, the reference kernel that "
                         "scales the FETCH_SIZE / WRITE_SIZE counters of a profiled run")
@@ -111,12 +113,12 @@ def kernel_timings(ns, torch, dev, m, n, stream, reps=10):
     return {k: (s.elapsed_time(e) / reps, flops[k]) for k, (s, e) in out.items()}
 
 
-def source_digest():
-    """sha256 over the GEMM kernel sources; recorded HBM-traffic counters
-    apply only to the kernel they were taken from."""
+def source_digest(files=("gemm.hip", "nvfp4_device.hpp")):
+    """sha256 over kernel sources; recorded HBM-traffic counters apply only
+    to the kernels they were taken from."""
     import hashlib
     h = hashlib.sha256()
-    for f in ("gemm.hip", "nvfp4_device.hpp"):
+    for f in files:
         with open(os.path.join(ROOT, "newton_schulz_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
@@ -127,6 +129,11 @@ def source_digest():
 # what the counter reads for a plain copy of known size; see profiles/.
 DOMINANT_TRAFFIC = {"src_sha256": "363d1c41511f59121901871fb4283f57ea55485230a150b1c2893897923e7e5c",
                     "bytes_per_launch": 440327111}
+# HBM bytes of one quantize + dequantize pair of the 2^28 BF16 tensor (the
+# maximum, encode and decode kernels), measured the same way.
+QUANT_TRAFFIC = {"src_sha256": "2a1965ee9e7894210eed719c51af7bb9e79d0cf66106c3a5d10500321b48da8d",
+                 "bytes_per_pair": 1916115558}
+QUANT_UNIQUE_BYTES_PER_ELEM = (2 + 0.5 + 1 / 16) + (0.5 + 1 / 16 + 2)
 
 
 def bf16_ns_ms(torch, G, coeffs, stream, reps=10):
@@ -200,6 +207,61 @@ def cpu_baseline(G, clip, coeffs, m, n):
                       f"(numpy/BLAS), {el:.1f} s wall"}
 
 
+def copy_probe(torch, dev):
+    """Three plain 256 MiB device copies: the reference kernel whose
+    FETCH_SIZE / WRITE_SIZE readings scale those of a profiled run."""
+    src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+def quant_line(ns, torch, synth, dev, stream, args):
+    """The standalone quantizer + dequantizer on the 2^28 BF16 tensor."""
+    qbits, _ = synth.quant_workload()
+    xq = torch.from_numpy(qbits.view(np.int16)).view(torch.bfloat16).to(dev)
+    rows, cols = xq.shape
+    codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev)
+    sg = torch.empty(1, dtype=torch.float32, device=dev)
+    qws = torch.empty(ns.nvfp4_quantize_workspace_bytes(rows, cols), dtype=torch.uint8, device=dev)
+    deq = torch.empty((rows, cols), dtype=torch.bfloat16, device=dev)
+
+    def qstep():
+        ns.nvfp4_quantize(xq, ns.NVFP4_ROWS, codes, scales, sg, workspace=qws, stream=stream)
+        ns.nvfp4_dequantize(codes, scales, sg, rows, cols, ns.NVFP4_ROWS, ns.NS_BF16, out=deq,
+                            stream=stream)
+    qms = time_events(qstep, args.quant_steps, args.quant_warmup, stream)
+    qbytes = QUANT_DESIGN_BYTES_PER_ELEM * rows * cols
+    gbps = qbytes / (qms * 1e-3) / 1e9
+    t_q = time_events(lambda: ns.nvfp4_quantize(xq, ns.NVFP4_ROWS, codes, scales, sg,
+                                                workspace=qws, stream=stream), 50, 5, stream)
+    t_d = time_events(lambda: ns.nvfp4_dequantize(codes, scales, sg, rows, cols, ns.NVFP4_ROWS,
+                                                  ns.NS_BF16, out=deq, stream=stream), 50, 5, stream)
+    traffic = None
+    if QUANT_TRAFFIC["src_sha256"] == source_digest(("quant.hip", "nvfp4_device.hpp")):
+        traffic = QUANT_TRAFFIC["bytes_per_pair"]
+    unique = QUANT_UNIQUE_BYTES_PER_ELEM * rows * cols
+    out = {
+        "metric": "nvfp4_quant HBM GB/s", "value": round(gbps, 1), "unit": "GB/s",
+        "bytes_basis": "design bytes, 7.125 B per element: the maximum pass reads the tensor, "
+                       "the encode pass reads it again (a global maximum cannot be known in one "
+                       "pass over a tensor twice the Infinity Cache) and writes codes and "
+                       "scales, the decode pass reads those and writes BF16; counters measure "
+                       "the same bytes (traffic)",
+        "workload": "16384x16384 BF16 Student-t(3)*0.02 with 0.1% x50, quantize (amax pass + "
+                    "encode) + dequantize to BF16, 1x16 blocks",
+        "ms": round(qms, 4), "quantize_ms": round(t_q, 4), "dequantize_ms": round(t_d, 4),
+        "design_bytes": int(qbytes),
+        "unique_bytes": int(unique), "unique_gbps": round(unique / (qms * 1e-3) / 1e9, 1),
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "traffic_unit": "HBM bytes per quantize + dequantize pair"}}
+    del xq, deq
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -213,6 +275,13 @@ def main():
 
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
+    if args.quant_only:
+        # the standalone quantizer alone (for profiling its kernels)
+        line = {"quant": quant_line(ns, torch, synth, dev, stream, args)}
+        if args.copy_probe:
+            copy_probe(torch, dev)
+        print(json.dumps(line), flush=True)
+        return
     coeffs = [synth.QUINTIC] * synth.STEPS
     spec = synth.ns_workload("ns3072x8192")
     G, bits, clip = synth.ns_matrix(spec, 0)
@@ -322,44 +391,11 @@ def main():
 
     if not args.no_quant:
         del ws
-        qbits, _ = synth.quant_workload()
-        xq = torch.from_numpy(qbits.view(np.int16)).view(torch.bfloat16).to(dev)
-        rows, cols = xq.shape
-        codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
-        scales = torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev)
-        sg = torch.empty(1, dtype=torch.float32, device=dev)
-        qws = torch.empty(ns.nvfp4_quantize_workspace_bytes(rows, cols), dtype=torch.uint8, device=dev)
-        deq = torch.empty((rows, cols), dtype=torch.bfloat16, device=dev)
-
-        def qstep():
-            ns.nvfp4_quantize(xq, ns.NVFP4_ROWS, codes, scales, sg, workspace=qws, stream=stream)
-            ns.nvfp4_dequantize(codes, scales, sg, rows, cols, ns.NVFP4_ROWS, ns.NS_BF16, out=deq,
-                                stream=stream)
-        qms = time_events(qstep, args.quant_steps, args.quant_warmup, stream)
-        qbytes = QUANT_DESIGN_BYTES_PER_ELEM * rows * cols
-        gbps = qbytes / (qms * 1e-3) / 1e9
-        t_q = time_events(lambda: ns.nvfp4_quantize(xq, ns.NVFP4_ROWS, codes, scales, sg,
-                                                    workspace=qws, stream=stream), 50, 5, stream)
-        t_d = time_events(lambda: ns.nvfp4_dequantize(codes, scales, sg, rows, cols, ns.NVFP4_ROWS,
-                                                      ns.NS_BF16, out=deq, stream=stream), 50, 5, stream)
-        line["quant"] = {
-            "metric": "nvfp4_quant HBM GB/s", "value": round(gbps, 1), "unit": "GB/s",
-            "workload": "16384x16384 BF16 Student-t(3)*0.02 with 0.1% x50, quantize (amax pass + "
-                        "encode) + dequantize to BF16, 1x16 blocks",
-            "ms": round(qms, 4), "quantize_ms": round(t_q, 4), "dequantize_ms": round(t_d, 4),
-            "design_bytes": int(qbytes),
-            "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
-                         "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None}}
-        del xq, deq
-
+        line["quant"] = quant_line(ns, torch, synth, dev, stream, args)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(G, clip, coeffs, m, n)
     if args.copy_probe:
-        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
+        copy_probe(torch, dev)
     print(json.dumps(line), flush=True)
 
 
