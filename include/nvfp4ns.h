@@ -90,6 +90,24 @@ ns_status nvfp4_quantize(const void* x, ns_dtype xt, int64_t rows, int64_t cols,
                          void* stream);
 
 /*
+ * nvfp4_quantize_noalloc — nvfp4_quantize without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  Its scratch, the
+ * nvfp4_quantize_workspace_bytes() (2 KiB) of partial tensor maxima, lives in
+ * a static device array of 2 KiB that each GPU the library runs on holds
+ * until the process ends; the call allocates nothing.  Every call on one GPU
+ * shares that array: calls that overlap on one GPU (concurrent streams)
+ * race and must be ordered by the caller.  The array is cleared by a kernel
+ * of each call.  Arguments, layouts, results and errors as nvfp4_quantize;
+ * NS_ERR_WORKSPACE if a shape ever needed more scratch than the array holds
+ * (none does: the scratch does not grow with the tensor); NS_ERR_HIP if the
+ * array's device address cannot be obtained.
+ */
+ns_status nvfp4_quantize_noalloc(const void* x, ns_dtype xt, int64_t rows, int64_t cols,
+                                 nvfp4_axis axis, uint8_t* codes, uint8_t* scales,
+                                 float* global_scale, void* stream);
+
+/*
  * nvfp4_quantize_rht — the quantizers of the §3.4 NS iteration with the
  * random Hadamard transform: Q_1x16(x H) (NVFP4_ROWS) or Q_16x1(H^T x)
  * (NVFP4_COLS, stored as the Q_1x16 layout of the transpose), where

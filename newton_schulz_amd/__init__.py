@@ -6,7 +6,7 @@ current stream.  There is no fallback: if the library is missing this
 module raises ImportError.
 
 Functions carry the C names:
-    nvfp4_quantize, nvfp4_quantize_rht, nvfp4_dequantize,
+    nvfp4_quantize, nvfp4_quantize_noalloc, nvfp4_quantize_rht, nvfp4_dequantize,
     nvfp4_gemm_workspace_bytes, nvfp4_gemm, ns_workspace_bytes, ns_workspace_layout,
     ns_orthogonalize, ns_orthogonalize_rht, ns_orthogonalize_ex,
     ns_abs_quantile_workspace_bytes, ns_abs_quantile,
@@ -60,6 +60,7 @@ class NsWorkspaceMap(ctypes.Structure):
 _SIGS = {
     "nvfp4_quantize_workspace_bytes": (_sz, [_i64, _i64]),
     "nvfp4_quantize": (_i, [_vp, _i, _i64, _i64, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "nvfp4_quantize_noalloc": (_i, [_vp, _i, _i64, _i64, _i, _vp, _vp, _vp, _vp]),
     "nvfp4_quantize_rht": (_i, [_vp, _i, _i64, _i64, _i, _u16, _vp, _vp, _vp, _vp, _sz, _vp]),
     "nvfp4_quantize_46": (_i, [_vp, _i, _i64, _i64, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
     "nvfp4_dequantize": (_i, [_vp, _vp, _vp, _i64, _i64, _i, _vp, _i, _vp]),
@@ -188,6 +189,29 @@ def nvfp4_quantize(x, axis=NVFP4_ROWS, codes=None, scales=None, global_scale=Non
     with torch.cuda.device(dev):
         _check(fn(_ptr(x), _dt(x), rows, cols, axis, _ptr(codes), _ptr(scales), _ptr(global_scale),
                   _ptr(workspace), workspace.numel(), _stream(stream, dev)), name)
+    return codes, scales, global_scale
+
+
+def nvfp4_quantize_noalloc(x, axis=NVFP4_ROWS, codes=None, scales=None, global_scale=None,
+                           stream=None):
+    """nvfp4_quantize through the allocation-free entry point (its scratch is
+    the library's static device array); outputs as nvfp4_quantize."""
+    torch = _torch()
+    _need_cuda(x)
+    rows, cols = x.shape
+    r, c = (rows, cols) if axis == NVFP4_ROWS else (cols, rows)
+    dev = x.device
+    if codes is None:
+        codes = torch.empty((r, c // 2), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty((r, c // 16), dtype=torch.uint8, device=dev)
+    if global_scale is None:
+        global_scale = torch.empty(1, dtype=torch.float32, device=dev)
+    _need_quant_outputs(x, rows, cols, codes, scales, global_scale, None)
+    with torch.cuda.device(dev):
+        _check(_lib.nvfp4_quantize_noalloc(_ptr(x), _dt(x), rows, cols, axis, _ptr(codes),
+                                           _ptr(scales), _ptr(global_scale),
+                                           _stream(stream, dev)), "nvfp4_quantize_noalloc")
     return codes, scales, global_scale
 
 

@@ -83,6 +83,39 @@ hipError_t group_streams(hipStream_t (&out)[kGroupStreams]) {
   return hipSuccess;
 }
 
+// ---- scratch of the allocation-free quantizer ------------------------------
+// nvfp4_quantize_noalloc keeps the quantizer's scratch (the partial words of
+// the tensor maximum, nvfp4_quantize_workspace_bytes()) in this array
+// instead of a caller workspace.  Each device holds its own copy until the
+// process ends; host code reaches it only through the address that
+// hipGetSymbolAddress returns on that device (the array's name is a
+// host-side stand-in).
+constexpr size_t kNoAllocScratchBytes = 2048;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+// The device address of `scratch` on the current device, looked up once per
+// device.  Null (and e set) if the lookup fails.
+void* scratch_address(hipError_t& e) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices];
+  int dev = 0;
+  e = hipGetDevice(&dev);
+  if (e != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) {
+    e = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return nullptr;
+    addr[dev] = p;
+  }
+  e = hipSuccess;
+  return addr[dev];
+}
+
 // A failed launch returns NS_ERR_HIP; with NVFP4NS_DEBUG set in the
 // environment the HIP error and the failing call are also printed.
 inline ns_status hip_failed(hipError_t e, const char* what, int line) {
@@ -343,6 +376,24 @@ ns_status nvfp4_quantize(const void* x, ns_dtype xt, int64_t rows, int64_t cols,
     NS_TRY(nvfp4::launch_quant_tiles(x, (Dt)xt, rows, cols, slot, global_scale, nullptr, nullptr,
                                      codes, scales, nullptr, s));
   return NS_OK;
+}
+
+ns_status nvfp4_quantize_noalloc(const void* x, ns_dtype xt, int64_t rows, int64_t cols,
+                                 nvfp4_axis axis, uint8_t* codes, uint8_t* scales,
+                                 float* global_scale, void* stream) {
+  // the scratch this call needs must fit the static array (it does for every
+  // shape: the quantizer's scratch does not grow with the tensor)
+  if (nvfp4_quantize_workspace_bytes(rows, cols) > kNoAllocScratchBytes) {
+    if (std::getenv("NVFP4NS_DEBUG"))
+      std::fprintf(stderr, "nvfp4ns: nvfp4_quantize_noalloc needs more than its %zu-byte scratch\n",
+                   kNoAllocScratchBytes);
+    return NS_ERR_WORKSPACE;
+  }
+  hipError_t e = hipSuccess;
+  void* ws = scratch_address(e);
+  if (!ws) return hip_failed(e, "hipGetSymbolAddress(scratch)", __LINE__);
+  return nvfp4_quantize(x, xt, rows, cols, axis, codes, scales, global_scale, ws,
+                        kNoAllocScratchBytes, stream);
 }
 
 ns_status nvfp4_quantize_rht(const void* x, ns_dtype xt, int64_t rows, int64_t cols,
