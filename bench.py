@@ -16,7 +16,9 @@ The same JSON line carries:
                 (16384 x 16384) in HBM GB/s against the 8 TB/s peak;
   bf16_ns       the same five steps in plain BF16 torch.matmul (hipBLASLt)
                 on the same GPU, for a like-for-like speedup;
-  cpu_baseline  the float64 oracle on the host cores, bounded sample.
+  cpu_baseline  the C++ oracle (float64 NS, exact quantizer, OpenMP) on the
+                host cores: the four single-GPU workloads, a bounded sample
+                of the largest.
 """
 import argparse
 import json
@@ -185,26 +187,47 @@ def grouped_line(ns, torch, synth, dev, stream, label, shapes, seed0, coeffs, cl
             "bf16_ms": round(bms, 3), "speedup_nvfp4_vs_bf16": round(bms / ms, 3)}
 
 
-def cpu_baseline(G, clip, coeffs, m, n):
-    from oracle import ns as N
+def cpu_model():
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # noqa: BLE001
-        threads = os.cpu_count() or 1
-    G64 = G.astype(np.float64)
-    done, t0 = 0, time.perf_counter()
-    while True:
-        N.ns_nvfp4(G64, coeffs[:1], clip=clip)
-        done += 1
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(synth, coeffs, steps4=2):
+    """The C++ oracle (plain C++ NVFP4 quantizer and float64 NS loop, OpenMP
+    over the host's cores) on the four single-GPU workloads: the 256 x 512
+    NS in full, the 2^28-element quantize + dequantize, the 2048^2 NS in
+    full and `steps4` NS steps of 3072 x 8192 (its rate stands for the five).
+    value = the 3072 x 8192 rate in algorithmic TFLOP/s."""
+    from oracle import native as C
+    from oracle.ns import ns_iteration_flops
+    res = {}
+    for name, k in (("ns256x512", len(coeffs)), ("ns2048", len(coeffs)), ("ns3072x8192", steps4)):
+        G, _, clip = synth.ns_matrix(synth.ns_workload(name), 0)
+        G64 = G.astype(np.float64)
+        t0 = time.perf_counter()
+        C.ns_nvfp4(G64, coeffs[:k], clip=clip)
         el = time.perf_counter() - t0
-        if el >= 10.0 or done >= len(coeffs):
-            break
-    flops = done * N.ns_iteration_flops(m, n)
-    return {"value": round(flops / el / 1e12, 5), "unit": "TFLOP/s", "cores": int(threads),
+        m, n = G.shape
+        res[name] = {"steps": k, "s": round(el, 3),
+                     "tflops": round(k * ns_iteration_flops(m, n) / el / 1e12, 5)}
+    _, qv = synth.quant_workload()
+    t0 = time.perf_counter()
+    C.dequantize_rows(C.quantize_rows(qv))
+    el = time.perf_counter() - t0
+    res["quant2p28"] = {"s": round(el, 3), "gbps": round(QUANT_DESIGN_BYTES_PER_ELEM * qv.size / el / 1e9, 2)}
+    return {"value": res["ns3072x8192"]["tflops"], "unit": "TFLOP/s", "cores": C.threads(),
             "kind": "oracle",
-            "sample": f"{done} NVFP4 NS step(s) of the 3072x8192 workload in float64 "
-                      f"(numpy/BLAS), {el:.1f} s wall"}
+            "sample": f"C++ oracle (float64 NS, exact-comparison quantizer, OpenMP, {C.threads()} "
+                      f"threads on {os.cpu_count()} logical CPUs, {cpu_model()}): "
+                      f"{steps4} of the 5 NS steps of 3072x8192 ({res['ns3072x8192']['s']} s; value "
+                      f"is their rate); in full: 256x512 NS {res['ns256x512']['s']} s, 2048^2 NS "
+                      f"{res['ns2048']['s']} s, 2^28 BF16 quantize+dequantize {res['quant2p28']['s']} s",
+            "per_workload": res}
 
 
 def copy_probe(torch, dev):
@@ -300,6 +323,18 @@ def main():
     flops = synth.STEPS * ns_iteration_flops(m, n)
     tflops = flops / (ms * 1e-3) / 1e12
 
+    # per-call spread: each call between its own pair of events (the events
+    # add a few microseconds to each); ms_per_step above is the back-to-back mean
+    per_call = []
+    for _ in range(args.steps):
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record(stream)
+        step()
+        s1.record(stream)
+        per_call.append((s0, s1))
+    torch.cuda.synchronize()
+    per_call = sorted(a.elapsed_time(b) for a, b in per_call)
+
     kt = kernel_timings(ns, torch, dev, m, n, stream)
     # share of one NS step: each GEMM runs once per iteration
     dom = max(kt, key=lambda k: kt[k][0])
@@ -326,6 +361,9 @@ def main():
                    "m": m, "n": n, "ns_steps": synth.STEPS, "operands": "nvfp4 (e2m1 x e4m3/16 + f32)",
                    "accumulate": "f32", "frac_of_peak": round(tflops / MFMA_F16_PEAK_TFLOPS, 4)},
         "roofline": roof,
+        "step_ms": {"median": round(float(np.median(per_call)), 4), "min": round(per_call[0], 4),
+                    "max": round(per_call[-1], 4), "calls": len(per_call),
+                    "how": "each call between its own pair of HIP events"},
         "wall_s_timed": round(wall, 3),
     }
 
@@ -393,7 +431,7 @@ def main():
         del ws
         line["quant"] = quant_line(ns, torch, synth, dev, stream, args)
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(G, clip, coeffs, m, n)
+        line["cpu_baseline"] = cpu_baseline(synth, coeffs)
     if args.copy_probe:
         copy_probe(torch, dev)
     print(json.dumps(line), flush=True)

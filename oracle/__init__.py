@@ -13,6 +13,10 @@ Projections, Optimizers, and Attention" (arXiv 2607.04422):
   every quantized operand along the contraction axis.
 * ``quantile`` — the p99 clip threshold as an order statistic of |G| (§3.4
   p99 outlier clipping, App. F Table 8 quantile ratio 0.99).
+* ``native``   — a ctypes loader of the C++ oracle (``cpp/nvfp4_oracle.cpp``): a
+  second, independently written quantizer and float64 NVFP4 NS loop with
+  OpenMP, pinned like this package and cross-checked against it; the
+  benchmark times it on the host cores.
 * ``ns``       — the Newton–Schulz iteration of the Root optimizer, exact
   (§2 "Root optimizer") and with NVFP4 operands (§3.4, the three-line NVFP4
   NS iteration, with or without the transform), plus the caller-side clip
