@@ -16,6 +16,8 @@ The same JSON line carries:
                 (16384 x 16384) in HBM GB/s against the 8 TB/s peak;
   bf16_ns       the same five steps in plain BF16 torch.matmul (hipBLASLt)
                 on the same GPU, for a like-for-like speedup;
+  accuracy      relative L2 error of plain NVFP4 NS and of its variants
+                (transform, adaptive 4/6, p99 clip) against unquantized NS;
   cpu_baseline  the C++ oracle (float64 NS, exact quantizer, OpenMP) on the
                 host cores: the four single-GPU workloads, a bounded sample
                 of the largest.
@@ -47,6 +49,8 @@ def parse():
     p.add_argument("--no-quant", action="store_true", help="skip the quantizer line")
     p.add_argument("--no-grouped", action="store_true",
                    help="skip the grouped batches (four 3072-wide blocks; the pages' d=4096/6144 blocks)")
+    p.add_argument("--no-accuracy", action="store_true",
+                   help="skip the accuracy table (NVFP4 variants against unquantized NS)")
     p.add_argument("--quant-only", action="store_true",
                    help="run only the standalone quantizer leg (for profiling its kernels)")
     p.add_argument("--copy-probe", action="store_true",
@@ -228,6 +232,57 @@ def cpu_baseline(synth, coeffs, steps4=2):
                       f"is their rate); in full: 256x512 NS {res['ns256x512']['s']} s, 2048^2 NS "
                       f"{res['ns2048']['s']} s, 2^28 BF16 quantize+dequantize {res['quant2p28']['s']} s",
             "per_workload": res}
+
+
+def exact_ns_f64(torch, G, coeffs, clip):
+    """Unquantized NS in float64 with torch on the GPU (the reference of the
+    accuracy table): X_0 = clamp(G) / (||clamp(G)||_F + 1e-7) on G^T if m > n,
+    then X <- a X + (b A + c A A) X with A = X X^T."""
+    X = G.double()
+    tr = X.shape[0] > X.shape[1]
+    if tr:
+        X = X.t().contiguous()
+    if clip != float("inf"):
+        X = X.clamp(-clip, clip)
+    X = X / (torch.linalg.norm(X) + 1e-7)
+    for a, b, c in coeffs:
+        A = X @ X.t()
+        X = a * X + (b * A + c * (A @ A)) @ X
+    return X.t() if tr else X
+
+
+def accuracy_table(ns, torch, synth, dev, stream):
+    """Relative L2 (Frobenius) error of the NVFP4 NS output against
+    unquantized float64 NS of the same input, clip and coefficients: plain
+    NVFP4, with the random Hadamard transform, with adaptive 4/6, with the
+    on-device 0.99-quantile clip, and with all three; the quintic and the
+    cubic, five steps, on the 256x512, 2048^2 and 3072x8192 workloads."""
+    table = {}
+    for name in ("ns256x512", "ns2048", "ns3072x8192"):
+        spec = synth.ns_workload(name)
+        G, bits, clip = synth.ns_matrix(spec, 0)
+        if spec["dtype"] == "bf16":
+            Gd = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+        else:
+            Gd = torch.from_numpy(G).to(dev)
+        masks = synth.rht_masks(synth.STEPS, seed=spec["seeds"][0])
+        q99 = float(ns.ns_abs_quantile(Gd, 0.99, stream=stream).item())
+        row = {}
+        for sname, coeffs in (("quintic", [synth.QUINTIC] * synth.STEPS),
+                              ("cubic", [(1.5, -0.5, 0.0)] * synth.STEPS)):
+            ref = {c: exact_ns_f64(torch, Gd, coeffs, c) for c in {clip, q99}}
+            runs = {"plain": dict(clip=clip), "rht": dict(clip=clip, rht_masks=masks),
+                    "46": dict(clip=clip, adaptive46=True),
+                    "p99": dict(clip_quantile=0.99),
+                    "rht+46+p99": dict(clip_quantile=0.99, rht_masks=masks, adaptive46=True)}
+            errs = {}
+            for vname, kw in runs.items():
+                out = ns.ns_orthogonalize_ex(Gd, coeffs, stream=stream, **kw).double()
+                r = ref[q99] if "clip_quantile" in kw else ref[clip]
+                errs[vname] = round(float(torch.linalg.norm(out - r) / torch.linalg.norm(r)), 4)
+            row[sname] = errs
+        table[name] = row
+    return table
 
 
 def copy_probe(torch, dev):
@@ -426,6 +481,12 @@ def main():
         ]
         torch.cuda.empty_cache()
         ws = None
+
+    if not args.no_accuracy:
+        line["accuracy"] = {
+            "what": "relative L2 error of the NVFP4 NS output against unquantized float64 NS "
+                    "(torch on the GPU) of the same input, clip and coefficients, five steps",
+            "table": accuracy_table(ns, torch, synth, dev, stream)}
 
     if not args.no_quant:
         del ws
