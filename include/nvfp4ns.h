@@ -170,7 +170,12 @@ ns_status nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales,
  *     left over after an equal number per CU be split along K across
  *     workgroups (FP32 partials summed in a fixed order, so results do not
  *     depend on timing).  ws = NULL, ws_bytes = 0 runs every tile whole.
- *     Calls sharing one ws must not overlap.
+ *     Calls sharing one ws must not overlap.  ws must be ordinary device
+ *     memory of the GPU that runs the call (hipMalloc, a torch tensor):
+ *     within one launch the K-parts of a tile hand their partials to the
+ *     part that sums them through ws, with stores and loads coherent at
+ *     device scope and a device-scope counter, which relies on ws being
+ *     device-local memory.
  * M, N, K must be positive multiples of 16.
  */
 size_t nvfp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int symmetric);

@@ -247,6 +247,36 @@ def test_split_k_sums_are_deterministic():
     assert np.linalg.norm(first[ii, jj] - want) <= TOL * np.linalg.norm(want)
 
 
+def test_split_k_hand_off_reads_this_launchs_partials():
+    """The K-parts of a split tile pass FP32 partials to the part that sums
+    them through the workspace.  Launches that share the workspace alternate
+    between X and D X, D a random diagonal of signs (the sign bit of each
+    E2M1 code flipped on the rows where D is -1): the exact products are
+    A and D A D, so every partial of a tile that mixes both kinds of rows
+    changes sign from one launch to the next, and a part that read a partial
+    left by the previous launch would break the bit-exact relation
+    out(D X) == D out(X) D."""
+    m, n = 3072, 8192
+    x = synth.gaussian(m, n, seed=29) / np.sqrt(m * n)
+    q = Q.quantize_rows(x)
+    d = np.where(np.random.default_rng(5).random(m) < 0.5, -1.0, 1.0).astype(np.float32)
+    c1, s1, g1 = dev_q(q)
+    flip = torch.from_numpy(np.where(d < 0, 0x88, 0).astype(np.uint8)).to(DEV)
+    c2 = torch.bitwise_xor(c1, flip[:, None])
+    ws = torch.empty(ns.nvfp4_gemm_workspace_bytes(m, m, n, True), dtype=torch.uint8, device=DEV)
+    out = torch.empty((m, m), dtype=torch.float32, device=DEV)
+    want1 = host(ns.nvfp4_gemm((c1, s1, g1), (c1, s1, g1), m, m, n, symmetric=True, out=out,
+                               workspace=ws)).copy()
+    want2 = want1 * d[:, None] * d[None, :]
+    assert np.count_nonzero(want2 != want1) > m * m // 4
+    for r in range(6):
+        for qd, want in (((c2, s1, g1), want2), ((c1, s1, g1), want1)):
+            out.fill_(float("nan"))
+            got = host(ns.nvfp4_gemm(qd, qd, m, m, n, symmetric=True, out=out, workspace=ws))
+            assert np.array_equal(got, want), r
+    print("[gemm] 3072^2 x 8192 split-K: 12 alternating launches exact", flush=True)
+
+
 def test_general_gemm_leftover_tiles_split_k():
     """A non-symmetric product whose tiles do not divide evenly over the CUs:
     the leftover tiles run as K-parts (partials summed in order by the last
