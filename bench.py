@@ -53,6 +53,9 @@ def parse():
                    help="skip the accuracy table (NVFP4 variants against unquantized NS)")
     p.add_argument("--quant-only", action="store_true",
                    help="run only the standalone quantizer leg (for profiling its kernels)")
+    p.add_argument("--gemm-only", action="store_true",
+                   help="run only the three products of one NS iteration at 3072x8192, as in "
+                        "the roofline leg (for profiling the GEMM kernels)")
     p.add_argument("--copy-probe", action="store_true",
                    help="finish with a plain 256 MiB device copy, the reference kernel that "
                         "scales the FETCH_SIZE / WRITE_SIZE counters of a profiled run")
@@ -359,6 +362,15 @@ def main():
         if args.copy_probe:
             copy_probe(torch, dev)
         print(json.dumps(line), flush=True)
+        return
+    if args.gemm_only:
+        # the three products alone, 10 launches each (for profiling their kernels)
+        kt = kernel_timings(ns, torch, dev, 3072, 8192, stream)
+        if args.copy_probe:
+            copy_probe(torch, dev)
+        print(json.dumps({"gemm_ms": {k: round(v[0], 4) for k, v in kt.items()},
+                          "gemm_tflops": {k: round(v[1] / (v[0] * 1e-3) / 1e12, 2)
+                                          for k, v in kt.items()}}), flush=True)
         return
     coeffs = [synth.QUINTIC] * synth.STEPS
     spec = synth.ns_workload("ns3072x8192")
