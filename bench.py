@@ -77,36 +77,44 @@ def time_events(fn, reps, warm, stream):
     return start.elapsed_time(end) / reps      # ms per call
 
 
-def kernel_timings(ns, torch, dev, m, n, stream, reps=10):
+def kernel_timings(ns, torch, dev, Gd, clip, coeffs, stream, reps=10):
     """The three products of an NS iteration launched through the C ABI on
-    the bench stream, each on operands quantized as inside
-    ns_orthogonalize.  Each product runs `reps` times back to back between
-    one pair of HIP events, after a spin kernel that keeps the GPU busy
-    while the host enqueues, so the interval holds the launches alone (a
-    pair of events around every single launch would add the events' own
-    processing, about 6 us, to each).  Returns {name: (average ms per
-    launch, algorithmic flops per launch)}."""
-    from synth import gaussian
-    X = torch.from_numpy((gaussian(m, n, seed=77) / np.sqrt(m * n)).astype(np.float32)).to(dev)
+    the bench stream, on the operands of the NS run itself: a two-step
+    ns_orthogonalize call on the workload leaves its second step's X, qX,
+    qX16, qA, qB and tensor scales in the workspace (ns_workspace_views).
+    The update product runs in place (addend = out = X, beta = a), as in the
+    iteration; the Gram products write the whole symmetric product (the
+    iteration keeps only the upper triangle).  Each product runs `reps`
+    times back to back between one pair of HIP events, after a spin kernel
+    that keeps the GPU busy while the host enqueues, so the interval holds
+    the launches alone (a pair of events around every single launch would
+    add the events' own processing, about 6 us, to each).  Returns {name:
+    (average ms per launch, algorithmic flops per launch)}."""
+    m, n = Gd.shape
+    wsn = torch.empty(ns.ns_workspace_bytes(m, n), dtype=torch.uint8, device=dev)
+    out = torch.empty((m, n), dtype=torch.float32, device=dev)
+    ns.ns_orthogonalize(Gd, coeffs[:2], clip, out=out, workspace=wsn, stream=stream)
+    v = ns.ns_workspace_views(wsn, m, n)
+    sg = v["sg"]
+    qx = (*v["qX"], sg[0:1])
+    qt = (*v["qX16"], sg[0:1])
+    qa = (*v["qA"], sg[1:2])
+    qb = (*v["qB"], sg[2:3])
+    X = v["X"]
+    a, b, c = coeffs[1]
     A = torch.empty((m, m), dtype=torch.float32, device=dev)
     Bm = torch.empty((m, m), dtype=torch.float32, device=dev)
-    Xo = torch.empty_like(X)
     sym = m * (m + 1)
     flops = {"gemm_gram_xxT": sym * n, "gemm_gram_aaT": sym * m, "gemm_update_bx": 2 * m * m * n}
-    qx = ns.nvfp4_quantize(X, ns.NVFP4_ROWS, stream=stream)
-    qt = ns.nvfp4_quantize(X, ns.NVFP4_COLS, stream=stream)
     ws = {k: torch.empty(max(1, ns.nvfp4_gemm_workspace_bytes(*mnk)), dtype=torch.uint8, device=dev)
           for k, mnk in (("g1", (m, m, n, True)), ("g2", (m, m, m, True)), ("g3", (m, n, m, False)))}
     g1 = lambda: ns.nvfp4_gemm(qx, qx, m, m, n, symmetric=True, out=A, workspace=ws["g1"], stream=stream)
-    g1()
-    qa = ns.nvfp4_quantize(A, ns.NVFP4_ROWS, stream=stream)
-    g2 = lambda: ns.nvfp4_gemm(qa, qa, m, m, m, symmetric=True, alpha=2.0315, beta=-4.775, addend=A,
+    g1()          # the whole symmetric A: the addend of the next product
+    g2 = lambda: ns.nvfp4_gemm(qa, qa, m, m, m, symmetric=True, alpha=c, beta=b, addend=A,
                                out=Bm, workspace=ws["g2"], stream=stream)
-    g2()
-    qb = ns.nvfp4_quantize(Bm, ns.NVFP4_ROWS, stream=stream)
-    g3 = lambda: ns.nvfp4_gemm(qb, qt, m, n, m, alpha=1.0, beta=3.4445, addend=X, out=Xo,
+    g3 = lambda: ns.nvfp4_gemm(qb, qt, m, n, m, alpha=1.0, beta=a, addend=X, out=X,
                                workspace=ws["g3"], stream=stream)
-    out = {}
+    res = {}
     for name, fn in (("gemm_gram_xxT", g1), ("gemm_gram_aaT", g2), ("gemm_update_bx", g3)):
         fn()
         fn()
@@ -117,9 +125,9 @@ def kernel_timings(ns, torch, dev, m, n, stream, reps=10):
         for _ in range(reps):
             fn()
         e.record(stream)
-        out[name] = (s, e)
+        res[name] = (s, e)
     torch.cuda.synchronize()
-    return {k: (s.elapsed_time(e) / reps, flops[k]) for k, (s, e) in out.items()}
+    return {k: (s.elapsed_time(e) / reps, flops[k]) for k, (s, e) in res.items()}
 
 
 def source_digest(files=("gemm.hip", "nvfp4_device.hpp")):
@@ -136,8 +144,8 @@ def source_digest(files=("gemm.hip", "nvfp4_device.hpp")):
 # HBM bytes per launch of the dominant kernel (X = a X + qB qX16^T at
 # 3072 x 8192), from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE, each scaled by
 # what the counter reads for a plain copy of known size; see profiles/.
-DOMINANT_TRAFFIC = {"src_sha256": "363d1c41511f59121901871fb4283f57ea55485230a150b1c2893897923e7e5c",
-                    "bytes_per_launch": 440327111}
+DOMINANT_TRAFFIC = {"src_sha256": "33a68630e7e0ae212c5e395a3d1b16402f72a99d8ab660a2aed152c2c4af387b",
+                    "bytes_per_launch": 440582758}
 # HBM bytes of one quantize + dequantize pair of the 2^28 BF16 tensor (the
 # maximum, encode and decode kernels), measured the same way.
 QUANT_TRAFFIC = {"src_sha256": "2a1965ee9e7894210eed719c51af7bb9e79d0cf66106c3a5d10500321b48da8d",
@@ -363,20 +371,20 @@ def main():
             copy_probe(torch, dev)
         print(json.dumps(line), flush=True)
         return
+    coeffs = [synth.QUINTIC] * synth.STEPS
+    spec = synth.ns_workload("ns3072x8192")
+    G, bits, clip = synth.ns_matrix(spec, 0)
+    m, n = G.shape
+    Gd = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
     if args.gemm_only:
         # the three products alone, 10 launches each (for profiling their kernels)
-        kt = kernel_timings(ns, torch, dev, 3072, 8192, stream)
+        kt = kernel_timings(ns, torch, dev, Gd, clip, coeffs, stream)
         if args.copy_probe:
             copy_probe(torch, dev)
         print(json.dumps({"gemm_ms": {k: round(v[0], 4) for k, v in kt.items()},
                           "gemm_tflops": {k: round(v[1] / (v[0] * 1e-3) / 1e12, 2)
                                           for k, v in kt.items()}}), flush=True)
         return
-    coeffs = [synth.QUINTIC] * synth.STEPS
-    spec = synth.ns_workload("ns3072x8192")
-    G, bits, clip = synth.ns_matrix(spec, 0)
-    m, n = G.shape
-    Gd = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
     out = torch.empty((m, n), dtype=torch.float32, device=dev)
     ws = torch.empty(ns.ns_workspace_bytes(m, n), dtype=torch.uint8, device=dev)
     step = lambda: ns.ns_orthogonalize(Gd, coeffs, clip, out=out, workspace=ws, stream=stream)
@@ -402,7 +410,7 @@ def main():
     torch.cuda.synchronize()
     per_call = sorted(a.elapsed_time(b) for a, b in per_call)
 
-    kt = kernel_timings(ns, torch, dev, m, n, stream)
+    kt = kernel_timings(ns, torch, dev, Gd, clip, coeffs, stream)
     # share of one NS step: each GEMM runs once per iteration
     dom = max(kt, key=lambda k: kt[k][0])
     dms, dflops = kt[dom]
