@@ -148,8 +148,8 @@ DOMINANT_TRAFFIC = {"src_sha256": "33a68630e7e0ae212c5e395a3d1b16402f72a99d8ab66
                     "bytes_per_launch": 440582758}
 # HBM bytes of one quantize + dequantize pair of the 2^28 BF16 tensor (the
 # maximum, encode and decode kernels), measured the same way.
-QUANT_TRAFFIC = {"src_sha256": "ac65033bb5dfa6f4b545b73b065c37e1da4d194922b2af654f9c7265dab63cdc",
-                 "bytes_per_pair": 1913946624}
+QUANT_TRAFFIC = {"src_sha256": "316be66944e644fba555c47203b3018c08789dd2a0a461ba89b2daacc53f1fd5",
+                 "bytes_per_pair": 1913510810}
 QUANT_UNIQUE_BYTES_PER_ELEM = (2 + 0.5 + 1 / 16) + (0.5 + 1 / 16 + 2)
 
 
