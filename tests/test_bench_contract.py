@@ -1,5 +1,5 @@
-"""The benchmark's command-line contract: one JSON line with the fields a
-driver reads, and a refusal of multi-GPU runs (the path runs on one GPU)."""
+"""The benchmark's command-line contract: one JSON line with the fields its
+consumers read, and a refusal of multi-GPU runs (the path runs on one GPU)."""
 import json
 import os
 import subprocess
