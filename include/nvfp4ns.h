@@ -24,8 +24,8 @@
  *   - `stream` is a hipStream_t (NULL = the default stream).  Every call
  *     only enqueues work on it and returns; nothing synchronises.  The
  *     caller owns all memory; the library allocates no device memory and
- *     keeps no data between calls (the grouped calls keep only their
- *     streams, see ns_orthogonalize_grouped).
+ *     keeps no data between calls (ns_orthogonalize_grouped and _ex keep
+ *     only their streams; ns_orthogonalize_grouped_on keeps nothing).
  *   - Arguments are validated before anything is enqueued; a negative
  *     status means nothing was launched.  NS_ERR_HIP means a launch failed.
  *   - Data-dependent cases are defined, never errors: a NaN or infinity in
@@ -329,6 +329,23 @@ ns_status ns_orthogonalize_grouped_ex(int count, const void* const* G, const int
                                       const int64_t* n, ns_dtype gt, const float* coeffs, int k,
                                       const float* clip, const ns_options* opt, void* const* out,
                                       ns_dtype ot, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * ns_orthogonalize_grouped_on — ns_orthogonalize_grouped_ex on streams the
+ * caller owns: the matrices run on streams[0 .. nstreams-1] (hipStream_t
+ * values, 1 <= nstreams <= 16, none NULL), forked from `stream` through an
+ * event and joined back into it, so the call is ordered on `stream` (work
+ * already queued on the given streams runs before their share) and can be
+ * captured into a graph.  The library keeps nothing between calls.  opt may
+ * be NULL: clip[i] per matrix, no transform, no 4/6.  Results equal
+ * ns_orthogonalize_grouped_ex's bit for bit.  NS_ERR_ARG for a bad stream
+ * list; other arguments and errors as ns_orthogonalize_grouped_ex.
+ */
+ns_status ns_orthogonalize_grouped_on(int count, const void* const* G, const int64_t* m,
+                                      const int64_t* n, ns_dtype gt, const float* coeffs, int k,
+                                      const float* clip, const ns_options* opt, void* const* out,
+                                      ns_dtype ot, void* ws, size_t ws_bytes,
+                                      void* const* streams, int nstreams, void* stream);
 
 #ifdef __cplusplus
 }

@@ -10,7 +10,8 @@ Functions carry the C names:
     nvfp4_gemm_workspace_bytes, nvfp4_gemm, ns_workspace_bytes, ns_workspace_layout,
     ns_orthogonalize, ns_orthogonalize_rht, ns_orthogonalize_ex,
     ns_abs_quantile_workspace_bytes, ns_abs_quantile,
-    ns_grouped_workspace_bytes, ns_orthogonalize_grouped, ns_orthogonalize_grouped_ex
+    ns_grouped_workspace_bytes, ns_orthogonalize_grouped, ns_orthogonalize_grouped_ex,
+    ns_orthogonalize_grouped_on
 """
 import ctypes
 import os
@@ -78,6 +79,8 @@ _SIGS = {
     "ns_orthogonalize_grouped": (_i, [_i, _vp, _vp, _vp, _i, _vp, _i, _vp, _vp, _i, _vp, _sz, _vp]),
     "ns_orthogonalize_grouped_ex": (_i, [_i, _vp, _vp, _vp, _i, _vp, _i, _vp, _vp, _vp, _i, _vp, _sz,
                                          _vp]),
+    "ns_orthogonalize_grouped_on": (_i, [_i, _vp, _vp, _vp, _i, _vp, _i, _vp, _vp, _vp, _i, _vp, _sz,
+                                         _vp, _i, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -551,4 +554,48 @@ def ns_orthogonalize_grouped_ex(Gs, coeffs, clips=None, clip_quantile=0.0, rht_m
                                                 _ptr(workspace), workspace.numel(),
                                                 _stream(stream, dev)),
                "ns_orthogonalize_grouped_ex")
+    return outs
+
+
+def ns_orthogonalize_grouped_on(Gs, coeffs, streams, clips=None, clip_quantile=0.0,
+                                rht_masks=None, adaptive46=False, out_dtype=NS_F32, outs=None,
+                                workspace=None, stream=None):
+    """ns_orthogonalize_grouped_ex on the caller's streams (a list of
+    torch.cuda.Stream, 1 to 16): the library keeps nothing between calls."""
+    torch = _torch()
+    cnt = len(Gs)
+    _need_cuda(*Gs)
+    dt = _dt(Gs[0])
+    if any(_dt(g) != dt for g in Gs):
+        raise TypeError("all inputs must share one dtype")
+    shapes = [tuple(g.shape) for g in Gs]
+    if outs is None:
+        outs = [torch.empty(s, dtype=_out_dtype(out_dtype), device=Gs[0].device) for s in shapes]
+    if workspace is None:
+        workspace = torch.empty(ns_grouped_workspace_bytes(shapes), dtype=torch.uint8,
+                                device=Gs[0].device)
+    _need_group(Gs, outs, workspace)
+    if clips is not None and len(clips) != cnt:
+        raise ValueError("one clip per matrix")
+    gp = (ctypes.c_void_p * cnt)(*[g.data_ptr() for g in Gs])
+    op = (ctypes.c_void_p * cnt)(*[o.data_ptr() for o in outs])
+    ms = (ctypes.c_int64 * cnt)(*[s[0] for s in shapes])
+    ns_ = (ctypes.c_int64 * cnt)(*[s[1] for s in shapes])
+    cl = (ctypes.c_float * cnt)(*[float(c) for c in clips]) if clips is not None else None
+    carr, k = _coeff_array(coeffs)
+    opt = NsOptions(float("inf"), float(clip_quantile), None, 1 if adaptive46 else 0)
+    marr = None
+    if rht_masks is not None:
+        if len(rht_masks) != k:
+            raise ValueError("one Hadamard mask per step")
+        marr = (ctypes.c_uint16 * k)(*[int(v) & 0xFFFF for v in rht_masks])
+        opt.rht_masks = ctypes.cast(marr, ctypes.POINTER(ctypes.c_uint16))
+    sarr = (ctypes.c_void_p * max(len(streams), 1))(*[s.cuda_stream for s in streams])
+    dev = Gs[0].device
+    with torch.cuda.device(dev):
+        _check(_lib.ns_orthogonalize_grouped_on(cnt, gp, ms, ns_, dt, carr, k, cl,
+                                                ctypes.byref(opt), op, _dt(outs[0]),
+                                                _ptr(workspace), workspace.numel(), sarr,
+                                                len(streams), _stream(stream, dev)),
+               "ns_orthogonalize_grouped_on")
     return outs

@@ -593,12 +593,14 @@ namespace {
 // from and joined back into `caller`: largest problem first (flops of one
 // step), each to the stream with the least work so far.  Every stream used is
 // joined back, also after an error.
+// Streams a grouped call may be given by its caller, at most.
+constexpr int kMaxCallerStreams = 16;
+
 template <class F>
-ns_status run_grouped(int count, const int64_t* m, const int64_t* n, hipStream_t caller, F&& run) {
-  hipStream_t ss[kGroupStreams];
-  NS_TRY(group_streams(ss));
-  const int used = count < kGroupStreams ? count : kGroupStreams;
-  hipEvent_t ev[kGroupStreams + 1] = {};      // ev[0] forks, ev[1 + j] joins stream j
+ns_status run_grouped_on(int count, const int64_t* m, const int64_t* n, hipStream_t caller,
+                         const hipStream_t* ss, int nss, F&& run) {
+  const int used = count < nss ? count : nss;
+  hipEvent_t ev[kMaxCallerStreams + 1] = {};  // ev[0] forks, ev[1 + j] joins stream j
   for (int j = 0; j <= used; ++j) {
     const hipError_t e = hipEventCreateWithFlags(&ev[j], hipEventDisableTiming);
     if (e != hipSuccess) {
@@ -617,7 +619,7 @@ ns_status run_grouped(int count, const int64_t* m, const int64_t* n, hipStream_t
   hipError_t e = hipEventRecord(ev[0], caller);
   for (int j = 0; j < used && e == hipSuccess; ++j) e = hipStreamWaitEvent(ss[j], ev[0], 0);
   if (e == hipSuccess) {
-    double load[kGroupStreams] = {};
+    double load[kMaxCallerStreams] = {};
     for (int i : order) {
       int j = 0;
       for (int t = 1; t < used; ++t) j = load[t] < load[j] ? t : j;
@@ -635,6 +637,14 @@ ns_status run_grouped(int count, const int64_t* m, const int64_t* n, hipStream_t
   if (st != NS_OK) return st;
   if (e != hipSuccess) return hip_failed(e, "group fork/join", __LINE__);
   return NS_OK;
+}
+
+// On the library's own streams of the current device.
+template <class F>
+ns_status run_grouped(int count, const int64_t* m, const int64_t* n, hipStream_t caller, F&& run) {
+  hipStream_t ss[kGroupStreams];
+  NS_TRY(group_streams(ss));
+  return run_grouped_on(count, m, n, caller, ss, kGroupStreams, run);
 }
 
 // The problems of a grouped call run concurrently: no output may touch
@@ -683,10 +693,48 @@ size_t ns_grouped_workspace_bytes(int count, const int64_t* m, const int64_t* n)
   return total;
 }
 
+}  // extern "C"
+
+namespace {
+ns_status grouped_ex_impl(int count, const void* const* G, const int64_t* m, const int64_t* n,
+                          ns_dtype gt, const float* coeffs, int k, const float* clip,
+                          const ns_options* opt, void* const* out, ns_dtype ot, void* ws,
+                          size_t ws_bytes, void* const* streams, int nstreams, void* stream);
+}  // namespace
+
+extern "C" {
+
 ns_status ns_orthogonalize_grouped_ex(int count, const void* const* G, const int64_t* m,
                                       const int64_t* n, ns_dtype gt, const float* coeffs, int k,
                                       const float* clip, const ns_options* opt, void* const* out,
                                       ns_dtype ot, void* ws, size_t ws_bytes, void* stream) {
+  return grouped_ex_impl(count, G, m, n, gt, coeffs, k, clip, opt, out, ot, ws, ws_bytes, nullptr,
+                         0, stream);
+}
+
+ns_status ns_orthogonalize_grouped_on(int count, const void* const* G, const int64_t* m,
+                                      const int64_t* n, ns_dtype gt, const float* coeffs, int k,
+                                      const float* clip, const ns_options* opt, void* const* out,
+                                      ns_dtype ot, void* ws, size_t ws_bytes,
+                                      void* const* streams, int nstreams, void* stream) {
+  if (!streams || nstreams < 1 || nstreams > kMaxCallerStreams) return NS_ERR_ARG;
+  for (int j = 0; j < nstreams; ++j)
+    if (!streams[j]) return NS_ERR_ARG;
+  const ns_options plain{INFINITY, 0.0, nullptr, 0};   // clip[i] per matrix, nothing else
+  return grouped_ex_impl(count, G, m, n, gt, coeffs, k, clip, opt ? opt : &plain, out, ot, ws,
+                         ws_bytes, streams, nstreams, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// The grouped call with options; streams = NULL runs on the library's own
+// streams, else on the caller's nstreams streams.
+ns_status grouped_ex_impl(int count, const void* const* G, const int64_t* m, const int64_t* n,
+                          ns_dtype gt, const float* coeffs, int k, const float* clip,
+                          const ns_options* opt, void* const* out, ns_dtype ot, void* ws,
+                          size_t ws_bytes, void* const* streams, int nstreams, void* stream) {
   if (count <= 0 || !G || !m || !n || !out || !opt) return NS_ERR_ARG;
   const double q = opt->clip_quantile;
   if (std::isnan(q) || q < 0.0 || q > 1.0) return NS_ERR_ARG;
@@ -704,12 +752,20 @@ ns_status ns_orthogonalize_grouped_ex(int count, const void* const* G, const int
   }
   uint8_t* base = static_cast<uint8_t*>(ws);
   const std::vector<size_t> off = group_offsets(count, m, n);
-  return run_grouped(count, m, n, as_stream(stream), [&](int i, hipStream_t s) {
+  auto one = [&](int i, hipStream_t s) {
     const float ci = q > 0.0 ? INFINITY : clip[i];
     return ns_run(G[i], gt, m[i], n[i], coeffs, k, ci, q, opt->rht_masks, opt->adaptive46 != 0, out[i], ot,
                   base + off[(size_t)i], s);
-  });
+  };
+  if (!streams) return run_grouped(count, m, n, as_stream(stream), one);
+  hipStream_t ss[kMaxCallerStreams];
+  for (int j = 0; j < nstreams; ++j) ss[j] = as_stream(streams[j]);
+  return run_grouped_on(count, m, n, as_stream(stream), ss, nstreams, one);
 }
+
+}  // namespace
+
+extern "C" {
 
 ns_status ns_orthogonalize_grouped(int count, const void* const* G, const int64_t* m,
                                    const int64_t* n, ns_dtype gt, const float* coeffs, int k,

@@ -141,6 +141,36 @@ def test_grouped_outputs_must_not_touch_other_problems():
                                         None) == ns.NS_ERR_ARG
 
 
+def test_grouped_on_stream_list_is_validated_on_host():
+    ns = pytest.importorskip("newton_schulz_amd")
+    lib = ns._lib
+    coeffs = (ctypes.c_float * 3)(3.4445, -4.775, 2.0315)
+    m = (ctypes.c_int64 * 2)(64, 64)
+    n = (ctypes.c_int64 * 2)(128, 128)
+    clip = (ctypes.c_float * 2)(1.0, 1.0)
+    wsb = lib.ns_grouped_workspace_bytes(2, m, n)
+    G = (ctypes.c_void_p * 2)(_addr(0).value, _addr(1).value)
+    out = (ctypes.c_void_p * 2)(_addr(2).value, _addr(3).value)
+
+    def call(streams, count):
+        return lib.ns_orthogonalize_grouped_on(2, G, m, n, 1, coeffs, 1, clip, None, out, 0,
+                                               _addr(4), wsb, streams, count, None)
+    s1 = (ctypes.c_void_p * 1)(_addr(5).value)
+    assert call(None, 1) == ns.NS_ERR_ARG                       # no list
+    assert call(s1, 0) == ns.NS_ERR_ARG                         # empty list
+    s17 = (ctypes.c_void_p * 17)(*[_addr(5).value] * 17)
+    assert call(s17, 17) == ns.NS_ERR_ARG                       # more than 16
+    s2 = (ctypes.c_void_p * 2)(_addr(5).value, None)
+    assert call(s2, 2) == ns.NS_ERR_ARG                         # a NULL stream
+    # a valid list reaches the other checks: problem 0 writes over problem 1's input
+    bad = (ctypes.c_void_p * 2)(_addr(1).value, _addr(3).value)
+    assert lib.ns_orthogonalize_grouped_on(2, G, m, n, 1, coeffs, 1, clip, None, bad, 0, _addr(4),
+                                           wsb, s1, 1, None) == ns.NS_ERR_ARG
+    # opt = NULL needs the per-matrix clips
+    assert lib.ns_orthogonalize_grouped_on(2, G, m, n, 1, coeffs, 1, None, None, out, 0, _addr(4),
+                                           wsb, s1, 1, None) == ns.NS_ERR_ARG
+
+
 def test_empty_shapes_are_refused_on_host():
     """Zero-sized matrices have no NVFP4 blocks: every entry point answers
     NS_ERR_SHAPE without enqueuing anything."""

@@ -94,3 +94,30 @@ def test_grouped_call_captures_across_its_streams():
         for i, (o, w) in enumerate(zip(outs, want)):
             assert np.array_equal(host(o), w), (r, i)
     print("[graph] grouped: 3 replays equal", flush=True)
+
+
+def test_grouped_call_on_caller_streams_captures():
+    """The grouped call on two caller-owned streams, captured from the
+    caller's stream, replays to the eager results."""
+    shapes = [(256, 512), (128, 128), (384, 640)]
+    Gs = [to_dev_bf16(synth.to_bf16(synth.student_t(r, c, seed=60 + i))[0])
+          for i, (r, c) in enumerate(shapes)]
+    coeffs = [CUBIC] * 3
+    clips = [0.05] * len(shapes)
+    outs = [torch.empty(s, dtype=torch.float32, device=Gs[0].device) for s in shapes]
+    ws = torch.empty(ns.ns_grouped_workspace_bytes(shapes), dtype=torch.uint8, device=Gs[0].device)
+    streams = [torch.cuda.Stream() for _ in range(2)]
+    call = lambda: ns.ns_orthogonalize_grouped_on(Gs, coeffs, streams, clips=clips, outs=outs,
+                                                  workspace=ws)
+    call()
+    torch.cuda.synchronize()
+    want = [host(o).copy() for o in outs]
+    graph = _capture(call)
+    for r in range(3):
+        for o in outs:
+            o.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, (o, w) in enumerate(zip(outs, want)):
+            assert np.array_equal(host(o), w), (r, i)
+    print("[graph] grouped on caller streams: 3 replays equal", flush=True)

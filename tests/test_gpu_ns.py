@@ -10,6 +10,8 @@ oracle's own float64 against a float32 replay) grows without bound.  Every
 quintic step is instead checked one by one in test_gpu_gemm.py (each GEMM
 fed the oracle's operands) and by the bit-exact quantizer tests.
 """
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -129,6 +131,48 @@ def test_grouped_matches_single_calls():
         single = _run(g, None, coeffs, clip)
         assert np.array_equal(host(o), single)
         _compare(host(o), g, coeffs, clip, f"grouped {g.shape}")
+
+
+def test_grouped_on_caller_streams_matches_grouped():
+    """The grouped call on the caller's streams (one, two and five of them,
+    more than there are matrices) gives the library-stream results bit for
+    bit, plain and with the on-device p99 clip; NULL options through the C
+    ABI give the plain results."""
+    shapes = [(128, 256), (256, 128), (96, 96), (64, 320)]
+    Gs = [to_dev_f32(synth.gaussian(r, c, seed=20 + i)) for i, (r, c) in enumerate(shapes)]
+    coeffs = [CUBIC] * 3
+    clips = [np.inf, 2.5, np.inf, 1.5]
+    want = [host(o).copy() for o in ns.ns_orthogonalize_grouped(Gs, coeffs, clips)]
+    want_q = [host(o).copy() for o in ns.ns_orthogonalize_grouped_ex(Gs, coeffs, clip_quantile=0.99)]
+    for k in (1, 2, 5):
+        streams = [torch.cuda.Stream() for _ in range(k)]
+        got = ns.ns_orthogonalize_grouped_on(Gs, coeffs, streams, clips=clips)
+        torch.cuda.synchronize()
+        for i, (o, w) in enumerate(zip(got, want)):
+            assert np.array_equal(host(o), w), (k, i)
+        got = ns.ns_orthogonalize_grouped_on(Gs, coeffs, streams, clip_quantile=0.99)
+        torch.cuda.synchronize()
+        for i, (o, w) in enumerate(zip(got, want_q)):
+            assert np.array_equal(host(o), w), ("p99", k, i)
+    # opt = NULL
+    outs = [torch.empty(s, dtype=torch.float32, device=DEV) for s in shapes]
+    ws = torch.empty(ns.ns_grouped_workspace_bytes(shapes), dtype=torch.uint8, device=DEV)
+    streams = [torch.cuda.Stream() for _ in range(2)]
+    cnt = len(shapes)
+    gp = (ctypes.c_void_p * cnt)(*[g.data_ptr() for g in Gs])
+    op = (ctypes.c_void_p * cnt)(*[o.data_ptr() for o in outs])
+    ms = (ctypes.c_int64 * cnt)(*[s[0] for s in shapes])
+    nn = (ctypes.c_int64 * cnt)(*[s[1] for s in shapes])
+    cl = (ctypes.c_float * cnt)(*clips)
+    carr = (ctypes.c_float * 9)(*[v for abc in coeffs for v in abc])
+    sarr = (ctypes.c_void_p * 2)(*[s.cuda_stream for s in streams])
+    cur = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    st = ns._lib.ns_orthogonalize_grouped_on(cnt, gp, ms, nn, ns.NS_F32, carr, 3, cl, None, op,
+                                             ns.NS_F32, ws.data_ptr(), ws.numel(), sarr, 2, cur)
+    assert st == ns.NS_OK
+    torch.cuda.synchronize()
+    for i, (o, w) in enumerate(zip(outs, want)):
+        assert np.array_equal(host(o), w), ("NULL options", i)
 
 
 def test_errors_are_reported():
