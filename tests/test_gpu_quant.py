@@ -162,6 +162,43 @@ def test_zero_nan_inf():
             assert np.all(np.isnan(out))
 
 
+def test_full_size_quantizer_whole_tensor():
+    """The same 2^28-element launch checked whole against the C++ oracle
+    (pinned byte for byte to the numpy one): every code and scale byte of
+    both layouts, s_g, and every dequantized BF16 value of the row layout."""
+    from oracle import native as C
+    rows = cols = 16384
+    print("[quant] generating 2^28-element workload", flush=True)
+    bits, vals = synth.quant_workload(rows, cols, seed=2)
+    xd = to_dev_bf16(bits)
+    codes, scales, sg = ns.nvfp4_quantize(xd, ns.NVFP4_ROWS)
+    out = ns.nvfp4_dequantize(codes, scales, sg, rows, cols, ns.NVFP4_ROWS, ns.NS_BF16)
+    print(f"[quant] C++ oracle on {C.threads()} threads", flush=True)
+    oq = C.quantize_rows(vals)
+    assert np.float32(host(sg)[0]).view(np.uint32) == np.float32(oq.global_scale).view(np.uint32)
+    gs, gc = host(scales), host(codes)
+    assert np.array_equal(gs, oq.scales), f"{np.count_nonzero(gs != oq.scales)} scale bytes differ"
+    assert np.array_equal(gc, oq.codes), f"{np.count_nonzero(gc != oq.codes)} code bytes differ"
+    del gs, gc
+    print("[quant] rows: codes and scales equal; checking dequantized values", flush=True)
+    got = host(out)
+    deq = C.dequantize_rows(oq)
+    for r0 in range(0, rows, 1024):                  # BF16 rounding in slices of 2^24 values
+        want = Q.round_to_bf16(deq[r0:r0 + 1024])
+        same = got[r0:r0 + 1024] == want
+        assert same.all(), f"rows {r0}..: {np.count_nonzero(~same)} dequantized values differ"
+        if r0 % 4096 == 0:
+            print(f"[quant] dequantized rows {r0}..{r0 + 1023} equal", flush=True)
+    del got, deq, out
+    print("[quant] column layout", flush=True)
+    ccodes, cscales, csg = ns.nvfp4_quantize(xd, ns.NVFP4_COLS)
+    oqc = C.quantize_rows(np.ascontiguousarray(vals.T))
+    assert np.float32(host(csg)[0]).view(np.uint32) == np.float32(oqc.global_scale).view(np.uint32)
+    assert np.array_equal(host(cscales), oqc.scales)
+    assert np.array_equal(host(ccodes), oqc.codes)
+    print("[quant] 2^28 elements: both layouts bit-exact", flush=True)
+
+
 def test_full_size_quantizer_sampled_rows():
     """16384 x 16384 BF16 Student-t tensor (2^28 elements), the launch the
     benchmark times: s_g from the whole tensor, 96 sampled rows bit-exact."""
