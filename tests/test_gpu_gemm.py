@@ -142,6 +142,50 @@ def test_full_size_gemms_sampled():
     assert np.linalg.norm(got - want) <= TOL * np.linalg.norm(want)
 
 
+def _within_fp32_sum_bound(got, exact, absdot, K, extra=0.0):
+    """Every entry within the error of a float32 sum of K exact products:
+    (K + 2) units of 2^-24 of the sum of the products' magnitudes, plus
+    `extra` (the roundings of an addend term)."""
+    err = np.abs(got.astype(np.float64) - exact)
+    bound = (K + 2) * 2.0 ** -24 * absdot + extra
+    bad = err > bound
+    assert not bad.any(), f"{np.count_nonzero(bad)} entries outside the bound; worst {np.max(err / (bound + 1e-300)):.3g}x"
+
+
+def test_full_size_gemms_whole():
+    """3072 x 8192 (the benchmark's shape), every output entry: GEMM1 (3072^2,
+    K = 8192, symmetric, split tiles summed in the kernel) and GEMM3 (3072 x
+    8192, K = 3072, beta X + qB qX16) against float64 products of the
+    dequantized operands (the C++ oracle), each entry within the float32
+    summation bound of its own terms."""
+    from oracle import native as C
+    m, n = 3072, 8192
+    rng = np.random.default_rng(14)
+    X = rng.standard_normal((m, n)).astype(np.float32)
+    qx = C.quantize_rows(X)
+    qx16 = C.quantize_rows(np.ascontiguousarray(X.T), amax=Q.tensor_amax(X))
+    Bm = rng.standard_normal((m, m)).astype(np.float32)
+    Bm = (Bm + Bm.T).astype(np.float32)
+    qb = C.quantize_rows(Bm)
+    print("[gemm] whole GEMM1 / GEMM3 on the GPU", flush=True)
+    qx_dev = dev_q(qx)
+    A = host(ns.nvfp4_gemm(qx_dev, qx_dev, m, m, n, symmetric=True))
+    Xg = host(ns.nvfp4_gemm(dev_q(qb), dev_q(qx16), m, n, m, alpha=1.0, beta=3.4445,
+                            addend=to_dev_f32(X)))
+    print("[gemm] C++ oracle products", flush=True)
+    dx = C.dequantize_rows(qx)
+    _within_fp32_sum_bound(A, C.gemm_nt(dx, dx, symmetric=True),
+                           C.gemm_nt(np.abs(dx), np.abs(dx), symmetric=True), n)
+    del dx, A
+    db, dx16 = C.dequantize_rows(qb), C.dequantize_rows(qx16)
+    prod = C.gemm_nt(db, dx16)
+    absprod = C.gemm_nt(np.abs(db), np.abs(dx16))
+    ax = 3.4445 * X.astype(np.float64)
+    # the addend term: beta * x rounded once, then the fused add rounds once more
+    _within_fp32_sum_bound(Xg, ax + prod, absprod, m, extra=2 * 2.0 ** -24 * (np.abs(ax) + absprod))
+    print("[gemm] 3072x8192: every entry of both products within the float32 bound", flush=True)
+
+
 def test_symmetric_gemm_split_k():
     """A symmetric product with fewer tiles than CUs: its tiles are split
     along K into eight parts whose FP32 partials the last part to finish
