@@ -3,7 +3,8 @@ against every tile size), value distributions, input types and axes that
 the fixed-shape tests do not name.  The same bars as there: the quantizer
 bit for bit (codes, scales, s_g, dequantized values), each product within
 1e-5 relative Frobenius error of the float64 product of the dequantized
-operands, NS (a stable schedule) within 2e-2 and the singular-value band."""
+operands and every entry within the float32 summation bound of its own
+terms, NS (a stable schedule) within 2e-2 and the singular-value band."""
 import numpy as np
 import pytest
 
@@ -91,10 +92,19 @@ def test_gemm_random_cases(case):
     qd = pd if sym else _dev_q(qq)
     got = host(ns.nvfp4_gemm(pd, qd, M, Nn, K, symmetric=sym, alpha=alpha, beta=beta,
                              addend=to_dev_f32(add) if beta != 0.0 else None))
-    want = alpha * N.gemm_nt(Q.dequantize_rows(qp), Q.dequantize_rows(qq))
+    dp, dq = Q.dequantize_rows(qp), Q.dequantize_rows(qq)
+    prod = alpha * N.gemm_nt(dp, dq)
+    absprod = abs(alpha) * N.gemm_nt(np.abs(dp), np.abs(dq))
+    u = 2.0 ** -24
+    want, bound = prod, (K + 2) * u * absprod
     if beta != 0.0:
-        want = want + beta * add.astype(np.float64)
+        badd = beta * add.astype(np.float64)
+        want = want + badd
+        bound = bound + 2 * u * (np.abs(badd) + absprod)
     assert rel_fro(got, want) <= 1e-5
+    # every entry within the float32 summation bound of its own terms
+    err = np.abs(got.astype(np.float64) - want)
+    assert (err <= bound).all(), float(np.max(err / np.maximum(bound, 1e-300)))
     if sym:
         assert np.array_equal(got, got.T)
 
