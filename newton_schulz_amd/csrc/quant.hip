@@ -47,15 +47,27 @@ constexpr int kUnroll = NVFP4_QUANT_UNROLL;     // items per lane per trip
 #define NVFP4_AMAX_UNROLL 8
 #endif
 constexpr int kAmaxUnroll = NVFP4_AMAX_UNROLL;
+constexpr int64_t kCachedTailBytes = (int64_t)96 << 20;
 
 typedef float float2_t __attribute__((ext_vector_type(2)));
 // Streaming accesses of the standalone quantizer's passes, with the
-// non-temporal hint: the tensor (twice the Infinity Cache) is read once per
-// pass and its codes or decoded values written once, so nothing is gained
-// by keeping the lines.  On 2^28 BF16 values (MI355X) the hint took the
-// quantize + dequantize pair from 403 to 359 us: the decode pass with
+// non-temporal hint: a tensor larger than the Infinity Cache (256 MB) is
+// read once per pass and its decoded values written once, so nothing is
+// gained by keeping those lines.  On 2^28 BF16 values (MI355X) the hint took
+// the quantize + dequantize pair from 403 to 359 us: the decode pass with
 // non-temporal stores from 143 to 110 us, the encode pass from 250 to 238
 // us with non-temporal loads; outputs unchanged.
+//
+// What the cache does keep is chosen: the maximum pass reads the last
+// kCachedTailBytes of the tensor last, with ordinary (allocating) loads, and
+// the encode pass, which walks from the end, reads that tail first, so it
+// comes from the cache; the encode pass stores its codes with ordinary
+// stores, last-written at the tensor's start, where a decode pass run next
+// begins.  Tail and codes (151 MB for 2^28 values) must fit the cache
+// together.  Measured on 2^28 BF16 values, interleaved runs on one MI355X:
+// the pair 347-348 us with every access non-temporal; 330 us with ordinary
+// code stores; with those and a cached tail of 64 / 96 / 128 / 192 MB 322 /
+// 320 / 335 / 356 us (a 192 MB tail without the code stores 339 us).
 typedef unsigned int nt_u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 load_nt(const uint4* p) {
   const nt_u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const nt_u32x4*>(p));
@@ -65,7 +77,6 @@ __device__ __forceinline__ void store_nt(uint4* p, uint4 r) {
   const nt_u32x4 v = {r.x, r.y, r.z, r.w};
   __builtin_nontemporal_store(v, reinterpret_cast<nt_u32x4*>(p));
 }
-__device__ __forceinline__ void store_nt(uint32_t* p, uint32_t v) { __builtin_nontemporal_store(v, p); }
 
 
 // 16 consecutive elements starting at element `idx` (a multiple of 16) as
@@ -143,86 +154,124 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(const void* x, int64_t n
       }
     }
   };
-  // this workgroup's chunk of rounds, kAmaxUnroll 16-byte loads in flight
-  // per lane
-  const int64_t rounds = (nvec + kThreads - 1) / kThreads;
-  const int64_t r0 = rounds * blockIdx.x / gridDim.x, r1 = rounds * (blockIdx.x + 1) / gridDim.x;
-  const int64_t e = r1 * kThreads < nvec ? r1 * kThreads : nvec;
-  int64_t i = r0 * kThreads + threadIdx.x;
-  for (; i + (kAmaxUnroll - 1) * kThreads < e; i += kAmaxUnroll * kThreads) {
-    uint4 w[kAmaxUnroll];
+  // this workgroup's chunk of the rounds of [v0, v1), kAmaxUnroll 16-byte
+  // loads in flight per lane
+  auto walk = [&](int64_t v0, int64_t v1, auto cached) {
+    auto ld = [&](int64_t k) {
+      if constexpr (decltype(cached)::value) return p[k];
+      else return load_nt(p + k);
+    };
+    const int64_t rounds = (v1 - v0 + kThreads - 1) / kThreads;
+    const int64_t r0 = rounds * blockIdx.x / gridDim.x, r1 = rounds * (blockIdx.x + 1) / gridDim.x;
+    const int64_t e = v0 + r1 * kThreads < v1 ? v0 + r1 * kThreads : v1;
+    int64_t i = v0 + r0 * kThreads + threadIdx.x;
+    for (; i + (kAmaxUnroll - 1) * kThreads < e; i += kAmaxUnroll * kThreads) {
+      uint4 w[kAmaxUnroll];
 #pragma unroll
-    for (int u = 0; u < kAmaxUnroll; ++u) w[u] = load_nt(p + i + u * kThreads);
+      for (int u = 0; u < kAmaxUnroll; ++u) w[u] = ld(i + u * kThreads);
 #pragma unroll
-    for (int u = 0; u < kAmaxUnroll; ++u) fold(w[u]);
-  }
-  for (; i < e; i += kThreads) fold(load_nt(p + i));
+      for (int u = 0; u < kAmaxUnroll; ++u) fold(w[u]);
+    }
+    for (; i < e; i += kThreads) fold(ld(i));
+  };
+  // the body streams; the tail, read last, is left in the Infinity Cache
+  // for the encode pass
+  const int64_t tail = nvec < kCachedTailBytes / 16 ? nvec : kCachedTailBytes / 16;
+  walk(0, nvec - tail, std::false_type{});
+  walk(nvec - tail, nvec, std::true_type{});
   amax_publish_block(m, slot);
 }
 
 // ------------------------------------------------------- row quantizer ----
 
+// Maximum over the G lanes of an aligned lane group (G = 2 or 4), on the
+// DPP crossbar: quad_perm [1,0,3,2] swaps lanes 2k and 2k+1, [2,3,0,1]
+// lanes 4k+j and 4k+j+2.  Every lane of a group is active or none is.
+template <int G>
+__device__ __forceinline__ uint32_t group_max_u32(uint32_t m) {
+  uint32_t t = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, false);
+  m = t > m ? t : m;
+  if constexpr (G == 4) {
+    t = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x4E, 0xF, 0xF, false);
+    m = t > m ? t : m;
+  }
+  return m;
+}
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
 // Each lane owns 16 bytes of input (8 BF16 or 4 FP32 values), so every
 // load instruction of a wave reads one contiguous kilobyte; the 2 or 4
-// lanes of a block combine their maxima with lane shuffles.  The grid walks
-// the tensor from its end to its start: the amax pass just read it front to
-// back, so the last part it read may still be in the Infinity Cache.
+// lanes of a block combine their maxima across the DPP crossbar.  The grid
+// walks the tensor from its end to its start: the amax pass just read it
+// front to back, so the last part it read may still be in the Infinity
+// Cache.  Lane i takes item items - 1 - (i xor (G - 1)): blocks in reverse
+// order, the lanes of a block in their own order.  Since the grid stride
+// is a multiple of G, a lane's next item is exactly one stride lower, so
+// the loop steps one index instead of recomputing it per access.
 template <Dt T>
 __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
     const void* x, int64_t nelem, const uint32_t* amax_slot, float* sg_out,
     uint8_t* codes, uint8_t* scales, uint32_t* zero_slot) {
   constexpr int EPL = T == Dt::F32 ? 4 : 8;   // elements per lane
   constexpr int G = 16 / EPL;                 // lanes per block
+  constexpr int LOG_G = G == 2 ? 1 : 2;
+  using Word = typename std::conditional<EPL == 8, uint32_t, uint16_t>::type;
   const float sg = global_scale_from_amax(amax_read(amax_slot));
   if (blockIdx.x == 0) {
     if (sg_out && threadIdx.x == 0) *sg_out = sg;
     if (zero_slot) amax_clear(zero_slot);
   }
-  const int64_t items = nelem / EPL, groups = items / G;
+  const int64_t items = nelem / EPL;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
-  auto encode_item = [&](int64_t i, uint4 w) {
-    const int li = (int)(i % G);
-    const int64_t blk = groups - 1 - i / G;
-    const int64_t item = blk * G + li;
+  const bool first = (threadIdx.x & (G - 1)) == 0;   // the lane that stores the scale
+  const uint4* src = reinterpret_cast<const uint4*>(x);
+  Word* dst = reinterpret_cast<Word*>(codes);
+  auto encode_item = [&](int64_t item, uint4 w) {
     uint32_t v[EPL];
+    uint32_t amax;
     if constexpr (T == Dt::F32) {
       v[0] = w.x; v[1] = w.y; v[2] = w.z; v[3] = w.w;
+      amax = 0;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const uint32_t a = v[e] & 0x7FFFFFFFu;
+        amax = a > amax ? a : amax;
+      }
     } else {
+      // the eight BF16 magnitudes compared as 16-bit pairs; a BF16 value's
+      // bits shifted up 16 are its FP32 bits, so the order is the same
+      u16x2 m = __builtin_bit_cast(u16x2, w.x & 0x7FFF7FFFu);
+      m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w.y & 0x7FFF7FFFu));
+      m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w.z & 0x7FFF7FFFu));
+      m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w.w & 0x7FFF7FFFu));
+      amax = (uint32_t)(m[0] > m[1] ? m[0] : m[1]) << 16;
       const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
       for (int t = 0; t < 4; ++t) { v[2 * t] = ws[t] << 16; v[2 * t + 1] = ws[t] & 0xFFFF0000u; }
     }
-    uint32_t amax = 0;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      const uint32_t a = v[e] & 0x7FFFFFFFu;
-      amax = a > amax ? a : amax;
-    }
-#pragma unroll
-    for (int o = 1; o < G; o <<= 1) {
-      const uint32_t t = __shfl_xor(amax, o, 64);
-      amax = t > amax ? t : amax;
-    }
+    amax = group_max_u32<G>(amax);
     const uint32_t sc = block_scale_byte(amax, sg);
     const uint32_t c = encode_lane<EPL>(v, sg, sc);
-    if constexpr (EPL == 8) store_nt(reinterpret_cast<uint32_t*>(codes) + item, c);
-    else reinterpret_cast<uint16_t*>(codes)[item] = (uint16_t)c;
-    if (li == 0) scales[blk] = (uint8_t)sc;
-  };
-  auto src = [&](int64_t i) {
-    return load_nt(reinterpret_cast<const uint4*>(x) + (groups - 1 - i / G) * G + i % G);
+    dst[item] = (Word)c;
+    if (first) scales[item >> LOG_G] = (uint8_t)sc;
   };
   // kUnroll items per lane per trip, all loads issued before any is encoded,
   // so that each lane keeps kUnroll * 16 bytes in flight
+  // the tensor's last kCachedTailBytes, which the maximum pass read last,
+  // come first in this walk and are read from the Infinity Cache
+  const int64_t tail_start = items - kCachedTailBytes / 16;
+  auto load_item = [&](int64_t k) { return k >= tail_start ? src[k] : load_nt(src + k); };
   int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  for (; i + (kUnroll - 1) * stride < items; i += kUnroll * stride) {
+  int64_t item = items - 1 - (i ^ (G - 1));
+  for (; i + (kUnroll - 1) * stride < items; i += kUnroll * stride, item -= kUnroll * stride) {
     uint4 w[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) w[u] = src(i + u * stride);
+    for (int u = 0; u < kUnroll; ++u) w[u] = load_item(item - u * stride);
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) encode_item(i + u * stride, w[u]);
+    for (int u = 0; u < kUnroll; ++u) encode_item(item - u * stride, w[u]);
   }
-  for (; i < items; i += stride) encode_item(i, src(i));
+  for (; i < items; i += stride, item -= stride) encode_item(item, load_item(item));
 }
 
 // ------------------------------------------- tiled quantizer, both axes ----
@@ -392,7 +441,12 @@ __global__ __launch_bounds__(kThreads) void amax_tiles_kernel(
 // to bf16, two at a time.  hi = RN_f32(u*sg) then RN_bf16(hi) equals the
 // single rounding unless hi landed exactly on a bf16 midpoint (low half
 // 0x8000) or is tiny (the f32 product may have lost bits to underflow);
-// those rare lanes take the exact double path.
+// those rare lanes take the exact double path.  Zero products take it too
+// (their exponent field is below the bound), which is exact and, measured,
+// no loss: the decode pass is bound by its store stream, and on 2^28 values
+// both a check that lets zeros through and one branch per eight values
+// instead of per value made it slower (122-125 us against 107; with 1024
+// workgroups instead of 8192, 110 us).
 __device__ __forceinline__ uint16_t product_to_bf16_exact(float u, float sg) {
   const double d = (double)u * (double)sg;   // exact
   const double a = fabs(d);

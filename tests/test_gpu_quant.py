@@ -162,6 +162,65 @@ def test_zero_nan_inf():
             assert np.all(np.isnan(out))
 
 
+def _bf16_midpoint_scales(u, rng, want):
+    """float32 tensor scales s_g for which RN_f32(u * s_g) has low half 0x8000,
+    a bf16 midpoint, with the exact product above it, below it, or on it."""
+    from fractions import Fraction
+    found = []
+    while len(found) < want:
+        hi = int(rng.integers(0x3000, 0x4F00))          # a normal bf16 value
+        m = np.uint32((hi << 16) | 0x8000).view(np.float32)
+        sg0 = np.float32(float(Fraction(float(m)) / Fraction(u)))
+        for d in range(-3, 4):
+            sg = np.float32(np.uint32(sg0.view(np.uint32) + np.uint32(d) if d >= 0
+                                      else sg0.view(np.uint32) - np.uint32(-d)).view(np.float32))
+            exact = Fraction(u) * Fraction(float(sg))         # <= 30 bits: exact in float64
+            f32 = np.float32(float(exact))
+            if int(f32.view(np.uint32)) & 0xFFFF == 0x8000:
+                found.append((sg, (exact > Fraction(float(f32))) - (exact < Fraction(float(f32)))))
+    return found
+
+
+@pytest.mark.parametrize("dtype", [ns.NS_BF16, ns.NS_F32])
+def test_decode_rounds_once_at_bf16_midpoints(dtype):
+    """Dequantized values u * s_g rounded once to bf16 (or f32), where the
+    float32 product lands exactly on a bf16 midpoint: with the exact product
+    above it, below it (double rounding would go the wrong way) and on it
+    (ties to even), each among random codes and scales of the same 8-value
+    items; and a tensor scale below 2^-90, where products can be tiny."""
+    rng = np.random.default_rng(11)
+    rows, cols = 64, 64
+    cases = []
+    for u, want in ((1.5, 8), (3.0, 4), (0.75, 4)):
+        cases += [(u, sg, side) for sg, side in _bf16_midpoint_scales(u, rng, want)]
+    cases += [(1.0, np.float32((1.0 + 2.0 ** -8) * 2.0 ** -7), 0),   # exact ties: u a power of two
+              (1.0, np.float32(1.0 + 2.0 ** -8), 0)]
+    sides = {c[2] for c in cases}
+    assert sides == {-1, 0, 1}, sides
+    cases.append((1.5, np.float32(2.0 ** -120 * 1.2345), 0))  # tiny products
+    q_of = {0.75: (1.5, 0x30), 1.5: (1.5, 0x38), 3.0: (3.0, 0x38), 1.0: (1.0, 0x38)}
+    e2m1 = {0.5: 1, 1.0: 2, 1.5: 3, 2.0: 4, 3.0: 5, 4.0: 6, 6.0: 7}
+    for n, (u, sg, side) in enumerate(cases):
+        codes = rng.integers(0, 256, (rows, cols // 2), dtype=np.uint8)
+        scales = rng.integers(0, 0x7F, (rows, cols // 16), dtype=np.uint8)
+        q, sbyte = q_of[u]
+        # the designed value at several positions, in both nibbles
+        for r, c in ((0, 0), (5, 17), (63, 63), (31, 8), (31, 9)):
+            scales[r, c // 16] = sbyte
+            nib = e2m1[q] | (8 if (r + c) % 3 == 0 else 0)
+            byte = codes[r, c // 2]
+            codes[r, c // 2] = (byte & 0xF0) | nib if c % 2 == 0 else (byte & 0x0F) | (nib << 4)
+        print(f"[dequant] case {n}: u={u} s_g={float(sg)!r} side={side}", flush=True)
+        oq = Q.NVFP4Tensor(codes=codes, scales=scales, global_scale=np.float32(sg), rows=rows, cols=cols)
+        exact = Q.dequantize_rows(oq)
+        want = Q.round_to_bf16(exact) if dtype == ns.NS_BF16 else exact.astype(np.float32).astype(np.float64)
+        got = host(ns.nvfp4_dequantize(torch.from_numpy(codes).to(DEV), torch.from_numpy(scales).to(DEV),
+                                       torch.tensor([sg], dtype=torch.float32, device=DEV),
+                                       rows, cols, ns.NVFP4_ROWS, dtype))
+        same = (got == want) & (np.signbit(got) == np.signbit(want))
+        assert same.all(), f"case {n}: {np.count_nonzero(~same)} values differ"
+
+
 def test_full_size_quantizer_whole_tensor():
     """The same 2^28-element launch checked whole against the C++ oracle
     (pinned byte for byte to the numpy one): every code and scale byte of
@@ -197,6 +256,37 @@ def test_full_size_quantizer_whole_tensor():
     assert np.array_equal(host(cscales), oqc.scales)
     assert np.array_equal(host(ccodes), oqc.codes)
     print("[quant] 2^28 elements: both layouts bit-exact", flush=True)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_tensor_maximum_on_either_side_of_the_cached_tail(dtype):
+    """A 128 MB tensor, larger than the last 96 MB that the maximum pass
+    reads last with allocating loads (and the encode pass first): the
+    tensor maximum planted at the start, just before and at the first
+    element of that tail, and at the end is found every time (s_g bit for
+    bit), and the rows around the planted element and the boundary encode
+    bit for bit."""
+    rows, cols = (8192, 4096) if dtype == "f32" else (8192, 8192)
+    esize = 4 if dtype == "f32" else 2
+    boundary = (rows * cols * esize - (96 << 20)) // esize   # first element of the tail
+    x = (np.random.default_rng(5).standard_normal((rows, cols)) * 1e-3).astype(np.float32)
+    xd, vals = _device_input(x, dtype)
+    big = 7.0                                    # exact in BF16, the unique maximum
+    want_sg = Q.global_scale(big)
+    for pos in (0, boundary - 1, boundary, rows * cols - 1):
+        r, c = divmod(pos, cols)
+        print(f"[quant] {dtype} maximum at element {pos} (row {r})", flush=True)
+        old = float(vals[r, c])
+        xd[r, c] = big
+        codes, scales, sg = ns.nvfp4_quantize(xd, ns.NVFP4_ROWS)
+        assert np.float32(host(sg)[0]).view(np.uint32) == np.float32(want_sg).view(np.uint32)
+        sel = np.unique([0, r, boundary // cols - 1, boundary // cols, rows - 1])
+        part = vals[sel].astype(np.float64)
+        part[np.searchsorted(sel, r), c] = big
+        oq = Q.quantize_rows(part, amax=big)
+        assert np.array_equal(host(scales)[sel], oq.scales)
+        assert np.array_equal(host(codes)[sel], oq.codes)
+        xd[r, c] = old
 
 
 def test_full_size_quantizer_sampled_rows():
