@@ -304,9 +304,13 @@ size_t ns_grouped_workspace_bytes(int count, const int64_t* m, const int64_t* n)
  *   m, n    HOST arrays of shapes.   clip  HOST array of per-matrix clips.
  *   ws      device scratch of ns_grouped_workspace_bytes() (one part per
  *           matrix).
- * The matrices run concurrently on up to four library-owned streams of the
- * current device (default priority, created on the first grouped call and
- * kept until the process ends), forked from `stream` through an event and
+ * Matrices that share an iterate shape (min(m, n) x max(m, n), either
+ * orientation) run in batches: each pass of a step is one launch for
+ * several of them, each matrix on its single call's kernels and tile
+ * schedule.  The batches run concurrently on up to four library-owned
+ * streams of the current device (default priority, created on the first
+ * grouped call and kept until the process ends), forked from `stream`
+ * through an event and
  * joined back into it: the call is ordered on `stream` like any other and
  * can be captured into a graph.  Each result equals its single call's bit
  * for bit.  Calls that overlap on one device share the streams.

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstddef>
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
@@ -11,6 +12,7 @@
 #include <cstring>
 #include <initializer_list>
 #include <mutex>
+#include <utility>
 #include <vector>
 
 #include "../../include/nvfp4ns.h"
@@ -307,6 +309,109 @@ ns_status ns_run(const void* G, ns_dtype gt, int64_t m, int64_t n, const float* 
   return NS_OK;
 }
 
+// ns_run (without the transform) for `count` matrices whose iterates share
+// one shape xm x xn (matrix j is G[j], m[j] x n[j], transposed when m > n),
+// with workspace regions of ns_layout size at ws + j * stride.  The passes
+// done once per call (clip quantile, norm, first quantization, write-out)
+// run per matrix; every pass of a step runs once for all of them, one
+// launch per phase with grid row y = matrix.  Each matrix runs the kernels
+// and tile schedules of its own ns_run in the same order, so every result
+// equals ns_run's bit for bit.  All three products need fast-path plans.
+ns_status ns_run_batch(int count, const void* const* G, ns_dtype gt, const int64_t* m,
+                       const int64_t* n, const float* coeffs, int k, const float* clip,
+                       double clip_q, bool a46, void* const* out, ns_dtype ot, uint8_t* ws,
+                       size_t stride, hipStream_t s) {
+  const uint32_t o46 = a46 ? 1u : 0u;
+  const NsLayout L = ns_layout(m[0], n[0]);
+  const int64_t xm = m[0] < n[0] ? m[0] : n[0], xn = m[0] < n[0] ? n[0] : m[0];
+  const int64_t bs = (int64_t)stride;
+  auto at = [&](int j, size_t off) { return ws + (size_t)j * stride + off; };
+  const bool any_split = L.total > L.gemm_part;
+
+  // once per matrix: clip, norm, and the first quantization of X
+  for (int j = 0; j < count; ++j) {
+    const bool tr = m[j] > n[j];
+    float* X = reinterpret_cast<float*>(at(j, L.X));
+    uint32_t* slot = reinterpret_cast<uint32_t*>(at(j, L.slot));
+    float* sg = reinterpret_cast<float*>(at(j, L.sg));
+    double* part = reinterpret_cast<double*>(at(j, L.part));
+    uint32_t* part_amax = reinterpret_cast<uint32_t*>(at(j, L.part_amax));
+    double* inv = reinterpret_cast<double*>(at(j, L.inv));
+    uint8_t* gws = at(j, L.gemm_part);
+    float* clipd = nullptr;
+    if (clip_q > 0.0) {
+      clipd = reinterpret_cast<float*>(at(j, L.clip));
+      NS_TRY(nvfp4::launch_abs_quantile(G[j], (Dt)gt, m[j] * n[j],
+                                        quantile_rank(clip_q, m[j] * n[j]), clipd, at(j, L.sel), s));
+    }
+    NS_TRY(nvfp4::launch_norm_partials(G[j], (Dt)gt, m[j] * n[j], clip[j], clipd, part, part_amax,
+                                       s));
+    NS_TRY(nvfp4::launch_norm_finalize(part, part_amax, inv, slot, slot + kSlotWords,
+                                       slot + 2 * kSlotWords,
+                                       any_split ? reinterpret_cast<uint32_t*>(gws) : nullptr,
+                                       (int)(nvfp4::kGemmCounterBytes / sizeof(uint32_t)), s));
+    if (tr) {
+      NS_TRY(nvfp4::launch_normalize(G[j], (Dt)gt, xm, xn, true, clip[j], clipd, inv, X, slot, s));
+      NS_TRY(nvfp4::launch_quant_tiles(X, Dt::F32, xm, xn, slot, sg, at(j, L.qx_c), at(j, L.qx_s),
+                                       at(j, L.qt_c), at(j, L.qt_s), slot + kSlotWords, s, nullptr,
+                                       nullptr, nvfp4::RhtArg{0u, 0u, o46}));
+    } else {
+      NS_TRY(nvfp4::launch_normalize_quant_tiles(G[j], (Dt)gt, xm, xn, clip[j], clipd, inv, X, slot,
+                                                 sg, at(j, L.qx_c), at(j, L.qx_s), at(j, L.qt_c),
+                                                 at(j, L.qt_s), slot + kSlotWords, a46, s));
+    }
+  }
+
+  // the steps, each phase one launch for every matrix (matrix 0's pointers)
+  float* X = reinterpret_cast<float*>(at(0, L.X));
+  float* A = reinterpret_cast<float*>(at(0, L.A));
+  float* B = reinterpret_cast<float*>(at(0, L.B));
+  float* sg = reinterpret_cast<float*>(at(0, L.sg));
+  uint32_t* slot = reinterpret_cast<uint32_t*>(at(0, L.slot));
+  uint32_t *slotX = slot, *slotA = slot + kSlotWords, *slotB = slot + 2 * kSlotWords;
+  float *sgX = sg, *sgA = sg + 1, *sgB = sg + 2;
+  uint8_t* gws = at(0, L.gemm_part);
+  // per matrix: where its last update product writes (its output, or X)
+  std::vector<float*> direct((size_t)count);
+  for (int j = 0; j < count; ++j)
+    direct[(size_t)j] = (m[j] <= n[j] && ot == NS_F32) ? static_cast<float*>(out[j])
+                                                       : reinterpret_cast<float*>(at(j, L.X));
+  for (int it = 0; it < k; ++it) {
+    const float a = coeffs[3 * it], b = coeffs[3 * it + 1], c = coeffs[3 * it + 2];
+    if (it > 0)
+      NS_TRY(nvfp4::launch_quant_tiles(X, Dt::F32, xm, xn, slotX, sgX, at(0, L.qx_c), at(0, L.qx_s),
+                                       at(0, L.qt_c), at(0, L.qt_s), slotA, s, nullptr, nullptr,
+                                       nvfp4::RhtArg{0u, 0u, o46}, count, bs));
+    nvfp4::GemmProblem g1{at(0, L.qx_c), at(0, L.qx_s), sgX, at(0, L.qx_c), at(0, L.qx_s), sgX,
+                          xm, xm, xn, 1, 1.0f, 0.0f, nullptr, A, slotA, 1, 1, count, bs};
+    NS_TRY(nvfp4::launch_gemm(g1, L.p1, gws, false, s));
+    NS_TRY(nvfp4::launch_quant_sym_tiles(A, xm, slotA, sgA, at(0, L.qa_c), at(0, L.qa_s), slotB,
+                                         a46, s, count, bs));
+    nvfp4::GemmProblem g2{at(0, L.qa_c), at(0, L.qa_s), sgA, at(0, L.qa_c), at(0, L.qa_s), sgA,
+                          xm, xm, xm, 1, c, b, A, B, slotB, 1, 1, count, bs};
+    NS_TRY(nvfp4::launch_gemm(g2, L.p2, gws, false, s));
+    NS_TRY(nvfp4::launch_quant_sym_tiles(B, xm, slotB, sgB, at(0, L.qb_c), at(0, L.qb_s), slotX,
+                                         a46, s, count, bs));
+    nvfp4::GemmProblem g3{at(0, L.qb_c), at(0, L.qb_s), sgB, at(0, L.qt_c), at(0, L.qt_s), sgX,
+                          xm, xn, xm, 0, 1.0f, a, X, X, slotX, 1, 0, count, bs};
+    // the last step of an FP32, untransposed matrix writes straight into
+    // its output, as its single call does (the others keep X in place)
+    if (it == k - 1 && direct.size() == (size_t)count) g3.out_each = direct.data();
+    NS_TRY(nvfp4::launch_gemm(g3, L.p3, gws, false, s));
+  }
+  for (int j = 0; j < count; ++j)
+    if (!(k > 0 && direct[(size_t)j] == out[j]))
+      NS_TRY(nvfp4::launch_write_out(reinterpret_cast<float*>(at(j, L.X)), xm, xn, m[j] > n[j],
+                                     out[j], (Dt)ot, s));
+  return NS_OK;
+}
+
+// A batch needs every product on the fast path (K a multiple of 128).
+bool batchable(int64_t m, int64_t n) {
+  const NsLayout L = ns_layout(m, n);
+  return L.p1.fast && L.p2.fast && L.p3.fast;
+}
+
 ns_status validate_ns(const void* G, int gt, int64_t m, int64_t n, const float* coeffs, int k,
                       float clip, const void* out, int ot) {
   if (!G || !out || !coeffs || k <= 0 || !dtype_ok(gt) || !dtype_ok(ot)) return NS_ERR_ARG;
@@ -589,15 +694,15 @@ ns_status ns_abs_quantile(const void* x, ns_dtype xt, int64_t count, double q, f
 
 namespace {
 
-// Runs run(i, stream) for problems 0 .. count-1 on the group streams, forked
-// from and joined back into `caller`: largest problem first (flops of one
-// step), each to the stream with the least work so far.  Every stream used is
+// Runs run(i, stream) for work items 0 .. count-1 on the group streams,
+// forked from and joined back into `caller`: largest item first (cost[i]),
+// each to the stream with the least work so far.  Every stream used is
 // joined back, also after an error.
 // Streams a grouped call may be given by its caller, at most.
 constexpr int kMaxCallerStreams = 16;
 
 template <class F>
-ns_status run_grouped_on(int count, const int64_t* m, const int64_t* n, hipStream_t caller,
+ns_status run_grouped_on(int count, const std::vector<double>& cost, hipStream_t caller,
                          const hipStream_t* ss, int nss, F&& run) {
   const int used = count < nss ? count : nss;
   hipEvent_t ev[kMaxCallerStreams + 1] = {};  // ev[0] forks, ev[1 + j] joins stream j
@@ -608,13 +713,10 @@ ns_status run_grouped_on(int count, const int64_t* m, const int64_t* n, hipStrea
       return hip_failed(e, "hipEventCreateWithFlags", __LINE__);
     }
   }
-  auto cost = [&](int i) {
-    const double a = (double)m[i], b = (double)n[i];
-    return a * b * (a < b ? a : b);
-  };
   std::vector<int> order((size_t)count);
   for (int i = 0; i < count; ++i) order[(size_t)i] = i;
-  std::stable_sort(order.begin(), order.end(), [&](int x, int y) { return cost(x) > cost(y); });
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int x, int y) { return cost[(size_t)x] > cost[(size_t)y]; });
   ns_status st = NS_OK;
   hipError_t e = hipEventRecord(ev[0], caller);
   for (int j = 0; j < used && e == hipSuccess; ++j) e = hipStreamWaitEvent(ss[j], ev[0], 0);
@@ -625,7 +727,7 @@ ns_status run_grouped_on(int count, const int64_t* m, const int64_t* n, hipStrea
       for (int t = 1; t < used; ++t) j = load[t] < load[j] ? t : j;
       st = run(i, ss[j]);
       if (st != NS_OK) break;
-      load[j] += cost(i);
+      load[j] += cost[(size_t)i];
     }
     for (int j = 0; j < used; ++j) {
       hipError_t ej = hipEventRecord(ev[1 + j], ss[j]);
@@ -641,10 +743,10 @@ ns_status run_grouped_on(int count, const int64_t* m, const int64_t* n, hipStrea
 
 // On the library's own streams of the current device.
 template <class F>
-ns_status run_grouped(int count, const int64_t* m, const int64_t* n, hipStream_t caller, F&& run) {
+ns_status run_grouped(int count, const std::vector<double>& cost, hipStream_t caller, F&& run) {
   hipStream_t ss[kGroupStreams];
   NS_TRY(group_streams(ss));
-  return run_grouped_on(count, m, n, caller, ss, kGroupStreams, run);
+  return run_grouped_on(count, cost, caller, ss, kGroupStreams, run);
 }
 
 // The problems of a grouped call run concurrently: no output may touch
@@ -667,15 +769,105 @@ ns_status check_group(int count, const void* const* G, const int64_t* m, const i
   return NS_OK;
 }
 
-// Byte offset of problem i's workspace in a grouped call.
-std::vector<size_t> group_offsets(int count, const int64_t* m, const int64_t* n) {
-  std::vector<size_t> off((size_t)count);
-  size_t o = 0;
+// The work items of a grouped call.  Matrices that share an iterate shape
+// (min(m, n) x max(m, n)) form a class, in order of first appearance,
+// members in call order; each class's workspace parts are contiguous, one
+// stride apart (the part size depends on the iterate shape only), and the
+// total is the sum of the parts, as ns_grouped_workspace_bytes counts it.
+// A class of matrices too small to fill the GPU alone (Gram products of
+// fewer than two 128 x 128 tiles per CU) is one work item, one batch: that
+// is where batching pays, by evening out the tile schedule.  A larger class
+// is cut into as many runs of consecutive members as there are streams, so
+// that it spreads over all of them in items of equal cost.  Matrices that
+// cannot be batched (a transform, products off the fast path) are one work
+// item each.  Measured on one MI355X, five quintic steps, interleaved runs
+// against one matrix per item: the four 3072-wide blocks 28.6-28.7 -> 26.1-26.2
+// ms, the pages' blocks at d = 4096 62.4-62.6 -> 59.4-59.5 ms, at d = 6144
+// 159.8-160.2 -> 159.7-160.1 ms; large classes as single matrices instead:
+// 61.0-61.3 and 158.9-159.5 ms; large classes in runs of at most the group's
+// cost over the stream count (coarser items, worse balance) 1-2 ms slower at
+// d = 6144.
+constexpr int64_t kFillTiles = 2 * 256;
+struct GroupPlan {
+  std::vector<std::vector<int>> items;   // member indices per run
+  std::vector<size_t> off;               // per matrix: byte offset of its part
+  std::vector<size_t> stride;            // per run: bytes between members' parts
+  std::vector<double> cost;              // per run: sum of m n min(m, n)
+};
+
+GroupPlan plan_group(int count, const int64_t* m, const int64_t* n, int nstreams, bool batches) {
+  std::vector<std::pair<int64_t, int64_t>> keys;
+  std::vector<std::vector<int>> classes;
+  auto cost_of = [&](int i) {
+    const double a = (double)m[i], b = (double)n[i];
+    return a * b * (a < b ? a : b);
+  };
   for (int i = 0; i < count; ++i) {
-    off[(size_t)i] = o;
-    o += ns_workspace_bytes(m[i], n[i]);
+    const std::pair<int64_t, int64_t> key{m[i] < n[i] ? m[i] : n[i], m[i] < n[i] ? n[i] : m[i]};
+    size_t c = 0;
+    while (c < keys.size() && keys[c] != key) ++c;
+    if (c == keys.size()) {
+      keys.push_back(key);
+      classes.emplace_back();
+    }
+    classes[c].push_back(i);
   }
-  return off;
+  GroupPlan P;
+  P.off.assign((size_t)count, 0);
+  size_t o = 0;
+  for (const std::vector<int>& cls : classes) {
+    const size_t part = ns_workspace_bytes(m[cls[0]], n[cls[0]]);
+    const double each = cost_of(cls[0]);
+    const bool small = ns_layout(m[cls[0]], n[cls[0]]).p1.tiles < kFillTiles;
+    const size_t ns_ = (size_t)(nstreams > 0 ? nstreams : 1);
+    size_t run = small ? cls.size() : (cls.size() + ns_ - 1) / ns_;
+    if (!batches || !batchable(m[cls[0]], n[cls[0]]) || run < 1) run = 1;   // one matrix per item
+    if (run > (size_t)nvfp4::kMaxBatchOut) run = nvfp4::kMaxBatchOut;
+    for (size_t a = 0; a < cls.size(); a += run) {
+      const size_t b = a + run < cls.size() ? a + run : cls.size();
+      P.items.emplace_back(cls.begin() + (std::ptrdiff_t)a, cls.begin() + (std::ptrdiff_t)b);
+      P.stride.push_back(part);
+      P.cost.push_back(each * (double)(b - a));
+      for (size_t t = a; t < b; ++t) {
+        P.off[(size_t)cls[t]] = o;
+        o += part;
+      }
+    }
+  }
+  return P;
+}
+
+// Run c of a grouped call on stream s: one batch when it has several
+// members and no transform (see ns_run_batch), else its members one by one.
+template <class One>
+ns_status run_class(const GroupPlan& P, int c, const void* const* G, ns_dtype gt,
+                    const int64_t* m, const int64_t* n, const float* coeffs, int k,
+                    const float* clip, double clip_q, const uint16_t* masks, bool a46,
+                    void* const* out, ns_dtype ot, uint8_t* base, hipStream_t s, One&& one) {
+  const std::vector<int>& mem = P.items[(size_t)c];
+  const int first = mem[0];
+  if (mem.size() < 2 || masks || !batchable(m[first], n[first])) {
+    for (int i : mem) {
+      const ns_status st = one(i, s);
+      if (st != NS_OK) return st;
+    }
+    return NS_OK;
+  }
+  const size_t cnt = mem.size();
+  std::vector<const void*> g(cnt);
+  std::vector<void*> o(cnt);
+  std::vector<int64_t> mm(cnt), nn(cnt);
+  std::vector<float> cl(cnt);
+  for (size_t j = 0; j < cnt; ++j) {
+    const int i = mem[j];
+    g[j] = G[i];
+    o[j] = out[i];
+    mm[j] = m[i];
+    nn[j] = n[i];
+    cl[j] = clip_q > 0.0 ? INFINITY : clip[i];
+  }
+  return ns_run_batch((int)cnt, g.data(), gt, mm.data(), nn.data(), coeffs, k, cl.data(), clip_q,
+                      a46, o.data(), ot, base + P.off[(size_t)first], P.stride[(size_t)c], s);
 }
 
 }  // namespace
@@ -751,16 +943,22 @@ ns_status grouped_ex_impl(int count, const void* const* G, const int64_t* m, con
     if (st != NS_OK) return st;
   }
   uint8_t* base = static_cast<uint8_t*>(ws);
-  const std::vector<size_t> off = group_offsets(count, m, n);
+  const GroupPlan P = plan_group(count, m, n, streams ? nstreams : kGroupStreams, !opt->rht_masks);
+  const bool a46 = opt->adaptive46 != 0;
   auto one = [&](int i, hipStream_t s) {
     const float ci = q > 0.0 ? INFINITY : clip[i];
-    return ns_run(G[i], gt, m[i], n[i], coeffs, k, ci, q, opt->rht_masks, opt->adaptive46 != 0, out[i], ot,
-                  base + off[(size_t)i], s);
+    return ns_run(G[i], gt, m[i], n[i], coeffs, k, ci, q, opt->rht_masks, a46, out[i], ot,
+                  base + P.off[(size_t)i], s);
   };
-  if (!streams) return run_grouped(count, m, n, as_stream(stream), one);
+  auto cls = [&](int c, hipStream_t s) {
+    return run_class(P, c, G, gt, m, n, coeffs, k, clip, q, opt->rht_masks, a46, out, ot, base, s,
+                     one);
+  };
+  const int items = (int)P.items.size();
+  if (!streams) return run_grouped(items, P.cost, as_stream(stream), cls);
   hipStream_t ss[kMaxCallerStreams];
   for (int j = 0; j < nstreams; ++j) ss[j] = as_stream(streams[j]);
-  return run_grouped_on(count, m, n, as_stream(stream), ss, nstreams, one);
+  return run_grouped_on(items, P.cost, as_stream(stream), ss, nstreams, cls);
 }
 
 }  // namespace
@@ -783,10 +981,14 @@ ns_status ns_orthogonalize_grouped(int count, const void* const* G, const int64_
     if (st != NS_OK) return st;
   }
   uint8_t* base = static_cast<uint8_t*>(ws);
-  const std::vector<size_t> off = group_offsets(count, m, n);
-  return run_grouped(count, m, n, as_stream(stream), [&](int i, hipStream_t s) {
+  const GroupPlan P = plan_group(count, m, n, kGroupStreams, true);
+  auto one = [&](int i, hipStream_t s) {
     return ns_run(G[i], gt, m[i], n[i], coeffs, k, clip[i], 0.0, nullptr, false, out[i], ot,
-                  base + off[(size_t)i], s);
+                  base + P.off[(size_t)i], s);
+  };
+  return run_grouped((int)P.items.size(), P.cost, as_stream(stream), [&](int c, hipStream_t s) {
+    return run_class(P, c, G, gt, m, n, coeffs, k, clip, 0.0, nullptr, false, out, ot, base, s,
+                     one);
   });
 }
 

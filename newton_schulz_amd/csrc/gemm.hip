@@ -37,6 +37,8 @@
 // partials are summed in part order (deterministic): by the part that
 // finishes last, inside the product kernel, when the whole tiles are long
 // enough to hide that work, else by a second kernel; see FastArgs.
+#include <cstddef>
+
 #include "launch.hpp"
 #include "nvfp4_device.hpp"
 
@@ -120,7 +122,55 @@ struct FastArgs {
   int parts;            // K-parts of a leftover tile (1: leftovers run whole)
   float* partials;
   uint32_t* counters;   // per split tile, K-parts finished; null: a second kernel sums
+  int64_t bstride;      // bytes between the problems of a batched launch (grid y)
 };
+
+// Outputs of the problems of a batched launch, when given one by one (n > 0).
+// The first argument of the product kernels, so that it sits at the start
+// of the kernel-argument segment (explicit arguments are laid out in order
+// at their natural alignment): entry y is then one scalar load from there,
+// instead of all of them copied to registers or scratch.
+struct OutTable {
+  int n;
+  float* outs[kMaxBatchOut];
+};
+static_assert(offsetof(OutTable, outs) == 8, "OutTable layout");
+
+__device__ __forceinline__ float* table_out(int y) {
+  typedef float* __attribute__((address_space(4))) const* KPtr;
+  typedef const __attribute__((address_space(4))) uint8_t* KBytes;
+  const KBytes k = (KBytes)__builtin_amdgcn_kernarg_segment_ptr();
+  return ((KPtr)(k + offsetof(OutTable, outs)))[y];
+}
+
+template <class T>
+__device__ __forceinline__ T* shift_bytes(T* p, int64_t off) {
+  return p ? reinterpret_cast<T*>(reinterpret_cast<uintptr_t>(p) + off) : p;
+}
+
+// Problem blockIdx.y of a batched launch: every pointer moves by its
+// offset (wave-uniform, so the operand bases stay in scalar registers).
+// Workgroup (x, y) has linear id y * units + x, and units is a multiple of
+// kXcds, so it runs on the XCD its unit has in a single launch.
+__device__ __forceinline__ void select_problem(FastArgs& a, int nout) {
+  const int64_t off = (int64_t)blockIdx.y * a.bstride;
+  GemmProblem& g = a.g;
+  g.codes_p = shift_bytes(g.codes_p, off);
+  g.scales_p = shift_bytes(g.scales_p, off);
+  g.sg_p = shift_bytes(g.sg_p, off);
+  g.codes_q = shift_bytes(g.codes_q, off);
+  g.scales_q = shift_bytes(g.scales_q, off);
+  g.sg_q = shift_bytes(g.sg_q, off);
+  g.addend = shift_bytes(g.addend, off);
+  if (nout) {
+    g.out = table_out((int)blockIdx.y);
+  } else {
+    g.out = shift_bytes(g.out, off);
+  }
+  g.amax_out = shift_bytes(g.amax_out, off);
+  a.partials = shift_bytes(a.partials, off);
+  a.counters = shift_bytes(a.counters, off);
+}
 
 // The last K-part of a split tile sums the parts inside the product kernel
 // when a whole tile runs at least this many K-stages; the summing then
@@ -548,10 +598,13 @@ __device__ __forceinline__ size_t partial_index(int b, int q, int thread) {
 // FIXUP: the last K-part of a split tile sums the parts (a.counters set);
 // otherwise gemm_reduce_kernel does.  Two instantiations, so that products
 // without split tiles keep the plain kernel's code.
-template <class C, bool SYM, bool FIXUP>
-__global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_fast_kernel(FastArgs a) {
+// BATCH: one problem per grid row (select_problem); a separate
+// instantiation, so that single launches keep the plain kernel's code.
+template <class C, bool SYM, bool FIXUP, bool BATCH>
+__global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_fast_kernel(const OutTable t, FastArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::NST * C::kStage];
   __shared__ uint32_t last_part;
+  if constexpr (BATCH) select_problem(a, t.n);
   const GemmProblem& g = a.g;
 
   // ---- work unit: a whole tile or a K-part of a leftover tile (unit_of)
@@ -814,9 +867,10 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_fast_kernel(F
 // s, summed over the K-parts in part order, then that block's epilogue.
 // Workgroups: split tiles x waves x FM x FN, so the partials stream in
 // with many loads in flight.
-template <class C, bool SYM>
-__global__ __launch_bounds__(64) void gemm_reduce_kernel(FastArgs a) {
+template <class C, bool SYM, bool BATCH>
+__global__ __launch_bounds__(64) void gemm_reduce_kernel(const OutTable t, FastArgs a) {
   constexpr int kBlocks = C::FM * C::FN;
+  if constexpr (BATCH) select_problem(a, t.n);
   const int bid = (int)blockIdx.x;
   const int s = bid / (C::kWaves * kBlocks), rem = bid % (C::kWaves * kBlocks);
   const int w = rem / kBlocks, b = rem % kBlocks, i = b / C::FN, j = b % C::FN;
@@ -1138,27 +1192,38 @@ hipError_t launch_with(const GemmProblem& g, const GemmPlan& p, void* ws, bool z
   a.partials = p.splits > 1 ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + kGemmCounterBytes)
                             : nullptr;
   a.counters = p.fixup ? static_cast<uint32_t*>(ws) : nullptr;
+  a.bstride = g.batch > 1 ? g.batch_stride : 0;
+  OutTable t{};
+  if (g.batch > 1 && g.out_each) {
+    if (g.batch > kMaxBatchOut) return hipErrorInvalidValue;
+    t.n = g.batch;
+    for (int i = 0; i < g.batch; ++i) t.outs[i] = g.out_each[i];
+  }
+  if (g.batch > 1 && zero_counters) return hipErrorInvalidValue;
   if (p.fixup && zero_counters) {
     zero_counters_kernel<<<1, 256, 0, s>>>(a.counters, (int)p.split_tiles);
     const hipError_t ez = hipGetLastError();
     if (ez != hipSuccess) return ez;
   }
-  const dim3 grid((unsigned)p.units);
-  if (g.symmetric && p.fixup)
-    gemm_fast_kernel<C, true, true><<<grid, C::kThreads, 0, s>>>(a);
-  else if (g.symmetric)
-    gemm_fast_kernel<C, true, false><<<grid, C::kThreads, 0, s>>>(a);
-  else if (p.fixup)
-    gemm_fast_kernel<C, false, true><<<grid, C::kThreads, 0, s>>>(a);
-  else
-    gemm_fast_kernel<C, false, false><<<grid, C::kThreads, 0, s>>>(a);
+  const dim3 grid((unsigned)p.units, (unsigned)g.batch);
+  const bool b = g.batch > 1;
+#define NVFP4_FAST(SY, FX)                                                              \
+  do {                                                                                  \
+    if (b) gemm_fast_kernel<C, SY, FX, true><<<grid, C::kThreads, 0, s>>>(t, a);        \
+    else gemm_fast_kernel<C, SY, FX, false><<<grid, C::kThreads, 0, s>>>(t, a);         \
+  } while (0)
+  if (g.symmetric && p.fixup) NVFP4_FAST(true, true);
+  else if (g.symmetric) NVFP4_FAST(true, false);
+  else if (p.fixup) NVFP4_FAST(false, true);
+  else NVFP4_FAST(false, false);
+#undef NVFP4_FAST
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1 || p.fixup) return e;
-  const unsigned rgrid = (unsigned)(p.split_tiles * C::kWaves * C::FM * C::FN);
-  if (g.symmetric)
-    gemm_reduce_kernel<C, true><<<dim3(rgrid), 64, 0, s>>>(a);
-  else
-    gemm_reduce_kernel<C, false><<<dim3(rgrid), 64, 0, s>>>(a);
+  const dim3 rgrid((unsigned)(p.split_tiles * C::kWaves * C::FM * C::FN), (unsigned)g.batch);
+  if (g.symmetric && b) gemm_reduce_kernel<C, true, true><<<rgrid, 64, 0, s>>>(t, a);
+  else if (g.symmetric) gemm_reduce_kernel<C, true, false><<<rgrid, 64, 0, s>>>(t, a);
+  else if (b) gemm_reduce_kernel<C, false, true><<<rgrid, 64, 0, s>>>(t, a);
+  else gemm_reduce_kernel<C, false, false><<<rgrid, 64, 0, s>>>(t, a);
   return hipGetLastError();
 }
 
@@ -1179,6 +1244,7 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool symmetric, bool allow_s
 
 hipError_t launch_gemm(const GemmProblem& g, const GemmPlan& p, void* ws, bool zero_counters,
                        hipStream_t s) {
+  if (g.batch < 1 || (g.batch > 1 && (!p.fast || g.batch_stride <= 0))) return hipErrorInvalidValue;
   if (!p.fast) {
     if (g.symmetric) {
       const int64_t nt = (g.M + GBM - 1) / GBM;

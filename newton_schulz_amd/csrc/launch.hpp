@@ -37,9 +37,13 @@ hipError_t launch_quant_rows(const void* x, Dt xt, int64_t rows, int64_t cols,
 // Q_1x16 of a symmetric m x m FP32 matrix of which only the tiles on or
 // above the diagonal (64 x 64) are read: the column blocks of tile (I, J)
 // are the row blocks of tile (J, I).
+// With batch > 1 the launch quantizes `batch` matrices, each with every
+// pointer moved by b * bstride bytes from matrix 0's (the same holds for
+// launch_quant_tiles).
 hipError_t launch_quant_sym_tiles(const float* x, int64_t m, const uint32_t* amax_slot,
                                   float* sg_out, uint8_t* codes, uint8_t* scales,
-                                  uint32_t* zero_slot, bool adaptive46, hipStream_t s);
+                                  uint32_t* zero_slot, bool adaptive46, hipStream_t s,
+                                  int batch = 1, int64_t bstride = 0);
 
 // Q_1x16 and/or Q_16x1 of a rows x cols matrix through 64x64 LDS tiles, one
 // read of x for both layouts.  Either output pair may be null.  The column
@@ -52,7 +56,8 @@ hipError_t launch_quant_tiles(const void* x, Dt xt, int64_t rows, int64_t cols,
                               uint8_t* col_codes, uint8_t* col_scales,
                               uint32_t* zero_slot, hipStream_t s,
                               const uint32_t* amax_c = nullptr, float* sg_out_c = nullptr,
-                              RhtArg rht = RhtArg{0u, 0u, 0u});
+                              RhtArg rht = RhtArg{0u, 0u, 0u}, int batch = 1,
+                              int64_t bstride = 0);
 // The first NS quantization fused with the normalisation: X = clamp(G) * inv
 // (G is rows x cols, the X layout), written to X and quantized in both
 // layouts in the same pass.  amax_slot must already hold max |X| (from
@@ -90,7 +95,17 @@ struct GemmProblem {
   int amax_parts;   // amax_out is an amax slot of partials (1) or one word (0)
   int upper_only;   // symmetric: tiles wholly above the diagonal skip their
                    // mirror (only row <= col and the diagonal tiles are stored)
+  // `batch` problems of one shape in one launch: problem b's pointers (every
+  // one above, and the GEMM workspace) are problem 0's plus b * batch_stride
+  // bytes.  Each runs its single-problem schedule, so its result equals the
+  // single launch's bit for bit.  Needs a fast-path plan.
+  int batch = 1;
+  int64_t batch_stride = 0;
+  // batched: with out_each (a host array of `batch` pointers, at most
+  // kMaxBatchOut) problem b writes its result to out_each[b] instead
+  float* const* out_each = nullptr;
 };
+constexpr int kMaxBatchOut = 32;
 
 // Launch plan of one product: the fast path needs K % 128 == 0 and picks a
 // tile shape from the tile count; tiles left over after an equal number per

@@ -304,14 +304,34 @@ __device__ __forceinline__ float clamp_nan(float x, float c) {
   return x > c ? c : (x < -c ? -c : x);
 }
 
+template <class P>
+__device__ __forceinline__ P* shift_bytes(P* p, int64_t off) {
+  return p ? reinterpret_cast<P*>(reinterpret_cast<uintptr_t>(p) + off) : p;
+}
+
+// With bstride != 0 the launch covers one tensor per grid row y, each at
+// the same byte offsets as tensor 0 plus y * bstride (every pointer moves).
 template <Dt T, bool ROWS, bool COLS, bool NORM = false>
 __global__ __launch_bounds__(kThreads) void quant_tile_kernel(
     const void* x, int64_t rows, int64_t cols, uint32_t tiles_x, const uint32_t* amax_slot,
     float* sg_out, uint8_t* row_codes, uint8_t* row_scales, uint8_t* col_codes,
     uint8_t* col_scales, uint32_t* zero_slot, const uint32_t* amax_c, float* sg_out_c,
-    RhtArg rht, NormArg nrm, uint32_t sym) {
+    RhtArg rht, NormArg nrm, uint32_t sym, int64_t bstride) {
   static_assert(!NORM || COLS, "the normalised X is written from the LDS tile");
   __shared__ uint32_t tile[64][65];
+  if (bstride) {
+    const int64_t off = (int64_t)blockIdx.y * bstride;
+    x = shift_bytes(x, off);
+    amax_slot = shift_bytes(amax_slot, off);
+    sg_out = shift_bytes(sg_out, off);
+    row_codes = shift_bytes(row_codes, off);
+    row_scales = shift_bytes(row_scales, off);
+    col_codes = shift_bytes(col_codes, off);
+    col_scales = shift_bytes(col_scales, off);
+    zero_slot = shift_bytes(zero_slot, off);
+    amax_c = shift_bytes(amax_c, off);
+    sg_out_c = shift_bytes(sg_out_c, off);
+  }
   const float sg = global_scale_from_amax(amax_read(amax_slot));
   const float sgc = amax_c ? global_scale_from_amax(amax_read(amax_c)) : sg;
   if (blockIdx.x == 0) {
@@ -625,15 +645,18 @@ hipError_t launch_quant_tiles(const void* x, Dt xt, int64_t rows, int64_t cols,
                               const uint32_t* amax_slot, float* sg_out, uint8_t* row_codes,
                               uint8_t* row_scales, uint8_t* col_codes, uint8_t* col_scales,
                               uint32_t* zero_slot, hipStream_t s, const uint32_t* amax_c,
-                              float* sg_out_c, RhtArg rht) {
+                              float* sg_out_c, RhtArg rht, int batch, int64_t bstride) {
   uint32_t tiles_x, grid;
   if (!tile_grid(rows, cols, tiles_x, grid)) return hipErrorInvalidValue;
+  if (batch < 1 || (batch > 1 && bstride <= 0)) return hipErrorInvalidValue;
   const bool R = row_codes != nullptr, C = col_codes != nullptr;
+  const dim3 g2(grid, (unsigned)batch);
+  const int64_t bs = batch > 1 ? bstride : 0;
 #define NVFP4_QT(T, RR, CC)                                                                   \
-  quant_tile_kernel<T, RR, CC><<<grid, kThreads, 0, s>>>(x, rows, cols, tiles_x, amax_slot,   \
-                                                         sg_out, row_codes, row_scales,       \
-                                                         col_codes, col_scales, zero_slot,    \
-                                                         amax_c, sg_out_c, rht, NormArg{}, 0u)
+  quant_tile_kernel<T, RR, CC><<<g2, kThreads, 0, s>>>(x, rows, cols, tiles_x, amax_slot,     \
+                                                       sg_out, row_codes, row_scales,         \
+                                                       col_codes, col_scales, zero_slot,      \
+                                                       amax_c, sg_out_c, rht, NormArg{}, 0u, bs)
   if (xt == Dt::F32) {
     if (R && C) NVFP4_QT(Dt::F32, true, true);
     else if (R) NVFP4_QT(Dt::F32, true, false);
@@ -649,12 +672,14 @@ hipError_t launch_quant_tiles(const void* x, Dt xt, int64_t rows, int64_t cols,
 
 hipError_t launch_quant_sym_tiles(const float* x, int64_t m, const uint32_t* amax_slot,
                                   float* sg_out, uint8_t* codes, uint8_t* scales,
-                                  uint32_t* zero_slot, bool adaptive46, hipStream_t s) {
+                                  uint32_t* zero_slot, bool adaptive46, hipStream_t s, int batch,
+                                  int64_t bstride) {
   uint32_t tiles_x, grid;
   if (!tile_grid(m, m, tiles_x, grid)) return hipErrorInvalidValue;
-  quant_tile_kernel<Dt::F32, true, true><<<grid, kThreads, 0, s>>>(
+  if (batch < 1 || (batch > 1 && bstride <= 0)) return hipErrorInvalidValue;
+  quant_tile_kernel<Dt::F32, true, true><<<dim3(grid, (unsigned)batch), kThreads, 0, s>>>(
       x, m, m, tiles_x, amax_slot, sg_out, codes, scales, codes, scales, zero_slot, nullptr,
-      nullptr, RhtArg{0u, 0u, adaptive46 ? 1u : 0u}, NormArg{}, 1u);
+      nullptr, RhtArg{0u, 0u, adaptive46 ? 1u : 0u}, NormArg{}, 1u, batch > 1 ? bstride : 0);
   return hipGetLastError();
 }
 
@@ -671,11 +696,11 @@ hipError_t launch_normalize_quant_tiles(const void* G, Dt gt, int64_t rows, int6
   if (gt == Dt::F32)
     quant_tile_kernel<Dt::F32, true, true, true><<<grid, kThreads, 0, s>>>(
         G, rows, cols, tiles_x, amax_slot, sg_out, row_codes, row_scales, col_codes, col_scales,
-        zero_slot, nullptr, nullptr, o, nrm, 0u);
+        zero_slot, nullptr, nullptr, o, nrm, 0u, 0);
   else
     quant_tile_kernel<Dt::BF16, true, true, true><<<grid, kThreads, 0, s>>>(
         G, rows, cols, tiles_x, amax_slot, sg_out, row_codes, row_scales, col_codes, col_scales,
-        zero_slot, nullptr, nullptr, o, nrm, 0u);
+        zero_slot, nullptr, nullptr, o, nrm, 0u, 0);
   return hipGetLastError();
 }
 
