@@ -144,13 +144,13 @@ def source_digest(files=("gemm.hip", "nvfp4_device.hpp")):
 # HBM bytes per launch of the dominant kernel (X = a X + qB qX16^T at
 # 3072 x 8192), from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE, each scaled by
 # what the counter reads for a plain copy of known size; see profiles/.
-DOMINANT_TRAFFIC = {"src_sha256": "33a68630e7e0ae212c5e395a3d1b16402f72a99d8ab660a2aed152c2c4af387b",
-                    "bytes_per_launch": 440582758}
+DOMINANT_TRAFFIC = {"src_sha256": "82b033f4fafa1a11d3d466ddffede122894488489d27196ca58669389e7bc7c7",
+                    "bytes_per_launch": 440814182}
 # Bytes of one quantize + dequantize pair of the 2^28 BF16 tensor (the
 # maximum, encode and decode kernels) between the L2 caches and memory,
 # measured the same way (Infinity Cache hits included).
-QUANT_TRAFFIC = {"src_sha256": "35bcfe0e877f81645b1ced7921eed5e6d102bcae6301fc819939011501838261",
-                 "bytes_per_pair": 1914486170}
+QUANT_TRAFFIC = {"src_sha256": "f6258c02a85d0e75b6e1bea954da76025bb12d9b3b4dd2e5b2149210d396836b",
+                 "bytes_per_pair": 1914557747}
 QUANT_UNIQUE_BYTES_PER_ELEM = (2 + 0.5 + 1 / 16) + (0.5 + 1 / 16 + 2)
 # Of the design bytes, the Infinity Cache can serve the encode pass's re-read
 # of the tensor's last 96 MiB (read last by the maximum pass, first by the
