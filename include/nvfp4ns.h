@@ -196,9 +196,8 @@ size_t ns_workspace_bytes(int64_t m, int64_t n);
  * the caller beyond ns_workspace_bytes().  The iterate is xm x xn with
  * xm = min(m, n), xn = max(m, n) (G^T when m > n).
  *   x                  FP32 X [xm][xn]
- *   a, b               FP32 A and B [xm][xm]; without the transform only the
- *                      elements with row <= col are written (A and B are
- *                      symmetric), with it the whole matrix
+ *   a, b               FP32 A and B [xm][xm]; only the elements with
+ *                      row <= col are written (A and B are symmetric)
  *   qx_codes/_scales   Q_1x16(X [H]): [xm][xn/2] codes, [xm][xn/16] scales
  *   qt_codes/_scales   Q_16x1([H^T] X) stored as rows of X^T: [xn][xm/2], [xn][xm/16]
  *   qa_codes/_scales   Q_1x16(A [H]): [xm][xm/2], [xm][xm/16]

@@ -247,20 +247,22 @@ ns_status ns_run(const void* G, ns_dtype gt, int64_t m, int64_t n, const float* 
       NS_TRY(nvfp4::launch_amax_tiles(X, Dt::F32, xm, xn, slotX, slotXc, h, s));
       NS_TRY(nvfp4::launch_quant_tiles(X, Dt::F32, xm, xn, slotX, sgX, ws + L.qx_c, ws + L.qx_s,
                                        ws + L.qt_c, ws + L.qt_s, nullptr, s, slotXc, sgXc, h));
+      // A = qX qX^T, upper triangle only (as without the transform)
       nvfp4::GemmProblem g1{ws + L.qx_c, ws + L.qx_s, sgX, ws + L.qx_c, ws + L.qx_s, sgX,
-                            xm, xm, xn, 1, 1.0f, 0.0f, nullptr, A, nullptr, 0};
+                            xm, xm, xn, 1, 1.0f, 0.0f, nullptr, A, nullptr, 0, 1};
       NS_TRY(nvfp4::launch_gemm(g1, L.p1, gws, false, s));
-      // qA = Q_1x16(A H)
-      NS_TRY(nvfp4::launch_amax_tiles(A, Dt::F32, xm, xm, slotA, nullptr, h, s));
-      NS_TRY(nvfp4::launch_quant_tiles(A, Dt::F32, xm, xm, slotA, sgA, ws + L.qa_c, ws + L.qa_s,
-                                       nullptr, nullptr, nullptr, s, nullptr, nullptr, h));
+      // qA = Q_1x16(A H), from the tiles on and above the diagonal: the row
+      // blocks of a lower tile are the column blocks of its mirror
+      NS_TRY(nvfp4::launch_amax_sym_tiles(A, xm, slotA, h, s));
+      NS_TRY(nvfp4::launch_quant_sym_tiles(A, xm, slotA, sgA, ws + L.qa_c, ws + L.qa_s, nullptr,
+                                           a46, s, 1, 0, 1u, h.mask));
       nvfp4::GemmProblem g2{ws + L.qa_c, ws + L.qa_s, sgA, ws + L.qa_c, ws + L.qa_s, sgA,
-                            xm, xm, xm, 1, c, b, A, B, nullptr, 0};
+                            xm, xm, xm, 1, c, b, A, B, nullptr, 0, 1};
       NS_TRY(nvfp4::launch_gemm(g2, L.p2, gws, false, s));
-      // qB = Q_1x16(B H)
-      NS_TRY(nvfp4::launch_amax_tiles(B, Dt::F32, xm, xm, slotB, nullptr, h, s));
-      NS_TRY(nvfp4::launch_quant_tiles(B, Dt::F32, xm, xm, slotB, sgB, ws + L.qb_c, ws + L.qb_s,
-                                       nullptr, nullptr, nullptr, s, nullptr, nullptr, h));
+      // qB = Q_1x16(B H), likewise
+      NS_TRY(nvfp4::launch_amax_sym_tiles(B, xm, slotB, h, s));
+      NS_TRY(nvfp4::launch_quant_sym_tiles(B, xm, slotB, sgB, ws + L.qb_c, ws + L.qb_s, nullptr,
+                                           a46, s, 1, 0, 1u, h.mask));
       const bool direct = it == k - 1 && !tr && ot == NS_F32;
       nvfp4::GemmProblem g3{ws + L.qb_c, ws + L.qb_s, sgB, ws + L.qt_c, ws + L.qt_s, sgXc,
                             xm, xn, xm, 0, 1.0f, a, X, direct ? static_cast<float*>(out) : X,

@@ -40,10 +40,13 @@ hipError_t launch_quant_rows(const void* x, Dt xt, int64_t rows, int64_t cols,
 // With batch > 1 the launch quantizes `batch` matrices, each with every
 // pointer moved by b * bstride bytes from matrix 0's (the same holds for
 // launch_quant_tiles).
+// With rht_on every block (row blocks, and the column blocks that stand for
+// the row blocks of the lower tiles) is first multiplied by H^r of rht_mask.
 hipError_t launch_quant_sym_tiles(const float* x, int64_t m, const uint32_t* amax_slot,
                                   float* sg_out, uint8_t* codes, uint8_t* scales,
                                   uint32_t* zero_slot, bool adaptive46, hipStream_t s,
-                                  int batch = 1, int64_t bstride = 0);
+                                  int batch = 1, int64_t bstride = 0, uint32_t rht_on = 0,
+                                  uint32_t rht_mask = 0);
 
 // Q_1x16 and/or Q_16x1 of a rows x cols matrix through 64x64 LDS tiles, one
 // read of x for both layouts.  Either output pair may be null.  The column
@@ -72,6 +75,11 @@ hipError_t launch_normalize_quant_tiles(const void* G, Dt gt, int64_t rows, int6
 // column blocks into slot_c (either may be null); the caller zeroes them.
 hipError_t launch_amax_tiles(const void* x, Dt xt, int64_t rows, int64_t cols, uint32_t* slot_r,
                              uint32_t* slot_c, RhtArg rht, hipStream_t s);
+// Maximum of |A H^r| over the row blocks of a symmetric m x m FP32 matrix of
+// which only the tiles on or above the diagonal are read, into slot (the
+// caller zeroes it).
+hipError_t launch_amax_sym_tiles(const float* x, int64_t m, uint32_t* slot, RhtArg rht,
+                                 hipStream_t s);
 
 // Exact dequantisation of a Q_1x16 tensor; rows x cols output.
 hipError_t launch_dequant_rows(const uint8_t* codes, const uint8_t* scales, const float* sg,

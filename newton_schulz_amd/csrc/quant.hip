@@ -407,12 +407,18 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(
 
 // Tensor maxima of the transformed row blocks (x H^r, into slot_r) and/or
 // column blocks (H^r^T x, into slot_c), same tiling as quant_tile_kernel.
+// With `sym` the input is a symmetric square matrix of which only the tiles
+// on or above the diagonal are read, as in quant_tile_kernel: the column
+// blocks of tile (I, J) are the row blocks of tile (J, I), so both go to
+// slot_r (slot_c == slot_r), and a diagonal tile counts its rows only.
 template <Dt T>
 __global__ __launch_bounds__(kThreads) void amax_tiles_kernel(
     const void* x, int64_t rows, int64_t cols, uint32_t tiles_x, uint32_t* slot_r,
-    uint32_t* slot_c, RhtArg rht) {
+    uint32_t* slot_c, RhtArg rht, uint32_t sym) {
   __shared__ uint32_t tile[64][65];
   const int64_t r0 = tile_row0(tiles_x), c0 = tile_col0(tiles_x);
+  if (sym && r0 > c0) return;   // below the diagonal: done by tile (J, I)
+  if (sym && r0 == c0) slot_c = nullptr;
   const int tr = threadIdx.x >> 2, tc = (threadIdx.x & 3) * 16;
   const bool in = (r0 + tr < rows) && (c0 + tc < cols);
   uint32_t v[16];
@@ -673,13 +679,14 @@ hipError_t launch_quant_tiles(const void* x, Dt xt, int64_t rows, int64_t cols,
 hipError_t launch_quant_sym_tiles(const float* x, int64_t m, const uint32_t* amax_slot,
                                   float* sg_out, uint8_t* codes, uint8_t* scales,
                                   uint32_t* zero_slot, bool adaptive46, hipStream_t s, int batch,
-                                  int64_t bstride) {
+                                  int64_t bstride, uint32_t rht_on, uint32_t rht_mask) {
   uint32_t tiles_x, grid;
   if (!tile_grid(m, m, tiles_x, grid)) return hipErrorInvalidValue;
   if (batch < 1 || (batch > 1 && bstride <= 0)) return hipErrorInvalidValue;
   quant_tile_kernel<Dt::F32, true, true><<<dim3(grid, (unsigned)batch), kThreads, 0, s>>>(
       x, m, m, tiles_x, amax_slot, sg_out, codes, scales, codes, scales, zero_slot, nullptr,
-      nullptr, RhtArg{0u, 0u, adaptive46 ? 1u : 0u}, NormArg{}, 1u, batch > 1 ? bstride : 0);
+      nullptr, RhtArg{rht_on, rht_mask, adaptive46 ? 1u : 0u}, NormArg{}, 1u,
+      batch > 1 ? bstride : 0);
   return hipGetLastError();
 }
 
@@ -709,9 +716,17 @@ hipError_t launch_amax_tiles(const void* x, Dt xt, int64_t rows, int64_t cols, u
   uint32_t tiles_x, grid;
   if (!tile_grid(rows, cols, tiles_x, grid)) return hipErrorInvalidValue;
   if (xt == Dt::F32)
-    amax_tiles_kernel<Dt::F32><<<grid, kThreads, 0, s>>>(x, rows, cols, tiles_x, slot_r, slot_c, rht);
+    amax_tiles_kernel<Dt::F32><<<grid, kThreads, 0, s>>>(x, rows, cols, tiles_x, slot_r, slot_c, rht, 0u);
   else
-    amax_tiles_kernel<Dt::BF16><<<grid, kThreads, 0, s>>>(x, rows, cols, tiles_x, slot_r, slot_c, rht);
+    amax_tiles_kernel<Dt::BF16><<<grid, kThreads, 0, s>>>(x, rows, cols, tiles_x, slot_r, slot_c, rht, 0u);
+  return hipGetLastError();
+}
+
+hipError_t launch_amax_sym_tiles(const float* x, int64_t m, uint32_t* slot, RhtArg rht,
+                                 hipStream_t s) {
+  uint32_t tiles_x, grid;
+  if (!tile_grid(m, m, tiles_x, grid)) return hipErrorInvalidValue;
+  amax_tiles_kernel<Dt::F32><<<grid, kThreads, 0, s>>>(x, m, m, tiles_x, slot, slot, rht, 1u);
   return hipGetLastError();
 }
 

@@ -79,11 +79,10 @@ def test_variant_step_from_gpu_state(variant, j):
         def quant(T, sel):            # Q_1x16 of the FP32 butterfly transform, tensor-wide s_g
             t = rht_rows_f32(T, mask).astype(np.float64)
             return Q.quantize_rows(t[sel], amax=Q.tensor_amax(t))
-        A, B = h["A"].astype(np.float64), h["B"].astype(np.float64)   # whole under the transform
     else:
         def quant(T, sel):
             return Q.quantize_rows(T[sel], amax=Q.tensor_amax(T), adaptive46=True)
-        A, B = _sym(h["A"]), _sym(h["B"])
+    A, B = _sym(h["A"]), _sym(h["B"])             # upper triangles stored
     _same_rows(h["qX"], quant(X64, rows), rows, f"{variant} qX")
     _same_rows(h["qX16"], quant(np.ascontiguousarray(X64.T), rows), rows, f"{variant} qX16")
     _same_rows(h["qA"], quant(A, rows), rows, f"{variant} qA")
