@@ -398,11 +398,11 @@ ns_status ns_run_batch(int count, const void* const* G, ns_dtype gt, const int64
                           xm, xn, xm, 0, 1.0f, a, X, X, slotX, 1, 0, count, bs};
     // the last step of an FP32, untransposed matrix writes straight into
     // its output, as its single call does (the others keep X in place)
-    if (it == k - 1 && direct.size() == (size_t)count) g3.out_each = direct.data();
+    if (it == k - 1) g3.out_each = direct.data();
     NS_TRY(nvfp4::launch_gemm(g3, L.p3, gws, false, s));
   }
-  for (int j = 0; j < count; ++j)
-    if (!(k > 0 && direct[(size_t)j] == out[j]))
+  for (int j = 0; j < count; ++j)   // k >= 1 (validated): the others hold X_k in X
+    if (direct[(size_t)j] != out[j])
       NS_TRY(nvfp4::launch_write_out(reinterpret_cast<float*>(at(j, L.X)), xm, xn, m[j] > n[j],
                                      out[j], (Dt)ot, s));
   return NS_OK;
