@@ -131,26 +131,31 @@ def kernel_timings(ns, torch, dev, Gd, clip, coeffs, stream, reps=10):
 
 
 def source_digest(files=("gemm.hip", "nvfp4_device.hpp")):
-    """sha256 over kernel sources; recorded HBM-traffic counters apply only
-    to the kernels they were taken from."""
+    """sha256 over the kernel sources' code (comments and blank lines left
+    out); recorded HBM-traffic counters apply only to the code they were
+    taken from."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(ROOT, "newton_schulz_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "newton_schulz_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        lines = (re.sub(r"//.*", "", line).rstrip() for line in text.splitlines())
+        h.update("\n".join(line for line in lines if line).encode())
     return h.hexdigest()
 
 
 # HBM bytes per launch of the dominant kernel (X = a X + qB qX16^T at
 # 3072 x 8192), from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE, each scaled by
 # what the counter reads for a plain copy of known size; see profiles/.
-DOMINANT_TRAFFIC = {"src_sha256": "82b033f4fafa1a11d3d466ddffede122894488489d27196ca58669389e7bc7c7",
+DOMINANT_TRAFFIC = {"src_sha256": "34d51842fcde937eac067413ac5a37e5f4a34b0f1c5664549163c48697cbda75",
                     "bytes_per_launch": 440814182}
 # Bytes of one quantize + dequantize pair of the 2^28 BF16 tensor (the
 # maximum, encode and decode kernels) between the L2 caches and memory,
 # measured the same way (Infinity Cache hits included).
-QUANT_TRAFFIC = {"src_sha256": "f6258c02a85d0e75b6e1bea954da76025bb12d9b3b4dd2e5b2149210d396836b",
-                 "bytes_per_pair": 1914557747}
+QUANT_TRAFFIC = {"src_sha256": "7daac3cd0efa17fb7423ad5edf9acbee54c4b1352622e7e06f165cfd9ef83508",
+                 "bytes_per_pair": 1914543616}
 QUANT_UNIQUE_BYTES_PER_ELEM = (2 + 0.5 + 1 / 16) + (0.5 + 1 / 16 + 2)
 # Of the design bytes, the Infinity Cache can serve the encode pass's re-read
 # of the tensor's last 96 MiB (read last by the maximum pass, first by the

@@ -600,6 +600,8 @@ __device__ __forceinline__ size_t partial_index(int b, int q, int thread) {
 // without split tiles keep the plain kernel's code.
 // BATCH: one problem per grid row (select_problem); a separate
 // instantiation, so that single launches keep the plain kernel's code.
+// `t` must stay the first parameter: table_out reads it at offset 0 of the
+// kernel-argument segment.
 template <class C, bool SYM, bool FIXUP, bool BATCH>
 __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_fast_kernel(const OutTable t, FastArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::NST * C::kStage];
@@ -867,7 +869,7 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_fast_kernel(c
 // s, summed over the K-parts in part order, then that block's epilogue.
 // Workgroups: split tiles x waves x FM x FN, so the partials stream in
 // with many loads in flight.
-template <class C, bool SYM, bool BATCH>
+template <class C, bool SYM, bool BATCH>   // `t` first, as in gemm_fast_kernel
 __global__ __launch_bounds__(64) void gemm_reduce_kernel(const OutTable t, FastArgs a) {
   constexpr int kBlocks = C::FM * C::FN;
   if constexpr (BATCH) select_problem(a, t.n);
