@@ -3,7 +3,9 @@
 step are one launch each for the whole class, with each matrix on the
 kernels and tile schedule of its single call.  Every result must equal its
 single call bit for bit: with both output types, with the on-device
-quantile clip and adaptive 4/6, for classes mixed with matrices the batch
+quantile clip and adaptive 4/6, with split Gram products summed in the
+product kernel and by the separate reduce kernel, for classes mixed with
+matrices the batch
 does not take (one member, a K off the fast path, the random Hadamard
 transform), and on the benchmark's four-block batch and the pages' d = 4096
 decoder blocks at full size."""
@@ -73,6 +75,19 @@ def test_class_options_equal_single_calls(opts):
             kw["clip"] = clips[i]
         single = ns.ns_orthogonalize_ex(g, coeffs, **kw)
         assert _same(o, single), (shapes[i], opts)
+
+
+def test_split_products_summed_by_the_reduce_kernel():
+    """A class whose Gram product splits its tiles along K but is too short
+    to sum them inside the product kernel (1024 x 2048: 36 tiles, K = 2048
+    in two parts of four stages), so the batched reduce kernel sums them."""
+    shapes = [(1024, 2048), (2048, 1024), (1024, 2048)]
+    Gs = _inputs(shapes, 360)
+    coeffs = [synth.QUINTIC] * 2 + [CUBIC]
+    clips = [0.05, 0.07, 0.09]
+    outs = ns.ns_orthogonalize_grouped(Gs, coeffs, clips)
+    for i, (g, o, c) in enumerate(zip(Gs, outs, clips)):
+        assert _same(o, ns.ns_orthogonalize(g, coeffs, c)), shapes[i]
 
 
 def test_transform_keeps_per_matrix_runs():
