@@ -48,13 +48,28 @@ def test_quantile_ties_zeros_and_nonfinite():
     y[:30] = np.nan
     y[30:60] = -np.inf
     _check(y, to_dev_f32(y), "1.5% non-finite")            # q >= 0.99 reaches NaN
-    # the same inputs in BF16 (whose keys are selected in two radix passes)
+    # the same inputs in BF16 (whose 15-bit keys are counted in one pass)
     for label, arr in (("integer ties", x), ("all zero", z), ("1.5% non-finite", y)):
         bits, vals = synth.to_bf16(arr)
         _check(vals, to_dev_bf16(bits), f"bf16 {label}")
-    # BF16 magnitudes that differ only in the bits the second pass fixes
+    # BF16 magnitudes that differ only in their low mantissa bits
     bits, vals = synth.to_bf16(np.linspace(1.0, 1.0625, 4096, dtype=np.float32))
     _check(vals, to_dev_bf16(bits), "bf16 one binade")
+
+
+def test_quantile_every_bf16_pattern():
+    """All 65536 BF16 bit patterns (both signs, subnormals, infinities and
+    NaNs) in a shuffled order: every one of the 2^15 magnitude keys occurs
+    twice, so each quantile lands on a known key."""
+    pats = np.random.default_rng(4).permutation(np.arange(1 << 16, dtype=np.uint32)).astype(np.uint16)
+    vals = (pats.astype(np.uint32) << 16).view(np.float32)
+    qs = [1 / 65536, 0.25, 0.5, 0.75, 0.9, 0.99, 0.999, 1.0]
+    xd = to_dev_bf16(pats)
+    for q in qs:
+        got = np.float32(host(ns.ns_abs_quantile(xd, q))[0])
+        want = QT.abs_quantile(vals, q)
+        print(f"[quantile] every bf16 pattern q={q} gpu={got!r} oracle={want!r}", flush=True)
+        assert got.view(np.uint32) == np.float32(want).view(np.uint32), q
 
 
 def test_quantile_full_size_gradient():
