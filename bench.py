@@ -482,7 +482,7 @@ def main():
                               "quantized operand (extra amax passes over the transformed tensors)"}
 
     # the same step with the clip taken on the device as the 0.99 quantile of
-    # |G| (radix-selection passes over G before the normalisation: two for BF16)
+    # |G| (a histogram selection over G before the normalisation: one pass for BF16)
     qstep_ = lambda: ns.ns_orthogonalize_ex(Gd, coeffs, clip_quantile=0.99, out=out, workspace=ws,
                                             stream=stream)
     qms_ = time_events(qstep_, args.steps, args.warmup, stream)
@@ -493,7 +493,7 @@ def main():
     line["ns_p99_clip"] = {"ms": round(qms_, 4), "value": round(flops / (qms_ * 1e-3) / 1e12, 2),
                            "unit": "TFLOP/s", "quantile_ms": round(sel_ms, 4),
                            "what": "ns_orthogonalize_ex with clip_quantile=0.99: the clip is the "
-                                   "0.99 quantile of |G| found on the device (radix selection)"}
+                                   "0.99 quantile of |G| found on the device (one-pass histogram selection)"}
 
     # the same step with adaptive 4/6 block scaling on every quantization
     # (each block keeps the better of its M = 6 and M = 4 encodings)
