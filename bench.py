@@ -164,6 +164,14 @@ QUANT_UNIQUE_BYTES_PER_ELEM = (2 + 0.5 + 1 / 16) + (0.5 + 1 / 16 + 2)
 QUANT_CACHED_TAIL_BYTES = 96 << 20
 
 
+def iteration_flops(m, n):
+    """Algorithmic flops of one NS step on an m x n matrix (the iterate is
+    min(m, n) x max(m, n)): the two Gram products count their upper triangle
+    with the diagonal, m(m+1)n and m(m+1)m, the update product 2 m^2 n."""
+    m, n = min(m, n), max(m, n)
+    return m * (m + 1) * n + m * (m + 1) * m + 2 * m * m * n
+
+
 def bf16_ns_ms(torch, G, coeffs, stream, reps=10):
     def run():
         X = G.float()
@@ -180,7 +188,6 @@ def grouped_line(ns, torch, synth, dev, stream, label, shapes, seed0, coeffs, cl
                  reps=3, warm=1):
     """Grouped NS over a batch of BF16 gradients drawn on the device (the
     lowrank value model), against BF16 torch NS of the same batch."""
-    from oracle.ns import ns_iteration_flops
     Gs = [synth.device_lowrank_bf16(r, c, seed0 + i, dev) for i, (r, c) in enumerate(shapes)]
     outs = [torch.empty(s, dtype=torch.float32, device=dev) for s in shapes]
     ws = torch.empty(ns.ns_grouped_workspace_bytes(shapes), dtype=torch.uint8, device=dev)
@@ -194,7 +201,7 @@ def grouped_line(ns, torch, synth, dev, stream, label, shapes, seed0, coeffs, cl
                                                   stream=stream)
         clip_what = "clip 8 x RMS(G) per matrix"
     ms = time_events(run, reps, warm, stream)
-    flops = sum(len(coeffs) * ns_iteration_flops(r, c) for r, c in shapes)
+    flops = sum(len(coeffs) * iteration_flops(r, c) for r, c in shapes)
 
     def bf16_batch():
         for g in Gs:
@@ -233,7 +240,6 @@ def cpu_baseline(synth, coeffs):
     batch's time extrapolated from the two.  value = the 3072 x 8192 rate in
     algorithmic TFLOP/s."""
     from oracle import native as C
-    from oracle.ns import ns_iteration_flops
     res = {}
     for name in ("ns256x512", "ns2048", "ns3072x8192", "ns4blocks"):
         G, _, clip = synth.ns_matrix(synth.ns_workload(name), 0)
@@ -244,7 +250,7 @@ def cpu_baseline(synth, coeffs):
         m, n = G.shape
         key = name if name != "ns4blocks" else "ns4blocks_3072x3072"
         res[key] = {"steps": len(coeffs), "s": round(el, 3),
-                    "tflops": round(len(coeffs) * ns_iteration_flops(m, n) / el / 1e12, 5)}
+                    "tflops": round(len(coeffs) * iteration_flops(m, n) / el / 1e12, 5)}
     sq, big = res["ns4blocks_3072x3072"]["s"], res["ns3072x8192"]["s"]
     res["ns4blocks_estimate"] = {"s": round(16 * sq + 8 * big, 1),
                                  "how": "16 x the 3072^2 matrix + 8 x the 3072x8192 one "
@@ -388,7 +394,6 @@ def main():
     import torch
     import newton_schulz_amd as ns
     import synth
-    from oracle.ns import ns_iteration_flops
 
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
@@ -423,7 +428,7 @@ def main():
     t0 = time.perf_counter()
     ms = time_events(step, args.steps, 0, stream)
     wall = time.perf_counter() - t0
-    flops = synth.STEPS * ns_iteration_flops(m, n)
+    flops = synth.STEPS * iteration_flops(m, n)
     tflops = flops / (ms * 1e-3) / 1e12
 
     # per-call spread: each call between its own pair of events (the events
@@ -509,6 +514,22 @@ def main():
     bms = bf16_ns_ms(torch, Gd, coeffs, stream)
     line["bf16_ns"] = {"ms": round(bms, 4), "speedup_nvfp4_vs_bf16": round(bms / ms, 3),
                        "what": "torch.mm in bf16 (hipBLASLt), full products, same 5 steps"}
+
+    # the square 2048^2 gradient (same value model, clip 8 x RMS), five steps
+    G2, bits2, clip2 = synth.ns_matrix(synth.ns_workload("ns2048"), 0)
+    G2d = torch.from_numpy(bits2.view(np.int16)).view(torch.bfloat16).to(dev)
+    out2 = torch.empty(G2.shape, dtype=torch.float32, device=dev)
+    ws2 = torch.empty(ns.ns_workspace_bytes(*G2.shape), dtype=torch.uint8, device=dev)
+    s2 = lambda: ns.ns_orthogonalize(G2d, coeffs, clip2, out=out2, workspace=ws2, stream=stream)
+    ms2 = time_events(s2, args.steps, args.warmup, stream)
+    flops2 = synth.STEPS * iteration_flops(*G2.shape)
+    bms2 = bf16_ns_ms(torch, G2d, coeffs, stream)
+    line["ns2048"] = {"ms": round(ms2, 4), "value": round(flops2 / (ms2 * 1e-3) / 1e12, 2),
+                      "unit": "TFLOP/s", "algorithmic_tflop": round(flops2 / 1e12, 4),
+                      "bf16_ms": round(bms2, 4), "speedup_nvfp4_vs_bf16": round(bms2 / ms2, 3),
+                      "what": "ns_orthogonalize on the 2048^2 BF16 gradient (rank-32 signal + "
+                              "noise + 0.1% outliers x50, seed 3), clip 8 x RMS, quintic x5"}
+    del out2, ws2
 
     if not args.no_grouped:
         del ws

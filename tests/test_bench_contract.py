@@ -28,6 +28,16 @@ def test_more_than_one_gpu_is_refused():
     assert not r.stdout.strip()
 
 
+def test_flop_count_is_the_oracles_definition():
+    """bench.py counts algorithmic flops itself (the timed legs import
+    nothing from the oracle); the count must equal the oracle's."""
+    import bench
+    from oracle.ns import ns_iteration_flops
+    for m, n in ((256, 512), (2048, 2048), (3072, 8192), (8192, 3072), (144, 400)):
+        assert bench.iteration_flops(m, n) == ns_iteration_flops(m, n)
+    assert abs(5 * bench.iteration_flops(3072, 8192) - 1.305e12) < 1e9
+
+
 def _roofline_ok(roof, bound, unit):
     assert roof["bound"] == bound and roof["unit"] == unit
     assert roof["achieved"] > 0 and roof["peak"] > 0
@@ -44,7 +54,7 @@ def test_short_bench_line_has_the_contract_fields():
     d = _json_line(r.stdout)
     for k in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
               "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config",
-              "roofline", "step_ms", "quant"):
+              "roofline", "step_ms", "quant", "ns2048"):
         assert k in d, k
     assert d["n_gpus"] == 1 and d["steps"] == 2 and d["warmup"] == 1
     assert d["higher_is_better"] is True and d["data"] == "synthetic"
