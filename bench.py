@@ -484,7 +484,7 @@ def main():
     line["ns_rht"] = {"ms": round(rms_, 4), "value": round(flops / (rms_ * 1e-3) / 1e12, 2),
                       "unit": "TFLOP/s",
                       "what": "ns_orthogonalize_rht: the same step with H_16^r on every "
-                              "quantized operand (extra amax passes over the transformed tensors)"}
+                              "quantized operand (the products' epilogues fold the transformed maxima of their outputs)"}
 
     # the same step with the clip taken on the device as the 0.99 quantile of
     # |G| (a histogram selection over G before the normalisation: one pass for BF16)

@@ -235,38 +235,71 @@ ns_status ns_run(const void* G, ns_dtype gt, int64_t m, int64_t n, const float* 
   // untransformed and untransposed: the first quantization pass also
   // normalises G into X (max |X| is already in slotX)
   const bool fused = !masks && !tr;
+  // transformed: the products fold the transformed maxima (all three plans
+  // on 128 x 128 row-line tiles, unsplit or summed in the product kernel)
+  const bool fused_rht = masks && nvfp4::plan_rht_maxima(L.p1) && nvfp4::plan_rht_maxima(L.p2) &&
+                         nvfp4::plan_rht_maxima(L.p3);
   if (!fused) NS_TRY(nvfp4::launch_normalize(G, (Dt)gt, xm, xn, tr, clip, clipd, inv, X, slotX, s));
 
   for (int it = 0; it < k; ++it) {
     const float a = coeffs[3 * it], b = coeffs[3 * it + 1], c = coeffs[3 * it + 2];
     if (masks) {
       const nvfp4::RhtArg h{1u, (uint32_t)masks[it], o46};
-      zero_words_kernel<<<1, 256, 0, s>>>(slot, 4 * kSlotWords);
-      NS_TRY(hipGetLastError());
+      // fused: each product's epilogue folds the transformed maxima of its
+      // output (the next quantizer's s_g) into that quantizer's slot, and
+      // the passes clear the slots the next producer folds into, as in the
+      // plain step; otherwise a maximum pass per quantized tensor
+      const bool fx = fused_rht;
+      if (!fx || it == 0) {
+        zero_words_kernel<<<1, 256, 0, s>>>(slot, 4 * kSlotWords);
+        NS_TRY(hipGetLastError());
+        NS_TRY(nvfp4::launch_amax_tiles(X, Dt::F32, xm, xn, slotX, slotXc, h, s));
+      }
+      // the next step's X H and H^T X maxima come from this step's update
+      // product (none after the last step)
+      const bool next_max = fx && it + 1 < k;
       // qX = Q_1x16(X H), qX16 = Q_16x1(H^T X), each with its own s_g
-      NS_TRY(nvfp4::launch_amax_tiles(X, Dt::F32, xm, xn, slotX, slotXc, h, s));
       NS_TRY(nvfp4::launch_quant_tiles(X, Dt::F32, xm, xn, slotX, sgX, ws + L.qx_c, ws + L.qx_s,
-                                       ws + L.qt_c, ws + L.qt_s, nullptr, s, slotXc, sgXc, h));
+                                       ws + L.qt_c, ws + L.qt_s, fx ? slotA : nullptr, s, slotXc,
+                                       sgXc, h));
       // A = qX qX^T, upper triangle only (as without the transform)
       nvfp4::GemmProblem g1{ws + L.qx_c, ws + L.qx_s, sgX, ws + L.qx_c, ws + L.qx_s, sgX,
-                            xm, xm, xn, 1, 1.0f, 0.0f, nullptr, A, nullptr, 0, 1};
+                            xm, xm, xn, 1, 1.0f, 0.0f, nullptr, A, fx ? slotA : nullptr, 1, 1};
+      if (fx) {
+        g1.rht_on = 1;
+        g1.rht_mask = h.mask;
+        g1.clear_a = next_max ? slotX : nullptr;    // read by this step's quantizer only
+        g1.clear_b = next_max ? slotXc : nullptr;
+      }
       NS_TRY(nvfp4::launch_gemm(g1, L.p1, gws, false, s));
       // qA = Q_1x16(A H), from the tiles on and above the diagonal: the row
       // blocks of a lower tile are the column blocks of its mirror
-      NS_TRY(nvfp4::launch_amax_sym_tiles(A, xm, slotA, h, s));
-      NS_TRY(nvfp4::launch_quant_sym_tiles(A, xm, slotA, sgA, ws + L.qa_c, ws + L.qa_s, nullptr,
-                                           a46, s, 1, 0, 1u, h.mask));
+      if (!fx) NS_TRY(nvfp4::launch_amax_sym_tiles(A, xm, slotA, h, s));
+      NS_TRY(nvfp4::launch_quant_sym_tiles(A, xm, slotA, sgA, ws + L.qa_c, ws + L.qa_s,
+                                           fx ? slotB : nullptr, a46, s, 1, 0, 1u, h.mask));
       nvfp4::GemmProblem g2{ws + L.qa_c, ws + L.qa_s, sgA, ws + L.qa_c, ws + L.qa_s, sgA,
-                            xm, xm, xm, 1, c, b, A, B, nullptr, 0, 1};
+                            xm, xm, xm, 1, c, b, A, B, fx ? slotB : nullptr, 1, 1};
+      if (fx) {
+        g2.rht_on = 1;
+        g2.rht_mask = h.mask;
+      }
       NS_TRY(nvfp4::launch_gemm(g2, L.p2, gws, false, s));
       // qB = Q_1x16(B H), likewise
-      NS_TRY(nvfp4::launch_amax_sym_tiles(B, xm, slotB, h, s));
+      if (!fx) NS_TRY(nvfp4::launch_amax_sym_tiles(B, xm, slotB, h, s));
       NS_TRY(nvfp4::launch_quant_sym_tiles(B, xm, slotB, sgB, ws + L.qb_c, ws + L.qb_s, nullptr,
                                            a46, s, 1, 0, 1u, h.mask));
       const bool direct = it == k - 1 && !tr && ot == NS_F32;
       nvfp4::GemmProblem g3{ws + L.qb_c, ws + L.qb_s, sgB, ws + L.qt_c, ws + L.qt_s, sgXc,
                             xm, xn, xm, 0, 1.0f, a, X, direct ? static_cast<float*>(out) : X,
                             nullptr, 0};
+      if (next_max) {
+        // X' H (rows) and H'^T X' (columns) under the next step's transform
+        g3.rht_on = 1;
+        g3.rht_mask = (uint32_t)masks[it + 1];
+        g3.amax_out = slotX;
+        g3.amax_out_c = slotXc;
+        g3.amax_parts = 1;
+      }
       NS_TRY(nvfp4::launch_gemm(g3, L.p3, gws, false, s));
       if (direct) return NS_OK;
       continue;

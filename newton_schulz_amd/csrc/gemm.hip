@@ -525,7 +525,10 @@ __device__ __forceinline__ void load_addend(const GemmProblem& g, int64_t m0, in
 // In place (addend == out) every position is read, by load_addend, before
 // the lane that owns it stores it, and mirrored stores land below the
 // diagonal, which no tile reads.
-template <class C, bool SYM>
+//
+// KEEP (transformed maxima follow): acc keeps the written values, 0 outside
+// the matrix, and no amax is published here.
+template <class C, bool SYM, bool KEEP = false>
 __device__ __forceinline__ void epilogue(const GemmProblem& g, floatx16 (&acc)[C::FM][C::FN],
                                          const float (&ad)[C::FM][C::FN][16], int64_t m0, int64_t n0,
                                          int wm, int wn, int lane) {
@@ -565,6 +568,7 @@ __device__ __forceinline__ void epilogue(const GemmProblem& g, floatx16 (&acc)[C
             const uint32_t ab = abs_bits(v);
             amax = ab > amax ? ab : amax;
           }
+          if constexpr (KEEP) acc[i][j][r] = (r0 + dr < g.M && c0 + j * 32 < g.N) ? v : 0.0f;
           v4[t] = v;
         }
         if constexpr (SYM) {
@@ -584,7 +588,85 @@ __device__ __forceinline__ void epilogue(const GemmProblem& g, floatx16 (&acc)[C
         }
       }
     }
-  if (g.amax_out) amax_publish_wave(amax, g.amax_out, g.amax_parts != 0);
+  if constexpr (!KEEP)
+    if (g.amax_out) amax_publish_wave(amax, g.amax_out, g.amax_parts != 0);
+}
+
+// Transformed maxima of the tile the epilogue just wrote (its values in acc,
+// 0 outside the matrix), staged through the idle stage buffers as a
+// BM x BN float tile: every 16-block of a row (and of a column) is multiplied
+// by H^r with rht16, the operation order of the quantizer's own transform,
+// so the maxima are those of the tensor the quantizer encodes, bit for bit.
+// Symmetric, upper-only products: a diagonal tile is completed from its
+// upper triangle (the mirror the epilogue stores) and counts its rows; a
+// tile above the diagonal counts its rows and its columns (the rows of its
+// mirror), both into amax_out.  Otherwise rows go to amax_out and columns to
+// amax_out_c.
+template <class C, bool SYM>
+__device__ __forceinline__ void rht_tile_maxima(const GemmProblem& g, const floatx16 (&acc)[C::FM][C::FN],
+                                                int64_t m0, int64_t n0, int wm, int wn, int lane,
+                                                uint8_t* smem) {
+  constexpr int LD = C::BN + 4;   // row pitch in floats (16-byte aligned rows)
+  static_assert((size_t)C::BM * LD * 4 <= (size_t)C::NST * C::kStage, "tile does not fit the stage buffers");
+  float* T = reinterpret_cast<float*>(smem);
+  const bool diag = SYM && m0 == n0;
+  const int h = lane >> 5, c32 = lane & 31;
+  __syncthreads();   // every wave is done with the stage buffers
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int dr = wm * C::FM * 32 + i * 32 + 8 * (r >> 2) + (r & 3) + 4 * h;
+        const int dc = wn * C::FN * 32 + j * 32 + c32;
+        const float v = acc[i][j][r];
+        if (!diag || dr <= dc) T[dr * LD + dc] = v;
+        if (diag && dr < dc) T[dc * LD + dr] = v;
+      }
+  __syncthreads();
+  uint32_t mr = 0, mc = 0;
+  const int tid = (int)threadIdx.x;
+  constexpr int kRowBlocks = C::BM * (C::BN / 16), kColBlocks = (C::BM / 16) * C::BN;
+  for (int b = tid; b < kRowBlocks; b += C::kThreads) {
+    const int row = b / (C::BN / 16), cb = b % (C::BN / 16);
+    uint32_t v[16];
+#pragma unroll
+    for (int e = 0; e < 16; e += 4) {
+      const float4 w = *reinterpret_cast<const float4*>(T + row * LD + 16 * cb + e);
+      v[e] = __float_as_uint(w.x);
+      v[e + 1] = __float_as_uint(w.y);
+      v[e + 2] = __float_as_uint(w.z);
+      v[e + 3] = __float_as_uint(w.w);
+    }
+    rht16(v, g.rht_mask);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const uint32_t a = abs_bits(v[e]);
+      mr = a > mr ? a : mr;
+    }
+  }
+  if (!diag) {
+    for (int b = tid; b < kColBlocks; b += C::kThreads) {
+      const int col = b % C::BN, rb = b / C::BN;
+      uint32_t v[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) v[e] = __float_as_uint(T[(16 * rb + e) * LD + col]);
+      rht16(v, g.rht_mask);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const uint32_t a = abs_bits(v[e]);
+        mc = a > mc ? a : mc;
+      }
+    }
+  }
+  if constexpr (SYM) {
+    mr = mc > mr ? mc : mr;
+    if (g.amax_out) amax_publish_wave(mr, g.amax_out, g.amax_parts != 0);
+  } else {
+    if (g.amax_out) amax_publish_wave(mr, g.amax_out, g.amax_parts != 0);
+    if (g.amax_out_c) amax_publish_wave(mc, g.amax_out_c, g.amax_parts != 0);
+  }
 }
 
 // FP32 partials of a K-part: per (block b = i*FN + j, quarter q) a run of
@@ -602,12 +684,20 @@ __device__ __forceinline__ size_t partial_index(int b, int q, int thread) {
 // instantiation, so that single launches keep the plain kernel's code.
 // `t` must stay the first parameter: table_out reads it at offset 0 of the
 // kernel-argument segment.
-template <class C, bool SYM, bool FIXUP, bool BATCH>
+// RHTMAX: transformed maxima instead of max |out| (rht_tile_maxima); a
+// separate instantiation, so that the other launches keep their code.
+template <class C, bool SYM, bool FIXUP, bool BATCH, bool RHTMAX = false>
 __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_fast_kernel(const OutTable t, FastArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::NST * C::kStage];
   __shared__ uint32_t last_part;
   if constexpr (BATCH) select_problem(a, t.n);
   const GemmProblem& g = a.g;
+  if constexpr (RHTMAX) {
+    if (blockIdx.x == 0) {
+      if (g.clear_a) amax_clear(g.clear_a);
+      if (g.clear_b) amax_clear(g.clear_b);
+    }
+  }
 
   // ---- work unit: a whole tile or a K-part of a leftover tile (unit_of)
   Unit un;
@@ -862,7 +952,12 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_fast_kernel(c
       if (g.addend) load_addend<C, SYM>(g, m0, n0, wm, wn, lane, ad);
     }
   }
-  epilogue<C, SYM>(g, acc, ad, m0, n0, wm, wn, lane);
+  if constexpr (RHTMAX) {
+    epilogue<C, SYM, true>(g, acc, ad, m0, n0, wm, wn, lane);
+    rht_tile_maxima<C, SYM>(g, acc, m0, n0, wm, wn, lane, smem);
+  } else {
+    epilogue<C, SYM>(g, acc, ad, m0, n0, wm, wn, lane);
+  }
 }
 
 // One wave per workgroup: block (i, j) of wave w's sub-tile of split tile
@@ -1214,6 +1309,20 @@ hipError_t launch_with(const GemmProblem& g, const GemmPlan& p, void* ws, bool z
     if (b) gemm_fast_kernel<C, SY, FX, true><<<grid, C::kThreads, 0, s>>>(t, a);        \
     else gemm_fast_kernel<C, SY, FX, false><<<grid, C::kThreads, 0, s>>>(t, a);         \
   } while (0)
+  if (g.rht_on) {
+    // transformed maxima: 128 x 128 row-line tiles, single launches, no
+    // second summing kernel (plan_rht_maxima)
+    if constexpr (C::kLines && C::BM == 128 && C::BN == 128) {
+      if (b || (p.splits > 1 && !p.fixup)) return hipErrorInvalidValue;
+      if (g.symmetric && p.fixup) gemm_fast_kernel<C, true, true, false, true><<<grid, C::kThreads, 0, s>>>(t, a);
+      else if (g.symmetric) gemm_fast_kernel<C, true, false, false, true><<<grid, C::kThreads, 0, s>>>(t, a);
+      else if (p.fixup) gemm_fast_kernel<C, false, true, false, true><<<grid, C::kThreads, 0, s>>>(t, a);
+      else gemm_fast_kernel<C, false, false, false, true><<<grid, C::kThreads, 0, s>>>(t, a);
+      return hipGetLastError();
+    } else {
+      return hipErrorInvalidValue;
+    }
+  }
   if (g.symmetric && p.fixup) NVFP4_FAST(true, true);
   else if (g.symmetric) NVFP4_FAST(true, false);
   else if (p.fixup) NVFP4_FAST(false, true);
@@ -1247,6 +1356,7 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool symmetric, bool allow_s
 hipError_t launch_gemm(const GemmProblem& g, const GemmPlan& p, void* ws, bool zero_counters,
                        hipStream_t s) {
   if (g.batch < 1 || (g.batch > 1 && (!p.fast || g.batch_stride <= 0))) return hipErrorInvalidValue;
+  if (g.rht_on && (!plan_rht_maxima(p) || g.batch > 1)) return hipErrorInvalidValue;
   if (!p.fast) {
     if (g.symmetric) {
       const int64_t nt = (g.M + GBM - 1) / GBM;

@@ -112,6 +112,19 @@ struct GemmProblem {
   // batched: with out_each (a host array of `batch` pointers, at most
   // kMaxBatchOut) problem b writes its result to out_each[b] instead
   float* const* out_each = nullptr;
+  // transformed maxima (single launches on 128 x 128 tiles with 256-wide
+  // stages, tiles unsplit or summed in the product kernel): with rht_on the
+  // epilogue folds max |out H^r| over the row blocks into amax_out and
+  // max |H^r^T out| over the column blocks into amax_out_c -- for a
+  // symmetric product stored upper-only, the column blocks of a tile above
+  // the diagonal stand for the row blocks of its mirror and go to amax_out
+  // too -- instead of max |out|.  clear_a / clear_b (may be null): amax
+  // slots that workgroup 0 zeroes first.
+  int rht_on = 0;
+  uint32_t rht_mask = 0;
+  uint32_t* amax_out_c = nullptr;
+  uint32_t* clear_a = nullptr;
+  uint32_t* clear_b = nullptr;
 };
 constexpr int kMaxBatchOut = 32;
 
@@ -134,6 +147,10 @@ struct GemmPlan {
   size_t partial_bytes, ws_bytes;
 };
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool symmetric, bool allow_split);
+// Whether a product of this plan can fold transformed maxima (rht_on).
+inline bool plan_rht_maxima(const GemmPlan& p) {
+  return p.fast && p.cfg == 0 && (p.splits == 1 || p.fixup);
+}
 // ws: the plan's workspace.  The counters must be zero when the product
 // starts; every launch leaves them zero.  zero_counters clears them first
 // (a small kernel) for callers that cannot guarantee that.

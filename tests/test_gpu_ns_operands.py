@@ -196,6 +196,52 @@ def test_rht_operands_bit_exact():
     _sg_equal(h["sg"][2], qb.global_scale, "rht s_g(BH)")
 
 
+@pytest.mark.parametrize("case", ["gauss256x512", "gauss512x256", "full3072x8192"])
+def test_rht_fused_maxima_operands(case):
+    """The transform on shapes whose three products run 128 x 128 row-line
+    tiles: the maxima behind the last step's tensor scales are folded into
+    the epilogues of the products that wrote X (the previous step's update
+    product, under this step's transform), A and B (the Gram products; at
+    3072 their split tiles are summed in the product kernel first).  Every
+    s_g equals the oracle's on the GPU's own tensors and the codes of all
+    rows (sampled rows at full size) match byte for byte."""
+    from oracle.rht import rht_rows_f32
+    if case == "full3072x8192":
+        G, bits, clip = synth.ns_matrix(synth.ns_workload("ns3072x8192"), 0)
+        Gd, k = to_dev_bf16(bits), 2
+    else:
+        m, n = (256, 512) if case == "gauss256x512" else (512, 256)
+        G, clip, k = synth.gaussian(m, n, seed=21), np.inf, 3
+        Gd = to_dev_f32(G)
+    masks = [0xA5C3, 0x3C5A, 0x0FF1][:k]
+    coeffs = [QUINTIC] * k
+    print(f"[operands] rht {case} k={k}: GPU calls", flush=True)
+    _, h = _run(Gd, coeffs, clip, rht_masks=masks)
+    m, n = Gd.shape
+    if m <= n:
+        X = h["X"]                    # X_{k-1}: the last product wrote `out`
+    else:                             # transposed calls keep X_k; X_{k-1} from k - 1 steps
+        X = host(ns.ns_orthogonalize_ex(Gd, coeffs[:k - 1], clip=clip, rht_masks=masks[:k - 1])).T
+    X = np.ascontiguousarray(X, dtype=np.float32)
+    A, B = _sym(h["A"]), _sym(h["B"])
+    mk = masks[-1]
+    xm, xn = X.shape
+    if case == "full3072x8192":
+        rng = np.random.default_rng(31)
+        rows = np.unique(np.concatenate([rng.integers(0, xm, 24), [0, 127, 128, 3071]]))
+        cols = np.unique(np.concatenate([rng.integers(0, xn, 24), [0, 8191]]))
+    else:
+        rows, cols = np.arange(xm), np.arange(xn)
+    print(f"[operands] rht {case}: oracle", flush=True)
+    for label, t, got, sg_i, sel in (("qX", X, h["qX"], 0, rows), ("qX16", X.T, h["qX16"], 3, cols),
+                                     ("qA", A, h["qA"], 1, rows), ("qB", B, h["qB"], 2, rows)):
+        th = rht_rows_f32(t, mk).astype(np.float64)
+        amax = Q.tensor_amax(th)
+        _sg_equal(h["sg"][sg_i], Q.global_scale(amax), f"rht {case} s_g of {label}")
+        want = Q.quantize_rows(th[sel], amax=amax)
+        _same((got[0][sel], got[1][sel]), want, f"rht {case} {label}")
+
+
 @pytest.mark.parametrize("k", [1, 2])
 def test_full_size_operands_sampled_rows(k):
     """3072 x 8192 BF16 gradient, the benchmark's call: sampled rows of every
