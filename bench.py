@@ -185,13 +185,23 @@ def bf16_ns_ms(torch, G, coeffs, stream, reps=10):
 
 
 def grouped_line(ns, torch, synth, dev, stream, label, shapes, seed0, coeffs, clip_quantile,
-                 reps=3, warm=1):
+                 reps=3, warm=1, route=False):
     """Grouped NS over a batch of BF16 gradients drawn on the device (the
-    lowrank value model), against BF16 torch NS of the same batch."""
+    lowrank value model), against BF16 torch NS of the same batch.  route:
+    the pages' full route, the random Hadamard transform (one seeded 16-bit
+    sign mask per step) and adaptive 4/6 on every quantization besides the
+    quantile clip."""
     Gs = [synth.device_lowrank_bf16(r, c, seed0 + i, dev) for i, (r, c) in enumerate(shapes)]
     outs = [torch.empty(s, dtype=torch.float32, device=dev) for s in shapes]
     ws = torch.empty(ns.ns_grouped_workspace_bytes(shapes), dtype=torch.uint8, device=dev)
-    if clip_quantile:
+    if route:
+        masks = [int(v) for v in np.random.default_rng(seed0).integers(0, 1 << 16, len(coeffs))]
+        run = lambda: ns.ns_orthogonalize_grouped_ex(Gs, coeffs, clip_quantile=clip_quantile,
+                                                     rht_masks=masks, adaptive46=True, outs=outs,
+                                                     workspace=ws, stream=stream)
+        clip_what = (f"clip at the {clip_quantile} quantile of each |G| (on the device), random "
+                     "Hadamard transform and adaptive 4/6 on every quantization")
+    elif clip_quantile:
         run = lambda: ns.ns_orthogonalize_grouped_ex(Gs, coeffs, clip_quantile=clip_quantile,
                                                      outs=outs, workspace=ws, stream=stream)
         clip_what = f"clip at the {clip_quantile} quantile of each |G| (on the device)"
@@ -543,6 +553,10 @@ def main():
                          "the pages' four decoder blocks at d=4096 (d_ff 11008, 32 heads, 8 KV "
                          "heads; 28 matrices), quintic x5", synth.pages_block_shapes(4096), 6000,
                          coeffs, 0.99),
+            grouped_line(ns, torch, synth, dev, stream,
+                         "the pages' four decoder blocks at d=4096, their full route (transform, "
+                         "adaptive 4/6, p99 clip), quintic x5", synth.pages_block_shapes(4096),
+                         6000, coeffs, 0.99, route=True),
             grouped_line(ns, torch, synth, dev, stream,
                          "the pages' four decoder blocks at d=6144 (d_ff 13824, 48 heads, 8 KV "
                          "heads; 28 matrices), quintic x5", synth.pages_block_shapes(6144), 7000,
