@@ -592,10 +592,44 @@ __device__ __forceinline__ void epilogue(const GemmProblem& g, floatx16 (&acc)[C
     if (g.amax_out) amax_publish_wave(amax, g.amax_out, g.amax_parts != 0);
 }
 
+// max |x H^r| over one 16-block x (raw float bits), as rht16 followed by
+// the maximum of the magnitudes would give it: the same sign flips and FP32
+// butterfly, with the final multiplication by 1/4 applied once to the
+// largest magnitude (x -> RN(x / 4) is monotone and odd, so the largest of
+// the rounded quarters is the rounded quarter of the largest; NaN stays NaN).
+__device__ __forceinline__ uint32_t rht16_amax(const uint32_t (&v)[16], uint32_t mask) {
+  float f[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) f[j] = __uint_as_float(v[j] ^ (((mask >> j) & 1u) << 31));
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i & h) continue;
+      const float a = f[i], b = f[i + h];
+      f[i] = a + b;
+      f[i + h] = a - b;
+    }
+  }
+  uint32_t m = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const uint32_t a = abs_bits(__float_as_uint(f[j]));
+    m = a > m ? a : m;
+  }
+  return __float_as_uint(__uint_as_float(m) * 0.25f);
+}
+
+// Workgroup barrier after this wave's LDS accesses have completed (global
+// memory operations stay in flight).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Transformed maxima of the tile the epilogue just wrote (its values in acc,
 // 0 outside the matrix), staged through the idle stage buffers as a
 // BM x BN float tile: every 16-block of a row (and of a column) is multiplied
-// by H^r with rht16, the operation order of the quantizer's own transform,
+// by H^r in the operation order of the quantizer's own transform (rht16_amax),
 // so the maxima are those of the tensor the quantizer encodes, bit for bit.
 // Symmetric, upper-only products: a diagonal tile is completed from its
 // upper triangle (the mirror the epilogue stores) and counts its rows; a
@@ -611,7 +645,11 @@ __device__ __forceinline__ void rht_tile_maxima(const GemmProblem& g, const floa
   float* T = reinterpret_cast<float*>(smem);
   const bool diag = SYM && m0 == n0;
   const int h = lane >> 5, c32 = lane & 31;
-  __syncthreads();   // every wave is done with the stage buffers
+  // Barriers that order LDS only: __syncthreads' workgroup fence would also
+  // wait for the epilogue's global stores, which nothing here reads.  Every
+  // wave is done with the stage buffers here (their DMA writes were waited
+  // for in the last K-stage, their reads fed the MFMAs).
+  lds_barrier();
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
 #pragma unroll
@@ -624,7 +662,7 @@ __device__ __forceinline__ void rht_tile_maxima(const GemmProblem& g, const floa
         if (!diag || dr <= dc) T[dr * LD + dc] = v;
         if (diag && dr < dc) T[dc * LD + dr] = v;
       }
-  __syncthreads();
+  lds_barrier();
   uint32_t mr = 0, mc = 0;
   const int tid = (int)threadIdx.x;
   constexpr int kRowBlocks = C::BM * (C::BN / 16), kColBlocks = (C::BM / 16) * C::BN;
@@ -639,12 +677,8 @@ __device__ __forceinline__ void rht_tile_maxima(const GemmProblem& g, const floa
       v[e + 2] = __float_as_uint(w.z);
       v[e + 3] = __float_as_uint(w.w);
     }
-    rht16(v, g.rht_mask);
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const uint32_t a = abs_bits(v[e]);
-      mr = a > mr ? a : mr;
-    }
+    const uint32_t a = rht16_amax(v, g.rht_mask);
+    mr = a > mr ? a : mr;
   }
   if (!diag) {
     for (int b = tid; b < kColBlocks; b += C::kThreads) {
@@ -652,12 +686,8 @@ __device__ __forceinline__ void rht_tile_maxima(const GemmProblem& g, const floa
       uint32_t v[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) v[e] = __float_as_uint(T[(16 * rb + e) * LD + col]);
-      rht16(v, g.rht_mask);
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const uint32_t a = abs_bits(v[e]);
-        mc = a > mc ? a : mc;
-      }
+      const uint32_t a = rht16_amax(v, g.rht_mask);
+      mc = a > mc ? a : mc;
     }
   }
   if constexpr (SYM) {
