@@ -187,7 +187,9 @@ NsLayout ns_layout(int64_t m, int64_t n) {
 // operand is first multiplied along K by that step's random Hadamard
 // transform H^r: qX = Q_1x16(X H), qX16 = Q_16x1(H^T X) (own s_g),
 // qA = Q_1x16(A H) (= Q_16x1(H^T A)^T since A is symmetric), qB = Q_1x16(B H);
-// the maxima of the transformed tensors come from their own tiled pass.
+// the maxima of the transformed tensors are folded into the epilogue of the
+// product that writes each tensor (the first step's X, and every tensor of
+// shapes whose products cannot, take a tiled maximum pass instead).
 // 1-based rank of the q-quantile among n values: ceil(q n) in double,
 // clamped to [1, n].
 uint32_t quantile_rank(double q, int64_t n) {
