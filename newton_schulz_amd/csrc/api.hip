@@ -346,18 +346,20 @@ ns_status ns_run(const void* G, ns_dtype gt, int64_t m, int64_t n, const float* 
   return NS_OK;
 }
 
-// ns_run (without the transform) for `count` matrices whose iterates share
-// one shape xm x xn (matrix j is G[j], m[j] x n[j], transposed when m > n),
+// ns_run for `count` matrices whose iterates share one shape xm x xn
+// (matrix j is G[j], m[j] x n[j], transposed when m > n),
 // with workspace regions of ns_layout size at ws + j * stride.  The passes
 // done once per call (clip quantile, norm, first quantization, write-out)
 // run per matrix; every pass of a step runs once for all of them, one
 // launch per phase with grid row y = matrix.  Each matrix runs the kernels
 // and tile schedules of its own ns_run in the same order, so every result
-// equals ns_run's bit for bit.  All three products need fast-path plans.
+// equals ns_run's bit for bit.  All three products need fast-path plans,
+// and with the transform (`masks`) plans that fold the transformed maxima
+// (batchable).  The transformed step's first maximum pass runs per matrix.
 ns_status ns_run_batch(int count, const void* const* G, ns_dtype gt, const int64_t* m,
                        const int64_t* n, const float* coeffs, int k, const float* clip,
-                       double clip_q, bool a46, void* const* out, ns_dtype ot, uint8_t* ws,
-                       size_t stride, hipStream_t s) {
+                       double clip_q, const uint16_t* masks, bool a46, void* const* out,
+                       ns_dtype ot, uint8_t* ws, size_t stride, hipStream_t s) {
   const uint32_t o46 = a46 ? 1u : 0u;
   const NsLayout L = ns_layout(m[0], n[0]);
   const int64_t xm = m[0] < n[0] ? m[0] : n[0], xn = m[0] < n[0] ? n[0] : m[0];
@@ -387,7 +389,14 @@ ns_status ns_run_batch(int count, const void* const* G, ns_dtype gt, const int64
                                        slot + 2 * kSlotWords,
                                        any_split ? reinterpret_cast<uint32_t*>(gws) : nullptr,
                                        (int)(nvfp4::kGemmCounterBytes / sizeof(uint32_t)), s));
-    if (tr) {
+    if (masks) {
+      // as ns_run's transformed call: X0, then the maxima of X0 H and H^T X0
+      NS_TRY(nvfp4::launch_normalize(G[j], (Dt)gt, xm, xn, tr, clip[j], clipd, inv, X, slot, s));
+      zero_words_kernel<<<1, 256, 0, s>>>(slot, 4 * kSlotWords);
+      NS_TRY(hipGetLastError());
+      NS_TRY(nvfp4::launch_amax_tiles(X, Dt::F32, xm, xn, slot, slot + 3 * kSlotWords,
+                                      nvfp4::RhtArg{1u, (uint32_t)masks[0], o46}, s));
+    } else if (tr) {
       NS_TRY(nvfp4::launch_normalize(G[j], (Dt)gt, xm, xn, true, clip[j], clipd, inv, X, slot, s));
       NS_TRY(nvfp4::launch_quant_tiles(X, Dt::F32, xm, xn, slot, sg, at(j, L.qx_c), at(j, L.qx_s),
                                        at(j, L.qt_c), at(j, L.qt_s), slot + kSlotWords, s, nullptr,
@@ -405,8 +414,9 @@ ns_status ns_run_batch(int count, const void* const* G, ns_dtype gt, const int64
   float* B = reinterpret_cast<float*>(at(0, L.B));
   float* sg = reinterpret_cast<float*>(at(0, L.sg));
   uint32_t* slot = reinterpret_cast<uint32_t*>(at(0, L.slot));
-  uint32_t *slotX = slot, *slotA = slot + kSlotWords, *slotB = slot + 2 * kSlotWords;
-  float *sgX = sg, *sgA = sg + 1, *sgB = sg + 2;
+  uint32_t *slotX = slot, *slotA = slot + kSlotWords, *slotB = slot + 2 * kSlotWords,
+           *slotXc = slot + 3 * kSlotWords;
+  float *sgX = sg, *sgA = sg + 1, *sgB = sg + 2, *sgXc = sg + 3;
   uint8_t* gws = at(0, L.gemm_part);
   // per matrix: where its last update product writes (its output, or X)
   std::vector<float*> direct((size_t)count);
@@ -415,6 +425,41 @@ ns_status ns_run_batch(int count, const void* const* G, ns_dtype gt, const int64
                                                        : reinterpret_cast<float*>(at(j, L.X));
   for (int it = 0; it < k; ++it) {
     const float a = coeffs[3 * it], b = coeffs[3 * it + 1], c = coeffs[3 * it + 2];
+    if (masks) {
+      // ns_run's transformed step, each phase one launch for every matrix
+      const nvfp4::RhtArg h{1u, (uint32_t)masks[it], o46};
+      const bool next_max = it + 1 < k;
+      NS_TRY(nvfp4::launch_quant_tiles(X, Dt::F32, xm, xn, slotX, sgX, at(0, L.qx_c), at(0, L.qx_s),
+                                       at(0, L.qt_c), at(0, L.qt_s), slotA, s, slotXc, sgXc, h,
+                                       count, bs));
+      nvfp4::GemmProblem g1{at(0, L.qx_c), at(0, L.qx_s), sgX, at(0, L.qx_c), at(0, L.qx_s), sgX,
+                            xm, xm, xn, 1, 1.0f, 0.0f, nullptr, A, slotA, 1, 1, count, bs};
+      g1.rht_on = 1;
+      g1.rht_mask = h.mask;
+      g1.clear_a = next_max ? slotX : nullptr;
+      g1.clear_b = next_max ? slotXc : nullptr;
+      NS_TRY(nvfp4::launch_gemm(g1, L.p1, gws, false, s));
+      NS_TRY(nvfp4::launch_quant_sym_tiles(A, xm, slotA, sgA, at(0, L.qa_c), at(0, L.qa_s), slotB,
+                                           a46, s, count, bs, 1u, h.mask));
+      nvfp4::GemmProblem g2{at(0, L.qa_c), at(0, L.qa_s), sgA, at(0, L.qa_c), at(0, L.qa_s), sgA,
+                            xm, xm, xm, 1, c, b, A, B, slotB, 1, 1, count, bs};
+      g2.rht_on = 1;
+      g2.rht_mask = h.mask;
+      NS_TRY(nvfp4::launch_gemm(g2, L.p2, gws, false, s));
+      NS_TRY(nvfp4::launch_quant_sym_tiles(B, xm, slotB, sgB, at(0, L.qb_c), at(0, L.qb_s), nullptr,
+                                           a46, s, count, bs, 1u, h.mask));
+      nvfp4::GemmProblem g3{at(0, L.qb_c), at(0, L.qb_s), sgB, at(0, L.qt_c), at(0, L.qt_s), sgXc,
+                            xm, xn, xm, 0, 1.0f, a, X, X, nullptr, 1, 0, count, bs};
+      if (next_max) {
+        g3.rht_on = 1;
+        g3.rht_mask = (uint32_t)masks[it + 1];
+        g3.amax_out = slotX;
+        g3.amax_out_c = slotXc;
+      }
+      if (it == k - 1) g3.out_each = direct.data();
+      NS_TRY(nvfp4::launch_gemm(g3, L.p3, gws, false, s));
+      continue;
+    }
     if (it > 0)
       NS_TRY(nvfp4::launch_quant_tiles(X, Dt::F32, xm, xn, slotX, sgX, at(0, L.qx_c), at(0, L.qx_s),
                                        at(0, L.qt_c), at(0, L.qt_s), slotA, s, nullptr, nullptr,
@@ -443,9 +488,13 @@ ns_status ns_run_batch(int count, const void* const* G, ns_dtype gt, const int64
   return NS_OK;
 }
 
-// A batch needs every product on the fast path (K a multiple of 128).
-bool batchable(int64_t m, int64_t n) {
+// A batch needs every product on the fast path (K a multiple of 128), and
+// with the transform (rht) products that fold the transformed maxima.
+bool batchable(int64_t m, int64_t n, bool rht) {
   const NsLayout L = ns_layout(m, n);
+  if (rht)
+    return nvfp4::plan_rht_maxima(L.p1) && nvfp4::plan_rht_maxima(L.p2) &&
+           nvfp4::plan_rht_maxima(L.p3);
   return L.p1.fast && L.p2.fast && L.p3.fast;
 }
 
@@ -832,7 +881,7 @@ struct GroupPlan {
   std::vector<double> cost;              // per run: sum of m n min(m, n)
 };
 
-GroupPlan plan_group(int count, const int64_t* m, const int64_t* n, int nstreams, bool batches) {
+GroupPlan plan_group(int count, const int64_t* m, const int64_t* n, int nstreams, bool rht) {
   std::vector<std::pair<int64_t, int64_t>> keys;
   std::vector<std::vector<int>> classes;
   auto cost_of = [&](int i) {
@@ -858,7 +907,7 @@ GroupPlan plan_group(int count, const int64_t* m, const int64_t* n, int nstreams
     const bool small = ns_layout(m[cls[0]], n[cls[0]]).p1.tiles < kFillTiles;
     const size_t ns_ = (size_t)(nstreams > 0 ? nstreams : 1);
     size_t run = small ? cls.size() : (cls.size() + ns_ - 1) / ns_;
-    if (!batches || !batchable(m[cls[0]], n[cls[0]]) || run < 1) run = 1;   // one matrix per item
+    if (!batchable(m[cls[0]], n[cls[0]], rht) || run < 1) run = 1;   // one matrix per item
     if (run > (size_t)nvfp4::kMaxBatchOut) run = nvfp4::kMaxBatchOut;
     for (size_t a = 0; a < cls.size(); a += run) {
       const size_t b = a + run < cls.size() ? a + run : cls.size();
@@ -875,7 +924,7 @@ GroupPlan plan_group(int count, const int64_t* m, const int64_t* n, int nstreams
 }
 
 // Run c of a grouped call on stream s: one batch when it has several
-// members and no transform (see ns_run_batch), else its members one by one.
+// members (see ns_run_batch), else its members one by one.
 template <class One>
 ns_status run_class(const GroupPlan& P, int c, const void* const* G, ns_dtype gt,
                     const int64_t* m, const int64_t* n, const float* coeffs, int k,
@@ -883,7 +932,7 @@ ns_status run_class(const GroupPlan& P, int c, const void* const* G, ns_dtype gt
                     void* const* out, ns_dtype ot, uint8_t* base, hipStream_t s, One&& one) {
   const std::vector<int>& mem = P.items[(size_t)c];
   const int first = mem[0];
-  if (mem.size() < 2 || masks || !batchable(m[first], n[first])) {
+  if (mem.size() < 2 || !batchable(m[first], n[first], masks != nullptr)) {
     for (int i : mem) {
       const ns_status st = one(i, s);
       if (st != NS_OK) return st;
@@ -904,7 +953,7 @@ ns_status run_class(const GroupPlan& P, int c, const void* const* G, ns_dtype gt
     cl[j] = clip_q > 0.0 ? INFINITY : clip[i];
   }
   return ns_run_batch((int)cnt, g.data(), gt, mm.data(), nn.data(), coeffs, k, cl.data(), clip_q,
-                      a46, o.data(), ot, base + P.off[(size_t)first], P.stride[(size_t)c], s);
+                      masks, a46, o.data(), ot, base + P.off[(size_t)first], P.stride[(size_t)c], s);
 }
 
 }  // namespace
@@ -980,7 +1029,8 @@ ns_status grouped_ex_impl(int count, const void* const* G, const int64_t* m, con
     if (st != NS_OK) return st;
   }
   uint8_t* base = static_cast<uint8_t*>(ws);
-  const GroupPlan P = plan_group(count, m, n, streams ? nstreams : kGroupStreams, !opt->rht_masks);
+  const GroupPlan P = plan_group(count, m, n, streams ? nstreams : kGroupStreams,
+                                 opt->rht_masks != nullptr);
   const bool a46 = opt->adaptive46 != 0;
   auto one = [&](int i, hipStream_t s) {
     const float ci = q > 0.0 ? INFINITY : clip[i];
@@ -1018,7 +1068,7 @@ ns_status ns_orthogonalize_grouped(int count, const void* const* G, const int64_
     if (st != NS_OK) return st;
   }
   uint8_t* base = static_cast<uint8_t*>(ws);
-  const GroupPlan P = plan_group(count, m, n, kGroupStreams, true);
+  const GroupPlan P = plan_group(count, m, n, kGroupStreams, false);
   auto one = [&](int i, hipStream_t s) {
     return ns_run(G[i], gt, m[i], n[i], coeffs, k, clip[i], 0.0, nullptr, false, out[i], ot,
                   base + P.off[(size_t)i], s);

@@ -152,6 +152,7 @@ __device__ __forceinline__ T* shift_bytes(T* p, int64_t off) {
 // offset (wave-uniform, so the operand bases stay in scalar registers).
 // Workgroup (x, y) has linear id y * units + x, and units is a multiple of
 // kXcds, so it runs on the XCD its unit has in a single launch.
+template <bool RHTMAX>
 __device__ __forceinline__ void select_problem(FastArgs& a, int nout) {
   const int64_t off = (int64_t)blockIdx.y * a.bstride;
   GemmProblem& g = a.g;
@@ -168,6 +169,11 @@ __device__ __forceinline__ void select_problem(FastArgs& a, int nout) {
     g.out = shift_bytes(g.out, off);
   }
   g.amax_out = shift_bytes(g.amax_out, off);
+  if constexpr (RHTMAX) {
+    g.amax_out_c = shift_bytes(g.amax_out_c, off);
+    g.clear_a = shift_bytes(g.clear_a, off);
+    g.clear_b = shift_bytes(g.clear_b, off);
+  }
   a.partials = shift_bytes(a.partials, off);
   a.counters = shift_bytes(a.counters, off);
 }
@@ -720,7 +726,7 @@ template <class C, bool SYM, bool FIXUP, bool BATCH, bool RHTMAX = false>
 __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_fast_kernel(const OutTable t, FastArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::NST * C::kStage];
   __shared__ uint32_t last_part;
-  if constexpr (BATCH) select_problem(a, t.n);
+  if constexpr (BATCH) select_problem<RHTMAX>(a, t.n);
   const GemmProblem& g = a.g;
   if constexpr (RHTMAX) {
     if (blockIdx.x == 0) {
@@ -997,7 +1003,7 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void gemm_fast_kernel(c
 template <class C, bool SYM, bool BATCH>   // `t` first, as in gemm_fast_kernel
 __global__ __launch_bounds__(64) void gemm_reduce_kernel(const OutTable t, FastArgs a) {
   constexpr int kBlocks = C::FM * C::FN;
-  if constexpr (BATCH) select_problem(a, t.n);
+  if constexpr (BATCH) select_problem<false>(a, t.n);
   const int bid = (int)blockIdx.x;
   const int s = bid / (C::kWaves * kBlocks), rem = bid % (C::kWaves * kBlocks);
   const int w = rem / kBlocks, b = rem % kBlocks, i = b / C::FN, j = b % C::FN;
@@ -1339,15 +1345,20 @@ hipError_t launch_with(const GemmProblem& g, const GemmPlan& p, void* ws, bool z
     if (b) gemm_fast_kernel<C, SY, FX, true><<<grid, C::kThreads, 0, s>>>(t, a);        \
     else gemm_fast_kernel<C, SY, FX, false><<<grid, C::kThreads, 0, s>>>(t, a);         \
   } while (0)
+#define NVFP4_RHT(SY, FX)                                                               \
+  do {                                                                                  \
+    if (b) gemm_fast_kernel<C, SY, FX, true, true><<<grid, C::kThreads, 0, s>>>(t, a);  \
+    else gemm_fast_kernel<C, SY, FX, false, true><<<grid, C::kThreads, 0, s>>>(t, a);   \
+  } while (0)
   if (g.rht_on) {
-    // transformed maxima: 128 x 128 row-line tiles, single launches, no
-    // second summing kernel (plan_rht_maxima)
+    // transformed maxima: 128 x 128 row-line tiles, no second summing
+    // kernel (plan_rht_maxima)
     if constexpr (C::kLines && C::BM == 128 && C::BN == 128) {
-      if (b || (p.splits > 1 && !p.fixup)) return hipErrorInvalidValue;
-      if (g.symmetric && p.fixup) gemm_fast_kernel<C, true, true, false, true><<<grid, C::kThreads, 0, s>>>(t, a);
-      else if (g.symmetric) gemm_fast_kernel<C, true, false, false, true><<<grid, C::kThreads, 0, s>>>(t, a);
-      else if (p.fixup) gemm_fast_kernel<C, false, true, false, true><<<grid, C::kThreads, 0, s>>>(t, a);
-      else gemm_fast_kernel<C, false, false, false, true><<<grid, C::kThreads, 0, s>>>(t, a);
+      if (p.splits > 1 && !p.fixup) return hipErrorInvalidValue;
+      if (g.symmetric && p.fixup) NVFP4_RHT(true, true);
+      else if (g.symmetric) NVFP4_RHT(true, false);
+      else if (p.fixup) NVFP4_RHT(false, true);
+      else NVFP4_RHT(false, false);
       return hipGetLastError();
     } else {
       return hipErrorInvalidValue;
@@ -1358,6 +1369,7 @@ hipError_t launch_with(const GemmProblem& g, const GemmPlan& p, void* ws, bool z
   else if (p.fixup) NVFP4_FAST(false, true);
   else NVFP4_FAST(false, false);
 #undef NVFP4_FAST
+#undef NVFP4_RHT
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1 || p.fixup) return e;
   const dim3 rgrid((unsigned)(p.split_tiles * C::kWaves * C::FM * C::FN), (unsigned)g.batch);
@@ -1386,7 +1398,7 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool symmetric, bool allow_s
 hipError_t launch_gemm(const GemmProblem& g, const GemmPlan& p, void* ws, bool zero_counters,
                        hipStream_t s) {
   if (g.batch < 1 || (g.batch > 1 && (!p.fast || g.batch_stride <= 0))) return hipErrorInvalidValue;
-  if (g.rht_on && (!plan_rht_maxima(p) || g.batch > 1)) return hipErrorInvalidValue;
+  if (g.rht_on && !plan_rht_maxima(p)) return hipErrorInvalidValue;
   if (!p.fast) {
     if (g.symmetric) {
       const int64_t nt = (g.M + GBM - 1) / GBM;

@@ -112,8 +112,8 @@ struct GemmProblem {
   // batched: with out_each (a host array of `batch` pointers, at most
   // kMaxBatchOut) problem b writes its result to out_each[b] instead
   float* const* out_each = nullptr;
-  // transformed maxima (single launches on 128 x 128 tiles with 256-wide
-  // stages, tiles unsplit or summed in the product kernel): with rht_on the
+  // transformed maxima (128 x 128 tiles with 256-wide stages, tiles
+  // unsplit or summed in the product kernel): with rht_on the
   // epilogue folds max |out H^r| over the row blocks into amax_out and
   // max |H^r^T out| over the column blocks into amax_out_c -- for a
   // symmetric product stored upper-only, the column blocks of a tile above

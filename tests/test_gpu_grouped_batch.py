@@ -5,10 +5,9 @@ kernels and tile schedule of its single call.  Every result must equal its
 single call bit for bit: with both output types, with the on-device
 quantile clip and adaptive 4/6, with split Gram products summed in the
 product kernel and by the separate reduce kernel, for classes mixed with
-matrices the batch
-does not take (one member, a K off the fast path, the random Hadamard
-transform), and on the benchmark's four-block batch and the pages' d = 4096
-decoder blocks at full size."""
+matrices the batch does not take (one member, a K off the fast path), with
+the random Hadamard transform, and on the benchmark's four-block batch and
+the pages' d = 4096 decoder blocks at full size (also on their full route)."""
 import numpy as np
 import pytest
 import torch
@@ -90,16 +89,27 @@ def test_split_products_summed_by_the_reduce_kernel():
         assert _same(o, ns.ns_orthogonalize(g, coeffs, c)), shapes[i]
 
 
-def test_transform_keeps_per_matrix_runs():
-    """With the random Hadamard transform the class runs matrix by matrix
-    (the transform's passes are not batched); results as single calls."""
-    shapes = [(256, 512), (512, 256), (256, 512)]
+@pytest.mark.parametrize("opts", ["rht", "route"])
+def test_transform_batches_equal_single_calls(opts):
+    """With the random Hadamard transform a class also runs as one batch
+    when its products fold the transformed maxima (256- and 512-wide
+    iterates here; (384, 384) with K = 384 does not, and runs matrix by
+    matrix); every result equals its single call bit for bit, also on the
+    pages' full route (transform, adaptive 4/6, quantile clip)."""
+    shapes = [(256, 512), (512, 256), (256, 512), (512, 512), (512, 512), (384, 384), (384, 384)]
     Gs = _inputs(shapes, 340, bf16=False)
-    coeffs = [CUBIC] * 2
-    masks = synth.rht_masks(2, seed=9)
-    outs = ns.ns_orthogonalize_grouped_ex(Gs, coeffs, clips=[0.1] * 3, rht_masks=masks)
-    for g, o in zip(Gs, outs):
-        assert _same(o, ns.ns_orthogonalize_ex(g, coeffs, clip=0.1, rht_masks=masks))
+    coeffs = [synth.QUINTIC, synth.QUINTIC, CUBIC]
+    masks = synth.rht_masks(3, seed=9)
+    if opts == "rht":
+        outs = ns.ns_orthogonalize_grouped_ex(Gs, coeffs, clips=[0.1] * len(shapes), rht_masks=masks)
+        single = lambda g: ns.ns_orthogonalize_ex(g, coeffs, clip=0.1, rht_masks=masks)
+    else:
+        outs = ns.ns_orthogonalize_grouped_ex(Gs, coeffs, clip_quantile=0.99, rht_masks=masks,
+                                              adaptive46=True)
+        single = lambda g: ns.ns_orthogonalize_ex(g, coeffs, clip_quantile=0.99, rht_masks=masks,
+                                                  adaptive46=True)
+    for s_, g, o in zip(shapes, Gs, outs):
+        assert _same(o, single(g)), (opts, s_)
 
 
 def _device_batch(shapes, seed0):
@@ -112,7 +122,7 @@ def _device_batch(shapes, seed0):
     return Gs, clips
 
 
-@pytest.mark.parametrize("which", ["ns4blocks", "pages_d4096"])
+@pytest.mark.parametrize("which", ["ns4blocks", "pages_d4096", "pages_d4096_route"])
 def test_full_size_batches_equal_single_calls(which):
     if which == "ns4blocks":
         shapes = synth.ns_workload("ns4blocks")["shapes"]
@@ -122,10 +132,18 @@ def test_full_size_batches_equal_single_calls(which):
     coeffs = [synth.QUINTIC] * 5
     print(f"[batch] {which}: {len(shapes)} matrices, grouped call", flush=True)
     ws = torch.empty(ns.ns_grouped_workspace_bytes(shapes), dtype=torch.uint8, device=DEV)
-    outs = ns.ns_orthogonalize_grouped(Gs, coeffs, clips, workspace=ws)
+    if which == "pages_d4096_route":
+        # the pages' full route: transform, adaptive 4/6, p99 clip
+        masks = synth.rht_masks(5, seed=11)
+        outs = ns.ns_orthogonalize_grouped_ex(Gs, coeffs, clip_quantile=0.99, rht_masks=masks,
+                                              adaptive46=True, workspace=ws)
+        single = lambda g, c: ns.ns_orthogonalize_ex(g, coeffs, clip_quantile=0.99, rht_masks=masks,
+                                                     adaptive46=True)
+    else:
+        outs = ns.ns_orthogonalize_grouped(Gs, coeffs, clips, workspace=ws)
+        single = lambda g, c: ns.ns_orthogonalize(g, coeffs, c)
     torch.cuda.synchronize()
     del ws
     for i, (g, o, c) in enumerate(zip(Gs, outs, clips)):
-        single = ns.ns_orthogonalize(g, coeffs, c)
-        assert _same(o, single), (which, i, shapes[i])
+        assert _same(o, single(g, c)), (which, i, shapes[i])
     print(f"[batch] {which}: every matrix equal to its single call", flush=True)
