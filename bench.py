@@ -149,8 +149,8 @@ def source_digest(files=("gemm.hip", "nvfp4_device.hpp")):
 # HBM bytes per launch of the dominant kernel (X = a X + qB qX16^T at
 # 3072 x 8192), from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE, each scaled by
 # what the counter reads for a plain copy of known size; see profiles/.
-DOMINANT_TRAFFIC = {"src_sha256": "f609f7586526b8552ecd76cebbc56922935a02b6f76ee95f1e07d105c516b497",
-                    "bytes_per_launch": 440511653}
+DOMINANT_TRAFFIC = {"src_sha256": "75794f1efd41fced31aff27c81f9d13bb8e6609d5dcd98459d730eb955e4337e",
+                    "bytes_per_launch": 440739011}
 # Bytes of one quantize + dequantize pair of the 2^28 BF16 tensor (the
 # maximum, encode and decode kernels) between the L2 caches and memory,
 # measured the same way (Infinity Cache hits included).
