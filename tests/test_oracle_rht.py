@@ -131,3 +131,33 @@ def test_transformed_quantized_ns_tracks_exact_ns():
 def test_one_mask_per_step_is_required():
     with pytest.raises(ValueError):
         N.ns_nvfp4(np.ones((16, 16)), [(1.5, -0.5, 0.0)] * 2, rht_masks=[1])
+
+
+@pytest.mark.parametrize("scale", [1.0, 2.0 ** -120, 2.0 ** -140, 2.0 ** 120])
+def test_block_maximum_commutes_with_the_quarter_scaling(scale):
+    """The tensor maximum of the transformed blocks may be taken before the
+    butterfly's final multiplication by 1/4 and scaled once: x -> RN(x / 4)
+    is monotone and odd in float32, subnormal results included, so
+    max_i |RN(f_i / 4)| = RN(max_i |f_i| / 4).  Checked against the FP32
+    butterfly of the transform on blocks whose values land in the normal,
+    subnormal and near-overflow ranges."""
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal((512, 64)) * scale).astype(np.float32)
+    for mask in (0x0000, 0xA5C3, 0xFFFF):
+        full = R.rht_rows_f32(x, mask)                       # includes the 1/4
+        s = R.sign_vector(mask).astype(np.float32)
+        v = (x.reshape(512, 4, 16) * s).astype(np.float32)
+        h = 1
+        while h < 16:                                         # the butterfly without the 1/4
+            out = v.copy()
+            for i in range(16):
+                if i & h:
+                    continue
+                out[..., i] = v[..., i] + v[..., i + h]
+                out[..., i + h] = v[..., i] - v[..., i + h]
+            v = out
+            h *= 2
+        blockmax = np.abs(v).max(axis=-1).astype(np.float32)
+        want = np.abs(full).reshape(512, 4, 16).max(axis=-1)
+        got = (blockmax * np.float32(0.25)).astype(np.float32)
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), (scale, mask)
