@@ -121,6 +121,27 @@ def test_zero_and_nan_inputs():
     assert np.all(np.isfinite(out))
 
 
+@pytest.mark.parametrize("transform", [False, True])
+def test_zero_and_nan_inputs_on_the_fast_path(transform):
+    """256 x 512: every product on 128 x 128 row-line tiles, and with the
+    transform the maxima folded into their epilogues.  A zero gradient stays
+    zero (every s_g is 0); one NaN or infinity makes every output NaN (the
+    maxima, integer maxima on the magnitude bits, keep the NaN)."""
+    masks = synth.rht_masks(3, seed=4)
+
+    def run(g):
+        out = ns.ns_orthogonalize_ex(to_dev_f32(g), [QUINTIC] * 3, clip=np.inf,
+                                     rht_masks=masks if transform else None)
+        return host(out)
+    z = np.zeros((256, 512), np.float32)
+    assert np.array_equal(run(z), z)
+    g = synth.gaussian(256, 512, seed=6)
+    g[17, 300] = np.nan
+    assert np.all(np.isnan(run(g)))
+    g[17, 300] = -np.inf
+    assert np.all(np.isnan(run(g)))
+
+
 def test_grouped_matches_single_calls():
     shapes = [(128, 256), (256, 128), (96, 96), (64, 320)]
     Gs = [synth.gaussian(r, c, seed=10 + i) for i, (r, c) in enumerate(shapes)]
