@@ -196,15 +196,18 @@ def test_rht_operands_bit_exact():
     _sg_equal(h["sg"][2], qb.global_scale, "rht s_g(BH)")
 
 
-@pytest.mark.parametrize("case", ["gauss256x512", "gauss512x256", "full3072x8192"])
-def test_rht_fused_maxima_operands(case):
+@pytest.mark.parametrize("case,adaptive46", [("gauss256x512", False), ("gauss512x256", False),
+                                             ("gauss256x512", True), ("gauss512x256", True),
+                                             ("full3072x8192", False)])
+def test_rht_fused_maxima_operands(case, adaptive46):
     """The transform on shapes whose three products run 128 x 128 row-line
     tiles: the maxima behind the last step's tensor scales are folded into
     the epilogues of the products that wrote X (the previous step's update
     product, under this step's transform), A and B (the Gram products; at
     3072 their split tiles are summed in the product kernel first).  Every
     s_g equals the oracle's on the GPU's own tensors and the codes of all
-    rows (sampled rows at full size) match byte for byte."""
+    rows (sampled rows at full size) match byte for byte; with adaptive 4/6
+    too (the pages' route)."""
     from oracle.rht import rht_rows_f32
     if case == "full3072x8192":
         G, bits, clip = synth.ns_matrix(synth.ns_workload("ns3072x8192"), 0)
@@ -216,12 +219,13 @@ def test_rht_fused_maxima_operands(case):
     masks = [0xA5C3, 0x3C5A, 0x0FF1][:k]
     coeffs = [QUINTIC] * k
     print(f"[operands] rht {case} k={k}: GPU calls", flush=True)
-    _, h = _run(Gd, coeffs, clip, rht_masks=masks)
+    _, h = _run(Gd, coeffs, clip, adaptive46=adaptive46, rht_masks=masks)
     m, n = Gd.shape
     if m <= n:
         X = h["X"]                    # X_{k-1}: the last product wrote `out`
     else:                             # transposed calls keep X_k; X_{k-1} from k - 1 steps
-        X = host(ns.ns_orthogonalize_ex(Gd, coeffs[:k - 1], clip=clip, rht_masks=masks[:k - 1])).T
+        X = host(ns.ns_orthogonalize_ex(Gd, coeffs[:k - 1], clip=clip, rht_masks=masks[:k - 1],
+                                        adaptive46=adaptive46)).T
     X = np.ascontiguousarray(X, dtype=np.float32)
     A, B = _sym(h["A"]), _sym(h["B"])
     mk = masks[-1]
@@ -238,8 +242,8 @@ def test_rht_fused_maxima_operands(case):
         th = rht_rows_f32(t, mk).astype(np.float64)
         amax = Q.tensor_amax(th)
         _sg_equal(h["sg"][sg_i], Q.global_scale(amax), f"rht {case} s_g of {label}")
-        want = Q.quantize_rows(th[sel], amax=amax)
-        _same((got[0][sel], got[1][sel]), want, f"rht {case} {label}")
+        want = Q.quantize_rows(th[sel], amax=amax, adaptive46=adaptive46)
+        _same((got[0][sel], got[1][sel]), want, f"rht {case} a46={adaptive46} {label}")
 
 
 @pytest.mark.parametrize("k", [1, 2])
