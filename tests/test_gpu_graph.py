@@ -33,9 +33,11 @@ def _capture(fn):
 
 # 384 x 8192: the Gram product's leftover tiles are split along K, so its
 # K-parts and their reduce run on a side stream forked from the call's stream
+# 256 x 512 with the transform: the products fold the transformed maxima
 @pytest.mark.parametrize("variant,shape", [("plain", (384, 640)), ("plain", (384, 8192)),
                                            ("p99 clip + transform", (384, 640)),
-                                           ("adaptive 4/6", (384, 640))])
+                                           ("adaptive 4/6", (384, 640)),
+                                           ("full route", (256, 512))])
 def test_graph_replays_match_eager(variant, shape):
     G = synth.student_t(*shape, seed=31)
     bits, _ = synth.to_bf16(G)
@@ -49,6 +51,10 @@ def test_graph_replays_match_eager(variant, shape):
     elif variant == "adaptive 4/6":
         call = lambda g: ns.ns_orthogonalize_ex(g, coeffs, clip=0.05, adaptive46=True,
                                                 out=out, workspace=ws)
+    elif variant == "full route":
+        masks = synth.rht_masks(len(coeffs), seed=3)
+        call = lambda g: ns.ns_orthogonalize_ex(g, coeffs, clip_quantile=0.99, rht_masks=masks,
+                                                adaptive46=True, out=out, workspace=ws)
     else:
         masks = synth.rht_masks(len(coeffs), seed=3)
         call = lambda g: ns.ns_orthogonalize_ex(g, coeffs, clip_quantile=0.99, rht_masks=masks,
@@ -70,9 +76,12 @@ def test_graph_replays_match_eager(variant, shape):
         assert np.array_equal(got, want), (variant, shape, r)
 
 
-def test_grouped_call_captures_across_its_streams():
+@pytest.mark.parametrize("route", [False, True])
+def test_grouped_call_captures_across_its_streams(route):
     """A grouped call forks onto internal streams and joins them back into
-    the caller's stream; captured, it replays to the eager results."""
+    the caller's stream; captured, it replays to the eager results (also on
+    the pages' full route, whose 256 x 512 class runs as one transformed
+    batch)."""
     shapes = [(256, 512), (512, 256), (128, 128), (384, 640), (64, 192)]
     Gs = [to_dev_bf16(synth.to_bf16(synth.student_t(r, c, seed=40 + i))[0])
           for i, (r, c) in enumerate(shapes)]
@@ -80,11 +89,18 @@ def test_grouped_call_captures_across_its_streams():
     clips = [0.05] * len(shapes)
     outs = [torch.empty(s, dtype=torch.float32, device=Gs[0].device) for s in shapes]
     ws = torch.empty(ns.ns_grouped_workspace_bytes(shapes), dtype=torch.uint8, device=Gs[0].device)
-    call = lambda: ns.ns_orthogonalize_grouped(Gs, coeffs, clips, outs=outs, workspace=ws)
+    if route:
+        masks = synth.rht_masks(len(coeffs), seed=5)
+        opts = dict(clip_quantile=0.99, rht_masks=masks, adaptive46=True)
+        call = lambda: ns.ns_orthogonalize_grouped_ex(Gs, coeffs, outs=outs, workspace=ws, **opts)
+        single = lambda g, c: ns.ns_orthogonalize_ex(g, coeffs, **opts)
+    else:
+        call = lambda: ns.ns_orthogonalize_grouped(Gs, coeffs, clips, outs=outs, workspace=ws)
+        single = lambda g, c: ns.ns_orthogonalize(g, coeffs, c)
     call()
     want = [host(o).copy() for o in outs]
     for g, w, c in zip(Gs, want, clips):                  # each equals its single call
-        assert np.array_equal(host(ns.ns_orthogonalize(g, coeffs, c)), w)
+        assert np.array_equal(host(single(g, c)), w)
     graph = _capture(call)
     for r in range(3):
         for o in outs:
